@@ -1,0 +1,218 @@
+"""fp64 CPU oracle for absorbed-MLA decode under decode context parallelism (DCP).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
+leg of the benchmark may import this module; the product library never does, and
+this module imports nothing from the product (it shares no kernels, helpers,
+tables or constants with it).  It is the plain definition written out in fp64
+with NumPy, slow on purpose and meant to be checked by eye against the pages:
+
+* "[Attention] add DCP support for FLASH_ATTN_MLA backend" (vLLM PR #24453),
+  review thread: the "Normal" causal mask with the query rows as the last tokens,
+  and the "DCP Rank 0 / DCP Rank 1" interleaved masks (keys {0,2,4} and {1,3,5});
+  the dcp=2, query_len=2 "AB" example where a row can have seqlen_k = 0.
+* "vllm.v1.attention.backends.mla.flashattn_mla" API page, ``_forward_decode``:
+  the absorbed form (q_pe against k_pe, q_nope against the latent c_kv, the
+  latent as the value), one softmax scale, causal, the LSE returned per
+  (token, head) in [B, H] order.
+* "[Attention] DCP sparse MLA output-merge optimizations" (vLLM PR #48196):
+  the exact LSE-weighted merge of the per-rank partials, per-row valid counts,
+  and the W_UV projection that commutes with the merge.
+
+Readings where the pages are silent (all listed in the design notes):
+``seq_lens`` holds the global total S_b including the request's query tokens;
+query row i of a request with Q_b rows sits at global position S_b - Q_b + i;
+the LSE is the natural log of the sum of exp(scaled score); an empty row has
+output 0 and LSE -inf; a shard's partial counts as valid iff its per-row count
+(or, without counts, its LSE) is positive (finite).
+
+Parity of every function here is pinned by the CPU tests (worked masks printed on
+the PR #24453 page, brute force, torch's SDPA, closed forms and the merge
+identities); nothing in this file is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+D_LATENT = 512
+D_ROPE = 64
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 storage bits (uint16) to float64."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Where the query rows sit, and which keys each row sees on each shard
+# ---------------------------------------------------------------------------
+
+def query_rows(seq_lens, query_start_loc):
+    """For every query token t: (request b, row i within b, global position p).
+
+    PR #24453 thread, "Normal" mask: the Q query rows of a request are its last Q
+    tokens, so row i of request b is at global position S_b - Q_b + i and sees
+    keys 0..p (bottom-right causal alignment).
+    """
+    seq_lens = [int(s) for s in seq_lens]
+    qsl = [int(x) for x in query_start_loc]
+    rows = []
+    for b in range(len(seq_lens)):
+        q_b = qsl[b + 1] - qsl[b]
+        for i in range(q_b):
+            rows.append((b, i, seq_lens[b] - q_b + i))
+    return rows
+
+
+def visible_keys(p: int, W: int, r: int) -> list[int]:
+    """Global positions a query row at position p attends to on shard r.
+
+    PR #24453 thread, "DCP Rank 0/1" masks: shard r holds the keys with
+    position mod W == r, and the causal rule keeps those at or before p.
+    Listed in shard-local order (position p' is local index p' div W).
+    """
+    return [k for k in range(p + 1) if k % W == r]
+
+
+def visible_count(p: int, W: int, r: int) -> int:
+    """Closed form of len(visible_keys(p, W, r)): the per-row, per-shard seqlen_k.
+
+    The keys k <= p with k = r (mod W) are r, r+W, ..., so their number is
+    ceil((p + 1 - r) / W) when p >= r and 0 otherwise.
+    """
+    n = p + 1 - r
+    return 0 if n <= 0 else (n + W - 1) // W
+
+
+def shard_length(S: int, W: int, r: int) -> int:
+    """Tokens of a request with S global tokens stored on shard r (= visible_count(S-1))."""
+    return visible_count(S - 1, W, r) if S > 0 else 0
+
+
+def dense_mask(S: int, Q: int, W: int = 1, r: int = 0) -> np.ndarray:
+    """Boolean [Q, S] mask over GLOBAL key positions, built entry by entry.
+
+    mask[i, k] is True iff key k is causally visible to query row i (k <= S-Q+i)
+    and key k is stored on shard r (k mod W == r).  With W = 1 this is the
+    "Normal" matrix of the PR #24453 thread; its columns restricted to one shard's
+    keys give the "DCP Rank r" matrices.
+    """
+    m = np.zeros((Q, S), dtype=bool)
+    for i in range(Q):
+        for k in range(S):
+            m[i, k] = (k <= S - Q + i) and (k % W == r)
+    return m
+
+
+def row_counts(seq_lens, query_start_loc, W: int, r: int) -> np.ndarray:
+    """Per query token t, its seqlen_k on shard r (int32 [T])."""
+    return np.array([visible_count(p, W, r) for (_, _, p) in query_rows(seq_lens, query_start_loc)],
+                    dtype=np.int32)
+
+
+def shard_lengths(seq_lens, W: int, r: int) -> np.ndarray:
+    """Per request, the number of its tokens stored on shard r (int32 [B])."""
+    return np.array([shard_length(int(s), W, r) for s in seq_lens], dtype=np.int32)
+
+
+# ---------------------------------------------------------------------------
+# Attention of one query token over a set of keys
+# ---------------------------------------------------------------------------
+
+def attend(q_nope: np.ndarray, q_pe: np.ndarray, keys: np.ndarray, scale: float):
+    """Absorbed-MLA attention of one query token (all heads) over the given key rows.
+
+    q_nope [H,512], q_pe [H,64], keys [n,576] (c_kv | k_pe), all float64.
+    Score of head h and key j: scale * (q_nope[h].c_kv[j] + q_pe[h].k_pe[j])
+    (flashattn_mla page: q=q_pe against k=k_pe, q_v=q_nope against v=c_kv, one
+    softmax_scale).  The value is c_kv itself.  Returns out [H,512] (softmax-
+    weighted sum of c_kv) and lse [H] = ln sum_j exp(score).  With no keys the row
+    is empty: out = 0, lse = -inf.
+    """
+    H = q_nope.shape[0]
+    n = keys.shape[0]
+    if n == 0:
+        return np.zeros((H, D_LATENT)), np.full(H, -np.inf)
+    c = keys[:, :D_LATENT]
+    k_pe = keys[:, D_LATENT:]
+    s = scale * (q_nope @ c.T + q_pe @ k_pe.T)          # [H, n]
+    m = s.max(axis=1, keepdims=True)
+    lse = m[:, 0] + np.log(np.exp(s - m).sum(axis=1))
+    p = np.exp(s - lse[:, None])
+    return p @ c, lse
+
+
+def decode_partial(seq_lens, query_start_loc, q_nope_bits, q_pe_bits, global_kv, scale: float,
+                   W: int = 1, r: int = 0, tokens=None):
+    """Shard r's partial attention for every query token (or the listed ones).
+
+    ``global_kv(b)`` returns request b's global token rows [S_b, 576] as bf16 bits.
+    Each row attends to visible_keys(p, W, r).  Returns out [n,H,512], lse [n,H]
+    (float64) for the selected tokens in the order given.
+    """
+    rows = query_rows(seq_lens, query_start_loc)
+    sel = range(len(rows)) if tokens is None else [int(t) for t in tokens]
+    H = q_nope_bits.shape[1]
+    outs = np.zeros((len(sel), H, D_LATENT))
+    lses = np.zeros((len(sel), H))
+    cache = {}
+    for n_out, t in enumerate(sel):
+        b, _, p = rows[t]
+        if b not in cache:
+            cache.clear()
+            cache[b] = bf16_bits_to_f64(global_kv(b))
+        keys = cache[b][visible_keys(p, W, r)]
+        outs[n_out], lses[n_out] = attend(bf16_bits_to_f64(q_nope_bits[t]),
+                                          bf16_bits_to_f64(q_pe_bits[t]), keys, scale)
+    return outs, lses
+
+
+# ---------------------------------------------------------------------------
+# Merge of per-shard partials, and the W_UV up-projection
+# ---------------------------------------------------------------------------
+
+def lse_merge(outs: np.ndarray, lses: np.ndarray, valid=None):
+    """Exact LSE-weighted merge over shards (PR #48196, _dcp_lse_merge).
+
+    outs [W,T,H,D], lses [W,T,H]; valid [W,T] per-row counts (a shard is used for
+    row t iff valid[w,t] > 0) or None (used iff its lse is finite).  Invalid
+    partials are never read, whatever they hold.  Merged LSE = ln sum_w exp(lse_w)
+    over the used shards; merged out = sum_w exp(lse_w - LSE) * out_w.  A row with
+    no used shard gives out 0 and LSE -inf.
+    """
+    outs = np.asarray(outs, dtype=np.float64)
+    lses = np.asarray(lses, dtype=np.float64)
+    W, T, H = lses.shape
+    out = np.zeros(outs.shape[1:])
+    lse = np.full((T, H), -np.inf)
+    for t in range(T):
+        for h in range(H):
+            used = [w for w in range(W)
+                    if (valid[w][t] > 0 if valid is not None else np.isfinite(lses[w, t, h]))]
+            if not used:
+                continue
+            m = max(lses[w, t, h] for w in used)
+            total = m + math.log(sum(math.exp(lses[w, t, h] - m) for w in used))
+            lse[t, h] = total
+            out[t, h] = sum(math.exp(lses[w, t, h] - total) * outs[w, t, h] for w in used)
+    return out, lse
+
+
+def v_up_proj(o: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
+    """Per-head up-projection y[t,h,:] = o[t,h,:] @ W_UV[h] (512 -> 128)."""
+    return np.einsum("thk,hkn->thn", o, w_uv)
+
+
+def merge_then_project(outs, lses, valid, w_uv):
+    """Merge the latent partials, then project by W_UV."""
+    o, lse = lse_merge(outs, lses, valid)
+    return v_up_proj(o, w_uv), lse
+
+
+def project_then_merge(outs, lses, valid, w_uv):
+    """Project every shard's partial by W_UV, then merge (PR #48196's order)."""
+    outs = np.asarray(outs, dtype=np.float64)
+    proj = np.stack([v_up_proj(outs[w], w_uv) for w in range(outs.shape[0])])
+    return lse_merge(proj, lses, valid)

@@ -1,0 +1,263 @@
+"""Checks that pin the fp64 oracle to facts outside itself.
+
+Each check returns True when the oracle passes it.  The oracle tests assert that
+every check passes; the mutation tests plant a plausible mistake in the oracle and
+assert that at least one check then fails, which shows the checks can see it.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import torch
+
+from oracle import mla_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _bits(x):
+    """float64 -> bf16 bits by truncating float32 (inputs here are chosen bf16-exact)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32)
+    return (u >> 16).astype(np.uint16)
+
+
+def load_worked_masks():
+    out = []
+    with open(os.path.join(GOLDEN, "pr24453_worked_masks.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            name, W, r, keys, rows = line.split()
+            out.append(dict(name=name, W=int(W), r=0 if r == "-" else int(r),
+                            keys=[int(k) for k in keys.split(",")],
+                            rows=[[c == "1" for c in row] for row in rows.split(",")]))
+    return out
+
+
+def check_worked_masks() -> bool:
+    """The oracle's masks and counts reproduce the page's 6-key, 4-row, dcp=2 matrices."""
+    S, Q = 6, 4
+    for m in load_worked_masks():
+        W, r = m["W"], m["r"]
+        dense = O.dense_mask(S, Q, W, r)
+        # the page lists only the keys this rank holds, in column order
+        if [k for k in range(S) if k % W == r] != m["keys"]:
+            return False
+        sub = dense[:, m["keys"]]
+        want = np.array(m["rows"])
+        if sub.shape != want.shape or not np.array_equal(sub, want):
+            return False
+        # closed-form counts and explicit visible sets agree with the matrix rows
+        rows = O.query_rows([S], [0, Q])
+        for i, (_, _, p) in enumerate(rows):
+            if O.visible_count(p, W, r) != int(want[i].sum()):
+                return False
+            if O.visible_keys(p, W, r) != [k for k, on in zip(m["keys"], want[i]) if on]:
+                return False
+        if list(O.row_counts([S], [0, Q], W, r)) != [int(x) for x in want.sum(axis=1)]:
+            return False
+    return True
+
+
+def check_ab_example() -> bool:
+    """dcp=2, query_len=2 over a 2-token request: rank 0 sees {1,1}, rank 1 sees {0,1}."""
+    with open(os.path.join(GOLDEN, "pr24453_ab_example.txt")) as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            r, counts = line.split()
+            want = [int(c) for c in counts.split(",")]
+            if list(O.row_counts([2], [0, 2], 2, int(r))) != want:
+                return False
+    return True
+
+
+def check_counts_bruteforce(max_w=8, max_s=80, max_q=9) -> bool:
+    """Closed-form counts == explicit enumeration, and the shards partition the keys."""
+    for W in range(1, max_w + 1):
+        for S in range(1, max_s):
+            for Q in range(1, min(max_q, S) + 1):
+                rows = O.query_rows([S], [0, Q])
+                tot = np.zeros(Q, dtype=np.int64)
+                for r in range(W):
+                    dm = O.dense_mask(S, Q, W, r) if (S < 24 and Q < 5) else None
+                    for i, (_, _, p) in enumerate(rows):
+                        n = O.visible_count(p, W, r)
+                        if n != sum(1 for k in range(p + 1) if k % W == r):
+                            return False
+                        if dm is not None and n != int(dm[i].sum()):
+                            return False
+                        tot[i] += n
+                    if O.shard_length(S, W, r) != len(range(r, S, W)):
+                        return False
+                if list(tot) != [p + 1 for (_, _, p) in rows]:
+                    return False
+    return True
+
+
+def _rand_case(rng, S, Q, H, zero_q=False):
+    kv = rng.standard_normal((S, 576)).astype(np.float32)
+    qn = rng.standard_normal((Q, H, 512)).astype(np.float32)
+    qp = rng.standard_normal((Q, H, 64)).astype(np.float32)
+    if zero_q:
+        qn[:] = 0
+        qp[:] = 0
+    return _bits(kv), _bits(qn), _bits(qp)
+
+
+def check_against_sdpa(seed=0) -> bool:
+    """Unsharded and sharded oracle outputs == torch SDPA (fp64, CPU, explicit mask)."""
+    rng = np.random.default_rng(seed)
+    scale = 1 / math.sqrt(192)
+    for (S, Q, H, W) in [(6, 4, 3, 1), (9, 3, 2, 2), (13, 5, 4, 3), (31, 1, 2, 1), (40, 7, 2, 4)]:
+        kvb, qnb, qpb = _rand_case(rng, S, Q, H)
+        kv = O.bf16_bits_to_f64(kvb)
+        q = np.concatenate([O.bf16_bits_to_f64(qnb), O.bf16_bits_to_f64(qpb)], axis=-1)  # [Q,H,576]
+        for r in range(W):
+            out, lse = O.decode_partial([S], [0, Q], qnb, qpb, lambda b: kvb, scale, W, r)
+            mask = torch.from_numpy(O.dense_mask(S, Q, W, r))  # [Q, S]
+            nonempty = mask.any(dim=1).numpy()
+            qt = torch.from_numpy(q).permute(1, 0, 2).unsqueeze(0)            # [1,H,Q,576]
+            kt = torch.from_numpy(kv).expand(1, H, S, 576)
+            vt = torch.from_numpy(kv[:, :512]).expand(1, H, S, 512)
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qt, kt, vt, attn_mask=mask.expand(1, H, Q, S), scale=scale)
+            ref = ref[0].permute(1, 0, 2).numpy()                              # [Q,H,512]
+            if not np.allclose(out[nonempty], ref[nonempty], rtol=1e-12, atol=1e-12):
+                return False
+            if np.any(out[~nonempty] != 0) or np.any(lse[~nonempty] != -np.inf):
+                return False
+            # LSE through SDPA: with one-hot values SDPA returns the softmax weights
+            # w[j]; then lse = score[j] - ln w[j] for any visible key j.
+            eye = torch.eye(S, dtype=torch.float64).expand(1, H, S, S)
+            wts = torch.nn.functional.scaled_dot_product_attention(
+                qt, kt, eye, attn_mask=mask.expand(1, H, Q, S), scale=scale)[0].numpy()  # [H,Q,S]
+            scores = scale * np.einsum("qhd,sd->hqs", q, kv)
+            for i in np.nonzero(nonempty)[0]:
+                j = int(np.nonzero(mask[i].numpy())[0][-1])
+                want = scores[:, i, j] - np.log(wts[:, i, j])
+                if not np.allclose(lse[i], want, rtol=0, atol=1e-10):
+                    return False
+    return True
+
+
+def check_closed_forms(seed=1) -> bool:
+    """q = 0 gives lse = ln(count) and the mean of the visible latents; one key gives c_0."""
+    rng = np.random.default_rng(seed)
+    scale = 1 / math.sqrt(192)
+    S, Q, H, W = 23, 4, 2, 3
+    kvb, qnb, qpb = _rand_case(rng, S, Q, H, zero_q=True)
+    kv = O.bf16_bits_to_f64(kvb)
+    for r in range(W):
+        out, lse = O.decode_partial([S], [0, Q], qnb, qpb, lambda b: kvb, scale, W, r)
+        for i in range(Q):
+            p = S - Q + i
+            keys = [k for k in range(p + 1) if k % W == r]
+            if not np.allclose(lse[i], math.log(len(keys)), atol=1e-14):
+                return False
+            if not np.allclose(out[i], kv[keys, :512].mean(axis=0)[None], atol=1e-13):
+                return False
+    # one visible key: out is that key's latent exactly, lse its scaled score
+    kvb, qnb, qpb = _rand_case(rng, 1, 1, H)
+    out, lse = O.decode_partial([1], [0, 1], qnb, qpb, lambda b: kvb, scale, 1, 0)
+    kv = O.bf16_bits_to_f64(kvb)
+    s0 = scale * (O.bf16_bits_to_f64(qnb[0]) @ kv[0, :512] + O.bf16_bits_to_f64(qpb[0]) @ kv[0, 512:])
+    return np.array_equal(out[0], np.repeat(kv[:1, :512], H, axis=0)) and np.allclose(lse[0], s0, atol=1e-13)
+
+
+def _sharded_case(rng, seq_lens, q_lens, H, W):
+    qsl = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    T = int(qsl[-1])
+    kvs = [_bits(rng.standard_normal((s, 576)).astype(np.float32)) for s in seq_lens]
+    qnb = _bits(rng.standard_normal((T, H, 512)).astype(np.float32))
+    qpb = _bits(rng.standard_normal((T, H, 64)).astype(np.float32))
+    return qsl, kvs, qnb, qpb
+
+
+def check_merge_equals_unsharded(seed=2) -> bool:
+    """merge over the W shards' partials == attention over all keys (fp64 exact algebra)."""
+    rng = np.random.default_rng(seed)
+    scale = 1 / math.sqrt(192)
+    for seq_lens, q_lens, H, W in [([6, 9], [4, 3], 2, 2), ([2, 3, 17], [2, 3, 5], 2, 4),
+                                   ([12, 30], [1, 6], 3, 8), ([5], [5], 1, 3)]:
+        qsl, kvs, qnb, qpb = _sharded_case(rng, seq_lens, q_lens, H, W)
+        full, full_lse = O.decode_partial(seq_lens, qsl, qnb, qpb, lambda b: kvs[b], scale, 1, 0)
+        parts = [O.decode_partial(seq_lens, qsl, qnb, qpb, lambda b: kvs[b], scale, W, r)
+                 for r in range(W)]
+        outs = np.stack([p[0] for p in parts])
+        lses = np.stack([p[1] for p in parts])
+        valid = np.stack([O.row_counts(seq_lens, qsl, W, r) for r in range(W)])
+        for v in (valid, None):
+            m, ml = O.lse_merge(outs, lses, v)
+            if not (np.allclose(m, full, atol=1e-12) and np.allclose(ml, full_lse, atol=1e-12)):
+                return False
+    return True
+
+
+def check_merge_identities(seed=3) -> bool:
+    """Single valid shard is the identity; W copies add ln W; shard order is irrelevant;
+    invalid partials are ignored whatever they hold."""
+    rng = np.random.default_rng(seed)
+    W, T, H, D = 4, 3, 2, 8
+    outs = rng.standard_normal((W, T, H, D))
+    lses = rng.standard_normal((W, T, H)) * 3
+    valid = np.ones((W, T), dtype=np.int32)
+    m1, l1 = O.lse_merge(outs[:1], lses[:1], valid[:1])
+    if not (np.allclose(m1, outs[0], atol=1e-15) and np.allclose(l1, lses[0], atol=1e-15)):
+        return False
+    same = np.repeat(outs[:1], W, axis=0)
+    same_l = np.repeat(lses[:1], W, axis=0)
+    m2, l2 = O.lse_merge(same, same_l, valid)
+    if not (np.allclose(m2, outs[0], atol=1e-13) and np.allclose(l2, lses[0] + math.log(W), atol=1e-13)):
+        return False
+    perm = rng.permutation(W)
+    m3, l3 = O.lse_merge(outs, lses, valid)
+    m4, l4 = O.lse_merge(outs[perm], lses[perm], valid[perm])
+    if not (np.allclose(m3, m4, atol=1e-13) and np.allclose(l3, l4, atol=1e-13)):
+        return False
+    # poison shard 1 of row 0 and mark it invalid: result equals merging the rest
+    po, pl = outs.copy(), lses.copy()
+    po[1, 0] = np.nan
+    pl[1, 0] = np.nan
+    v = valid.copy()
+    v[1, 0] = 0
+    m5, l5 = O.lse_merge(po, pl, v)
+    keep = [0, 2, 3]
+    m6, l6 = O.lse_merge(outs[keep][:, :1], lses[keep][:, :1], valid[keep][:, :1])
+    if not (np.allclose(m5[0], m6[0], atol=1e-13) and np.allclose(l5[0], l6[0], atol=1e-13)):
+        return False
+    # a row with no valid shard: out 0, lse -inf
+    v0 = valid.copy()
+    v0[:, 2] = 0
+    m7, l7 = O.lse_merge(po, pl, v0)
+    if np.any(m7[2] != 0) or np.any(l7[2] != -np.inf):
+        return False
+    # hand-computed 2-shard case: lse_w = ln 1, ln 3 -> weights 1/4, 3/4, LSE = ln 4
+    o2 = np.array([[[[1.0, 0.0]]], [[[0.0, 1.0]]]])
+    l2w = np.log(np.array([[[1.0]], [[3.0]]]))
+    m8, l8 = O.lse_merge(o2, l2w, None)
+    return np.allclose(m8[0, 0], [0.25, 0.75], atol=1e-15) and abs(l8[0, 0] - math.log(4)) < 1e-15
+
+
+def check_wuv_commutes(seed=4) -> bool:
+    """merge-then-project == project-then-merge, and the projection is o @ W_UV[h]."""
+    rng = np.random.default_rng(seed)
+    W, T, H = 3, 4, 2
+    outs = rng.standard_normal((W, T, H, 512))
+    lses = rng.standard_normal((W, T, H))
+    valid = (rng.random((W, T)) > 0.3).astype(np.int32)
+    valid[0] = 1
+    w_uv = 0.02 * rng.standard_normal((H, 512, 128))
+    a, la = O.merge_then_project(outs, lses, valid, w_uv)
+    b, lb = O.project_then_merge(outs, lses, valid, w_uv)
+    if not (np.allclose(a, b, atol=1e-12) and np.array_equal(la, lb)):
+        return False
+    y = O.v_up_proj(outs[0], w_uv)
+    return np.allclose(y[1, 1], outs[0, 1, 1] @ w_uv[1], atol=1e-13)
+
+
+ALL_CHECKS = [check_worked_masks, check_ab_example, check_counts_bruteforce, check_against_sdpa,
+              check_closed_forms, check_merge_equals_unsharded, check_merge_identities,
+              check_wuv_commutes]

@@ -1,0 +1,106 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check the pins see them.
+
+Each mutant replaces one oracle function with a wrong variant; at least one pin
+must then fail.  This guards the pins themselves against being too weak.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import mla_oracle as O
+from tests import _pins
+
+
+def _count_drop_plus_one(p, W, r):          # forgets that key p itself is visible
+    n = p - r
+    return 0 if n <= 0 else (n + W - 1) // W
+
+
+def _count_floor(p, W, r):                  # floor instead of ceil
+    n = p + 1 - r
+    return 0 if n <= 0 else n // W
+
+
+def _rows_top_left(seq_lens, qsl):          # query rows at the first Q positions
+    rows = []
+    for b in range(len(seq_lens)):
+        for i in range(int(qsl[b + 1]) - int(qsl[b])):
+            rows.append((b, i, i))
+    return rows
+
+
+def _keys_wrong_residue(p, W, r):           # shard r holds p mod W == W-1-r
+    return [k for k in range(p + 1) if k % W == (W - 1 - r)]
+
+
+_real_attend = O.attend
+
+
+def _attend_no_pe(q_nope, q_pe, keys, scale):    # drops the rope term
+    return _real_attend(q_nope, np.zeros_like(q_pe), keys, scale)
+
+
+def _attend_double_scale(q_nope, q_pe, keys, scale):
+    return _real_attend(q_nope, q_pe, keys, 2 * scale)
+
+
+def _attend_log2(q_nope, q_pe, keys, scale):     # LSE in base 2
+    out, lse = _real_attend(q_nope, q_pe, keys, scale)
+    return out, lse / math.log(2)
+
+
+def _merge_wrong_sign(outs, lses, valid=None):
+    outs = np.asarray(outs, dtype=np.float64)
+    lses = np.asarray(lses, dtype=np.float64)
+    W, T, H = lses.shape
+    out = np.zeros(outs.shape[1:])
+    lse = np.full((T, H), -np.inf)
+    for t in range(T):
+        for h in range(H):
+            used = [w for w in range(W) if (valid[w][t] > 0 if valid is not None else np.isfinite(lses[w, t, h]))]
+            if not used:
+                continue
+            m = max(lses[w, t, h] for w in used)
+            total = m + math.log(sum(math.exp(lses[w, t, h] - m) for w in used))
+            lse[t, h] = total
+            out[t, h] = sum(math.exp(total - lses[w, t, h]) * outs[w, t, h] for w in used) / W
+    return out, lse
+
+
+def _vup_transposed(o, w_uv):               # uses W_UV[h]^T-like indexing
+    return np.einsum("thk,hkn->thn", o, w_uv[:, :, ::-1])
+
+
+MUTANTS = [
+    ("visible_count", _count_drop_plus_one),
+    ("visible_count", _count_floor),
+    ("query_rows", _rows_top_left),
+    ("visible_keys", _keys_wrong_residue),
+    ("attend", _attend_no_pe),
+    ("attend", _attend_double_scale),
+    ("attend", _attend_log2),
+    ("lse_merge", _merge_wrong_sign),
+]
+
+
+@pytest.mark.parametrize("name,fn", MUTANTS, ids=[f"{n}:{f.__name__}" for n, f in MUTANTS])
+def test_pins_catch_mutant(monkeypatch, name, fn):
+    monkeypatch.setattr(O, name, fn)
+    results = {c.__name__: _safe(c) for c in _pins.ALL_CHECKS
+               if c is not _pins.check_counts_bruteforce}
+    results["check_counts_bruteforce"] = _safe(lambda: _pins.check_counts_bruteforce(5, 30, 5))
+    assert not all(results.values()), f"no pin failed for mutant {name}:{fn.__name__}"
+
+
+def test_pins_catch_projection_mutant(monkeypatch):
+    # the projection only enters the commute check through v_up_proj's definition
+    monkeypatch.setattr(O, "v_up_proj", _vup_transposed)
+    assert not _pins.check_wuv_commutes()
+
+
+def _safe(check):
+    try:
+        return bool(check())
+    except Exception:
+        return False
