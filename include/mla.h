@@ -1,0 +1,179 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) absorbed-MLA decode library with decode
+ * context parallelism (DCP).
+ *
+ * The operations are the ones the vLLM pages describe:
+ *  - "vllm.v1.attention.backends.mla.flashattn_mla" API page, _forward_decode:
+ *    absorbed MLA decode over a paged latent cache (q_pe against k_pe, q_nope
+ *    against the latent c_kv, c_kv as the value, one softmax scale, causal),
+ *    returning the output and the per-(token, head) LSE in [tokens, heads] order.
+ *  - PR #24453 ("add DCP support for FLASH_ATTN_MLA backend"), review thread:
+ *    global token p is stored on DCP rank p mod W, and with more than one query
+ *    row per request each row gets its own per-rank seqlen_k (the interleaved
+ *    causal mask; a row may see no key on a rank).
+ *  - PR #48196 ("DCP sparse MLA output-merge optimizations"): the exact
+ *    LSE-weighted merge of per-rank partials with per-row valid counts, and the
+ *    W_UV up-projection, which commutes with the merge.
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or keeps a pointer after the call returns, and it
+ *    keeps no state between calls except a per-device "is this gfx950" flag.
+ *  - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream)
+ *    and the call returns without waiting.  No call reads device memory on the
+ *    host, so all calls can be captured in a HIP graph.
+ *  - bf16 tensors are passed as `const void*` holding IEEE bfloat16 bits.
+ *  - Errors are returned as mla_status codes; the library never aborts.  Host-
+ *    visible argument errors are detected before anything is enqueued.
+ *    Device-side preconditions (listed per call) are the caller's contract.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t mla_status;
+
+#define MLA_OK               0
+#define MLA_ERR_NULL        -1  /* a required pointer is NULL                      */
+#define MLA_ERR_SHAPE       -2  /* a size, stride or rank argument is out of range  */
+#define MLA_ERR_UNSUPPORTED -3  /* current device is not gfx950                     */
+#define MLA_ERR_WORKSPACE   -4  /* workspace too small for the requested splits      */
+#define MLA_ERR_HIP         -5  /* a HIP runtime call or kernel launch failed        */
+
+/* Fixed head dimensions of the absorbed form. */
+#define MLA_D_LATENT 512   /* kv_lora_rank: c_kv, q_nope and output width */
+#define MLA_D_ROPE    64   /* qk_rope_head_dim: k_pe and q_pe width       */
+#define MLA_D_ROW    576   /* one cache row: c_kv | k_pe                  */
+#define MLA_D_V      128   /* v_head_dim: width after W_UV                */
+#define MLA_MAX_HEADS 128
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* mla_status_string(mla_status status);
+
+/*
+ * mla_decode_partial -- one DCP rank's absorbed-MLA attention over its shard of
+ * the paged latent cache ("flashattn_mla" _forward_decode with the PR #24453
+ * interleaved mask).
+ *
+ * Requests b = 0..B-1 own the query tokens t in [query_start_loc[b],
+ * query_start_loc[b+1]); Q_b is their count and T = query_start_loc[B].
+ * seq_lens[b] = S_b is the request's GLOBAL token count, its own Q_b query
+ * tokens included; query row i of b sits at global position p = S_b - Q_b + i.
+ * On rank r of W the request's tokens p = r, r+W, ... are stored in local order
+ * j = p div W: local token j lives in physical block block_table[b*bt_stride +
+ * j / page_size], slot j % page_size.  Row p sees the local tokens
+ * j < ceil((p + 1 - r) / W) (0 if p < r) -- its per-rank seqlen_k.
+ *
+ * For every token t and head h, with the visible local keys j:
+ *   s_j  = scale * (q_nope[t,h,:] . c_kv_j + q_pe[t,h,:] . k_pe_j)
+ *   lse  = ln sum_j exp(s_j)                       (natural log, fp32)
+ *   out  = sum_j exp(s_j - lse) * c_kv_j           (bf16, round to nearest even)
+ * A row that sees no key on this rank gets out = 0 and lse = -inf.
+ *
+ * Layouts (all last dimensions contiguous):
+ *   q_nope   bf16 [T,H,512], element (t,h,d) at q_nope + t*qn_stride_t + h*qn_stride_h + d
+ *            (strides in elements)
+ *   q_pe     bf16 [T,H,64], strides qp_stride_t / qp_stride_h in elements; may
+ *            alias q_nope + 512 when q is one [T,H,576] tensor
+ *   kv_cache bf16 [num_blocks, page_size, 576]; block stride kv_block_stride
+ *            elements (>= page_size*576); row stride 576 elements
+ *   block_table int32 [B, bt_stride]; entries past a request's last block are
+ *            never read (may be -1)
+ *   seq_lens int32 [B]; query_start_loc int32 [B+1], query_start_loc[0] = 0,
+ *            nondecreasing
+ *   out      bf16 [T,H,512] contiguous;  lse fp32 [T,H] contiguous
+ *
+ * Host integers: max_query_len >= every Q_b and max_seq_len >= every S_b are
+ * upper bounds that size the launch grid (nothing is read back from the
+ * device).  num_splits caps how many workgroups split one row's keys
+ * ("num_splits" of the varlen kernel call on the flashattn_mla page):
+ * 0 = choose automatically, 1 = never split, k = at most k.  Splitting needs
+ * `workspace` of at least mla_decode_workspace_size(...) bytes (any alignment
+ * of 256 bytes); with workspace == NULL the call runs unsplit.
+ *
+ * Returns MLA_OK, or MLA_ERR_NULL / MLA_ERR_SHAPE (B<0, T<0, H outside
+ * [1,128], page_size<1, cp_world<1, cp_rank outside [0,cp_world), strides
+ * smaller than the data, scale not finite) / MLA_ERR_WORKSPACE /
+ * MLA_ERR_UNSUPPORTED / MLA_ERR_HIP.  B == 0 or T == 0 enqueues nothing and
+ * returns MLA_OK (the grid is sized from host ints and may be empty).
+ * Device-side contract: Q_b <= S_b <= max_seq_len, Q_b <= max_query_len,
+ * block ids valid for every stored local token.
+ */
+mla_status mla_decode_partial(
+    const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
+    const void* q_pe, int64_t qp_stride_t, int64_t qp_stride_h,
+    const void* kv_cache, int64_t kv_block_stride, int32_t page_size,
+    const int32_t* block_table, int32_t bt_stride,
+    const int32_t* seq_lens, const int32_t* query_start_loc,
+    int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
+    int32_t cp_world, int32_t cp_rank, float scale, int32_t num_splits,
+    void* out, float* lse,
+    void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Bytes of workspace mla_decode_partial needs for the same host arguments
+ * (0 when the plan does not split).  Pure host arithmetic, no device access.
+ * Returns (size_t)-1 for invalid arguments.
+ */
+size_t mla_decode_workspace_size(int32_t B, int32_t T, int32_t H, int32_t max_query_len,
+                                 int32_t max_seq_len, int32_t cp_world, int32_t num_splits);
+
+/*
+ * mla_lse_merge -- exact LSE-weighted merge of W per-rank partials
+ * (PR #48196, _dcp_lse_merge, with per-row valid counts).
+ *
+ *   outs  bf16 [W,T,H,512] contiguous (rank r's partial at outs + r*T*H*512)
+ *   lses  fp32 [W,T,H] contiguous (natural-log LSE, -inf for empty rows)
+ *   valid int32 [W,T] per-row key counts, or NULL.  Rank w takes part in row t
+ *         iff valid[w*T+t] > 0 (with NULL: iff its lse is > -inf).  Partials of
+ *         ranks that do not take part are never read, whatever they hold.
+ *   out   bf16 [T,H,512]:  out = sum_w exp(lse_w - LSE) * outs_w
+ *   out_lse fp32 [T,H] or NULL:  LSE = ln sum_w exp(lse_w)
+ * A row with no participating rank gets out = 0 and LSE = -inf.
+ * Returns MLA_OK, MLA_ERR_NULL, MLA_ERR_SHAPE (W<1, T<0, H outside [1,128]),
+ * MLA_ERR_UNSUPPORTED or MLA_ERR_HIP; T == 0 is a no-op.
+ */
+mla_status mla_lse_merge(const void* outs, const float* lses, const int32_t* valid,
+                         int32_t W, int32_t T, int32_t H,
+                         void* out, float* out_lse, void* hip_stream);
+
+/*
+ * mla_merge_v_up_proj -- the merge fused with the per-head W_UV up-projection
+ * (PR #48196, _dcp_merge_and_v_up_proj; exact because the merge is linear in
+ * the partials and the projection is linear).
+ *
+ *   outs, lses, valid, W, T, H   as in mla_lse_merge
+ *   W_UV  bf16 [H,512,128] contiguous:  y[t,h,:] = merged_out[t,h,:] @ W_UV[h]
+ *   out   bf16 [T,H,128] contiguous
+ *   out_lse fp32 [T,H] or NULL
+ * The merged latent row is rounded to bf16 before the projection (fp32
+ * accumulation).  Returns as mla_lse_merge.
+ */
+mla_status mla_merge_v_up_proj(const void* outs, const float* lses, const int32_t* valid,
+                               int32_t W, int32_t T, int32_t H, const void* W_UV,
+                               void* out, float* out_lse, void* hip_stream);
+
+/*
+ * mla_dcp_local_seqlens -- the per-row, per-rank seqlen_k of the interleaved
+ * mask (PR #24453 review thread), computed on the device by the same device
+ * function the decode kernel uses.  row_seqlen int32 [T] (row t's visible key
+ * count on rank cp_rank; usable directly as `valid[cp_rank]` of the merge) and
+ * shard_len int32 [B] (request b's tokens stored on the rank), either may be
+ * NULL.  Returns MLA_OK, MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED or
+ * MLA_ERR_HIP.
+ */
+mla_status mla_dcp_local_seqlens(const int32_t* seq_lens, const int32_t* query_start_loc,
+                                 int32_t B, int32_t T, int32_t cp_world, int32_t cp_rank,
+                                 int32_t* row_seqlen, int32_t* shard_len, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

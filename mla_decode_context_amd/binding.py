@@ -1,0 +1,218 @@
+"""Thin Python binding of libmla (argument marshalling only).
+
+Every function here takes torch tensors that already live on the GPU, checks
+dtype/shape/contiguity on the host, and forwards raw device pointers, strides
+and sizes to the C ABI declared in ``include/mla.h``.  No step of the
+computation happens here; there is no fallback path.  If the shared library has
+not been built, loading it raises immediately.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmla.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "mla.h")
+
+MLA_OK = 0
+D_LATENT, D_ROPE, D_ROW, D_V = 512, 64, 576, 128
+
+_lib = None
+
+_c_void_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+
+
+class MlaError(RuntimeError):
+    pass
+
+
+def load_library():
+    """Load libmla.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise MlaError(f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_status_string.argtypes = [_i32]
+    lib.mla_decode_partial.restype = _i32
+    lib.mla_decode_partial.argtypes = [
+        _c_void_p, _i64, _i64, _c_void_p, _i64, _i64, _c_void_p, _i64, _i32,
+        _c_void_p, _i32, _c_void_p, _c_void_p,
+        _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
+        _c_void_p, _c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p]
+    lib.mla_decode_workspace_size.restype = ctypes.c_size_t
+    lib.mla_decode_workspace_size.argtypes = [_i32] * 7
+    lib.mla_lse_merge.restype = _i32
+    lib.mla_lse_merge.argtypes = [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
+                                  _c_void_p, _c_void_p, _c_void_p]
+    lib.mla_merge_v_up_proj.restype = _i32
+    lib.mla_merge_v_up_proj.argtypes = [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
+                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p]
+    lib.mla_dcp_local_seqlens.restype = _i32
+    lib.mla_dcp_local_seqlens.argtypes = [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32,
+                                          _c_void_p, _c_void_p, _c_void_p]
+    _lib = lib
+    return lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/mla.h."""
+    text = open(HEADER).read()
+    return re.findall(r"^\s*(?:mla_status|size_t|const char\*)\s+(mla_\w+)\s*\(", text, re.M)
+
+
+def _check(status: int, what: str):
+    if status != MLA_OK:
+        msg = load_library().mla_status_string(status).decode()
+        raise MlaError(f"{what} failed: {msg} ({status})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, name, dims=None):
+    if t.dtype != dtype:
+        raise MlaError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise MlaError(f"{name}: must be a GPU tensor")
+    if dims is not None and t.dim() != dims:
+        raise MlaError(f"{name}: expected {dims} dims, got shape {tuple(t.shape)}")
+
+
+def workspace_size(B, T, H, max_query_len, max_seq_len, cp_world, num_splits=0) -> int:
+    n = load_library().mla_decode_workspace_size(B, T, H, max_query_len, max_seq_len, cp_world, num_splits)
+    if n == ctypes.c_size_t(-1).value:
+        raise MlaError("mla_decode_workspace_size: invalid arguments")
+    return int(n)
+
+
+def mla_decode_partial(q_nope, q_pe, kv_cache, block_table, seq_lens, query_start_loc,
+                       cp_world, cp_rank, scale, out, lse, *, max_query_len, max_seq_len,
+                       workspace=None, num_splits=0, stream=None):
+    """One DCP rank's partial attention; writes ``out`` [T,H,512] bf16 and ``lse`` [T,H] fp32."""
+    lib = load_library()
+    _need(q_nope, torch.bfloat16, "q_nope", 3)
+    _need(q_pe, torch.bfloat16, "q_pe", 3)
+    _need(kv_cache, torch.bfloat16, "kv_cache", 3)
+    _need(block_table, torch.int32, "block_table", 2)
+    _need(seq_lens, torch.int32, "seq_lens", 1)
+    _need(query_start_loc, torch.int32, "query_start_loc", 1)
+    _need(out, torch.bfloat16, "out", 3)
+    _need(lse, torch.float32, "lse", 2)
+    T, H, dn = q_nope.shape
+    if dn != D_LATENT or tuple(q_pe.shape) != (T, H, D_ROPE):
+        raise MlaError("q_nope/q_pe: expected [T,H,512] / [T,H,64]")
+    if T == 0:
+        # nothing to compute; the C call is a no-op but still validates the scalars
+        qn_st, qn_sh, qp_st, qp_sh = H * D_LATENT, D_LATENT, H * D_ROPE, D_ROPE
+    else:
+        if q_nope.stride(2) != 1 or q_pe.stride(2) != 1:
+            raise MlaError("q_nope/q_pe: the last dim must be contiguous")
+        qn_st, qn_sh, qp_st, qp_sh = q_nope.stride(0), q_nope.stride(1), q_pe.stride(0), q_pe.stride(1)
+    nblk, page, row = kv_cache.shape
+    if row != D_ROW or kv_cache.stride(2) != 1 or kv_cache.stride(1) != D_ROW:
+        raise MlaError("kv_cache: expected [num_blocks, page_size, 576] with contiguous rows")
+    B = seq_lens.shape[0]
+    if query_start_loc.shape[0] != B + 1 or block_table.shape[0] != B or block_table.stride(1) != 1:
+        raise MlaError("seq_lens/query_start_loc/block_table sizes disagree")
+    if tuple(out.shape) != (T, H, D_LATENT) or (T and not out.is_contiguous()):
+        raise MlaError("out: expected contiguous [T,H,512]")
+    if tuple(lse.shape) != (T, H) or (T and not lse.is_contiguous()):
+        raise MlaError("lse: expected contiguous [T,H]")
+    if not (seq_lens.is_contiguous() and query_start_loc.is_contiguous()):
+        raise MlaError("seq_lens/query_start_loc must be contiguous")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.mla_decode_partial(
+        _ptr(q_nope), qn_st, qn_sh,
+        _ptr(q_pe), qp_st, qp_sh,
+        _ptr(kv_cache), kv_cache.stride(0), page,
+        _ptr(block_table), block_table.stride(0),
+        _ptr(seq_lens), _ptr(query_start_loc),
+        B, T, H, int(max_query_len), int(max_seq_len), int(cp_world), int(cp_rank), float(scale),
+        int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "mla_decode_partial")
+
+
+def mla_lse_merge(outs, lses, valid, out, out_lse=None, stream=None):
+    """Merge W partials: outs [W,T,H,512] bf16, lses [W,T,H] fp32, valid [W,T] int32 or None."""
+    lib = load_library()
+    _need(outs, torch.bfloat16, "outs", 4)
+    _need(lses, torch.float32, "lses", 3)
+    W, T, H, d = outs.shape
+    if d != D_LATENT or tuple(lses.shape) != (W, T, H) or (T and not (outs.is_contiguous() and lses.is_contiguous())):
+        raise MlaError("outs/lses: expected contiguous [W,T,H,512] / [W,T,H]")
+    if valid is not None:
+        _need(valid, torch.int32, "valid", 2)
+        if tuple(valid.shape) != (W, T) or not valid.is_contiguous():
+            raise MlaError("valid: expected contiguous [W,T]")
+    _need(out, torch.bfloat16, "out", 3)
+    if tuple(out.shape) != (T, H, D_LATENT) or not out.is_contiguous():
+        raise MlaError("out: expected contiguous [T,H,512]")
+    if out_lse is not None:
+        _need(out_lse, torch.float32, "out_lse", 2)
+        if tuple(out_lse.shape) != (T, H) or not out_lse.is_contiguous():
+            raise MlaError("out_lse: expected contiguous [T,H]")
+    st = lib.mla_lse_merge(_ptr(outs), _ptr(lses), _ptr(valid), W, T, H, _ptr(out), _ptr(out_lse),
+                           _stream(stream))
+    _check(st, "mla_lse_merge")
+
+
+def mla_merge_v_up_proj(outs, lses, valid, W_UV, out, out_lse=None, stream=None):
+    """Merge W partials and project by W_UV [H,512,128]: out [T,H,128] bf16."""
+    lib = load_library()
+    _need(outs, torch.bfloat16, "outs", 4)
+    _need(lses, torch.float32, "lses", 3)
+    _need(W_UV, torch.bfloat16, "W_UV", 3)
+    W, T, H, d = outs.shape
+    if d != D_LATENT or tuple(lses.shape) != (W, T, H) or (T and not (outs.is_contiguous() and lses.is_contiguous())):
+        raise MlaError("outs/lses: expected contiguous [W,T,H,512] / [W,T,H]")
+    if tuple(W_UV.shape) != (H, D_LATENT, D_V) or not W_UV.is_contiguous():
+        raise MlaError("W_UV: expected contiguous [H,512,128]")
+    if valid is not None:
+        _need(valid, torch.int32, "valid", 2)
+        if tuple(valid.shape) != (W, T) or not valid.is_contiguous():
+            raise MlaError("valid: expected contiguous [W,T]")
+    _need(out, torch.bfloat16, "out", 3)
+    if tuple(out.shape) != (T, H, D_V) or not out.is_contiguous():
+        raise MlaError("out: expected contiguous [T,H,128]")
+    if out_lse is not None:
+        _need(out_lse, torch.float32, "out_lse", 2)
+        if tuple(out_lse.shape) != (T, H) or not out_lse.is_contiguous():
+            raise MlaError("out_lse: expected contiguous [T,H]")
+    st = lib.mla_merge_v_up_proj(_ptr(outs), _ptr(lses), _ptr(valid), W, T, H, _ptr(W_UV), _ptr(out),
+                                 _ptr(out_lse), _stream(stream))
+    _check(st, "mla_merge_v_up_proj")
+
+
+def mla_dcp_local_seqlens(seq_lens, query_start_loc, T, cp_world, cp_rank, row_seqlen=None,
+                          shard_len=None, stream=None):
+    """Per-row visible key counts [T] and per-request stored token counts [B] on rank cp_rank."""
+    lib = load_library()
+    _need(seq_lens, torch.int32, "seq_lens", 1)
+    _need(query_start_loc, torch.int32, "query_start_loc", 1)
+    B = seq_lens.shape[0]
+    if row_seqlen is not None:
+        _need(row_seqlen, torch.int32, "row_seqlen", 1)
+        if row_seqlen.shape[0] != T:
+            raise MlaError("row_seqlen: expected [T]")
+    if shard_len is not None:
+        _need(shard_len, torch.int32, "shard_len", 1)
+        if shard_len.shape[0] != B:
+            raise MlaError("shard_len: expected [B]")
+    st = lib.mla_dcp_local_seqlens(_ptr(seq_lens), _ptr(query_start_loc), B, int(T), int(cp_world),
+                                   int(cp_rank), _ptr(row_seqlen), _ptr(shard_len), _stream(stream))
+    _check(st, "mla_dcp_local_seqlens")

@@ -1,0 +1,207 @@
+// C ABI of libmla: argument validation, launch planning and kernel launches.
+// The call contracts are documented in include/mla.h.
+#include <math.h>
+#include <string.h>
+
+#include "mla.h"
+#include "mla_kernels.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_device_state[kMaxDevices];   // 0 unknown, 1 gfx950, -1 other
+
+mla_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_UNSUPPORTED;
+  int st = __atomic_load_n(&g_device_state[dev], __ATOMIC_ACQUIRE);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MLA_ERR_HIP;
+    st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    __atomic_store_n(&g_device_state[dev], st, __ATOMIC_RELEASE);
+  }
+  return st == 1 ? MLA_OK : MLA_ERR_UNSUPPORTED;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+constexpr int kStep = 32;          // keys per inner step of the decode kernel
+constexpr int kTargetGroups = 1024;  // busy workgroups wanted per launch (4 per CU)
+constexpr int kMinChunk = 256;     // auto splits never go below this many keys
+constexpr int kMaxGridY = 65535;
+
+// Launch plan: heads per workgroup and keys per split.  Depends only on host
+// integers so that the workspace size can be computed in advance.
+struct Plan {
+  int mtiles;       // 16-head tiles per workgroup (1 or 2)
+  int hblocks;      // workgroups per token along heads
+  int chunk;        // keys per split
+  int max_splits;   // grid extent along splits
+};
+
+Plan make_plan(int T, int H, int max_seq_len, int W, int num_splits, bool split_ok) {
+  Plan p;
+  const int ht = (H + 15) / 16;
+  p.mtiles = ht >= 2 ? 2 : 1;
+  p.hblocks = (int)ceil_div(ht, p.mtiles);
+  // A row's visible local keys never exceed ceil(max_seq_len / W).
+  const int64_t lmax = max_seq_len > 0 ? ceil_div(max_seq_len, W) : 0;
+  const int64_t lr = round_up(lmax > 0 ? lmax : 1, kStep);
+  int64_t chunk = lr;
+  if (split_ok && num_splits != 1 && lmax > 0) {
+    if (num_splits > 1) {
+      chunk = round_up(ceil_div(lmax, num_splits), kStep);
+    } else {
+      // Rows are on average about half as long as the bound; aim for
+      // kTargetGroups busy workgroups.
+      const int64_t base = (int64_t)T * p.hblocks;
+      const int64_t want = ceil_div(2 * kTargetGroups, base > 0 ? base : 1);
+      if (want > 1) chunk = round_up(ceil_div(lmax, want), kStep);
+      if (chunk < kMinChunk) chunk = kMinChunk;
+    }
+    if (chunk > lr) chunk = lr;
+    if (ceil_div(lr, chunk) > kMaxGridY) chunk = round_up(ceil_div(lr, kMaxGridY), kStep);
+  }
+  p.chunk = (int)chunk;
+  p.max_splits = (int)ceil_div(lr, chunk);
+  return p;
+}
+
+size_t workspace_bytes_for(const Plan& p, int T, int H) {
+  if (p.max_splits <= 1) return 0;
+  const size_t rows = (size_t)p.max_splits * T * H;
+  return rows * MLA_D_LATENT * sizeof(float) + rows * sizeof(float) + 256;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: a size, stride, rank or alignment is out of range";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: the current device is not gfx950";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace too small for the split plan";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP runtime call or kernel launch failed";
+    default: return "unknown mla_status";
+  }
+}
+
+size_t mla_decode_workspace_size(int32_t B, int32_t T, int32_t H, int32_t max_query_len,
+                                 int32_t max_seq_len, int32_t cp_world, int32_t num_splits) {
+  if (B < 0 || T < 0 || H < 1 || H > MLA_MAX_HEADS || max_query_len < 0 || max_seq_len < 0 ||
+      cp_world < 1 || num_splits < 0)
+    return (size_t)-1;
+  if (B == 0 || T == 0) return 0;
+  const Plan p = make_plan(T, H, max_seq_len, cp_world, num_splits, true);
+  return workspace_bytes_for(p, T, H);
+}
+
+mla_status mla_decode_partial(
+    const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
+    const void* q_pe, int64_t qp_stride_t, int64_t qp_stride_h,
+    const void* kv_cache, int64_t kv_block_stride, int32_t page_size,
+    const int32_t* block_table, int32_t bt_stride,
+    const int32_t* seq_lens, const int32_t* query_start_loc,
+    int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
+    int32_t cp_world, int32_t cp_rank, float scale, int32_t num_splits,
+    void* out, float* lse,
+    void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (B < 0 || T < 0 || H < 1 || H > MLA_MAX_HEADS || page_size < 1 || cp_world < 1 ||
+      cp_rank < 0 || cp_rank >= cp_world || max_query_len < 0 || max_seq_len < 0 ||
+      num_splits < 0 || !isfinite(scale))
+    return MLA_ERR_SHAPE;
+  if (B == 0 && T > 0) return MLA_ERR_SHAPE;   // tokens without requests
+  if (B == 0 || T == 0) return MLA_OK;
+  if (!q_nope || !q_pe || !kv_cache || !block_table || !seq_lens || !query_start_loc || !out || !lse)
+    return MLA_ERR_NULL;
+  // Vector loads need 16-byte rows of q_nope / cache and 8-byte rows of q_pe.
+  if (qn_stride_h < MLA_D_LATENT || qn_stride_t < (int64_t)H * qn_stride_h || qn_stride_h % 8 ||
+      qn_stride_t % 8 || !aligned(q_nope, 16))
+    return MLA_ERR_SHAPE;
+  if (qp_stride_h < MLA_D_ROPE || qp_stride_t < (int64_t)(H - 1) * qp_stride_h + MLA_D_ROPE ||
+      qp_stride_h % 4 || qp_stride_t % 4 || !aligned(q_pe, 8))
+    return MLA_ERR_SHAPE;
+  if (kv_block_stride < (int64_t)page_size * MLA_D_ROW || kv_block_stride % 8 || !aligned(kv_cache, 16))
+    return MLA_ERR_SHAPE;
+  if (bt_stride < 1 || !aligned(out, 16)) return MLA_ERR_SHAPE;
+  mla_status st = check_device();
+  if (st != MLA_OK) return st;
+
+  const Plan plan = make_plan(T, H, max_seq_len, cp_world, num_splits, workspace != nullptr);
+  const size_t need = workspace_bytes_for(plan, T, H);
+  if (need > 0 && workspace_bytes < need) return MLA_ERR_WORKSPACE;
+
+  mla::DecodeParams p;
+  p.q_nope = (const uint16_t*)q_nope; p.qn_st = qn_stride_t; p.qn_sh = qn_stride_h;
+  p.q_pe = (const uint16_t*)q_pe; p.qp_st = qp_stride_t; p.qp_sh = qp_stride_h;
+  p.kv = (const uint16_t*)kv_cache; p.kv_bs = kv_block_stride; p.P = page_size;
+  p.bt = block_table; p.bt_stride = bt_stride;
+  p.seq_lens = seq_lens; p.qsl = query_start_loc;
+  p.B = B; p.T = T; p.H = H; p.W = cp_world; p.r = cp_rank;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  p.chunk = plan.chunk; p.hblocks = plan.hblocks; p.max_splits = plan.max_splits;
+  p.out = (uint16_t*)out; p.lse = lse;
+  p.ws_o = nullptr; p.ws_lse = nullptr;
+  if (plan.max_splits > 1) {
+    char* base = (char*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+    const size_t rows = (size_t)plan.max_splits * T * H;
+    p.ws_o = (float*)base;
+    p.ws_lse = (float*)(base + rows * MLA_D_LATENT * sizeof(float));
+  }
+  hipError_t e = mla::launch_decode(p, plan.mtiles, plan.max_splits, (hipStream_t)hip_stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+static mla_status merge_common(const void* outs, const float* lses, const int32_t* valid, int32_t W,
+                               int32_t T, int32_t H, const void* W_UV, bool proj, void* out,
+                               float* out_lse, void* hip_stream) {
+  if (W < 1 || T < 0 || H < 1 || H > MLA_MAX_HEADS) return MLA_ERR_SHAPE;
+  if (T == 0) return MLA_OK;
+  if (!outs || !lses || !out || (proj && !W_UV)) return MLA_ERR_NULL;
+  if (!aligned(outs, 16) || !aligned(out, 16) || (proj && !aligned(W_UV, 16))) return MLA_ERR_SHAPE;
+  mla_status st = check_device();
+  if (st != MLA_OK) return st;
+  mla::MergeParams p;
+  p.outs = (const uint16_t*)outs; p.lses = lses; p.valid = valid;
+  p.W = W; p.T = T; p.H = H;
+  p.wuv = (const uint16_t*)W_UV; p.out = (uint16_t*)out; p.out_lse = out_lse;
+  hipError_t e = proj ? mla::launch_merge_v_up(p, (hipStream_t)hip_stream)
+                      : mla::launch_lse_merge(p, (hipStream_t)hip_stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_lse_merge(const void* outs, const float* lses, const int32_t* valid,
+                         int32_t W, int32_t T, int32_t H,
+                         void* out, float* out_lse, void* hip_stream) {
+  return merge_common(outs, lses, valid, W, T, H, nullptr, false, out, out_lse, hip_stream);
+}
+
+mla_status mla_merge_v_up_proj(const void* outs, const float* lses, const int32_t* valid,
+                               int32_t W, int32_t T, int32_t H, const void* W_UV,
+                               void* out, float* out_lse, void* hip_stream) {
+  return merge_common(outs, lses, valid, W, T, H, W_UV, true, out, out_lse, hip_stream);
+}
+
+mla_status mla_dcp_local_seqlens(const int32_t* seq_lens, const int32_t* query_start_loc,
+                                 int32_t B, int32_t T, int32_t cp_world, int32_t cp_rank,
+                                 int32_t* row_seqlen, int32_t* shard_len, void* hip_stream) {
+  if (B < 0 || T < 0 || cp_world < 1 || cp_rank < 0 || cp_rank >= cp_world) return MLA_ERR_SHAPE;
+  if (B == 0 && T > 0) return MLA_ERR_SHAPE;
+  if (B == 0 && T == 0) return MLA_OK;
+  if (!seq_lens || !query_start_loc) return MLA_ERR_NULL;
+  mla_status st = check_device();
+  if (st != MLA_OK) return st;
+  hipError_t e = mla::launch_local_seqlens(seq_lens, query_start_loc, B, T, cp_world, cp_rank,
+                                           row_seqlen, shard_len, (hipStream_t)hip_stream);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // extern "C"

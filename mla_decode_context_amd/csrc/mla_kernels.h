@@ -1,0 +1,45 @@
+// Kernel parameter blocks and host-side launchers (internal to libmla).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct DecodeParams {
+  const uint16_t* q_nope;  int64_t qn_st, qn_sh;   // element strides
+  const uint16_t* q_pe;    int64_t qp_st, qp_sh;
+  const uint16_t* kv;      int64_t kv_bs;          // block stride in elements
+  int32_t P;                                        // page size (tokens per block)
+  const int32_t* bt;       int32_t bt_stride;
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  int32_t B, T, H, W, r;
+  float scale_log2;        // softmax scale * log2(e): scores are kept in base 2
+  int32_t chunk;           // keys per split (multiple of the 32-key step)
+  int32_t hblocks;         // head blocks per query token
+  int32_t max_splits;      // grid extent along splits
+  uint16_t* out;           // bf16 [T,H,512]
+  float* lse;              // fp32 [T,H]
+  float* ws_o;             // fp32 [splits,T,H,512] split partials (normalised)
+  float* ws_lse;           // fp32 [splits,T,H]
+};
+
+struct MergeParams {
+  const uint16_t* outs;    // bf16 [W,T,H,512]
+  const float* lses;       // fp32 [W,T,H]
+  const int32_t* valid;    // int32 [W,T] or null
+  int32_t W, T, H;
+  const uint16_t* wuv;     // bf16 [H,512,128] (merge + projection only)
+  uint16_t* out;           // bf16 [T,H,512] or [T,H,128]
+  float* out_lse;          // fp32 [T,H] or null
+};
+
+// Heads handled by one decode workgroup: 16 * mtiles, mtiles in {1,2}.
+hipError_t launch_decode(const DecodeParams& p, int mtiles, int max_splits, hipStream_t stream);
+hipError_t launch_local_seqlens(const int32_t* seq_lens, const int32_t* qsl, int B, int T, int W,
+                                int r, int32_t* row_seqlen, int32_t* shard_len, hipStream_t stream);
+hipError_t launch_lse_merge(const MergeParams& p, hipStream_t stream);
+hipError_t launch_merge_v_up(const MergeParams& p, hipStream_t stream);
+
+}  // namespace mla

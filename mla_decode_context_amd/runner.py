@@ -1,0 +1,85 @@
+"""Drive one DCP decode step on one GPU through the C ABI.
+
+All W ranks' paged caches live on the same GPU as separate tensors.  One step
+is: every rank's partial attention (``mla_decode_partial`` with cp_rank = r),
+the per-row valid counts of every rank (``mla_dcp_local_seqlens``), then the
+merge -- ``mla_lse_merge``, or ``mla_merge_v_up_proj`` when W_UV is given.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as mla
+
+
+def _bf16(a: np.ndarray, device) -> torch.Tensor:
+    """uint16 bf16 bits (host) -> bf16 tensor on the device."""
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def _i32(a: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+
+class DeviceWorkload:
+    """Device copies of a ``workloads.Workload`` plus output buffers."""
+
+    def __init__(self, wl, device="cuda", num_splits: int = 0):
+        self.wl = wl
+        self.device = torch.device(device)
+        dev = self.device
+        self.B, self.T, self.H, self.W = wl.B, wl.T, wl.H, wl.W
+        self.scale = wl.scale
+        self.max_query_len = wl.max_query_len
+        self.max_seq_len = wl.max_seq_len
+        self.num_splits = num_splits
+        self.q_nope = _bf16(wl.q_nope, dev)
+        self.q_pe = _bf16(wl.q_pe, dev)
+        self.seq_lens = _i32(wl.seq_lens, dev)
+        self.qsl = _i32(wl.query_start_loc, dev)
+        self.caches = [_bf16(sh.cache, dev) for sh in wl.shards]
+        self.tables = [_i32(sh.block_table, dev) for sh in wl.shards]
+        self.w_uv = _bf16(wl.w_uv, dev) if wl.w_uv is not None else None
+        T, H, W = self.T, self.H, self.W
+        self.outs = torch.empty((W, T, H, 512), dtype=torch.bfloat16, device=dev)
+        self.lses = torch.empty((W, T, H), dtype=torch.float32, device=dev)
+        self.valid = torch.empty((W, T), dtype=torch.int32, device=dev)
+        self.out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+        self.out_proj = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev) if self.w_uv is not None else None
+        self.out_lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        self.alloc_workspace(num_splits)
+
+    def alloc_workspace(self, num_splits: int):
+        self.num_splits = num_splits
+        n = mla.workspace_size(self.B, self.T, self.H, self.max_query_len, self.max_seq_len, self.W, num_splits)
+        self.workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=self.device) if n else None
+
+    def partial(self, r: int, stream=None):
+        mla.mla_decode_partial(
+            self.q_nope, self.q_pe, self.caches[r], self.tables[r], self.seq_lens, self.qsl,
+            self.W, r, self.scale, self.outs[r], self.lses[r],
+            max_query_len=self.max_query_len, max_seq_len=self.max_seq_len,
+            workspace=self.workspace, num_splits=self.num_splits, stream=stream)
+
+    def valid_counts(self, stream=None):
+        for r in range(self.W):
+            mla.mla_dcp_local_seqlens(self.seq_lens, self.qsl, self.T, self.W, r,
+                                      row_seqlen=self.valid[r], stream=stream)
+
+    def merge(self, stream=None):
+        mla.mla_lse_merge(self.outs, self.lses, self.valid, self.out, self.out_lse, stream=stream)
+
+    def merge_v_up(self, stream=None):
+        mla.mla_merge_v_up_proj(self.outs, self.lses, self.valid, self.w_uv, self.out_proj, self.out_lse,
+                                stream=stream)
+
+    def step(self, stream=None):
+        """One pass of the whole path: all ranks' partials, valid counts, merge."""
+        for r in range(self.W):
+            self.partial(r, stream)
+        self.valid_counts(stream)
+        if self.w_uv is not None:
+            self.merge_v_up(stream)
+        else:
+            self.merge(stream)

@@ -1,0 +1,82 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments with status codes before touching a device.
+No call here enqueues GPU work."""
+import ctypes
+
+import pytest
+
+from mla_decode_context_amd import binding
+
+lib = binding.load_library()
+
+OK, NULL, SHAPE, UNSUP, WS, HIP = 0, -1, -2, -3, -4, -5
+P = ctypes.c_void_p(16 * 1024)          # a dummy, aligned non-null "device" address (never dereferenced)
+
+
+def test_exports_every_declared_symbol():
+    names = binding.header_functions()
+    assert set(names) == {"mla_status_string", "mla_decode_partial", "mla_decode_workspace_size",
+                          "mla_lse_merge", "mla_merge_v_up_proj", "mla_dcp_local_seqlens"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in (OK, NULL, SHAPE, UNSUP, WS, HIP):
+        s = lib.mla_status_string(code).decode()
+        assert s.startswith("MLA_")
+    assert "unknown" in lib.mla_status_string(7).decode()
+
+
+def _decode(**kw):
+    a = dict(q_nope=P, qn_t=16 * 512, qn_h=512, q_pe=P, qp_t=16 * 64, qp_h=64, kv=P, kv_bs=16 * 576, page=16,
+             bt=P, bt_stride=4, seq=P, qsl=P, B=2, T=4, H=16, mq=2, ms=100, W=2, r=0, scale=0.07,
+             splits=0, out=P, lse=P, ws=None, ws_bytes=0)
+    a.update(kw)
+    return lib.mla_decode_partial(a["q_nope"], a["qn_t"], a["qn_h"], a["q_pe"], a["qp_t"], a["qp_h"], a["kv"],
+                                  a["kv_bs"], a["page"], a["bt"], a["bt_stride"], a["seq"], a["qsl"], a["B"],
+                                  a["T"], a["H"], a["mq"], a["ms"], a["W"], a["r"], a["scale"], a["splits"],
+                                  a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=0), SHAPE), (dict(H=129), SHAPE), (dict(B=-1), SHAPE), (dict(T=-1), SHAPE),
+    (dict(W=0), SHAPE), (dict(r=2), SHAPE), (dict(r=-1), SHAPE), (dict(page=0), SHAPE),
+    (dict(scale=float("nan")), SHAPE), (dict(scale=float("inf")), SHAPE), (dict(splits=-1), SHAPE),
+    (dict(B=0, T=3), SHAPE),
+    (dict(q_nope=None), NULL), (dict(kv=None), NULL), (dict(bt=None), NULL), (dict(lse=None), NULL),
+    (dict(qn_h=500), SHAPE), (dict(qn_t=512), SHAPE), (dict(qp_h=60), SHAPE), (dict(kv_bs=575 * 16), SHAPE),
+    (dict(q_nope=ctypes.c_void_p(16 * 1024 + 2)), SHAPE), (dict(bt_stride=0), SHAPE),
+    (dict(T=0), OK), (dict(B=0, T=0), OK), (dict(T=0, q_nope=None), OK),
+])
+def test_decode_argument_checks(kw, code):
+    assert _decode(**kw) == code
+
+
+def test_workspace_size_host_logic():
+    ws = lib.mla_decode_workspace_size
+    bad = ctypes.c_size_t(-1).value
+    assert ws(2, 4, 0, 1, 100, 1, 0) == bad
+    assert ws(2, 4, 16, 1, 100, 0, 0) == bad
+    assert ws(0, 0, 16, 1, 100, 1, 0) == 0
+    assert ws(4, 4, 16, 1, 100, 1, 1) == 0                   # never split
+    # a long row split 4 ways needs 4 fp32 partial rows + LSE per (t, h)
+    n = ws(1, 1, 16, 1, 4096, 1, 4)
+    assert n >= 4 * 16 * (512 + 1) * 4
+    assert ws(64, 64, 16, 1, 8192, 1, 0) > 0                 # the batch-64 decode splits automatically
+    assert ws(64, 64, 16, 1, 8192, 1, 2) < ws(64, 64, 16, 1, 8192, 1, 16)
+
+
+def test_merge_argument_checks():
+    m = lib.mla_lse_merge
+    assert m(P, P, None, 0, 4, 16, P, None, None) == SHAPE
+    assert m(P, P, None, 2, 4, 0, P, None, None) == SHAPE
+    assert m(None, P, None, 2, 4, 16, P, None, None) == NULL
+    assert m(P, P, None, 2, 0, 16, P, None, None) == OK
+    v = lib.mla_merge_v_up_proj
+    assert v(P, P, None, 2, 4, 16, None, P, None, None) == NULL
+    assert v(P, P, None, 2, -1, 16, P, P, None, None) == SHAPE
+    s = lib.mla_dcp_local_seqlens
+    assert s(P, P, 2, 4, 2, 2, P, P, None) == SHAPE
+    assert s(None, P, 2, 4, 2, 1, P, P, None) == NULL
+    assert s(P, P, 0, 0, 2, 1, P, P, None) == OK
