@@ -1,0 +1,280 @@
+"""Benchmark of the absorbed-MLA DCP decode path on one MI355X.
+
+Default workload (the headline line): plain decode, batch 64, one query row per
+request, 16 heads, W = 1, contexts drawn uniformly from 1024..8192 tokens, page
+64 with permuted physical blocks.  One step = one pass of the whole path over
+that batch: the decode kernel (row seqlens, paged gather, scores, masked online
+softmax, PV, split-K with the in-kernel combine, finalise).  With W = 1 the
+merge is the identity and is not run.
+
+Other workloads (reported under "configs", not in the headline value): the DCP
+ones run every rank's partial, the valid counts and the merge (or the merge
+fused with W_UV) per step.
+
+Printed: one JSON line.  ``value`` is KV-cache GB/s of the whole step (bytes of
+cache rows the method must read once, divided by the step time) with inputs
+already resident in HBM; ``roofline`` is the dominant kernel's algorithmic
+bytes per launch over its average launch duration (HIP events around every
+launch inside the timed region); ``cpu_baseline`` times the fp64 oracle on the
+host for the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "MLA decode KV GB/s (% of HBM peak) + query-tokens/s; merge GB/s"
+
+
+def workload_bytes(wl, valid):
+    """Algorithmic bytes and flops of one step, per shard call.
+
+    valid [W,T] holds every row's visible key count on every rank (from the
+    library's own mla_dcp_local_seqlens).  Bytes: each stored cache row once
+    (1152 B), q once (H*1152 B per row), out + LSE once (H*1028 B per row).
+    Flops: 2176 per visible (key, head, row) -- 1152 for the scores, 1024 for PV.
+    """
+    per_shard = []
+    for r in range(wl.W):
+        kv_tokens = int(sum(sh for sh in wl.shards[r].token_counts))
+        flops = float(valid[r].astype(np.float64).sum()) * wl.H * 2176.0
+        kv = kv_tokens * 1152
+        q = wl.T * wl.H * 1152
+        out = wl.T * wl.H * 1028
+        per_shard.append(dict(kv=kv, q=q, out=out, flops=flops, total=kv + q + out))
+    return per_shard
+
+
+def merge_bytes(wl, valid, proj: bool):
+    """Bytes the merge must move: participating partials + LSEs read, result written."""
+    n_part = int((valid > 0).sum()) * wl.H      # participating (rank, t, h) rows
+    read = n_part * (1024 + 4)
+    write = wl.T * wl.H * ((256 if proj else 1024) + 4)
+    wuv = wl.H * 512 * 128 * 2 if proj else 0
+    flops = wl.T * wl.H * 2.0 * 512 * 128 if proj else 0.0
+    return read + write + wuv, flops
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "mla_decode_context_amd", "csrc"))):
+        with open(os.path.join(ROOT, "mla_decode_context_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM traffic measured with rocprofv3 counters for this kernel source, if any."""
+    path = os.path.join(ROOT, "profiles", f"decode_kernel_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_workload(name, steps, warmup, torch, wl=None, headline=False):
+    from mla_decode_context_amd import workloads as WL
+    from mla_decode_context_amd.runner import DeviceWorkload
+
+    if wl is None:
+        wl = WL.make_workload(name, threads=16)
+    dw = DeviceWorkload(wl)
+    dw.valid_counts()
+    per_shard = workload_bytes(wl, dw.valid.cpu().numpy())
+    proj = wl.w_uv is not None
+    merging = wl.W > 1
+
+    def step(evs=None):
+        for r in range(wl.W):
+            if evs is not None:
+                evs[r][0].record()
+            dw.partial(r)
+            if evs is not None:
+                evs[r][1].record()
+        if merging:
+            dw.valid_counts()
+            if evs is not None:
+                evs[wl.W][0].record()
+            dw.merge_v_up() if proj else dw.merge()
+            if evs is not None:
+                evs[wl.W][1].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev_sets = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(wl.W + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(ev_sets[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+    dec_ms = np.array([[ev_sets[k][r][0].elapsed_time(ev_sets[k][r][1]) for r in range(wl.W)]
+                       for k in range(steps)])                      # [steps, W]
+    res = dict(workload=name, T=wl.T, B=wl.B, H=wl.H, W=wl.W, ms_per_step=ms_step)
+    kv_total = sum(p["kv"] for p in per_shard)
+    res["kv_GBps"] = kv_total / (ms_step * 1e-3) / 1e9
+    res["query_tokens_per_s"] = wl.T / (ms_step * 1e-3)
+    dec_avg = dec_ms.mean(axis=0)                                   # per shard, ms
+    res["decode_ms_per_shard"] = [round(float(x), 4) for x in dec_avg]
+    alg_bytes = np.array([p["total"] for p in per_shard], dtype=np.float64)
+    alg_flops = np.array([p["flops"] for p in per_shard], dtype=np.float64)
+    res["decode_alg_GBps"] = float((alg_bytes / (dec_avg * 1e-3)).sum() / len(dec_avg) / 1e9)
+    res["decode_kv_GBps"] = float(sum(p["kv"] for p in per_shard) / (dec_avg.sum() * 1e-3) / 1e9)
+    res["decode_TFLOPs"] = float(alg_flops.sum() / (dec_avg.sum() * 1e-3) / 1e12)
+    res["decode_pct_bf16_peak"] = 100.0 * res["decode_TFLOPs"] / BF16_PEAK_TFLOPS
+    res["decode_pct_hbm_peak"] = 100.0 * res["decode_alg_GBps"] / HBM_PEAK_GBPS
+    # one-rank view: the slowest rank's partial plus the merge (excludes the exchange)
+    if merging:
+        mg_ms = np.array([ev_sets[k][wl.W][0].elapsed_time(ev_sets[k][wl.W][1]) for k in range(steps)]).mean()
+        valid = dw.valid.cpu().numpy()
+        mbytes, mflops = merge_bytes(wl, valid, proj)
+        res["merge_kind"] = "merge+W_UV" if proj else "lse_merge"
+        res["merge_ms"] = float(mg_ms)
+        res["merge_GBps"] = mbytes / (mg_ms * 1e-3) / 1e9
+        res["merge_pct_hbm_peak"] = 100.0 * res["merge_GBps"] / HBM_PEAK_GBPS
+        res["query_tokens_per_s_one_rank"] = wl.T / ((dec_avg.max() + mg_ms) * 1e-3)
+    if headline:
+        res["_alg_bytes_per_launch"] = float(alg_bytes.mean())
+        res["_decode_avg_ms"] = float(dec_avg.mean())
+        res["_cold_kv_GBps"] = cold_kv(dw, wl, per_shard, torch)
+    del dw
+    torch.cuda.empty_cache()
+    return res, wl
+
+
+def cold_kv(dw, wl, per_shard, torch, reps=5):
+    """KV GB/s with the 256 MB last-level cache flushed (1 GiB write) before each step."""
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dw.device)
+    times = []
+    for _ in range(reps):
+        flush.fill_(1.0)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for r in range(wl.W):
+            dw.partial(r)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    del flush
+    kv = sum(p["kv"] for p in per_shard)
+    return kv / (float(np.median(times)) * 1e-3) / 1e9
+
+
+def cpu_baseline(wl, budget_s=20.0):
+    """The fp64 oracle on the host for the same workload, request by request, until
+    the whole batch is done or the time budget is spent."""
+    from oracle import mla_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    qsl = wl.query_start_loc
+    done_tokens = 0
+    done_kv = 0
+    spent = 0.0
+    reqs = 0
+    for b in range(wl.B):
+        kv = wl.global_kv(b)          # regenerating the inputs is not timed
+        toks = list(range(int(qsl[b]), int(qsl[b + 1])))
+        t0 = time.perf_counter()
+        for r in range(wl.W):
+            O.decode_partial(wl.seq_lens, qsl, wl.q_nope, wl.q_pe, lambda _b: kv, wl.scale, wl.W, r, tokens=toks)
+        spent += time.perf_counter() - t0
+        done_tokens += len(toks)
+        done_kv += int(sum(len(range(r, int(wl.seq_lens[b]), wl.W)) for r in range(wl.W))) * 1152
+        reqs += 1
+        if spent >= budget_s:
+            break
+    return dict(value=done_kv / spent / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+                sample=f"oracle decode of {reqs} of {wl.B} requests ({done_tokens} query rows, all ranks) "
+                       f"in {spent:.1f} s; query-tokens/s {done_tokens / spent:.3g}",
+                query_tokens_per_s=done_tokens / spent)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="plain")
+    ap.add_argument("--configs", default="mtp_dcp4,long_dcp8,mixed_wuv",
+                    help="comma-separated secondary workloads ('' for none)")
+    ap.add_argument("--config-steps", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (all DCP ranks are simulated on it); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from mla_decode_context_amd import binding
+    from mla_decode_context_amd import workloads as WL
+
+    binding.load_library()
+    torch.cuda.set_device(0)
+    print(f"[bench] {args.workload}: generating inputs", file=sys.stderr, flush=True)
+    head, wl = time_workload(args.workload, args.steps, args.warmup, torch, headline=True)
+    print(f"[bench] {args.workload}: {head['ms_per_step']:.4f} ms/step, {head['kv_GBps']:.1f} GB/s",
+          file=sys.stderr, flush=True)
+    configs = {}
+    for name in [c for c in args.configs.split(",") if c]:
+        print(f"[bench] {name}: generating inputs", file=sys.stderr, flush=True)
+        res, _ = time_workload(name, args.config_steps, 3, torch)
+        configs[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()}
+        print(f"[bench] {name}: {json.dumps(configs[name])}", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl)
+    achieved = head["_alg_bytes_per_launch"] / (head["_decode_avg_ms"] * 1e-3) / 1e9
+    traffic = load_traffic(args.workload)
+    cfg = WL.CONFIGS[args.workload]
+    line = {
+        "metric": METRIC,
+        "value": round(head["kv_GBps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "desc": cfg["desc"], "batch": wl.B, "query_rows": wl.T,
+                   "heads": wl.H, "dcp_world": wl.W, "page_size": wl.P, "seed": wl.seed},
+        "pct_hbm_peak": round(100.0 * head["kv_GBps"] / HBM_PEAK_GBPS, 2),
+        "query_tokens_per_s": round(head["query_tokens_per_s"], 1),
+        "kv_GBps_cold_llc": round(head["_cold_kv_GBps"], 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "decode_kernel<1>", "avg_launch_ms": round(head["_decode_avg_ms"], 5),
+                     "alg_bytes_per_launch": int(head["_alg_bytes_per_launch"])},
+        "merge_GBps": configs.get("mtp_dcp4", {}).get("merge_GBps"),
+        "cpu_baseline": cpu,
+        "configs": configs,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

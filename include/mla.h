@@ -94,8 +94,12 @@ const char* mla_status_string(mla_status status);
  * device).  num_splits caps how many workgroups split one row's keys
  * ("num_splits" of the varlen kernel call on the flashattn_mla page):
  * 0 = choose automatically, 1 = never split, k = at most k.  Splitting needs
- * `workspace` of at least mla_decode_workspace_size(...) bytes (any alignment
- * of 256 bytes); with workspace == NULL the call runs unsplit.
+ * `workspace` of at least mla_decode_workspace_size(...) bytes (any
+ * alignment); with workspace == NULL the call runs unsplit.  The workspace
+ * holds the split partials and the split tickets of the in-kernel combine:
+ * it must be zero-filled before its first use, every call leaves it ready for
+ * the next (tickets back at zero), and calls that overlap in time (e.g. on two
+ * streams) must not share one workspace.
  *
  * Returns MLA_OK, or MLA_ERR_NULL / MLA_ERR_SHAPE (B<0, T<0, H outside
  * [1,128], page_size<1, cp_world<1, cp_rank outside [0,cp_world), strides

@@ -70,10 +70,17 @@ Plan make_plan(int T, int H, int max_seq_len, int W, int num_splits, bool split_
   return p;
 }
 
+// Workspace layout (offsets from the 256-byte aligned base):
+//   int32 counters[T * hblocks]          split tickets, zero between calls
+//   fp32  lse[max_splits][T][H]          split LSEs
+//   fp32  o[max_splits][T][H][512]       normalised split partials
+size_t counters_bytes(const Plan& p, int T) { return (size_t)round_up((int64_t)T * p.hblocks * 4, 256); }
+size_t lse_bytes(const Plan& p, int T, int H) { return (size_t)round_up((int64_t)p.max_splits * T * H * 4, 256); }
+
 size_t workspace_bytes_for(const Plan& p, int T, int H) {
   if (p.max_splits <= 1) return 0;
   const size_t rows = (size_t)p.max_splits * T * H;
-  return rows * MLA_D_LATENT * sizeof(float) + rows * sizeof(float) + 256;
+  return counters_bytes(p, T) + lse_bytes(p, T, H) + rows * MLA_D_LATENT * sizeof(float) + 256;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -149,12 +156,12 @@ mla_status mla_decode_partial(
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   p.chunk = plan.chunk; p.hblocks = plan.hblocks; p.max_splits = plan.max_splits;
   p.out = (uint16_t*)out; p.lse = lse;
-  p.ws_o = nullptr; p.ws_lse = nullptr;
+  p.ws_o = nullptr; p.ws_lse = nullptr; p.counters = nullptr;
   if (plan.max_splits > 1) {
     char* base = (char*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
-    const size_t rows = (size_t)plan.max_splits * T * H;
-    p.ws_o = (float*)base;
-    p.ws_lse = (float*)(base + rows * MLA_D_LATENT * sizeof(float));
+    p.counters = (int32_t*)base;
+    p.ws_lse = (float*)(base + counters_bytes(plan, T));
+    p.ws_o = (float*)(base + counters_bytes(plan, T) + lse_bytes(plan, T, H));
   }
   hipError_t e = mla::launch_decode(p, plan.mtiles, plan.max_splits, (hipStream_t)hip_stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;

@@ -25,7 +25,8 @@
 //      B-operand layout.
 // The next step's rows are loaded while the current step computes.  When a
 // row's keys are split over several workgroups, each writes its normalised
-// partial (fp32) and LSE to the workspace and a second pass merges them.
+// partial (fp32) and LSE to the workspace and the last one to finish merges
+// them (exact LSE-weighted combine) in the same launch.
 #include "mla_common.h"
 #include "mla_kernels.h"
 
@@ -266,40 +267,50 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams a) {
       if (w == 0 && g == 0) a.ws_lse[((size_t)split * a.T + t) * a.H + h] = lse_v;
     }
   }
-}
+  if (nsplit == 1) return;
 
-// Merge the split partials of rows whose keys were split (one wave per (t, h)).
-__global__ __launch_bounds__(256) void split_combine_kernel(const DecodeParams a) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= a.T * a.H) return;
-  const int t = row / a.H;
-  const int h = row - t * a.H;
-  const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r);
-  const int ns = num_splits_of(ri.L, a.chunk, a.max_splits);
-  if (ns <= 1) return;
-  const size_t plane = (size_t)a.T * a.H;
-  float mx = -INFINITY;
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.ws_lse[s * plane + row]);
-  float sum = 0.f;
-  for (int s = 0; s < ns; ++s) sum += fast_exp2((a.ws_lse[s * plane + row] - mx) * kLog2e);
-  const float lse_tot = mx + fast_log2(sum) * kLn2;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < ns; ++s) {
-    const float wgt = fast_exp2((a.ws_lse[s * plane + row] - lse_tot) * kLog2e);
-    const float* src = a.ws_o + (s * plane + row) * kLatent + lane * 8;
-    const f32x4 x0 = *(const f32x4*)src;
-    const f32x4 x1 = *(const f32x4*)(src + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[e] += wgt * x0[e];
-      acc[4 + e] += wgt * x1[e];
-    }
+  // Split rows: the last of the row's splits to finish merges all partials.
+  // Each split publishes its partial (release fence), then takes a ticket;
+  // the holder of the last ticket acquires and merges, and puts the counter
+  // back to zero for the next call.
+  __shared__ int s_last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int ticket = atomicAdd(a.counters + blockIdx.x, 1);
+    s_last = ticket == nsplit - 1;
   }
-  *(u32x4*)(a.out + (size_t)row * kLatent + lane * 8) =
-      u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-            pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
-  if (lane == 0) a.lse[row] = lse_tot;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const size_t plane = (size_t)a.T * a.H;
+  for (int hh = w; hh < 16 * MT; hh += 4) {
+    const int h = h0 + hh;
+    if (h >= a.H) break;
+    const size_t row = (size_t)t * a.H + h;
+    float mx = -INFINITY;
+    for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, a.ws_lse[sp * plane + row]);
+    float sum = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) sum += fast_exp2((a.ws_lse[sp * plane + row] - mx) * kLog2e);
+    const float lse_tot = mx + fast_log2(sum) * kLn2;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float wgt = fast_exp2((a.ws_lse[sp * plane + row] - lse_tot) * kLog2e);
+      const float* src = a.ws_o + (sp * plane + row) * kLatent + lane * 8;
+      const f32x4 x0 = *(const f32x4*)src;
+      const f32x4 x1 = *(const f32x4*)(src + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += wgt * x0[e];
+        acc[4 + e] += wgt * x1[e];
+      }
+    }
+    *(u32x4*)(a.out + row * kLatent + lane * 8) =
+        u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+              pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+    if (lane == 0) a.lse[row] = lse_tot;
+  }
+  if (threadIdx.x == 0) a.counters[blockIdx.x] = 0;
 }
 
 __global__ __launch_bounds__(256) void local_seqlens_kernel(const int32_t* seq_lens, const int32_t* qsl,
@@ -316,10 +327,6 @@ hipError_t launch_decode(const DecodeParams& p, int mtiles, int max_splits, hipS
     hipLaunchKernelGGL(decode_kernel<1>, grid, dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL(decode_kernel<2>, grid, dim3(256), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || max_splits <= 1) return e;
-  const unsigned rows = (unsigned)((int64_t)p.T * p.H);
-  hipLaunchKernelGGL(split_combine_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -23,6 +23,7 @@ struct DecodeParams {
   float* lse;              // fp32 [T,H]
   float* ws_o;             // fp32 [splits,T,H,512] split partials (normalised)
   float* ws_lse;           // fp32 [splits,T,H]
+  int32_t* counters;       // int32 [T*hblocks] split tickets; zero between calls
 };
 
 struct MergeParams {

@@ -53,7 +53,8 @@ class DeviceWorkload:
     def alloc_workspace(self, num_splits: int):
         self.num_splits = num_splits
         n = mla.workspace_size(self.B, self.T, self.H, self.max_query_len, self.max_seq_len, self.W, num_splits)
-        self.workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=self.device) if n else None
+        # zero-filled once: the split tickets must start at zero (calls reset them)
+        self.workspace = torch.zeros(n, dtype=torch.uint8, device=self.device) if n else None
 
     def partial(self, r: int, stream=None):
         mla.mla_decode_partial(
