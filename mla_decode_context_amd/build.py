@@ -15,6 +15,11 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 VALU ops stay off: hipcc emits ordinary fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA sources and results stay in ordinary VGPRs.  With accumulators in
+    # AGPRs, hipcc 7.2 for gfx950 copied accumulators through AGPR temporaries
+    # written a few cycles after an in-flight MFMA read them as its C operand,
+    # and workgroups of 32+ heads gave wrong results; this form has no such copies.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
 
@@ -31,8 +36,9 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    noise = ("is not a recognized feature for this target", "inline asm clobber list contains reserved",
+             "Reserved registers on the clobber list", "asm volatile(", "generated when compiling", "^")
+    err = "\n".join(l for l in res.stderr.splitlines() if not any(n in l for n in noise) and l.strip())
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():

@@ -29,8 +29,8 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 constexpr int kStep = 32;          // keys per inner step of the decode kernel
-constexpr int kTargetGroups = 1024;  // busy workgroups wanted per launch (4 per CU)
-constexpr int kMinChunk = 256;     // auto splits never go below this many keys
+constexpr int kTargetGroups = 512;   // busy workgroups wanted per launch (2 per CU)
+constexpr int kMinChunk = 1024;    // auto splits never go below this many keys
 constexpr int kMaxGridY = 65535;
 
 // Launch plan: heads per workgroup and keys per split.  Depends only on host

@@ -34,13 +34,12 @@ namespace mla {
 
 constexpr int kStep = 32;        // keys per inner step (K of the PV MFMA)
 constexpr int kSlab = 128;       // latent dims owned by one wave
-constexpr int kVStride = 144;    // LDS row stride of a wave's value slab (bf16): 288 B
+constexpr int kRowBytes = kRow * 2;              // 1152
+constexpr int kStageBytes = kStep * kRowBytes;   // 36 KiB: one step's rows
+constexpr int kStages = 3;                        // stages in the LDS ring
 
 __device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma_16x16x16(s16x4 a, s16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -48,8 +47,44 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // Transposed 64-bit LDS read: within each 16-lane group, lane i receives
 // element (i & 3) of the four-element chunk addressed by lane 4e + (i >> 2),
 // for e = 0..3.
-__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uint16_t*)p);
+__device__ __forceinline__ s16x4 lds_read_tr16_at(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uint8_t*)p);
+}
+
+// Direct-to-LDS load (gfx950 global_load_lds_dwordx4): each lane fetches 16
+// bytes from its own global address and the wave's 64 results fill the 1 KiB of
+// LDS starting at lds_block (wave-uniform; passed in M0).  Issued through asm so
+// that the compiler adds no wait of its own: the kernel orders these loads with
+// explicit vmcnt waits and barriers.  The asm is volatile with a memory clobber,
+// so no other memory access moves across it.  A write of M0 needs one wait state
+// before an LDS-DMA instruction reads it, hence the s_nop.
+__device__ __forceinline__ void dma_16B_to_lds(const void* src, const uint8_t* lds_block) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds_block);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds), "v"(src)
+               : "memory", "m0");
+}
+
+// Empty asm that "uses" a pointer, extending its registers' live range.
+__device__ __forceinline__ void keep_live(const void* p) { asm volatile("" : : "v"(p)); }
+
+// Device-scope (all-XCD coherent) accesses to the split workspace: relaxed
+// atomics at agent scope, which the compiler emits as plain loads and stores
+// with the device-coherence cache policy and no fences.
+__device__ __forceinline__ void store_device(float* p, float x, float y) {
+  const uint64_t v = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
+  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_device(const float* p) {
+  return __uint_as_float(__hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ f32x4 load_device4(const float* p) {
+  const uint64_t lo = __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi = __hip_atomic_load((const uint64_t*)p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return f32x4{__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+               __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32))};
 }
 
 // Splits of a row with L visible keys: ceil(L / chunk), at least 1, at most the
@@ -59,10 +94,83 @@ __device__ __forceinline__ int num_splits_of(int L, int chunk, int max_splits) {
   return n < max_splits ? n : max_splits;
 }
 
-template <int MT>
+// Split rows: the last of the row's splits to finish merges all partials.
+// Every split has already written its normalised partial and LSE for heads
+// h0 .. h0+nheads-1 of token t with device-scope stores.  Partials travel with
+// device-scope stores and loads, which write through to and read from the point
+// where all XCDs see the same memory, so publishing needs only the wait for this
+// workgroup's stores before its ticket -- no write-back of the whole L2 that a
+// device-scope fence would cost.  The holder of the last ticket merges (exact
+// LSE-weighted combine) and puts the counter back to zero for the next call.
+__device__ __forceinline__ void ticket_and_merge(const DecodeParams& a, int t, int h0, int nheads,
+                                                 int nsplit) {
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int ticket = __hip_atomic_fetch_add(a.counters + blockIdx.x, 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    s_last = ticket == nsplit - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // Merge: thread (head hl = tid / 16, dims 32*(tid % 16) .. +32) for each group
+  // of 16 heads in turn; two splits' loads are in flight at once.
+  const size_t plane = (size_t)a.T * a.H;
+  const int hl = threadIdx.x >> 4;          // 0..15
+  const int d0 = (threadIdx.x & 15) * 32;
+  for (int hg = 0; hg < nheads; hg += 16) {
+    const int h = h0 + hg + hl;
+    if (h < a.H) {
+      const size_t row = (size_t)t * a.H + h;
+      float mx = -INFINITY;
+      for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, load_device(a.ws_lse + sp * plane + row));
+      float sum = 0.f;
+      for (int sp = 0; sp < nsplit; ++sp) sum += fast_exp2((load_device(a.ws_lse + sp * plane + row) - mx) * kLog2e);
+      const float lse_tot = mx + fast_log2(sum) * kLn2;
+      f32x4 acc[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int sp0 = 0; sp0 < nsplit; sp0 += 2) {
+        f32x4 x[2][8];
+        float wgt[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int sp = min(sp0 + u, nsplit - 1);
+          wgt[u] = sp0 + u < nsplit ? fast_exp2((load_device(a.ws_lse + sp * plane + row) - lse_tot) * kLog2e) : 0.f;
+          const float* src = a.ws_o + (sp * plane + row) * kLatent + d0;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) x[u][k] = load_device4(src + 4 * k);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc[k] += wgt[u] * x[u][k];
+      }
+      uint16_t* op = a.out + row * kLatent + d0;
+#pragma unroll
+      for (int k = 0; k < 8; k += 2)
+        *(u32x4*)(op + 4 * k) = u32x4{pack_bf16x2(acc[k][0], acc[k][1]), pack_bf16x2(acc[k][2], acc[k][3]),
+                                      pack_bf16x2(acc[k + 1][0], acc[k + 1][1]),
+                                      pack_bf16x2(acc[k + 1][2], acc[k + 1][3])};
+      if ((threadIdx.x & 15) == 0) a.lse[row] = lse_tot;
+    }
+  }
+  if (threadIdx.x == 0) a.counters[blockIdx.x] = 0;
+}
+
+// vmcnt(n) operand of s_waitcnt (expcnt and lgkmcnt left at their maxima).
+#define MLA_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+
+template <int MT, int NS, bool kPage16>
 __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams a) {
-  __shared__ __attribute__((aligned(16))) uint16_t vslab[4][kStep * kVStride];
-  __shared__ __attribute__((aligned(16))) f32x4 sx[2][4][2][MT][64];
+  // One LDS block with a fixed layout: the NS-deep ring of 32-row stages (rows
+  // land here straight from HBM) at offset 0, then the double-buffered exchange
+  // of partial scores.  The direct-to-LDS loads only ever target the first
+  // NS * 36 KiB.
+  __shared__ __attribute__((aligned(16))) uint8_t lds_block[NS * kStageBytes + 2 * 4 * 2 * MT * 64 * 16];
+  uint8_t (*stage)[kStageBytes] = (uint8_t (*)[kStageBytes])lds_block;
+  f32x4 (*sx)[4][2][MT][64] = (f32x4 (*)[4][2][MT][64])(lds_block + NS * kStageBytes);
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -94,11 +202,14 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams a) {
   // the grid had fewer splits than ceil(L / chunk).
   const int j_begin = split * a.chunk;
   const int j_end = split == nsplit - 1 ? L : j_begin + a.chunk;
+  const int n_steps = (j_end - j_begin + kStep - 1) / kStep;
 
   // Query operand (B of S^T = K Q^T): lane (head lr, group g) holds, for k-step s,
-  // latent dims 128w + 32s + 8g .. +8, and rope dims 16w + 4g .. +4.
+  // latent dims 128w + 32s + 8g .. +8; for the rope step, groups 0 and 1 hold
+  // rope dims 16w + 8g .. +8 and groups 2 and 3 hold zeros (16 rope dims per
+  // wave padded to one 32-deep MFMA step).
   bf16x8 qc[MT][4];
-  s16x4 qp[MT];
+  bf16x8 qp[MT];
 #pragma unroll
   for (int mu = 0; mu < MT; ++mu) {
     const int h = h0 + 16 * mu + lr;
@@ -106,36 +217,86 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams a) {
       const uint16_t* qn = a.q_nope + (int64_t)t * a.qn_st + (int64_t)h * a.qn_sh + kSlab * w + 8 * g;
 #pragma unroll
       for (int s = 0; s < 4; ++s) qc[mu][s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qn + 32 * s));
-      const uint16_t* qr = a.q_pe + (int64_t)t * a.qp_st + (int64_t)h * a.qp_sh + 16 * w + 4 * g;
-      qp[mu] = __builtin_bit_cast(s16x4, *(const u32x2*)qr);
+      const uint16_t* qr = a.q_pe + (int64_t)t * a.qp_st + (int64_t)h * a.qp_sh + 16 * w + 8 * (g & 1);
+      const u32x2 q0 = *(const u32x2*)qr;
+      const u32x2 q1 = *(const u32x2*)(qr + 4);
+      qp[mu] = __builtin_bit_cast(bf16x8, g < 2 ? u32x4{q0[0], q0[1], q1[0], q1[1]} : u32x4{0u, 0u, 0u, 0u});
     } else {
 #pragma unroll
       for (int s = 0; s < 4; ++s) qc[mu][s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-      qp[mu] = s16x4{0, 0, 0, 0};
+      qp[mu] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
   }
+  // The q loads must land before the first stage wait counts only stage loads.
+  __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
 
   const int32_t* bt_row = a.bt + (int64_t)ri.b * a.bt_stride;
-  // Key operand (A of S^T): lane (key lr of half tau, group g) holds the same dims.
-  u32x4 kc[2][4];
-  u32x2 kp[2];
-  auto load_step = [&](int j0, u32x4 (&c)[2][4], u32x2 (&pr)[2]) {
+
+  // Stage fill: the 36 KiB stage is 36 blocks of 1 KiB, each written by one
+  // direct-to-LDS load instruction (lane l -> bytes 16l .. 16l+15 of the block);
+  // wave w issues blocks 9w .. 9w+8.  Byte o of the stage is row o / 1152, 16-byte
+  // chunk c = (o % 1152) / 16, which holds chunk c ^ (row & 7) of that cache row.
+  // Global addresses of the loads last issued by this wave.  They are kept live
+  // (see keep_live below) until the end of the step, so that no instruction
+  // writes their registers while the loads may still read them.
+  const uint16_t* dma_src[9];
+  // Per-lane constants of the stage layout: byte offset of this lane's 16 bytes
+  // within 32 consecutive cache rows (row * 1152 + swizzled chunk * 16), and
+  // whether the row is in the second half (rows 16..31) of the stage.
+  uint32_t lane_off[9];
+  bool lane_hi[9];
+  int lane_row[9];
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      const int j = j0 + 16 * tau + lr;
-      if (j < j_end) {
-        const int blk = bt_row[j / a.P];
-        const uint16_t* row = a.kv + (int64_t)blk * a.kv_bs + (int64_t)(j % a.P) * kRow;
+  for (int i = 0; i < 9; ++i) {
+    const int o = 1024 * (9 * w + i) + 16 * lane;
+    const int row = o / kRowBytes;
+    const int cpos = (o - row * kRowBytes) >> 4;
+    lane_row[i] = row;
+    lane_off[i] = (uint32_t)(row * kRowBytes + ((cpos ^ (row & 7)) << 4));
+    lane_hi[i] = row >= 16;
+  }
+  const uint8_t* kv_bytes = (const uint8_t*)a.kv;
+  auto issue_stage = [&](int j0, int buf) {
+    uint8_t* ldst = stage[buf] + 1024 * 9 * w;
+    if (kPage16 && j0 + kStep <= j_end) {
+      // Whole stage inside the split and page_size % 16 == 0: rows 0..15 lie in
+      // one page and rows 16..31 in one page, so two scalar block-table loads and
+      // one 64-bit add per load give every address.
+      const int pg0 = j0 / a.P;
+      const int pg1 = (j0 + 16) / a.P;
+      const int blk0 = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pg0];
+      const int blk1 = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pg1];
+      const uint8_t* base0 = kv_bytes + ((int64_t)blk0 * a.kv_bs + (int64_t)(j0 - pg0 * a.P) * kRow) * 2;
+      const uint8_t* base1 = kv_bytes + ((int64_t)blk1 * a.kv_bs + (int64_t)(j0 - pg1 * a.P) * kRow) * 2;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) c[tau][s] = *(const u32x4*)(row + kSlab * w + 32 * s + 8 * g);
-        pr[tau] = *(const u32x2*)(row + kLatent + 16 * w + 4 * g);
-      } else {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) c[tau][s] = u32x4{0u, 0u, 0u, 0u};
-        pr[tau] = u32x2{0u, 0u};
+      for (int i = 0; i < 9; ++i) {
+        dma_src[i] = (const uint16_t*)((lane_hi[i] ? base1 : base0) + lane_off[i]);
+        dma_16B_to_lds(dma_src[i], ldst + 1024 * i);
       }
+      return;
+    }
+    // Ragged or trailing stage (or any page size): keys at or past j_end are
+    // clamped to j_end - 1 (a real cached row: finite values, masked to
+    // probability 0 below), so every path issues the same loads.  A 1 KiB block
+    // covers at most two cache rows (ra and ra + 1), so two scalar block-table
+    // loads serve each block.
+#pragma unroll
+    for (int i = 0; i < 9; ++i) {
+      const int ra = (1024 * (9 * w + i)) / kRowBytes;
+      const int row = lane_row[i];
+      const int j = min(j0 + row, j_end - 1);
+      const int pa = __builtin_amdgcn_readfirstlane(min(j0 + ra, j_end - 1) / a.P);
+      const int pb2 = __builtin_amdgcn_readfirstlane(min(j0 + ra + 1, j_end - 1) / a.P);
+      const int ba = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pa];
+      const int bb = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pb2];
+      const int pg = j / a.P;              // pa or pb2
+      const int64_t rbase = (int64_t)(pg == pa ? ba : bb) * a.kv_bs + (int64_t)(j - pg * a.P) * kRow;
+      dma_src[i] = (const uint16_t*)(kv_bytes + rbase * 2 + (lane_off[i] - row * kRowBytes));
+      dma_16B_to_lds(dma_src[i], ldst + 1024 * i);
     }
   };
+  // LDS byte address of 16-byte chunk c of stage row r.
+  auto chunk_addr = [&](int r, int c) { return r * kRowBytes + ((c ^ (r & 7)) << 4); };
 
   float m_run[MT], l_run[MT];
   f32x4 o[8][MT];
@@ -147,32 +308,40 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams a) {
     for (int dt = 0; dt < 8; ++dt) o[dt][mu] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  uint16_t* vs = vslab[w];
-  load_step(j_begin, kc, kp);
-  int buf = 0;
-  for (int j0 = j_begin; j0 < j_end; j0 += kStep) {
-    u32x4 nc[2][4];
-    u32x2 np[2];
-    const bool more = j0 + kStep < j_end;
-    if (more) load_step(j0 + kStep, nc, np);
-
-    // This wave's latent slab of the 32 rows -> LDS (read back transposed below).
+  // Prologue: stages 0 .. NS-2 in flight.
 #pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        *(u32x4*)(vs + (16 * tau + lr) * kVStride + 32 * s + 8 * g) = kc[tau][s];
+  for (int s = 0; s < NS - 1; ++s) issue_stage(j_begin + kStep * s, s);
 
-    // Partial scores over this wave's dims.
+  for (int it = 0; it < n_steps; ++it) {
+    const int j0 = j_begin + kStep * it;
+    const int buf = it % NS;
+    // This wave's loads of stage `it` have landed once at most NS-2 newer stages
+    // (9 loads each) are outstanding; the barrier then makes every wave's part
+    // visible and also tells that all waves are done with the previous step's
+    // stage, which the issue below reuses.
+    __builtin_amdgcn_s_waitcnt(MLA_VMCNT(9 * (NS - 2)));
+    __builtin_amdgcn_s_barrier();
+    issue_stage(j0 + kStep * (NS - 1), (it + NS - 1) % NS);
+    const uint8_t* sb = stage[buf];
+
+    // Partial scores over this wave's dims: A = keys (lane: key lr of half tau,
+    // the same dims as the query operand).
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau) {
+      const int r = 16 * tau + lr;
+      bf16x8 kc[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kc[s] = *(const bf16x8*)(sb + chunk_addr(r, 16 * w + 4 * s + g));
+      // rope dims 16w + 8g .. +8 (chunk 64 + 2w + g) for groups 0 and 1; the
+      // zero query entries of groups 2 and 3 make their key entries irrelevant
+      const bf16x8 kp = *(const bf16x8*)(sb + chunk_addr(r, 64 + 2 * w + (g & 1)));
 #pragma unroll
       for (int mu = 0; mu < MT; ++mu) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma_16x16x32(__builtin_bit_cast(bf16x8, kc[tau][s]), qc[mu][s], acc);
-        acc = mfma_16x16x16(__builtin_bit_cast(s16x4, kp[tau]), qp[mu], acc);
-        sx[buf][w][tau][mu][lane] = acc;
+        for (int s = 0; s < 4; ++s) acc = mfma_16x16x32(kc[s], qc[mu][s], acc);
+        acc = mfma_16x16x32(kp, qp[mu], acc);
+        sx[it & 1][w][tau][mu][lane] = acc;
       }
     }
     __syncthreads();
@@ -186,10 +355,10 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams a) {
       float v[8];
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
-        f32x4 s4 = sx[buf][0][tau][mu][lane];
-        s4 += sx[buf][1][tau][mu][lane];
-        s4 += sx[buf][2][tau][mu][lane];
-        s4 += sx[buf][3][tau][mu][lane];
+        f32x4 s4 = sx[it & 1][0][tau][mu][lane];
+        s4 += sx[it & 1][1][tau][mu][lane];
+        s4 += sx[it & 1][2][tau][mu][lane];
+        s4 += sx[it & 1][3][tau][mu][lane];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = j0 + 16 * tau + 4 * g + r;
@@ -219,27 +388,25 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams a) {
       for (int dt = 0; dt < 8; ++dt) o[dt][mu] *= alpha;
     }
 
-    // O^T[d][head] += V^T[d][key] P^T[key][head] over this wave's 128 dims.
+    // O^T[d][head] += V^T[d][key] P^T[key][head] over this wave's 128 dims; the
+    // transposed LDS read gives lane (dim lr, group g) keys 4g..4g+3 (and +16)
+    // when source lane lr points at key 4g + (lr >> 2), dims 16dt + 4(lr & 3)..+4.
+    const int vr = 4 * g + (lr >> 2);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const uint16_t* src = vs + (4 * g + (lr >> 2)) * kVStride + 16 * dt + 4 * (lr & 3);
-      const s16x4 lo = lds_read_tr16(src);
-      const s16x4 hi = lds_read_tr16(src + 16 * kVStride);
+      const int c = 16 * w + 2 * dt + ((lr & 3) >> 1);
+      const int off = 8 * (lr & 1);
+      const s16x4 lo = lds_read_tr16_at(sb + chunk_addr(vr, c) + off);
+      const s16x4 hi = lds_read_tr16_at(sb + chunk_addr(vr + 16, c) + off);
       const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int mu = 0; mu < MT; ++mu) o[dt][mu] = mfma_16x16x32(va, pb[mu], o[dt][mu]);
     }
-
-    if (more) {
 #pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) kc[tau][s] = nc[tau][s];
-        kp[tau] = np[tau];
-      }
-    }
-    buf ^= 1;
+    for (int i = 0; i < 9; ++i) keep_live(dma_src[i]);
   }
+  // No stage load may still be writing LDS when the workgroup ends.
+  __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
 
   // Finalise: O^T tile (dt, mu) lane (head lr, group g) holds dims
   // 128w + 16dt + 4g + (0..3) of head h0 + 16mu + lr.
@@ -263,54 +430,19 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams a) {
     } else {
       float* wp = a.ws_o + (((size_t)split * a.T + t) * a.H + h) * kLatent + kSlab * w + 4 * g;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) *(f32x4*)(wp + 16 * dt) = o[dt][mu] * inv;
-      if (w == 0 && g == 0) a.ws_lse[((size_t)split * a.T + t) * a.H + h] = lse_v;
+      for (int dt = 0; dt < 8; ++dt) {
+        const f32x4 x = o[dt][mu] * inv;
+        store_device(wp + 16 * dt, x[0], x[1]);
+        store_device(wp + 16 * dt + 2, x[2], x[3]);
+      }
+      if (w == 0 && g == 0)
+        __hip_atomic_store((uint32_t*)a.ws_lse + ((size_t)split * a.T + t) * a.H + h, __float_as_uint(lse_v),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   if (nsplit == 1) return;
 
-  // Split rows: the last of the row's splits to finish merges all partials.
-  // Each split publishes its partial (release fence), then takes a ticket;
-  // the holder of the last ticket acquires and merges, and puts the counter
-  // back to zero for the next call.
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int ticket = atomicAdd(a.counters + blockIdx.x, 1);
-    s_last = ticket == nsplit - 1;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const size_t plane = (size_t)a.T * a.H;
-  for (int hh = w; hh < 16 * MT; hh += 4) {
-    const int h = h0 + hh;
-    if (h >= a.H) break;
-    const size_t row = (size_t)t * a.H + h;
-    float mx = -INFINITY;
-    for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, a.ws_lse[sp * plane + row]);
-    float sum = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) sum += fast_exp2((a.ws_lse[sp * plane + row] - mx) * kLog2e);
-    const float lse_tot = mx + fast_log2(sum) * kLn2;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float wgt = fast_exp2((a.ws_lse[sp * plane + row] - lse_tot) * kLog2e);
-      const float* src = a.ws_o + (sp * plane + row) * kLatent + lane * 8;
-      const f32x4 x0 = *(const f32x4*)src;
-      const f32x4 x1 = *(const f32x4*)(src + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[e] += wgt * x0[e];
-        acc[4 + e] += wgt * x1[e];
-      }
-    }
-    *(u32x4*)(a.out + row * kLatent + lane * 8) =
-        u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-              pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
-    if (lane == 0) a.lse[row] = lse_tot;
-  }
-  if (threadIdx.x == 0) a.counters[blockIdx.x] = 0;
+  ticket_and_merge(a, t, h0, 16 * MT, nsplit);
 }
 
 __global__ __launch_bounds__(256) void local_seqlens_kernel(const int32_t* seq_lens, const int32_t* qsl,
@@ -321,12 +453,306 @@ __global__ __launch_bounds__(256) void local_seqlens_kernel(const int32_t* seq_l
   if (shard_len && i < B) shard_len[i] = ceil_div_pos(seq_lens[i] - r, W);
 }
 
+
+// ---------------------------------------------------------------------------
+// Decode for up to 16 heads (one 16-head MFMA tile).
+//
+// With 16 heads the arithmetic is light (about 30 flop per cache byte) and the
+// kernel must keep HBM busy, so it is built for occupancy: 72 KiB of LDS and at
+// most 256 registers per lane, so two workgroups share a CU.  The four waves
+// form two pairs; each step, pair p takes a 16-key stage (keys 32i + 16p of
+// the split).  Both waves of a pair compute the full 576-wide scores of their
+// stage (duplicated; there is MFMA time to spare), run the same online softmax,
+// and split PV: wave half 0 owns latent dims 0..255, half 1 dims 256..511.  The
+// stage's rows land in the pair's 2-slot LDS ring straight from HBM (each wave
+// issues half of the stage's 18 direct-to-LDS loads).  After the loop the two
+// pairs' (max, sum, unnormalised output) states are merged through LDS.
+// ---------------------------------------------------------------------------
+constexpr int kPStep = 16;                             // keys per stage
+constexpr int kPStageBytes = kPStep * kRowBytes;       // 18 KiB
+constexpr int kPBlocks = kPStageBytes / 1024;          // 18 load instructions per stage
+constexpr int kPHalfBlocks = kPBlocks / 2;             // issued by each wave of the pair
+
+// Direct-to-LDS load with a wave-uniform 64-bit base (SGPRs) and a per-lane
+// 32-bit byte offset; see dma_16B_to_lds.
+__device__ __forceinline__ void dma_16B_to_lds_sbase(uint32_t lds_off, uint32_t voff, const void* base) {
+  // The base must live in SGPRs: take each 32-bit half from the first lane (it
+  // is uniform).  readfirstlane returns int: widen through uint32_t so that the
+  // low half is zero-extended, never sign-extended into the high half.
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint64_t sbase = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_off), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
+// max / sum over the four lanes l, l^16, l^32, l^48 (one MFMA column) with the
+// gfx950 lane-swap instructions (VALU, no LDS round trip).
+__device__ __forceinline__ float col_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float col_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <bool kPage16>
+__global__ __launch_bounds__(256, 2) void decode_kernel_h16(const DecodeParams a) {
+  // Two pair rings of two 18 KiB slots; reused for the cross-pair merge.
+  __shared__ __attribute__((aligned(16))) uint8_t lds_block[2 * 2 * kPStageBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, kept in SGPRs
+  const int pair = w >> 1;
+  const int half = w & 1;
+  const int lr = lane & 15;
+  const int g = lane >> 4;
+
+  const int t = blockIdx.x;                 // one 16-head block per token
+  const int split = blockIdx.y;
+  const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r);
+  const int L = ri.L;
+  const int nsplit = num_splits_of(L, a.chunk, (int)gridDim.y);
+  if (split >= nsplit) return;
+
+  if (L == 0) {
+    // The row sees no key on this rank: out = 0, lse = -inf.
+    for (int idx = threadIdx.x; idx < 16 * 64; idx += 256) {
+      const int h = idx >> 6;
+      const int c = idx & 63;
+      if (h < a.H) {
+        *(u32x4*)(a.out + ((size_t)t * a.H + h) * kLatent + c * 8) = u32x4{0u, 0u, 0u, 0u};
+        if (c == 0) a.lse[(size_t)t * a.H + h] = -INFINITY;
+      }
+    }
+    return;
+  }
+  const int j_begin = split * a.chunk;
+  const int j_end = split == nsplit - 1 ? L : j_begin + a.chunk;
+  const int n_steps = (j_end - j_begin + 2 * kPStep - 1) / (2 * kPStep);
+
+  // Query operand (B of S^T = K Q^T) over all 576 dims: lane (head lr, group g)
+  // holds dims 32s + 8g .. +8 for k-step s (s < 16: q_nope, s = 16, 17: q_pe).
+  bf16x8 q[18];
+  {
+    const int h = lr;
+    const bool ok = h < a.H;
+    const uint16_t* qn = a.q_nope + (int64_t)t * a.qn_st + (int64_t)(ok ? h : 0) * a.qn_sh + 8 * g;
+    const uint16_t* qr = a.q_pe + (int64_t)t * a.qp_st + (int64_t)(ok ? h : 0) * a.qp_sh + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const u32x4 v = *(const u32x4*)(qn + 32 * s);
+      q[s] = __builtin_bit_cast(bf16x8, ok ? v : u32x4{0u, 0u, 0u, 0u});
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const u32x2 v0 = *(const u32x2*)(qr + 32 * s);
+      const u32x2 v1 = *(const u32x2*)(qr + 32 * s + 4);
+      q[16 + s] = __builtin_bit_cast(bf16x8, ok ? u32x4{v0[0], v0[1], v1[0], v1[1]} : u32x4{0u, 0u, 0u, 0u});
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+
+  const int32_t* bt_row = a.bt + (int64_t)ri.b * a.bt_stride;
+  const uint8_t* kv_bytes = (const uint8_t*)a.kv;
+  uint8_t* ring = lds_block + pair * 2 * kPStageBytes;
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring);
+
+  // Stage layout: byte o of the 18 KiB stage is row o / 1152, 16-byte chunk
+  // c = (o % 1152) / 16, holding chunk c ^ (row & 7) of that cache row.  Block b
+  // (1 KiB) is written by one load: lane l -> bytes 1024b + 16l .. +16; this
+  // wave issues blocks b = 9*half + i.
+  auto lane_row = [&](int b) { return (1024 * b + 16 * lane) / kRowBytes; };
+  auto lane_off = [&](int b) {
+    const int o = 1024 * b + 16 * lane;
+    const int row = o / kRowBytes;
+    const int cpos = (o - row * kRowBytes) >> 4;
+    return (uint32_t)(row * kRowBytes + ((cpos ^ (row & 7)) << 4));
+  };
+  // Issue this wave's half of the pair's stage for step i into ring slot `slot`.
+  // Keys at or past j_end (a ragged or empty trailing stage) are clamped to key
+  // j_end - 1 -- a real cached row, masked to probability 0 -- so every path
+  // issues exactly kPHalfBlocks loads.
+  auto issue = [&](int i, int slot) {
+    const int j0 = j_begin + 2 * kPStep * i + kPStep * pair;
+    const uint32_t ldst = ring_lds + slot * kPStageBytes;
+    if (kPage16 && j0 + kPStep <= j_end) {
+      // page_size % 16 == 0: the stage's 16 rows are consecutive slots of one page.
+      const int pg = j0 / a.P;
+      const int blk = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pg];
+      const uint8_t* base = kv_bytes + ((int64_t)blk * a.kv_bs + (int64_t)(j0 - pg * a.P) * kRow) * 2;
+#pragma unroll
+      for (int i2 = 0; i2 < kPHalfBlocks; ++i2) {
+        const int b = kPHalfBlocks * half + i2;
+        dma_16B_to_lds_sbase(ldst + 1024 * b, lane_off(b), base);
+      }
+    } else {
+#pragma unroll
+      for (int i2 = 0; i2 < kPHalfBlocks; ++i2) {
+        const int b = kPHalfBlocks * half + i2;
+        const int row = lane_row(b);
+        const int ra = (1024 * b) / kRowBytes;     // the block spans rows ra and ra + 1
+        const int j = min(j0 + row, j_end - 1);
+        const int pa = __builtin_amdgcn_readfirstlane(min(j0 + ra, j_end - 1) / a.P);
+        const int pb2 = __builtin_amdgcn_readfirstlane(min(j0 + ra + 1, j_end - 1) / a.P);
+        const int ba = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pa];
+        const int bb = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pb2];
+        const int pg = j / a.P;                    // pa or pb2
+        const int64_t rbase = (int64_t)(pg == pa ? ba : bb) * a.kv_bs + (int64_t)(j - pg * a.P) * kRow;
+        dma_16B_to_lds(kv_bytes + rbase * 2 + (lane_off(b) - row * kRowBytes),
+                       ring + slot * kPStageBytes + 1024 * b);
+      }
+    }
+  };
+  auto chunk_addr = [&](int r, int c) { return r * kRowBytes + ((c ^ (r & 7)) << 4); };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[16];                    // O^T tiles over this wave's 256 dims
+#pragma unroll
+  for (int dt = 0; dt < 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue(0, 0);
+  for (int i = 0; i < n_steps; ++i) {
+    const int slot = i & 1;
+    // This wave's loads of step i have landed (the only ones outstanding); the
+    // barrier makes the partner's half visible and tells that every wave is
+    // done with step i-1, whose slot the next issue reuses.
+    __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+    __builtin_amdgcn_s_barrier();
+    if (i + 1 < n_steps) issue(i + 1, slot ^ 1);
+    const uint8_t* sb = ring + slot * kPStageBytes;
+    const int j0 = j_begin + 2 * kPStep * i + kPStep * pair;
+
+    // S^T[key][head] over 576 dims (A = keys: lane key lr, dims 32s + 8g), two
+    // accumulation chains; all 18 key operands are read before the MFMAs.
+    bf16x8 kk[18];
+#pragma unroll
+    for (int s = 0; s < 18; ++s) kk[s] = *(const bf16x8*)(sb + chunk_addr(lr, 4 * s + g));
+    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 18; s += 2) {
+      s0 = mfma_16x16x32(kk[s], q[s], s0);
+      s1 = mfma_16x16x32(kk[s + 1], q[s + 1], s1);
+    }
+    const f32x4 sc = s0 + s1;
+
+    // Online softmax (base 2).  Lane (head lr, group g) holds keys 4g + r.  A
+    // stage wholly past j_end (possible for pair 1 in the last step) changes
+    // nothing: its keys are masked and a row max of -inf is kept out of exp2.
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = (j0 + 4 * g + r < j_end) ? sc[r] * a.scale_log2 : -INFINITY;
+    const float mx = col_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    bf16x8 pb;
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float pe = fast_exp2(v[r] - m_use);
+      pb[r] = (__bf16)pe;
+      pb[4 + r] = (__bf16)0.f;
+      psum += pe;
+    }
+    l_run = l_run * alpha + psum;
+    // Rescale only when some head's running max moved (once it settles, never).
+    if (__builtin_amdgcn_read_exec() & __builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) o[dt] *= alpha;
+    }
+
+    // O^T[d][head] += V^T[d][key] P^T[key][head] over dims 256*half .. +256; K = 32
+    // with keys 16..31 zero.  The transposed read gives lane (dim lr, group g)
+    // keys 4g .. 4g+3 when source lane lr points at key 4g + (lr >> 2), dims
+    // 16dt + 4(lr & 3) .. +4.
+    const int vr = 4 * g + (lr >> 2);
+    s16x4 vt[16];
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) {
+      const int c = 32 * half + 2 * dt + ((lr & 3) >> 1);
+      vt[dt] = lds_read_tr16_at(sb + chunk_addr(vr, c) + 8 * (lr & 1));
+    }
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) {
+      const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vt[dt], s16x4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7));
+      o[dt] = mfma_16x16x32(va, pb, o[dt]);
+    }
+  }
+  l_run = col_sum(l_run);
+
+  // Cross-pair merge: the pair-1 wave of each half stores its state, the pair-0
+  // wave of the same half merges it with its own and writes the result.
+  __syncthreads();
+  f32x4* ost = (f32x4*)lds_block;                              // [half][dt][lane]
+  float* mst = (float*)(lds_block + 2 * 16 * 64 * 16);         // [half][head] max
+  float* lst = mst + 32;                                       // [half][head] sum
+  if (pair == 1) {
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) ost[(half * 16 + dt) * 64 + lane] = o[dt];
+    if (g == 0) {
+      mst[half * 16 + lr] = m_run;
+      lst[half * 16 + lr] = l_run;
+    }
+  }
+  __syncthreads();
+  if (pair == 0) {
+    const int h = lr;
+    const float m1 = mst[half * 16 + h];
+    const float l1 = lst[half * 16 + h];
+    const float M = fmaxf(m_run, m1);         // finite: pair 0 always saw a key
+    const float c0 = fast_exp2(m_run - M);
+    const float c1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - M);
+    const float Lsum = c0 * l_run + c1 * l1;
+    const float inv = 1.f / Lsum;
+    const float lse_v = (M + fast_log2(Lsum)) * kLn2;
+    if (h < a.H) {
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) {
+        const f32x4 x = (c0 * o[dt] + c1 * ost[(half * 16 + dt) * 64 + lane]) * inv;
+        const int d = 256 * half + 16 * dt + 4 * g;     // lane holds dims d .. d+3 of head h
+        if (nsplit == 1) {
+          *(u32x2*)(a.out + ((size_t)t * a.H + h) * kLatent + d) =
+              u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+        } else {
+          float* wp = a.ws_o + (((size_t)split * a.T + t) * a.H + h) * kLatent + d;
+          store_device(wp, x[0], x[1]);
+          store_device(wp + 2, x[2], x[3]);
+        }
+      }
+      if (half == 0 && g == 0) {
+        if (nsplit == 1)
+          a.lse[(size_t)t * a.H + h] = lse_v;
+        else
+          __hip_atomic_store((uint32_t*)a.ws_lse + ((size_t)split * a.T + t) * a.H + h, __float_as_uint(lse_v),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  if (nsplit == 1) return;
+  ticket_and_merge(a, t, 0, 16, nsplit);
+}
+
 hipError_t launch_decode(const DecodeParams& p, int mtiles, int max_splits, hipStream_t stream) {
   const dim3 grid((unsigned)(p.T * p.hblocks), (unsigned)max_splits);
-  if (mtiles == 1)
-    hipLaunchKernelGGL(decode_kernel<1>, grid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(decode_kernel<2>, grid, dim3(256), 0, stream, p);
+  const bool page16 = p.P % 16 == 0;
+  if (mtiles == 1) {
+    if (page16) hipLaunchKernelGGL((decode_kernel_h16<true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((decode_kernel_h16<false>), grid, dim3(256), 0, stream, p);
+  } else {
+    if (page16) hipLaunchKernelGGL((decode_kernel<2, kStages, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((decode_kernel<2, kStages, false>), grid, dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
