@@ -150,6 +150,7 @@ mla_status mla_decode_partial(
   p.q_nope = (const uint16_t*)q_nope; p.qn_st = qn_stride_t; p.qn_sh = qn_stride_h;
   p.q_pe = (const uint16_t*)q_pe; p.qp_st = qp_stride_t; p.qp_sh = qp_stride_h;
   p.kv = (const uint16_t*)kv_cache; p.kv_bs = kv_block_stride; p.P = page_size;
+  p.page_shift = (page_size & (page_size - 1)) == 0 ? __builtin_ctz((unsigned)page_size) : -1;
   p.bt = block_table; p.bt_stride = bt_stride;
   p.seq_lens = seq_lens; p.qsl = query_start_loc;
   p.B = B; p.T = T; p.H = H; p.W = cp_world; p.r = cp_rank;

@@ -568,16 +568,20 @@ __global__ __launch_bounds__(256, 2) void decode_kernel_h16(const DecodeParams a
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring);
 
   // Stage layout: byte o of the 18 KiB stage is row o / 1152, 16-byte chunk
-  // c = (o % 1152) / 16, holding chunk c ^ (row & 7) of that cache row.  Block b
-  // (1 KiB) is written by one load: lane l -> bytes 1024b + 16l .. +16; this
-  // wave issues blocks b = 9*half + i.
+  // c = (o % 1152) / 16, holding chunk c ^ (row & 7) of that cache row (rows
+  // start on the same LDS bank, so eight consecutive rows must use eight
+  // different chunks).  Block b (1 KiB) is written by one load: lane l -> bytes
+  // 1024b + 16l .. +16; this wave issues blocks b = 9*half + i, with the byte
+  // offsets below.
   auto lane_row = [&](int b) { return (1024 * b + 16 * lane) / kRowBytes; };
-  auto lane_off = [&](int b) {
-    const int o = 1024 * b + 16 * lane;
+  uint32_t doff[kPHalfBlocks];
+#pragma unroll
+  for (int i2 = 0; i2 < kPHalfBlocks; ++i2) {
+    const int o = 1024 * (kPHalfBlocks * half + i2) + 16 * lane;
     const int row = o / kRowBytes;
     const int cpos = (o - row * kRowBytes) >> 4;
-    return (uint32_t)(row * kRowBytes + ((cpos ^ (row & 7)) << 4));
-  };
+    doff[i2] = (uint32_t)(row * kRowBytes + ((cpos ^ (row & 7)) << 4));
+  }
   // Issue this wave's half of the pair's stage for step i into ring slot `slot`.
   // Keys at or past j_end (a ragged or empty trailing stage) are clamped to key
   // j_end - 1 -- a real cached row, masked to probability 0 -- so every path
@@ -587,14 +591,12 @@ __global__ __launch_bounds__(256, 2) void decode_kernel_h16(const DecodeParams a
     const uint32_t ldst = ring_lds + slot * kPStageBytes;
     if (kPage16 && j0 + kPStep <= j_end) {
       // page_size % 16 == 0: the stage's 16 rows are consecutive slots of one page.
-      const int pg = j0 / a.P;
+      const int pg = a.page_shift >= 0 ? j0 >> a.page_shift : j0 / a.P;
       const int blk = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pg];
       const uint8_t* base = kv_bytes + ((int64_t)blk * a.kv_bs + (int64_t)(j0 - pg * a.P) * kRow) * 2;
 #pragma unroll
-      for (int i2 = 0; i2 < kPHalfBlocks; ++i2) {
-        const int b = kPHalfBlocks * half + i2;
-        dma_16B_to_lds_sbase(ldst + 1024 * b, lane_off(b), base);
-      }
+      for (int i2 = 0; i2 < kPHalfBlocks; ++i2)
+        dma_16B_to_lds_sbase(ldst + 1024 * (kPHalfBlocks * half + i2), doff[i2], base);
     } else {
 #pragma unroll
       for (int i2 = 0; i2 < kPHalfBlocks; ++i2) {
@@ -608,12 +610,28 @@ __global__ __launch_bounds__(256, 2) void decode_kernel_h16(const DecodeParams a
         const int bb = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pb2];
         const int pg = j / a.P;                    // pa or pb2
         const int64_t rbase = (int64_t)(pg == pa ? ba : bb) * a.kv_bs + (int64_t)(j - pg * a.P) * kRow;
-        dma_16B_to_lds(kv_bytes + rbase * 2 + (lane_off(b) - row * kRowBytes),
+        dma_16B_to_lds(kv_bytes + rbase * 2 + (doff[i2] - row * kRowBytes),
                        ring + slot * kPStageBytes + 1024 * b);
       }
     }
   };
-  auto chunk_addr = [&](int r, int c) { return r * kRowBytes + ((c ^ (r & 7)) << 4); };
+  // Per-lane read bases, so that every read below is a base plus an immediate.
+  // Scores: lane (key lr, group g) reads chunk 4s + g of row lr; the swizzle only
+  // flips its low three bits, which depend on s through s & 1:
+  //   byte = lr*1152 + 128*(s >> 1) + 16*((4*(s & 1) + g) ^ (lr & 7)).
+  // PV: source lane (key vr, dims 4(lr & 3) ..) reads 8 bytes of chunk
+  // 32*half + 2dt + x, x = (lr & 3) >> 1, at byte 8(lr & 1); its low three bits
+  // depend on dt through dt & 3:
+  //   byte = vr*1152 + 512*half + 128*(dt >> 2) + 16*((2*(dt & 3) + x) ^ (vr & 7)) + 8(lr & 1).
+  const int k7 = lr & 7;
+  const uint32_t kbase0 = lr * kRowBytes + 16 * (g ^ k7);
+  const uint32_t kbase1 = lr * kRowBytes + 16 * ((4 + g) ^ k7);
+  const int vr = 4 * g + (lr >> 2);
+  const int v7 = vr & 7;
+  const int vx = (lr & 3) >> 1;
+  uint32_t vbase[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) vbase[m] = vr * kRowBytes + 512 * half + 16 * ((2 * m + vx) ^ v7) + 8 * (lr & 1);
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[16];                    // O^T tiles over this wave's 256 dims
@@ -623,12 +641,17 @@ __global__ __launch_bounds__(256, 2) void decode_kernel_h16(const DecodeParams a
   issue(0, 0);
   for (int i = 0; i < n_steps; ++i) {
     const int slot = i & 1;
-    // This wave's loads of step i have landed (the only ones outstanding); the
-    // barrier makes the partner's half visible and tells that every wave is
-    // done with step i-1, whose slot the next issue reuses.
-    __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+    // Step i+1's loads go out before step i is awaited (every wave finished
+    // step i-1, the previous user of that slot, at the end-of-step barrier), so
+    // two stages are in flight while this wave waits for its half of step i;
+    // the barrier then makes the partner's half visible.
+    if (i + 1 < n_steps) {
+      issue(i + 1, slot ^ 1);
+      __builtin_amdgcn_s_waitcnt(MLA_VMCNT(kPHalfBlocks));
+    } else {
+      __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+    }
     __builtin_amdgcn_s_barrier();
-    if (i + 1 < n_steps) issue(i + 1, slot ^ 1);
     const uint8_t* sb = ring + slot * kPStageBytes;
     const int j0 = j_begin + 2 * kPStep * i + kPStep * pair;
 
@@ -636,7 +659,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel_h16(const DecodeParams a
     // accumulation chains; all 18 key operands are read before the MFMAs.
     bf16x8 kk[18];
 #pragma unroll
-    for (int s = 0; s < 18; ++s) kk[s] = *(const bf16x8*)(sb + chunk_addr(lr, 4 * s + g));
+    for (int s = 0; s < 18; ++s) kk[s] = *(const bf16x8*)(sb + ((s & 1) ? kbase1 : kbase0) + 128 * (s >> 1));
     f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 18; s += 2) {
@@ -676,18 +699,17 @@ __global__ __launch_bounds__(256, 2) void decode_kernel_h16(const DecodeParams a
     // with keys 16..31 zero.  The transposed read gives lane (dim lr, group g)
     // keys 4g .. 4g+3 when source lane lr points at key 4g + (lr >> 2), dims
     // 16dt + 4(lr & 3) .. +4.
-    const int vr = 4 * g + (lr >> 2);
     s16x4 vt[16];
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt) {
-      const int c = 32 * half + 2 * dt + ((lr & 3) >> 1);
-      vt[dt] = lds_read_tr16_at(sb + chunk_addr(vr, c) + 8 * (lr & 1));
-    }
+    for (int dt = 0; dt < 16; ++dt)
+      vt[dt] = lds_read_tr16_at(sb + vbase[dt & 3] + 128 * (dt >> 2));
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) {
       const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vt[dt], s16x4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7));
       o[dt] = mfma_16x16x32(va, pb, o[dt]);
     }
+    // Every wave is done reading this slot before anyone refills it.
+    __builtin_amdgcn_s_barrier();
   }
   l_run = col_sum(l_run);
 

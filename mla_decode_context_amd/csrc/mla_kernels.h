@@ -11,6 +11,7 @@ struct DecodeParams {
   const uint16_t* q_pe;    int64_t qp_st, qp_sh;
   const uint16_t* kv;      int64_t kv_bs;          // block stride in elements
   int32_t P;                                        // page size (tokens per block)
+  int32_t page_shift;                               // log2(P) if P is a power of two, else -1
   const int32_t* bt;       int32_t bt_stride;
   const int32_t* seq_lens;
   const int32_t* qsl;
