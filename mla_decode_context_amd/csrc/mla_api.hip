@@ -32,14 +32,18 @@ constexpr int kStep = 32;          // keys per inner step of the decode kernel
 constexpr int kTargetGroups = 512;   // busy workgroups wanted per launch (2 per CU)
 constexpr int kMinChunk = 1024;    // auto splits never go below this many keys
 constexpr int kMaxGridY = 65535;
+// Balanced schedule of the 16-head kernel: one workgroup per CU of the
+// 256-CU part (the kernel's LDS allows one per CU).
+constexpr int kWorkers = 256;
 
-// Launch plan: heads per workgroup and keys per split.  Depends only on host
-// integers so that the workspace size can be computed in advance.
+// Launch plan: heads per workgroup and how keys are split.  Depends only on
+// host integers so that the workspace size can be computed in advance.
 struct Plan {
   int mtiles;       // 16-head tiles per workgroup (1 or 2)
   int hblocks;      // workgroups per token along heads
-  int chunk;        // keys per split
-  int max_splits;   // grid extent along splits
+  int chunk;        // keys per split (fixed-split grid)
+  int max_splits;   // grid extent along splits (fixed-split grid)
+  int workers;      // > 0: balanced schedule over this many workgroups
 };
 
 Plan make_plan(int T, int H, int max_seq_len, int W, int num_splits, bool split_ok) {
@@ -47,11 +51,14 @@ Plan make_plan(int T, int H, int max_seq_len, int W, int num_splits, bool split_
   const int ht = (H + 15) / 16;
   p.mtiles = ht >= 2 ? 2 : 1;
   p.hblocks = (int)ceil_div(ht, p.mtiles);
+  p.workers = 0;
   // A row's visible local keys never exceed ceil(max_seq_len / W).
   const int64_t lmax = max_seq_len > 0 ? ceil_div(max_seq_len, W) : 0;
   const int64_t lr = round_up(lmax > 0 ? lmax : 1, kStep);
   int64_t chunk = lr;
-  if (split_ok && num_splits != 1 && lmax > 0) {
+  if (split_ok && num_splits == 0 && p.mtiles == 1) {
+    p.workers = kWorkers;
+  } else if (split_ok && num_splits != 1 && lmax > 0) {
     if (num_splits > 1) {
       chunk = round_up(ceil_div(lmax, num_splits), kStep);
     } else {
@@ -72,15 +79,21 @@ Plan make_plan(int T, int H, int max_seq_len, int W, int num_splits, bool split_
 
 // Workspace layout (offsets from the 256-byte aligned base):
 //   int32 counters[T * hblocks]          split tickets, zero between calls
-//   fp32  lse[max_splits][T][H]          split LSEs
-//   fp32  o[max_splits][T][H][512]       normalised split partials
+//   int4  row_desc[T]                    balanced schedule only: pieces per row
+//   fp32  lse[slots][H]                  split LSEs
+//   fp32  o[slots][H][512]               normalised split partials
+// with slots = max_splits * T (fixed splits; slot split*T + t) or 2 * workers
+// (balanced schedule; two per workgroup).
+bool uses_workspace(const Plan& p) { return p.workers > 0 || p.max_splits > 1; }
+int64_t slots_of(const Plan& p, int T) { return p.workers > 0 ? 2 * (int64_t)p.workers : (int64_t)p.max_splits * T; }
 size_t counters_bytes(const Plan& p, int T) { return (size_t)round_up((int64_t)T * p.hblocks * 4, 256); }
-size_t lse_bytes(const Plan& p, int T, int H) { return (size_t)round_up((int64_t)p.max_splits * T * H * 4, 256); }
+size_t desc_bytes(const Plan& p, int T) { return p.workers > 0 ? (size_t)round_up((int64_t)T * 16, 256) : 0; }
+size_t lse_bytes(const Plan& p, int T, int H) { return (size_t)round_up(slots_of(p, T) * H * 4, 256); }
 
 size_t workspace_bytes_for(const Plan& p, int T, int H) {
-  if (p.max_splits <= 1) return 0;
-  const size_t rows = (size_t)p.max_splits * T * H;
-  return counters_bytes(p, T) + lse_bytes(p, T, H) + rows * MLA_D_LATENT * sizeof(float) + 256;
+  if (!uses_workspace(p)) return 0;
+  const size_t rows = (size_t)slots_of(p, T) * H;
+  return counters_bytes(p, T) + desc_bytes(p, T) + lse_bytes(p, T, H) + rows * MLA_D_LATENT * sizeof(float) + 256;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -157,14 +170,17 @@ mla_status mla_decode_partial(
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   p.chunk = plan.chunk; p.hblocks = plan.hblocks; p.max_splits = plan.max_splits;
   p.out = (uint16_t*)out; p.lse = lse;
-  p.ws_o = nullptr; p.ws_lse = nullptr; p.counters = nullptr;
-  if (plan.max_splits > 1) {
+  p.ws_o = nullptr; p.ws_lse = nullptr; p.counters = nullptr; p.row_desc = nullptr;
+  if (uses_workspace(plan)) {
     char* base = (char*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+    const size_t c_end = counters_bytes(plan, T);
+    const size_t d_end = c_end + desc_bytes(plan, T);
     p.counters = (int32_t*)base;
-    p.ws_lse = (float*)(base + counters_bytes(plan, T));
-    p.ws_o = (float*)(base + counters_bytes(plan, T) + lse_bytes(plan, T, H));
+    p.row_desc = plan.workers > 0 ? (int4*)(base + c_end) : nullptr;
+    p.ws_lse = (float*)(base + d_end);
+    p.ws_o = (float*)(base + d_end + lse_bytes(plan, T, H));
   }
-  hipError_t e = mla::launch_decode(p, plan.mtiles, plan.max_splits, (hipStream_t)hip_stream);
+  hipError_t e = mla::launch_decode(p, plan.mtiles, plan.max_splits, plan.workers, (hipStream_t)hip_stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

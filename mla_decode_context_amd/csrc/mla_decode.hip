@@ -94,69 +94,89 @@ __device__ __forceinline__ int num_splits_of(int L, int chunk, int max_splits) {
   return n < max_splits ? n : max_splits;
 }
 
-// Split rows: the last of the row's splits to finish merges all partials.
-// Every split has already written its normalised partial and LSE for heads
+// Where the partials of a split row live: piece k of the row (k = 0..np-1)
+// stores its heads at workspace row base + k*stride (+ adj0 for k = 0); a
+// workspace row holds H heads of 512 fp32 plus H LSEs.
+struct SlotMap {
+  int base, stride, adj0;
+  __device__ __forceinline__ int64_t row(int k) const {
+    return (int64_t)base + (int64_t)k * stride + (k == 0 ? adj0 : 0);
+  }
+};
+
+// Split rows: the last of the row's pieces to finish merges all partials.
+// Every piece has already written its normalised partial and LSE for heads
 // h0 .. h0+nheads-1 of token t with device-scope stores.  Partials travel with
 // device-scope stores and loads, which write through to and read from the point
 // where all XCDs see the same memory, so publishing needs only the wait for this
 // workgroup's stores before its ticket -- no write-back of the whole L2 that a
 // device-scope fence would cost.  The holder of the last ticket merges (exact
-// LSE-weighted combine) and puts the counter back to zero for the next call.
+// LSE-weighted combine, pieces in index order whatever the arrival order) and
+// puts the counter back to zero for the next call.
 __device__ __forceinline__ void ticket_and_merge(const DecodeParams& a, int t, int h0, int nheads,
-                                                 int nsplit) {
+                                                 int nsplit, SlotMap sm, int counter) {
   __shared__ int s_last;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const int ticket = __hip_atomic_fetch_add(a.counters + blockIdx.x, 1, __ATOMIC_RELAXED,
+    const int ticket = __hip_atomic_fetch_add(a.counters + counter, 1, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
     s_last = ticket == nsplit - 1;
   }
   __syncthreads();
   if (!s_last) return;
   // Merge: thread (head hl = tid / 16, dims 32*(tid % 16) .. +32) for each group
-  // of 16 heads in turn; two splits' loads are in flight at once.
-  const size_t plane = (size_t)a.T * a.H;
+  // of 16 heads in turn.  Online LSE combine over the pieces in index order,
+  // four pieces' LSEs and partials loaded together per round (each round is a
+  // trip to memory: partials are read at device scope).
   const int hl = threadIdx.x >> 4;          // 0..15
   const int d0 = (threadIdx.x & 15) * 32;
   for (int hg = 0; hg < nheads; hg += 16) {
     const int h = h0 + hg + hl;
     if (h < a.H) {
-      const size_t row = (size_t)t * a.H + h;
-      float mx = -INFINITY;
-      for (int sp = 0; sp < nsplit; ++sp) mx = fmaxf(mx, load_device(a.ws_lse + sp * plane + row));
-      float sum = 0.f;
-      for (int sp = 0; sp < nsplit; ++sp) sum += fast_exp2((load_device(a.ws_lse + sp * plane + row) - mx) * kLog2e);
-      const float lse_tot = mx + fast_log2(sum) * kLn2;
+      float m = -INFINITY, ssum = 0.f;
       f32x4 acc[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int sp0 = 0; sp0 < nsplit; sp0 += 2) {
-        f32x4 x[2][8];
-        float wgt[2];
+      for (int sp0 = 0; sp0 < nsplit; sp0 += 4) {
+        float l[4];
+        f32x4 x[4][8];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < 4; ++u) {
           const int sp = min(sp0 + u, nsplit - 1);
-          wgt[u] = sp0 + u < nsplit ? fast_exp2((load_device(a.ws_lse + sp * plane + row) - lse_tot) * kLog2e) : 0.f;
-          const float* src = a.ws_o + (sp * plane + row) * kLatent + d0;
+          const int64_t srow = sm.row(sp) * a.H + h;
+          l[u] = load_device(a.ws_lse + srow);
+          const float* src = a.ws_o + srow * kLatent + d0;
 #pragma unroll
           for (int k = 0; k < 8; ++k) x[u][k] = load_device4(src + 4 * k);
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < 4; ++u) {
+          const float mn = fmaxf(m, l[u]);
+          if (sp0 + u < nsplit && mn > -INFINITY) {
+            const float c_old = m == -INFINITY ? 0.f : fast_exp2((m - mn) * kLog2e);
+            const float c_new = fast_exp2((l[u] - mn) * kLog2e);
 #pragma unroll
-          for (int k = 0; k < 8; ++k) acc[k] += wgt[u] * x[u][k];
+            for (int k = 0; k < 8; ++k) acc[k] = acc[k] * c_old + x[u][k] * c_new;
+            ssum = ssum * c_old + c_new;
+            m = mn;
+          }
+        }
       }
+      const float inv = ssum > 0.f ? 1.f / ssum : 0.f;
+      const float lse_tot = ssum > 0.f ? m + fast_log2(ssum) * kLn2 : -INFINITY;
+      const size_t row = (size_t)t * a.H + h;
       uint16_t* op = a.out + row * kLatent + d0;
 #pragma unroll
       for (int k = 0; k < 8; k += 2)
-        *(u32x4*)(op + 4 * k) = u32x4{pack_bf16x2(acc[k][0], acc[k][1]), pack_bf16x2(acc[k][2], acc[k][3]),
-                                      pack_bf16x2(acc[k + 1][0], acc[k + 1][1]),
-                                      pack_bf16x2(acc[k + 1][2], acc[k + 1][3])};
+        *(u32x4*)(op + 4 * k) = u32x4{pack_bf16x2(acc[k][0] * inv, acc[k][1] * inv),
+                                      pack_bf16x2(acc[k][2] * inv, acc[k][3] * inv),
+                                      pack_bf16x2(acc[k + 1][0] * inv, acc[k + 1][1] * inv),
+                                      pack_bf16x2(acc[k + 1][2] * inv, acc[k + 1][3] * inv)};
       if ((threadIdx.x & 15) == 0) a.lse[row] = lse_tot;
     }
   }
-  if (threadIdx.x == 0) a.counters[blockIdx.x] = 0;
+  if (threadIdx.x == 0) a.counters[counter] = 0;
 }
 
 // vmcnt(n) operand of s_waitcnt (expcnt and lgkmcnt left at their maxima).
@@ -442,7 +462,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams a) {
   }
   if (nsplit == 1) return;
 
-  ticket_and_merge(a, t, h0, 16 * MT, nsplit);
+  ticket_and_merge(a, t, h0, 16 * MT, nsplit, SlotMap{t, a.T, 0}, (int)blockIdx.x);
 }
 
 __global__ __launch_bounds__(256) void local_seqlens_kernel(const int32_t* seq_lens, const int32_t* qsl,
@@ -457,21 +477,26 @@ __global__ __launch_bounds__(256) void local_seqlens_kernel(const int32_t* seq_l
 // ---------------------------------------------------------------------------
 // Decode for up to 16 heads (one 16-head MFMA tile).
 //
-// With 16 heads the arithmetic is light (about 30 flop per cache byte) and the
-// kernel must keep HBM busy, so it is built for occupancy: 72 KiB of LDS and at
-// most 256 registers per lane, so two workgroups share a CU.  The four waves
-// form two pairs; each step, pair p takes a 16-key stage (keys 32i + 16p of
-// the split).  Both waves of a pair compute the full 576-wide scores of their
-// stage (duplicated; there is MFMA time to spare), run the same online softmax,
-// and split PV: wave half 0 owns latent dims 0..255, half 1 dims 256..511.  The
-// stage's rows land in the pair's 2-slot LDS ring straight from HBM (each wave
-// issues half of the stage's 18 direct-to-LDS loads).  After the loop the two
-// pairs' (max, sum, unnormalised output) states are merged through LDS.
+// With 16 heads the arithmetic is light (about 30 flop per cache byte): the
+// kernel exists to keep HBM streaming.  Each of the four waves streams its own
+// 16-key stages -- stage s of a piece belongs to wave s mod 4, so the waves
+// together sweep 64 consecutive keys (72 KiB) at a time -- into a private
+// two-slot LDS ring with direct-to-LDS loads, and computes everything for its
+// stages alone: the 576-wide scores, the online softmax and PV over all 512
+// latent dims.  The next stage is issued before the current one is awaited,
+// and a wave waits only for its own loads: there is no barrier in the loop, so
+// one wave's slow load never stalls the others.  At the end of a piece the
+// four (max, sum, unnormalised output) states are merged through LDS.
+// 144 KiB of LDS: one workgroup per CU.
 // ---------------------------------------------------------------------------
-constexpr int kPStep = 16;                             // keys per stage
-constexpr int kPStageBytes = kPStep * kRowBytes;       // 18 KiB
-constexpr int kPBlocks = kPStageBytes / 1024;          // 18 load instructions per stage
-constexpr int kPHalfBlocks = kPBlocks / 2;             // issued by each wave of the pair
+constexpr int kWStage = 16;                             // keys per wave stage
+constexpr int kWStageBytes = kWStage * kRowBytes;       // 18 KiB
+constexpr int kWBlocks = kWStageBytes / 1024;           // 18 load instructions per stage
+constexpr int kWRing = 2;                               // slots per wave
+constexpr int kWLdsBytes = 4 * kWRing * kWStageBytes;   // 144 KiB
+
+// s_waitcnt operand: lgkmcnt(0), vmcnt and expcnt left at their maxima.
+#define MLA_LGKMCNT0 (15 | (3 << 14) | (7 << 4))
 
 // Direct-to-LDS load with a wave-uniform 64-bit base (SGPRs) and a per-lane
 // 32-bit byte offset; see dma_16B_to_lds.
@@ -504,40 +529,33 @@ __device__ __forceinline__ float col_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <bool kPage16>
-__global__ __launch_bounds__(256, 2) void decode_kernel_h16(const DecodeParams a) {
-  // Two pair rings of two 18 KiB slots; reused for the cross-pair merge.
-  __shared__ __attribute__((aligned(16))) uint8_t lds_block[2 * 2 * kPStageBytes];
+// Writes out = 0 and lse = -inf for heads 0..15 of a row that sees no key.
+__device__ __forceinline__ void write_empty_row(const DecodeParams& a, int t) {
+  for (int idx = threadIdx.x; idx < 16 * 64; idx += 256) {
+    const int h = idx >> 6;
+    const int c = idx & 63;
+    if (h < a.H) {
+      *(u32x4*)(a.out + ((size_t)t * a.H + h) * kLatent + c * 8) = u32x4{0u, 0u, 0u, 0u};
+      if (c == 0) a.lse[(size_t)t * a.H + h] = -INFINITY;
+    }
+  }
+}
 
+// One piece of work: local keys [j_begin, j_end) (0 < j_end - j_begin,
+// j_begin a multiple of 16) of row t (request b), heads 0..15.  With nsplit == 1
+// the piece is the whole row and writes out / lse; otherwise it writes its
+// partial to workspace row my_slot and takes part in the row's ticketed merge
+// (counter `counter`, slots `sm`).
+template <bool kPage16, bool kDeferMerge>
+__device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_block, int t, int b,
+                                          int j_begin, int j_end, int nsplit, int64_t my_slot, SlotMap sm,
+                                          int counter) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, kept in SGPRs
-  const int pair = w >> 1;
-  const int half = w & 1;
   const int lr = lane & 15;
   const int g = lane >> 4;
-
-  const int t = blockIdx.x;                 // one 16-head block per token
-  const int split = blockIdx.y;
-  const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r);
-  const int L = ri.L;
-  const int nsplit = num_splits_of(L, a.chunk, (int)gridDim.y);
-  if (split >= nsplit) return;
-
-  if (L == 0) {
-    // The row sees no key on this rank: out = 0, lse = -inf.
-    for (int idx = threadIdx.x; idx < 16 * 64; idx += 256) {
-      const int h = idx >> 6;
-      const int c = idx & 63;
-      if (h < a.H) {
-        *(u32x4*)(a.out + ((size_t)t * a.H + h) * kLatent + c * 8) = u32x4{0u, 0u, 0u, 0u};
-        if (c == 0) a.lse[(size_t)t * a.H + h] = -INFINITY;
-      }
-    }
-    return;
-  }
-  const int j_begin = split * a.chunk;
-  const int j_end = split == nsplit - 1 ? L : j_begin + a.chunk;
-  const int n_steps = (j_end - j_begin + 2 * kPStep - 1) / (2 * kPStep);
+  const int n_stages = (j_end - j_begin + kWStage - 1) / kWStage;
+  const int my_n = n_stages > w ? (n_stages - w + 3) / 4 : 0;       // stages w, w+4, w+8, ...
 
   // Query operand (B of S^T = K Q^T) over all 576 dims: lane (head lr, group g)
   // holds dims 32s + 8g .. +8 for k-step s (s < 16: q_nope, s = 16, 17: q_pe).
@@ -559,50 +577,45 @@ __global__ __launch_bounds__(256, 2) void decode_kernel_h16(const DecodeParams a
       q[16 + s] = __builtin_bit_cast(bf16x8, ok ? u32x4{v0[0], v0[1], v1[0], v1[1]} : u32x4{0u, 0u, 0u, 0u});
     }
   }
-  __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
 
-  const int32_t* bt_row = a.bt + (int64_t)ri.b * a.bt_stride;
+  const int32_t* bt_row = a.bt + (int64_t)b * a.bt_stride;
   const uint8_t* kv_bytes = (const uint8_t*)a.kv;
-  uint8_t* ring = lds_block + pair * 2 * kPStageBytes;
+  uint8_t* ring = lds_block + w * kWRing * kWStageBytes;
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring);
 
   // Stage layout: byte o of the 18 KiB stage is row o / 1152, 16-byte chunk
   // c = (o % 1152) / 16, holding chunk c ^ (row & 7) of that cache row (rows
   // start on the same LDS bank, so eight consecutive rows must use eight
-  // different chunks).  Block b (1 KiB) is written by one load: lane l -> bytes
-  // 1024b + 16l .. +16; this wave issues blocks b = 9*half + i, with the byte
-  // offsets below.
-  auto lane_row = [&](int b) { return (1024 * b + 16 * lane) / kRowBytes; };
-  uint32_t doff[kPHalfBlocks];
+  // different chunks).  Block i (1 KiB) is written by one load: lane l -> bytes
+  // 1024i + 16l .. +16, fetched from the byte offset below within the stage's
+  // 16 consecutive cache rows.
+  uint32_t doff[kWBlocks];
 #pragma unroll
-  for (int i2 = 0; i2 < kPHalfBlocks; ++i2) {
-    const int o = 1024 * (kPHalfBlocks * half + i2) + 16 * lane;
+  for (int i2 = 0; i2 < kWBlocks; ++i2) {
+    const int o = 1024 * i2 + 16 * lane;
     const int row = o / kRowBytes;
     const int cpos = (o - row * kRowBytes) >> 4;
     doff[i2] = (uint32_t)(row * kRowBytes + ((cpos ^ (row & 7)) << 4));
   }
-  // Issue this wave's half of the pair's stage for step i into ring slot `slot`.
-  // Keys at or past j_end (a ragged or empty trailing stage) are clamped to key
-  // j_end - 1 -- a real cached row, masked to probability 0 -- so every path
-  // issues exactly kPHalfBlocks loads.
-  auto issue = [&](int i, int slot) {
-    const int j0 = j_begin + 2 * kPStep * i + kPStep * pair;
-    const uint32_t ldst = ring_lds + slot * kPStageBytes;
-    if (kPage16 && j0 + kPStep <= j_end) {
+  // Issue piece stage st into ring slot `slot`.  Keys at or past j_end (the
+  // ragged last stage) are clamped to key j_end - 1 -- a real cached row, masked
+  // to probability 0 -- so every path issues exactly kWBlocks loads.
+  auto issue = [&](int st, int slot) {
+    const int j0 = j_begin + kWStage * st;
+    const uint32_t ldst = ring_lds + slot * kWStageBytes;
+    if (kPage16 && j0 + kWStage <= j_end) {
       // page_size % 16 == 0: the stage's 16 rows are consecutive slots of one page.
       const int pg = a.page_shift >= 0 ? j0 >> a.page_shift : j0 / a.P;
       const int blk = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pg];
       const uint8_t* base = kv_bytes + ((int64_t)blk * a.kv_bs + (int64_t)(j0 - pg * a.P) * kRow) * 2;
 #pragma unroll
-      for (int i2 = 0; i2 < kPHalfBlocks; ++i2)
-        dma_16B_to_lds_sbase(ldst + 1024 * (kPHalfBlocks * half + i2), doff[i2], base);
+      for (int i2 = 0; i2 < kWBlocks; ++i2) dma_16B_to_lds_sbase(ldst + 1024 * i2, doff[i2], base);
     } else {
 #pragma unroll
-      for (int i2 = 0; i2 < kPHalfBlocks; ++i2) {
-        const int b = kPHalfBlocks * half + i2;
-        const int row = lane_row(b);
-        const int ra = (1024 * b) / kRowBytes;     // the block spans rows ra and ra + 1
+      for (int i2 = 0; i2 < kWBlocks; ++i2) {
+        const int row = (1024 * i2 + 16 * lane) / kRowBytes;
+        const int ra = (1024 * i2) / kRowBytes;     // the block spans rows ra and ra + 1
         const int j = min(j0 + row, j_end - 1);
         const int pa = __builtin_amdgcn_readfirstlane(min(j0 + ra, j_end - 1) / a.P);
         const int pb2 = __builtin_amdgcn_readfirstlane(min(j0 + ra + 1, j_end - 1) / a.P);
@@ -610,8 +623,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel_h16(const DecodeParams a
         const int bb = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pb2];
         const int pg = j / a.P;                    // pa or pb2
         const int64_t rbase = (int64_t)(pg == pa ? ba : bb) * a.kv_bs + (int64_t)(j - pg * a.P) * kRow;
-        dma_16B_to_lds(kv_bytes + rbase * 2 + (doff[i2] - row * kRowBytes),
-                       ring + slot * kPStageBytes + 1024 * b);
+        dma_16B_to_lds(kv_bytes + rbase * 2 + (doff[i2] - row * kRowBytes), ring + slot * kWStageBytes + 1024 * i2);
       }
     }
   };
@@ -619,10 +631,10 @@ __global__ __launch_bounds__(256, 2) void decode_kernel_h16(const DecodeParams a
   // Scores: lane (key lr, group g) reads chunk 4s + g of row lr; the swizzle only
   // flips its low three bits, which depend on s through s & 1:
   //   byte = lr*1152 + 128*(s >> 1) + 16*((4*(s & 1) + g) ^ (lr & 7)).
-  // PV: source lane (key vr, dims 4(lr & 3) ..) reads 8 bytes of chunk
-  // 32*half + 2dt + x, x = (lr & 3) >> 1, at byte 8(lr & 1); its low three bits
-  // depend on dt through dt & 3:
-  //   byte = vr*1152 + 512*half + 128*(dt >> 2) + 16*((2*(dt & 3) + x) ^ (vr & 7)) + 8(lr & 1).
+  // PV: source lane (key vr, dims 16dt + 4(lr & 3) ..) reads 8 bytes of chunk
+  // 2dt + x, x = (lr & 3) >> 1, at byte 8(lr & 1); its low three bits depend on
+  // dt through dt & 3:
+  //   byte = vr*1152 + 128*(dt >> 2) + 16*((2*(dt & 3) + x) ^ (vr & 7)) + 8(lr & 1).
   const int k7 = lr & 7;
   const uint32_t kbase0 = lr * kRowBytes + 16 * (g ^ k7);
   const uint32_t kbase1 = lr * kRowBytes + 16 * ((4 + g) ^ k7);
@@ -631,46 +643,54 @@ __global__ __launch_bounds__(256, 2) void decode_kernel_h16(const DecodeParams a
   const int vx = (lr & 3) >> 1;
   uint32_t vbase[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) vbase[m] = vr * kRowBytes + 512 * half + 16 * ((2 * m + vx) ^ v7) + 8 * (lr & 1);
+  for (int m = 0; m < 4; ++m) vbase[m] = vr * kRowBytes + 16 * ((2 * m + vx) ^ v7) + 8 * (lr & 1);
 
   float m_run = -INFINITY, l_run = 0.f;
-  f32x4 o[16];                    // O^T tiles over this wave's 256 dims
+  f32x4 o[32];                    // O^T tiles over all 512 latent dims
 #pragma unroll
-  for (int dt = 0; dt < 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < 32; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  issue(0, 0);
-  for (int i = 0; i < n_steps; ++i) {
-    const int slot = i & 1;
-    // Step i+1's loads go out before step i is awaited (every wave finished
-    // step i-1, the previous user of that slot, at the end-of-step barrier), so
-    // two stages are in flight while this wave waits for its half of step i;
-    // the barrier then makes the partner's half visible.
-    if (i + 1 < n_steps) {
-      issue(i + 1, slot ^ 1);
-      __builtin_amdgcn_s_waitcnt(MLA_VMCNT(kPHalfBlocks));
+  // The first stage's loads travel together with the query loads.
+  if (my_n > 0) issue(w, 0);
+  __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+  for (int k = 0; k < my_n; ++k) {
+    const int slot = k & 1;
+    // The next stage goes out before this one is awaited.  Its slot was last
+    // read by the previous stage, whose LDS reads have all returned
+    // (lgkmcnt(0)); only this wave touches its ring, so no barrier is needed.
+    if (k + 1 < my_n) {
+      __builtin_amdgcn_s_waitcnt(MLA_LGKMCNT0);
+      issue(w + 4 * (k + 1), slot ^ 1);
+      __builtin_amdgcn_s_waitcnt(MLA_VMCNT(kWBlocks));
     } else {
       __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
     }
-    __builtin_amdgcn_s_barrier();
-    const uint8_t* sb = ring + slot * kPStageBytes;
-    const int j0 = j_begin + 2 * kPStep * i + kPStep * pair;
+    const uint8_t* sb = ring + slot * kWStageBytes;
+    const int j0 = j_begin + kWStage * (w + 4 * k);
 
     // S^T[key][head] over 576 dims (A = keys: lane key lr, dims 32s + 8g), two
-    // accumulation chains; all 18 key operands are read before the MFMAs.
-    bf16x8 kk[18];
-#pragma unroll
-    for (int s = 0; s < 18; ++s) kk[s] = *(const bf16x8*)(sb + ((s & 1) ? kbase1 : kbase0) + 128 * (s >> 1));
+    // accumulation chains.
     f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 18; s += 2) {
-      s0 = mfma_16x16x32(kk[s], q[s], s0);
-      s1 = mfma_16x16x32(kk[s + 1], q[s + 1], s1);
+    for (int h2 = 0; h2 < 2; ++h2) {
+      bf16x8 kk[9];
+#pragma unroll
+      for (int u = 0; u < 9; ++u) {
+        const int s = 9 * h2 + u;
+        kk[u] = *(const bf16x8*)(sb + ((s & 1) ? kbase1 : kbase0) + 128 * (s >> 1));
+      }
+#pragma unroll
+      for (int u = 0; u < 9; ++u) {
+        const int s = 9 * h2 + u;
+        if (s & 1) s1 = mfma_16x16x32(kk[u], q[s], s1);
+        else s0 = mfma_16x16x32(kk[u], q[s], s0);
+      }
     }
     const f32x4 sc = s0 + s1;
 
-    // Online softmax (base 2).  Lane (head lr, group g) holds keys 4g + r.  A
-    // stage wholly past j_end (possible for pair 1 in the last step) changes
-    // nothing: its keys are masked and a row max of -inf is kept out of exp2.
+    // Online softmax (base 2).  Lane (head lr, group g) holds keys 4g + r; keys
+    // at or past j_end are masked.  The stage always holds a visible key, but a
+    // row max of -inf is still kept out of exp2.
     float v[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) v[r] = (j0 + 4 * g + r < j_end) ? sc[r] * a.scale_log2 : -INFINITY;
@@ -692,85 +712,298 @@ __global__ __launch_bounds__(256, 2) void decode_kernel_h16(const DecodeParams a
     // Rescale only when some head's running max moved (once it settles, never).
     if (__builtin_amdgcn_read_exec() & __builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-      for (int dt = 0; dt < 16; ++dt) o[dt] *= alpha;
+      for (int dt = 0; dt < 32; ++dt) o[dt] *= alpha;
     }
 
-    // O^T[d][head] += V^T[d][key] P^T[key][head] over dims 256*half .. +256; K = 32
-    // with keys 16..31 zero.  The transposed read gives lane (dim lr, group g)
-    // keys 4g .. 4g+3 when source lane lr points at key 4g + (lr >> 2), dims
+    // O^T[d][head] += V^T[d][key] P^T[key][head] over all 512 dims; K = 32 with
+    // keys 16..31 zero.  The transposed read gives lane (dim lr, group g) keys
+    // 4g .. 4g+3 when source lane lr points at key 4g + (lr >> 2), dims
     // 16dt + 4(lr & 3) .. +4.
-    s16x4 vt[16];
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt)
-      vt[dt] = lds_read_tr16_at(sb + vbase[dt & 3] + 128 * (dt >> 2));
+    for (int d8 = 0; d8 < 4; ++d8) {
+      s16x4 vt[8];
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt) {
-      const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vt[dt], s16x4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[dt] = mfma_16x16x32(va, pb, o[dt]);
+      for (int u = 0; u < 8; ++u) {
+        const int dt = 8 * d8 + u;
+        vt[u] = lds_read_tr16_at(sb + vbase[dt & 3] + 128 * (dt >> 2));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int dt = 8 * d8 + u;
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vt[u], s16x4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[dt] = mfma_16x16x32(va, pb, o[dt]);
+      }
     }
-    // Every wave is done reading this slot before anyone refills it.
-    __builtin_amdgcn_s_barrier();
   }
   l_run = col_sum(l_run);
 
-  // Cross-pair merge: the pair-1 wave of each half stores its state, the pair-0
-  // wave of the same half merges it with its own and writes the result.
+  // Merge of the four waves' states: each stores its (max, sum, output) in LDS
+  // (the rings are free once every wave is past its loop), then wave w
+  // combines latent dims 128w .. 128w+127 and writes them.
   __syncthreads();
-  f32x4* ost = (f32x4*)lds_block;                              // [half][dt][lane]
-  float* mst = (float*)(lds_block + 2 * 16 * 64 * 16);         // [half][head] max
-  float* lst = mst + 32;                                       // [half][head] sum
-  if (pair == 1) {
+  f32x4* ost = (f32x4*)lds_block;                              // [wave][dt][lane]
+  float* mst = (float*)(lds_block + 4 * 32 * 64 * 16);         // [wave][head] max
+  float* lst = mst + 64;                                       // [wave][head] sum
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt) ost[(half * 16 + dt) * 64 + lane] = o[dt];
-    if (g == 0) {
-      mst[half * 16 + lr] = m_run;
-      lst[half * 16 + lr] = l_run;
-    }
+  for (int dt = 0; dt < 32; ++dt) ost[(w * 32 + dt) * 64 + lane] = o[dt];
+  if (g == 0) {
+    mst[w * 16 + lr] = m_run;
+    lst[w * 16 + lr] = l_run;
   }
   __syncthreads();
-  if (pair == 0) {
+  {
     const int h = lr;
-    const float m1 = mst[half * 16 + h];
-    const float l1 = lst[half * 16 + h];
-    const float M = fmaxf(m_run, m1);         // finite: pair 0 always saw a key
-    const float c0 = fast_exp2(m_run - M);
-    const float c1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - M);
-    const float Lsum = c0 * l_run + c1 * l1;
+    float mv[4], lv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      mv[u] = mst[u * 16 + h];
+      lv[u] = lst[u * 16 + h];
+    }
+    const float M = fmaxf(fmaxf(mv[0], mv[1]), fmaxf(mv[2], mv[3]));   // finite: wave 0 saw a key
+    float c[4];
+    float Lsum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      c[u] = mv[u] == -INFINITY ? 0.f : fast_exp2(mv[u] - M);
+      Lsum += c[u] * lv[u];
+    }
     const float inv = 1.f / Lsum;
     const float lse_v = (M + fast_log2(Lsum)) * kLn2;
     if (h < a.H) {
 #pragma unroll
-      for (int dt = 0; dt < 16; ++dt) {
-        const f32x4 x = (c0 * o[dt] + c1 * ost[(half * 16 + dt) * 64 + lane]) * inv;
-        const int d = 256 * half + 16 * dt + 4 * g;     // lane holds dims d .. d+3 of head h
+      for (int i = 0; i < 8; ++i) {
+        const int dt = 8 * w + i;
+        f32x4 x = c[0] * ost[(0 * 32 + dt) * 64 + lane];
+#pragma unroll
+        for (int u = 1; u < 4; ++u) x += c[u] * ost[(u * 32 + dt) * 64 + lane];
+        x *= inv;
+        const int d = 16 * dt + 4 * g;     // lane holds dims d .. d+3 of head h
         if (nsplit == 1) {
           *(u32x2*)(a.out + ((size_t)t * a.H + h) * kLatent + d) =
               u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+        } else if (kDeferMerge) {
+          // read by the combine kernel after this launch: plain stores
+          *(f32x4*)(a.ws_o + (my_slot * a.H + h) * kLatent + d) = x;
         } else {
-          float* wp = a.ws_o + (((size_t)split * a.T + t) * a.H + h) * kLatent + d;
+          float* wp = a.ws_o + (my_slot * a.H + h) * kLatent + d;
           store_device(wp, x[0], x[1]);
           store_device(wp + 2, x[2], x[3]);
         }
       }
-      if (half == 0 && g == 0) {
+      if (w == 0 && g == 0) {
         if (nsplit == 1)
           a.lse[(size_t)t * a.H + h] = lse_v;
+        else if (kDeferMerge)
+          a.ws_lse[my_slot * a.H + h] = lse_v;
         else
-          __hip_atomic_store((uint32_t*)a.ws_lse + ((size_t)split * a.T + t) * a.H + h, __float_as_uint(lse_v),
+          __hip_atomic_store((uint32_t*)a.ws_lse + my_slot * a.H + h, __float_as_uint(lse_v),
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
-  if (nsplit == 1) return;
-  ticket_and_merge(a, t, 0, 16, nsplit);
+  if (nsplit == 1 || kDeferMerge) return;
+  ticket_and_merge(a, t, 0, 16, nsplit, sm, counter);
 }
 
-hipError_t launch_decode(const DecodeParams& p, int mtiles, int max_splits, hipStream_t stream) {
-  const dim3 grid((unsigned)(p.T * p.hblocks), (unsigned)max_splits);
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Balanced schedule.  The launch's work is laid out on a line of units: row by
+// row in token order, each row takes kRowUnits (its fixed cost: query load,
+// pipeline fill, the four-wave merge) followed by one unit per 16-key stage.
+// Worker g (one workgroup) takes units [g*per, (g+1)*per) with
+// per = ceil(total / workers), so every worker streams the same number of cache
+// rows (to within one stage) whatever the length mix; a row cut by worker
+// boundaries becomes pieces that split_combine_kernel merges after the launch
+// (a separate launch spreads that merge over every CU instead of leaving each
+// row's pieces to one workgroup at the end).  A worker's
+// partial goes to workspace row 2g for the row it continues from its
+// predecessor (or that starts exactly on its boundary) and 2g + 1 for the row
+// it hands on, so pieces never share a slot.  Every wave computes the schedule
+// itself (same inputs, same result), so no barrier is needed.
+constexpr int kRowUnits = 4;
+constexpr int kMinUnitsPerWorker = 8;
+
+__device__ __forceinline__ int h16_stages(int L) { return (L + kWStage - 1) / kWStage; }
+
+__device__ __forceinline__ int request_units(const DecodeParams& a, int b) {
+  const int q0 = a.qsl[b];
+  const int Q = a.qsl[b + 1] - q0;
+  const int S = a.seq_lens[b];
+  int u = 0;
+  for (int i = 0; i < Q; ++i) u += kRowUnits + h16_stages(ceil_div_pos(S - Q + i + 1 - a.r, a.W));
+  return u;
+}
+
+template <bool kPage16, bool kBalanced>
+__global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a) {
+  // Four wave rings of two 18 KiB slots; reused for the four-wave merge.
+  __shared__ __attribute__((aligned(16))) uint8_t lds_block[kWLdsBytes];
+
+  if constexpr (!kBalanced) {
+    // Grid (token, split): split s takes keys [s*chunk, (s+1)*chunk) of the row.
+    const int t = blockIdx.x;
+    const int split = blockIdx.y;
+    const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r);
+    const int nsplit = num_splits_of(ri.L, a.chunk, (int)gridDim.y);
+    if (split >= nsplit) return;
+    if (ri.L == 0) {
+      write_empty_row(a, t);
+      return;
+    }
+    const int j_begin = split * a.chunk;
+    const int j_end = split == nsplit - 1 ? ri.L : j_begin + a.chunk;
+    h16_piece<kPage16, false>(a, lds_block, t, ri.b, j_begin, j_end, nsplit, (int64_t)split * a.T + t,
+                              SlotMap{t, a.T, 0}, t);
+  } else {
+    const int G = (int)gridDim.x;
+    const int g = (int)blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    // Units of this lane's request of the first 64; the total over all.
+    const int u_first = lane < a.B ? request_units(a, lane) : 0;
+    const int inc_first = wave_incl_scan(u_first);
+    int total = __shfl(inc_first, 63, 64);
+    for (int b0 = 64; b0 < a.B; b0 += 64) {
+      const int bb = b0 + lane;
+      total += __shfl(wave_incl_scan(bb < a.B ? request_units(a, bb) : 0), 63, 64);
+    }
+    int per = (total + G - 1) / G;
+    if (per < kMinUnitsPerWorker) per = kMinUnitsPerWorker;
+    const int x0 = g * per;
+    if (x0 >= total) return;
+    const int x1 = min(x0 + per, total);
+    // The request whose unit range holds x0 (requests without rows own none).
+    int b = 0, pos = 0, carry = 0;
+    for (int b0 = 0; b0 < a.B; b0 += 64) {
+      const int bb = b0 + lane;
+      const int u = b0 == 0 ? u_first : (bb < a.B ? request_units(a, bb) : 0);
+      const int inc = b0 == 0 ? inc_first : wave_incl_scan(u);
+      const bool hit = bb < a.B && carry + inc - u <= x0 && x0 < carry + inc;
+      const uint64_t m = __ballot(hit);
+      if (m) {
+        const int src = __ffsll((unsigned long long)m) - 1;
+        b = b0 + src;
+        pos = carry + __shfl(inc - u, src, 64);
+        break;
+      }
+      carry += __shfl(inc, 63, 64);
+    }
+    b = __builtin_amdgcn_readfirstlane(b);
+    pos = __builtin_amdgcn_readfirstlane(pos);
+    int q0 = a.qsl[b], Q = a.qsl[b + 1] - q0, S = a.seq_lens[b], i = 0;
+    while (pos < x1) {
+      if (i == Q) {      // next request; one exists because pos < total
+        ++b;
+        q0 = a.qsl[b];
+        Q = a.qsl[b + 1] - q0;
+        S = a.seq_lens[b];
+        i = 0;
+        continue;
+      }
+      const int L = ceil_div_pos(S - Q + i + 1 - a.r, a.W);
+      const int n = h16_stages(L);
+      const int t = q0 + i;
+      if (pos + kRowUnits + n > x0) {
+        if (L == 0) {
+          if (pos >= x0) {                           // the row's owner is the worker holding its start
+            write_empty_row(a, t);
+            if (threadIdx.x == 0) a.row_desc[t] = int4{0, 0, 0, 0};
+          }
+        } else {
+          const int s0 = pos + kRowUnits;           // unit of the row's first stage
+          const int lo = max(x0 - s0, 0);
+          const int hi = min(x1 - s0, n);
+          if (lo < hi) {
+            const int gf = s0 / per;                 // workers holding the row's stages: gf .. gl
+            const int gl = (s0 + n - 1) / per;
+            const SlotMap sm{2 * gf, 2, s0 == gf * per ? 0 : 1};
+            // The worker of the row's first piece tells the combine kernel how
+            // to find the row's pieces.
+            if (g == gf && threadIdx.x == 0) a.row_desc[t] = int4{gl - gf + 1, sm.base, sm.adj0, 0};
+            h16_piece<kPage16, true>(a, lds_block, t, b, lo * kWStage, min(hi * kWStage, L), gl - gf + 1,
+                                     sm.row(g - gf), sm, t);
+            __syncthreads();                         // LDS is reused by the next piece
+          }
+        }
+      }
+      pos += kRowUnits + n;
+      ++i;
+    }
+  }
+}
+
+// Merge of the pieces of rows that the balanced schedule split (exact LSE-
+// weighted combine, pieces in index order).  Workgroup (token t, dim quarter
+// qd): thread (head h = tid / 16, dims 128qd + 8(tid % 16) .. +8); rows that
+// were not split were finished by the decode kernel.
+__global__ __launch_bounds__(256) void split_combine_kernel(const DecodeParams a) {
+  const int t = blockIdx.x;
+  const int4 desc = a.row_desc[t];
+  const int np = desc.x;
+  if (np <= 1) return;
+  const SlotMap sm{desc.y, 2, desc.z};
+  const int h = threadIdx.x >> 4;
+  if (h >= a.H) return;
+  const int d0 = 128 * blockIdx.y + 8 * (threadIdx.x & 15);
+  float m = -INFINITY, ssum = 0.f;
+  f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  for (int sp0 = 0; sp0 < np; sp0 += 8) {
+    float l[8];
+    f32x4 x0[8], x1[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sp = min(sp0 + u, np - 1);
+      const int64_t srow = sm.row(sp) * a.H + h;
+      l[u] = a.ws_lse[srow];
+      const f32x4* src = (const f32x4*)(a.ws_o + srow * kLatent + d0);
+      x0[u] = src[0];
+      x1[u] = src[1];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float mn = fmaxf(m, l[u]);
+      if (sp0 + u < np && mn > -INFINITY) {
+        const float c_old = m == -INFINITY ? 0.f : fast_exp2((m - mn) * kLog2e);
+        const float c_new = fast_exp2((l[u] - mn) * kLog2e);
+        acc0 = acc0 * c_old + x0[u] * c_new;
+        acc1 = acc1 * c_old + x1[u] * c_new;
+        ssum = ssum * c_old + c_new;
+        m = mn;
+      }
+    }
+  }
+  const float inv = ssum > 0.f ? 1.f / ssum : 0.f;
+  const size_t row = (size_t)t * a.H + h;
+  *(u32x4*)(a.out + row * kLatent + d0) =
+      u32x4{pack_bf16x2(acc0[0] * inv, acc0[1] * inv), pack_bf16x2(acc0[2] * inv, acc0[3] * inv),
+            pack_bf16x2(acc1[0] * inv, acc1[1] * inv), pack_bf16x2(acc1[2] * inv, acc1[3] * inv)};
+  if (blockIdx.y == 0 && (threadIdx.x & 15) == 0)
+    a.lse[row] = ssum > 0.f ? m + fast_log2(ssum) * kLn2 : -INFINITY;
+}
+
+hipError_t launch_decode(const DecodeParams& p, int mtiles, int max_splits, int workers, hipStream_t stream) {
   const bool page16 = p.P % 16 == 0;
+  if (mtiles == 1 && workers > 0) {
+    const dim3 grid((unsigned)workers);
+    if (page16) hipLaunchKernelGGL((decode_kernel_h16<true, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((decode_kernel_h16<false, true>), grid, dim3(256), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(split_combine_kernel, dim3((unsigned)p.T, 4), dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)(p.T * p.hblocks), (unsigned)max_splits);
   if (mtiles == 1) {
-    if (page16) hipLaunchKernelGGL((decode_kernel_h16<true>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((decode_kernel_h16<false>), grid, dim3(256), 0, stream, p);
+    if (page16) hipLaunchKernelGGL((decode_kernel_h16<true, false>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((decode_kernel_h16<false, false>), grid, dim3(256), 0, stream, p);
   } else {
     if (page16) hipLaunchKernelGGL((decode_kernel<2, kStages, true>), grid, dim3(256), 0, stream, p);
     else hipLaunchKernelGGL((decode_kernel<2, kStages, false>), grid, dim3(256), 0, stream, p);

@@ -22,9 +22,10 @@ struct DecodeParams {
   int32_t max_splits;      // grid extent along splits
   uint16_t* out;           // bf16 [T,H,512]
   float* lse;              // fp32 [T,H]
-  float* ws_o;             // fp32 [splits,T,H,512] split partials (normalised)
-  float* ws_lse;           // fp32 [splits,T,H]
+  float* ws_o;             // fp32 [slots,H,512] split partials (normalised)
+  float* ws_lse;           // fp32 [slots,H]
   int32_t* counters;       // int32 [T*hblocks] split tickets; zero between calls
+  int4* row_desc;          // balanced schedule: per token {pieces, first slot, slot-0 offset, 0}
 };
 
 struct MergeParams {
@@ -37,8 +38,13 @@ struct MergeParams {
   float* out_lse;          // fp32 [T,H] or null
 };
 
-// Heads handled by one decode workgroup: 16 * mtiles, mtiles in {1,2}.
-hipError_t launch_decode(const DecodeParams& p, int mtiles, int max_splits, hipStream_t stream);
+// Heads handled by one decode workgroup: 16 * mtiles, mtiles in {1,2}.  With
+// mtiles == 1 and workers > 0 the launch is `workers` workgroups that share
+// the keys of all rows evenly (balanced schedule); otherwise the grid is
+// (tokens * head blocks, max_splits) with fixed-size splits of p.chunk keys.
+// The balanced launch is followed by a combine launch that merges the pieces
+// of the rows it split.
+hipError_t launch_decode(const DecodeParams& p, int mtiles, int max_splits, int workers, hipStream_t stream);
 hipError_t launch_local_seqlens(const int32_t* seq_lens, const int32_t* qsl, int B, int T, int W,
                                 int r, int32_t* row_seqlen, int32_t* shard_len, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeParams& p, hipStream_t stream);

@@ -56,6 +56,13 @@ class DeviceWorkload:
         # zero-filled once: the split tickets must start at zero (calls reset them)
         self.workspace = torch.zeros(n, dtype=torch.uint8, device=self.device) if n else None
 
+    def decode_kernel_name(self) -> str:
+        """Name of the decode kernel the library launches for this shape."""
+        page16 = "true" if self.wl.P % 16 == 0 else "false"
+        if self.H <= 16:
+            return f"decode_kernel_h16<{page16}>"
+        return f"decode_kernel<2, 3, {page16}>"
+
     def partial(self, r: int, stream=None):
         mla.mla_decode_partial(
             self.q_nope, self.q_pe, self.caches[r], self.tables[r], self.seq_lens, self.qsl,
