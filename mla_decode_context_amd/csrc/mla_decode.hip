@@ -829,15 +829,16 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // predecessor (or that starts exactly on its boundary) and 2g + 1 for the row
 // it hands on, so pieces never share a slot.  Every wave computes the schedule
 // itself (same inputs, same result), so no barrier is needed.
-constexpr int kRowUnits = 4;
+constexpr int kRowUnits = 8;
 constexpr int kMinUnitsPerWorker = 8;
 
 __device__ __forceinline__ int h16_stages(int L) { return (L + kWStage - 1) / kWStage; }
 
-__device__ __forceinline__ int request_units(const DecodeParams& a, int b) {
-  const int q0 = a.qsl[b];
-  const int Q = a.qsl[b + 1] - q0;
-  const int S = a.seq_lens[b];
+// Units of request b; also returns its first token q0, rows Q and length S.
+__device__ __forceinline__ int request_units(const DecodeParams& a, int b, int& q0, int& Q, int& S) {
+  q0 = a.qsl[b];
+  Q = a.qsl[b + 1] - q0;
+  S = a.seq_lens[b];
   int u = 0;
   for (int i = 0; i < Q; ++i) u += kRowUnits + h16_stages(ceil_div_pos(S - Q + i + 1 - a.r, a.W));
   return u;
@@ -867,13 +868,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a
     const int G = (int)gridDim.x;
     const int g = (int)blockIdx.x;
     const int lane = threadIdx.x & 63;
-    // Units of this lane's request of the first 64; the total over all.
-    const int u_first = lane < a.B ? request_units(a, lane) : 0;
+    // Every lane holds one request of the chunk [b0c, b0c + 64): its first
+    // token, rows, length and units.  Chunk 0 is kept; the total runs over all.
+    int lq0 = 0, lQ = 0, lS = 0;
+    const int u_first = lane < a.B ? request_units(a, lane, lq0, lQ, lS) : 0;
     const int inc_first = wave_incl_scan(u_first);
     int total = __shfl(inc_first, 63, 64);
     for (int b0 = 64; b0 < a.B; b0 += 64) {
       const int bb = b0 + lane;
-      total += __shfl(wave_incl_scan(bb < a.B ? request_units(a, bb) : 0), 63, 64);
+      int x, y, z;
+      total += __shfl(wave_incl_scan(bb < a.B ? request_units(a, bb, x, y, z) : 0), 63, 64);
     }
     int per = (total + G - 1) / G;
     if (per < kMinUnitsPerWorker) per = kMinUnitsPerWorker;
@@ -881,30 +885,47 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a
     if (x0 >= total) return;
     const int x1 = min(x0 + per, total);
     // The request whose unit range holds x0 (requests without rows own none).
-    int b = 0, pos = 0, carry = 0;
+    int b = 0, pos = 0, carry = 0, b0c = 0;
     for (int b0 = 0; b0 < a.B; b0 += 64) {
       const int bb = b0 + lane;
-      const int u = b0 == 0 ? u_first : (bb < a.B ? request_units(a, bb) : 0);
-      const int inc = b0 == 0 ? inc_first : wave_incl_scan(u);
+      int u = u_first, inc = inc_first;
+      if (b0 > 0) {
+        u = bb < a.B ? request_units(a, bb, lq0, lQ, lS) : 0;
+        inc = wave_incl_scan(u);
+      }
       const bool hit = bb < a.B && carry + inc - u <= x0 && x0 < carry + inc;
       const uint64_t m = __ballot(hit);
       if (m) {
         const int src = __ffsll((unsigned long long)m) - 1;
         b = b0 + src;
+        b0c = b0;
         pos = carry + __shfl(inc - u, src, 64);
         break;
       }
       carry += __shfl(inc, 63, 64);
     }
     b = __builtin_amdgcn_readfirstlane(b);
+    b0c = __builtin_amdgcn_readfirstlane(b0c);
     pos = __builtin_amdgcn_readfirstlane(pos);
-    int q0 = a.qsl[b], Q = a.qsl[b + 1] - q0, S = a.seq_lens[b], i = 0;
+    // Request fields come from the lane that holds them (no memory round trip)
+    // while b stays in the cached chunk.
+    auto fetch = [&](int bq, int& q0_, int& Q_, int& S_) {
+      if (bq - b0c < 64) {
+        q0_ = __builtin_amdgcn_readfirstlane(__shfl(lq0, bq - b0c, 64));
+        Q_ = __builtin_amdgcn_readfirstlane(__shfl(lQ, bq - b0c, 64));
+        S_ = __builtin_amdgcn_readfirstlane(__shfl(lS, bq - b0c, 64));
+      } else {
+        q0_ = a.qsl[bq];
+        Q_ = a.qsl[bq + 1] - q0_;
+        S_ = a.seq_lens[bq];
+      }
+    };
+    int q0, Q, S, i = 0;
+    fetch(b, q0, Q, S);
     while (pos < x1) {
       if (i == Q) {      // next request; one exists because pos < total
         ++b;
-        q0 = a.qsl[b];
-        Q = a.qsl[b + 1] - q0;
-        S = a.seq_lens[b];
+        fetch(b, q0, Q, S);
         i = 0;
         continue;
       }
