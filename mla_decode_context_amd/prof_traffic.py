@@ -2,7 +2,7 @@
 
 Two subcommands:
 
-  stats    DIR --kernel NAME --out FILE.md --cmd "..."
+  stats    DIR --kernel NAME[+NAME] --out FILE.md --cmd "..."
       Summarise ``*_kernel_stats.csv`` of a ``rocprofv3 --kernel-trace --stats``
       run: calls, average / min / max duration of every kernel.
 
@@ -31,7 +31,7 @@ sys.path.insert(0, os.path.dirname(_HERE))
 
 
 def _csvs(d, suffix):
-    out = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    out = sorted(set(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)))
     if not out:
         raise SystemExit(f"no *{suffix} under {d}")
     return out
@@ -52,10 +52,16 @@ def counter_per_dispatch(d, counter):
 
 
 def kernel_average(rows, kernel):
-    vals = [v for name, v in rows.values() if kernel in name]
-    if not vals:
-        raise SystemExit(f"no dispatch of {kernel}")
-    return sum(vals) / len(vals), len(vals)
+    """Average per dispatch of each "+"-separated kernel name, summed: the
+    traffic of one call that launches each of those kernels once."""
+    tot, counts = 0.0, []
+    for k in kernel.split("+"):
+        vals = [v for name, v in rows.values() if k in name]
+        if not vals:
+            raise SystemExit(f"no dispatch of {k}")
+        tot += sum(vals) / len(vals)
+        counts.append(len(vals))
+    return tot, min(counts)
 
 
 def copy_reading(rows, expect_bytes):
@@ -122,11 +128,15 @@ def cmd_stats(a):
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['Percentage']):.2f} |")
     if a.kernel:
-        sel = [r for r in rows if a.kernel in r["Name"]]
-        if sel:
-            r = sel[0]
-            lines += ["", f"Kernel of interest `{a.kernel}`: {r['Calls']} calls, average "
-                          f"{float(r['AverageNs']) / 1e3:.2f} us."]
+        tot = 0.0
+        for k in a.kernel.split("+"):
+            sel = [r for r in rows if k in r["Name"]]
+            if sel:
+                r = sel[0]
+                tot += float(r["AverageNs"])
+                lines += ["", f"Kernel `{k}`: {r['Calls']} calls, average {float(r['AverageNs']) / 1e3:.2f} us."]
+        if "+" in a.kernel:
+            lines += ["", f"One call launches each of these once: {tot / 1e3:.2f} us per call in total."]
     text = "\n".join(lines) + "\n"
     with open(a.out, "w") as f:
         f.write(text)
@@ -135,7 +145,7 @@ def cmd_stats(a):
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    sub = ap.add_subparsers(dest="cmd", required=True)
+    sub = ap.add_subparsers(dest="sub", required=True)
     s = sub.add_parser("stats")
     s.add_argument("dir")
     s.add_argument("--kernel", default="")
@@ -154,7 +164,7 @@ def main():
     t.add_argument("--cmd-write", required=True)
     t.add_argument("--out", required=True)
     a = ap.parse_args()
-    cmd_stats(a) if a.cmd == "stats" else cmd_traffic(a)
+    cmd_stats(a) if a.sub == "stats" else cmd_traffic(a)
 
 
 if __name__ == "__main__":

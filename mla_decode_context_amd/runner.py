@@ -57,10 +57,13 @@ class DeviceWorkload:
         self.workspace = torch.zeros(n, dtype=torch.uint8, device=self.device) if n else None
 
     def decode_kernel_name(self) -> str:
-        """Name of the decode kernel the library launches for this shape."""
+        """Kernels one mla_decode_partial call launches for this shape (with the
+        automatic split plan), joined by "+"."""
         page16 = "true" if self.wl.P % 16 == 0 else "false"
         if self.H <= 16:
-            return f"decode_kernel_h16<{page16}>"
+            if self.num_splits == 0 and self.workspace is not None:
+                return f"decode_kernel_h16<{page16}, true>+split_combine_kernel"
+            return f"decode_kernel_h16<{page16}, false>"
         return f"decode_kernel<2, 3, {page16}>"
 
     def partial(self, r: int, stream=None):
