@@ -9,17 +9,21 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla.so")
-SOURCES = ["mla_api.hip", "mla_decode.hip", "mla_merge.hip"]
+# (source, extra flags).  MFMA operands and results stay in ordinary VGPRs
+# (-amdgpu-mfma-vgpr-form=1): every kernel's accumulators fit in them, and that
+# form needs no copies through the accumulator registers.
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+SOURCES = [
+    ("mla_api.hip", []),
+    ("mla_decode.hip", _VGPR_FORM),
+    ("mla_merge.hip", _VGPR_FORM),
+    ("mla_decode_h128.hip", _VGPR_FORM),
+]
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU ops stay off: hipcc emits ordinary fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA sources and results stay in ordinary VGPRs.  With accumulators in
-    # AGPRs, hipcc 7.2 for gfx950 copied accumulators through AGPR temporaries
-    # written a few cycles after an in-flight MFMA read them as its C operand,
-    # and workgroups of 32+ heads gave wrong results; this form has no such copies.
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
 
@@ -29,20 +33,31 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False) -> str:
-    """Always recompile; returns the path of the shared library."""
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", LIB + ".tmp"]
+_NOISE = ("is not a recognized feature for this target", "inline asm clobber list contains reserved",
+          "Reserved registers on the clobber list", "asm volatile(", "generated when compiling", "^")
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = ("is not a recognized feature for this target", "inline asm clobber list contains reserved",
-             "Reserved registers on the clobber list", "asm volatile(", "generated when compiling", "^")
-    err = "\n".join(l for l in res.stderr.splitlines() if not any(n in l for n in noise) and l.strip())
+    err = "\n".join(l for l in res.stderr.splitlines() if not any(n in l for n in _NOISE) and l.strip())
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Always recompile (one object per source, then link); returns the library path."""
+    objs = []
+    for src, extra in SOURCES:
+        obj = os.path.join(PKG, "_build", src.replace(".hip", ".o"))
+        os.makedirs(os.path.dirname(obj), exist_ok=True)
+        _run([hipcc(), *HIPCC_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c",
+              os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"], verbose)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

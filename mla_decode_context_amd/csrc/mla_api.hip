@@ -35,10 +35,15 @@ constexpr int kMaxGridY = 65535;
 // Balanced schedule of the 16-head kernel: one workgroup per CU of the
 // 256-CU part (the kernel's LDS allows one per CU).
 constexpr int kWorkers = 256;
+// 128-head kernel: one workgroup per CU; automatic splits aim for this many
+// workgroups and never cut a row below kH128MinChunk keys.
+constexpr int kH128Groups = 256;
+constexpr int kH128MinChunk = 512;
 
 // Launch plan: heads per workgroup and how keys are split.  Depends only on
 // host integers so that the workspace size can be computed in advance.
 struct Plan {
+  bool h128;        // the 128-head kernel (one workgroup per token and split)
   int mtiles;       // 16-head tiles per workgroup (1 or 2)
   int hblocks;      // workgroups per token along heads
   int chunk;        // keys per split (fixed-split grid)
@@ -52,11 +57,25 @@ Plan make_plan(int T, int H, int max_seq_len, int W, int num_splits, bool split_
   p.mtiles = ht >= 2 ? 2 : 1;
   p.hblocks = (int)ceil_div(ht, p.mtiles);
   p.workers = 0;
+  p.h128 = H == 128;
   // A row's visible local keys never exceed ceil(max_seq_len / W).
   const int64_t lmax = max_seq_len > 0 ? ceil_div(max_seq_len, W) : 0;
   const int64_t lr = round_up(lmax > 0 ? lmax : 1, kStep);
   int64_t chunk = lr;
-  if (split_ok && num_splits == 0 && p.mtiles == 1) {
+  if (p.h128) {
+    // A split's partial is 256 KiB (128 heads x 512 fp32): split only when
+    // there are fewer tokens than CUs, or when asked to.
+    if (split_ok && lmax > 0 && num_splits != 1) {
+      if (num_splits > 1) {
+        chunk = round_up(ceil_div(lmax, num_splits), kStep);
+      } else {
+        const int64_t want = ceil_div(kH128Groups, T > 0 ? T : 1);
+        if (want > 1) chunk = round_up(ceil_div(lmax, want), kStep);
+        if (chunk < kH128MinChunk) chunk = kH128MinChunk;
+      }
+      if (chunk > lr) chunk = lr;
+    }
+  } else if (split_ok && num_splits == 0 && p.mtiles == 1) {
     p.workers = kWorkers;
   } else if (split_ok && num_splits != 1 && lmax > 0) {
     if (num_splits > 1) {
@@ -180,7 +199,8 @@ mla_status mla_decode_partial(
     p.ws_lse = (float*)(base + d_end);
     p.ws_o = (float*)(base + d_end + lse_bytes(plan, T, H));
   }
-  hipError_t e = mla::launch_decode(p, plan.mtiles, plan.max_splits, plan.workers, (hipStream_t)hip_stream);
+  hipError_t e = plan.h128 ? mla::launch_decode_h128(p, (hipStream_t)hip_stream)
+                           : mla::launch_decode(p, plan.mtiles, plan.max_splits, plan.workers, (hipStream_t)hip_stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -28,81 +28,15 @@
 // partial (fp32) and LSE to the workspace and the last one to finish merges
 // them (exact LSE-weighted combine) in the same launch.
 #include "mla_common.h"
+#include "mla_device.h"
 #include "mla_kernels.h"
 
 namespace mla {
 
 constexpr int kStep = 32;        // keys per inner step (K of the PV MFMA)
 constexpr int kSlab = 128;       // latent dims owned by one wave
-constexpr int kRowBytes = kRow * 2;              // 1152
 constexpr int kStageBytes = kStep * kRowBytes;   // 36 KiB: one step's rows
 constexpr int kStages = 3;                        // stages in the LDS ring
-
-__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// Transposed 64-bit LDS read: within each 16-lane group, lane i receives
-// element (i & 3) of the four-element chunk addressed by lane 4e + (i >> 2),
-// for e = 0..3.
-__device__ __forceinline__ s16x4 lds_read_tr16_at(const uint8_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uint8_t*)p);
-}
-
-// Direct-to-LDS load (gfx950 global_load_lds_dwordx4): each lane fetches 16
-// bytes from its own global address and the wave's 64 results fill the 1 KiB of
-// LDS starting at lds_block (wave-uniform; passed in M0).  Issued through asm so
-// that the compiler adds no wait of its own: the kernel orders these loads with
-// explicit vmcnt waits and barriers.  The asm is volatile with a memory clobber,
-// so no other memory access moves across it.  A write of M0 needs one wait state
-// before an LDS-DMA instruction reads it, hence the s_nop.
-__device__ __forceinline__ void dma_16B_to_lds(const void* src, const uint8_t* lds_block) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds_block);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(lds), "v"(src)
-               : "memory", "m0");
-}
-
-// Empty asm that "uses" a pointer, extending its registers' live range.
-__device__ __forceinline__ void keep_live(const void* p) { asm volatile("" : : "v"(p)); }
-
-// Device-scope (all-XCD coherent) accesses to the split workspace: relaxed
-// atomics at agent scope, which the compiler emits as plain loads and stores
-// with the device-coherence cache policy and no fences.
-__device__ __forceinline__ void store_device(float* p, float x, float y) {
-  const uint64_t v = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
-  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_device(const float* p) {
-  return __uint_as_float(__hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
-__device__ __forceinline__ f32x4 load_device4(const float* p) {
-  const uint64_t lo = __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint64_t hi = __hip_atomic_load((const uint64_t*)p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return f32x4{__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
-               __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32))};
-}
-
-// Splits of a row with L visible keys: ceil(L / chunk), at least 1, at most the
-// grid's split extent.
-__device__ __forceinline__ int num_splits_of(int L, int chunk, int max_splits) {
-  const int n = L > 0 ? (L + chunk - 1) / chunk : 1;
-  return n < max_splits ? n : max_splits;
-}
-
-// Where the partials of a split row live: piece k of the row (k = 0..np-1)
-// stores its heads at workspace row base + k*stride (+ adj0 for k = 0); a
-// workspace row holds H heads of 512 fp32 plus H LSEs.
-struct SlotMap {
-  int base, stride, adj0;
-  __device__ __forceinline__ int64_t row(int k) const {
-    return (int64_t)base + (int64_t)k * stride + (k == 0 ? adj0 : 0);
-  }
-};
 
 // Split rows: the last of the row's pieces to finish merges all partials.
 // Every piece has already written its normalised partial and LSE for heads
@@ -178,9 +112,6 @@ __device__ __forceinline__ void ticket_and_merge(const DecodeParams& a, int t, i
   }
   if (threadIdx.x == 0) a.counters[counter] = 0;
 }
-
-// vmcnt(n) operand of s_waitcnt (expcnt and lgkmcnt left at their maxima).
-#define MLA_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
 
 template <int MT, int NS, bool kPage16>
 __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams a) {
@@ -494,40 +425,6 @@ constexpr int kWStageBytes = kWStage * kRowBytes;       // 18 KiB
 constexpr int kWBlocks = kWStageBytes / 1024;           // 18 load instructions per stage
 constexpr int kWRing = 2;                               // slots per wave
 constexpr int kWLdsBytes = 4 * kWRing * kWStageBytes;   // 144 KiB
-
-// s_waitcnt operand: lgkmcnt(0), vmcnt and expcnt left at their maxima.
-#define MLA_LGKMCNT0 (15 | (3 << 14) | (7 << 4))
-
-// Direct-to-LDS load with a wave-uniform 64-bit base (SGPRs) and a per-lane
-// 32-bit byte offset; see dma_16B_to_lds.
-__device__ __forceinline__ void dma_16B_to_lds_sbase(uint32_t lds_off, uint32_t voff, const void* base) {
-  // The base must live in SGPRs: take each 32-bit half from the first lane (it
-  // is uniform).  readfirstlane returns int: widen through uint32_t so that the
-  // low half is zero-extended, never sign-extended into the high half.
-  const uint64_t b = (uint64_t)(uintptr_t)base;
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
-  const uint64_t sbase = ((uint64_t)hi << 32) | (uint64_t)lo;
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds_off), "v"(voff), "s"(sbase)
-               : "memory", "m0");
-}
-
-// max / sum over the four lanes l, l^16, l^32, l^48 (one MFMA column) with the
-// gfx950 lane-swap instructions (VALU, no LDS round trip).
-__device__ __forceinline__ float col_max(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float col_sum(float x) {
-  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // Writes out = 0 and lse = -inf for heads 0..15 of a row that sees no key.
 __device__ __forceinline__ void write_empty_row(const DecodeParams& a, int t) {

@@ -1,0 +1,411 @@
+// Absorbed-MLA decode for 128 heads on gfx950 (CDNA4): the MFMA-bound case.
+//
+// What is computed is the same as in mla_decode.hip ("flashattn_mla" API page,
+// _forward_decode; PR #24453 review thread for the per-row, per-rank
+// seqlen_k).  This file holds the kernel for H = 128, where every cache row is
+// used by 128 heads of every query row and the contraction dominates (about
+// 240 flop per cache byte per query row).
+//
+// Work decomposition.  A workgroup of 8 waves (two per SIMD) owns one query
+// token, a block of 64 heads and one split of the row's visible keys.  Per
+// 32-key stage:
+//   scores  wave w computes S^T[key][head] = K Q^T for heads 16(w & 3) ..+16
+//           and keys 16(w >> 2) .. +16 of the stage (MFMA 16x16x32, keys on M,
+//           heads on N; K straight from LDS, Q^T resident in VGPRs); the two
+//           waves holding a head exchange their maxima through LDS, run the
+//           online softmax (base 2, fp32) and write P (bf16, [head][key]) and
+//           the heads' rescale factors to LDS;
+//   PV      wave w accumulates O^T[dim][head] += V^T P^T for latent dims
+//           64w .. 64w+63 and all 64 heads (MFMA 32x32x16, V^T from transposed
+//           LDS reads, P^T from LDS).
+// Each wave's accumulators are 64 registers (64 heads x 64 dims), which leaves
+// room for two waves per SIMD.  The softmax keeps a lazy reference maximum
+// (it only moves when a stage's maximum exceeds it by more than 2^16), so the
+// accumulators are rescaled almost never.  Stages of 32 rows (36 KiB) arrive
+// by direct-to-LDS loads into a 4-slot ring, three stages ahead.  The two head
+// blocks of a token, and those of the next token (the other query row of an
+// MTP request), are consecutive work items placed on the same XCD and
+// dispatched back to back, so they share that XCD's L2 for the cache rows.  A
+// row split over several workgroups writes fp32 partials that
+// combine_fixed_kernel merges afterwards.
+#include "mla_common.h"
+#include "mla_device.h"
+#include "mla_kernels.h"
+
+namespace mla {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kXStep = 32;                          // keys per stage
+constexpr int kXStageBytes = kXStep * kRowBytes;    // 36 KiB
+constexpr int kXBlocks = kXStageBytes / 1024;       // 36 load instructions per stage
+constexpr int kXWaves = 8;
+constexpr int kXSlots = 4;                          // ring slots: three stages ahead
+constexpr int kXAhead = kXSlots - 1;
+constexpr int kXHeads = 64;                         // heads per workgroup
+constexpr int kPRow = 80;                           // LDS bytes per head row of P (64 + 16 pad)
+constexpr float kLazyLog2 = 16.f;                   // softmax reference moves past this margin
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Waits until this wave has at most `later` stages of loads outstanding; waves
+// 0..3 issue 5 loads per stage, waves 4..7 issue 4.
+__device__ __forceinline__ void wait_stages(bool five, int later) {
+  if (five) {
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(10));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(5));
+    else __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+  } else {
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(8));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(4));
+    else __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+  }
+}
+
+// LDS writes done, then a workgroup barrier.  (A plain __syncthreads would also
+// wait for the ring's loads still in flight.)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <bool kPage32>
+__global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kXSlots * kXStageBytes];   // 144 KiB
+  __shared__ __attribute__((aligned(16))) uint8_t p_lds[kXHeads * kPRow];        // P, [head][key] bf16
+  __shared__ float mx_lds[2][kXHeads];      // per key half: stage max of each head
+  __shared__ float alpha_lds[kXHeads];
+  __shared__ int rescale_lds[kXWaves];
+
+  // Item = (split, token, head block), head block fastest.  The hardware deals
+  // workgroups to the 8 XCDs round-robin by blockIdx; item x*per_xcd + k goes to
+  // blockIdx 8k + x, so consecutive items share an XCD and are dispatched one
+  // after the other.
+  const int hblocks = a.H / kXHeads;
+  const int per_xcd = (int)(gridDim.x >> 3);
+  const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (item >= a.T * hblocks * a.max_splits) return;
+  const int hb = item % hblocks;
+  const int t = (item / hblocks) % a.T;
+  const int split = item / (hblocks * a.T);
+  const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r);
+  const int L = ri.L;
+  const int nsplit = num_splits_of(L, a.chunk, a.max_splits);
+  if (split >= nsplit) return;
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h0 = kXHeads * hb;
+
+  if (L == 0) {
+    // The row sees no key on this rank: out = 0, lse = -inf (wave w: heads 8w..).
+    for (int idx = lane; idx < 8 * 64; idx += 64) {
+      const int h = h0 + 8 * w + (idx >> 6);
+      *(u32x4*)(a.out + ((size_t)t * a.H + h) * kLatent + 8 * (idx & 63)) = u32x4{0u, 0u, 0u, 0u};
+      if ((idx & 63) == 0) a.lse[(size_t)t * a.H + h] = -INFINITY;
+    }
+    return;
+  }
+  const int j_begin = split * a.chunk;
+  const int j_end = split == nsplit - 1 ? L : j_begin + a.chunk;
+  const int n_steps = (j_end - j_begin + kXStep - 1) / kXStep;
+
+  // Scores role: head group sg = w & 3, key half kt = w >> 2; lane (head qh =
+  // lane % 16, group g = lane / 16).
+  const int sg = w & 3;
+  const int kt = w >> 2;
+  const int qh = lane & 15;
+  const int g = lane >> 4;
+  const int hl_s = 16 * sg + qh;             // this lane's score head within the block
+  // Q^T operand (B of S^T = K Q^T): dims 32s + 8g .. +8 of the head for k-step s
+  // (s < 16: q_nope, s = 16, 17: q_pe).
+  bf16x8 q[18];
+  {
+    const int hs = h0 + hl_s;
+    const uint16_t* qn = a.q_nope + (int64_t)t * a.qn_st + (int64_t)hs * a.qn_sh + 8 * g;
+    const uint16_t* qr = a.q_pe + (int64_t)t * a.qp_st + (int64_t)hs * a.qp_sh + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) q[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qn + 32 * s));
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const u32x2 v0 = *(const u32x2*)(qr + 32 * s);
+      const u32x2 v1 = *(const u32x2*)(qr + 32 * s + 4);
+      q[16 + s] = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+
+  const int32_t* bt_row = a.bt + (int64_t)ri.b * a.bt_stride;
+  const uint8_t* kv_bytes = (const uint8_t*)a.kv;
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring);
+  const bool five = w < 4;                   // blocks w, w+8, .., below 36
+
+  // Stage layout as in the 16-head kernel: byte o of a stage is row o / 1152,
+  // 16-byte chunk c = (o % 1152) / 16, holding chunk c ^ (row & 7) of the row.
+  // Keys at or past j_end (a ragged last stage) are clamped to key j_end - 1, a
+  // real cached row masked to probability 0.
+  auto issue = [&](int i, int slot) {
+    const int j0 = j_begin + kXStep * i;
+    const uint32_t ldst = ring_lds + slot * kXStageBytes;
+    const bool fast = kPage32 && j0 + kXStep <= j_end;
+    const uint8_t* base = nullptr;
+    if (fast) {
+      // page_size % 32 == 0: the stage's 32 rows are consecutive slots of one page.
+      const int pg = a.page_shift >= 0 ? j0 >> a.page_shift : j0 / a.P;
+      const int blk = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pg];
+      base = kv_bytes + ((int64_t)blk * a.kv_bs + (int64_t)(j0 - pg * a.P) * kRow) * 2;
+    }
+#pragma unroll
+    for (int u = 0; u < 5; ++u) {
+      const int blkno = w + kXWaves * u;
+      if (u == 4 && !five) break;
+      const int o = 1024 * blkno + 16 * lane;
+      const int row = o / kRowBytes;
+      const int cpos = (o - row * kRowBytes) >> 4;
+      const uint32_t doff = (uint32_t)(row * kRowBytes + ((cpos ^ (row & 7)) << 4));
+      if (fast) {
+        dma_16B_to_lds_sbase(ldst + 1024 * blkno, doff, base);
+      } else {
+        const int ra = (1024 * blkno) / kRowBytes;   // the block spans rows ra and ra + 1
+        const int j = min(j0 + row, j_end - 1);
+        const int pa = __builtin_amdgcn_readfirstlane(min(j0 + ra, j_end - 1) / a.P);
+        const int pb2 = __builtin_amdgcn_readfirstlane(min(j0 + ra + 1, j_end - 1) / a.P);
+        const int ba = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pa];
+        const int bb = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pb2];
+        const int pg = j / a.P;
+        const int64_t rbase = (int64_t)(pg == pa ? ba : bb) * a.kv_bs + (int64_t)(j - pg * a.P) * kRow;
+        dma_16B_to_lds(kv_bytes + rbase * 2 + (doff - row * kRowBytes), ring + slot * kXStageBytes + 1024 * blkno);
+      }
+    }
+  };
+
+  // Score reads: lane (key qh of key half kt, group g) reads chunk 4s + g of
+  // row 16kt + qh: byte (16kt + qh)*1152 + 128*(s >> 1) + 16*((4*(s & 1) + g) ^ (qh & 7)).
+  const uint32_t kbase0 = (16 * kt + qh) * kRowBytes + 16 * (g ^ (qh & 7));
+  const uint32_t kbase1 = (16 * kt + qh) * kRowBytes + 16 * ((4 + g) ^ (qh & 7));
+  // PV: lane (dim row lane % 32 of a 32-dim tile, half hh = lane / 32) needs
+  // keys 16m + 8hh + (0..7) of its dim (MFMA m; keys in natural order, as P^T
+  // is stored).  V^T comes from two transposed reads per MFMA: within lane group
+  // G = lane / 16 (hh = G >> 1), source lane j of read r addresses key
+  // 16m + 8hh + 4r + (j >> 2) and dims 64w + 32dt + 16(G & 1) + 4(j & 3):
+  // chunk 8w + 4dt + 2(G & 1) + ((j & 3) >> 1), byte 8(j & 1).  The key's low
+  // three bits are 4r + (j >> 2).
+  const int hh = lane >> 5;
+  const int G = lane >> 4;
+  const int jj = lane & 15;
+  uint32_t vb[2][2];                        // [dt][r]
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int key = 8 * hh + 4 * r + (jj >> 2);
+      vb[dt][r] = key * kRowBytes + 128 * w + 16 * ((4 * dt + 2 * (G & 1) + ((jj & 3) >> 1)) ^ (key & 7)) + 8 * (jj & 1);
+    }
+  // P^T operand (B of O^T = V^T P^T): lane (head 32j + (lane % 32), half hh)
+  // reads keys 16m + 8hh .. +8 of that head's P row.
+  const uint32_t pbase = (uint32_t)((lane & 31) * kPRow + 16 * hh);
+
+  float m_run = -INFINITY, l_run = 0.f;     // score head hl_s; l_run over this wave's keys
+  f32x16 o[2][2];                           // O^T tiles [dim tile][head tile]
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][j][r] = 0.f;
+
+  for (int i = 0; i < kXAhead && i < n_steps; ++i) issue(i, i);
+  for (int i = 0; i < n_steps; ++i) {
+    // This wave's loads of stage i are done once at most the later stages'
+    // loads are outstanding; the barrier makes every wave's part visible, and
+    // every wave is past stage i - 1 (its ring slot, P and factors are free).
+    wait_stages(five, min(kXAhead - 1, n_steps - 1 - i));
+    asm volatile("s_barrier" ::: "memory");
+    if (i + kXAhead < n_steps) issue(i + kXAhead, (i + kXAhead) % kXSlots);
+    const uint8_t* sb = ring + (i % kXSlots) * kXStageBytes;
+    const int j0 = j_begin + kXStep * i + 16 * kt;      // first key of this wave's half
+
+    // ---- scores: 16 keys x 16 heads over 576 dims, two accumulation chains ----
+    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+    for (int s = 0; s < 18; s += 2) {
+      const bf16x8 k0 = *(const bf16x8*)(sb + kbase0 + 128 * (s >> 1));
+      const bf16x8 k1 = *(const bf16x8*)(sb + kbase1 + 128 * (s >> 1));
+      s0 = mfma_16x16x32(k0, q[s], s0);
+      s1 = mfma_16x16x32(k1, q[s + 1], s1);
+    }
+    const f32x4 sc = s0 + s1;
+    // Lane (head qh, group g) holds keys j0 + 4g + r.
+    float v[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v[r] = (j0 + 4 * g + r < j_end) ? sc[r] * a.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, v[r]);
+    }
+    mx = col_max(mx);
+    if (g == 0) mx_lds[kt][hl_s] = mx;
+    lds_barrier();
+    mx = fmaxf(mx_lds[0][hl_s], mx_lds[1][hl_s]);   // both halves: the same value
+    // Lazy reference: m_run only moves when the stage max exceeds it by more
+    // than kLazyLog2 (or on the first stage), so p = 2^(s - m_run) <= 2^16.
+    float alpha = 1.f;
+    bool bump = false;
+    if (mx > m_run + kLazyLog2) {
+      bump = m_run > -INFINITY;               // O holds something to rescale
+      alpha = bump ? fast_exp2(m_run - mx) : 0.f;
+      m_run = mx;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float pe[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pe[r] = fast_exp2(v[r] - m_use);
+      psum += pe[r];
+    }
+    l_run = l_run * alpha + psum;
+    // P row of head hl_s: keys 16kt + 4g .. +4 at byte 2*(16kt + 4g).
+    *(u32x2*)(p_lds + hl_s * kPRow + 32 * kt + 8 * g) = u32x2{pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3])};
+    if (kt == 0 && g == 0) alpha_lds[hl_s] = alpha;
+    const bool moved = (__builtin_amdgcn_read_exec() & __builtin_amdgcn_ballot_w64(bump)) != 0;
+    if (lane == 0) rescale_lds[w] = moved ? 1 : 0;
+    lds_barrier();
+
+    // ---- PV for dims 64w .. 64w+63, all 64 heads ----
+    int any = 0;
+#pragma unroll
+    for (int u = 0; u < kXWaves; ++u) any |= rescale_lds[u];
+    if (any) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float al = alpha_lds[32 * j + (lane & 31)];
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) o[dt][j] *= al;
+      }
+    }
+    bf16x8 pbv[2][2];                        // [head tile][key half]
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) pbv[j][m] = *(const bf16x8*)(p_lds + pbase + 32 * j * kPRow + 32 * m);
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const uint8_t* vp = sb + 16 * m * kRowBytes;
+        const s16x4 lo = lds_read_tr16_at(vp + vb[dt][0]);
+        const s16x4 hi = lds_read_tr16_at(vp + vb[dt][1]);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) o[dt][j] = mfma_32x32x16(va, pbv[j][m], o[dt][j]);
+      }
+    }
+  }
+  l_run = col_sum(l_run);
+
+  // Normalisers of all 64 heads through LDS (the P area is free after a barrier).
+  __syncthreads();
+  float* l_lds = (float*)p_lds;              // [key half][head]
+  float* m_lds = l_lds + 2 * kXHeads;
+  if (g == 0) {
+    l_lds[kt * kXHeads + hl_s] = l_run;
+    if (kt == 0) m_lds[hl_s] = m_run;
+  }
+  __syncthreads();
+  if (kt == 0 && g == 0) {
+    const float lsum = l_lds[hl_s] + l_lds[kXHeads + hl_s];
+    const float lse_v = (m_run + fast_log2(lsum)) * kLn2;
+    const int hs = h0 + hl_s;
+    if (nsplit == 1) a.lse[(size_t)t * a.H + hs] = lse_v;
+    else a.ws_lse[((size_t)split * a.T + t) * a.H + hs] = lse_v;
+  }
+  // Lane (dim row, half hh) of tile (dt, j) holds head 32j + (lane % 32) and
+  // dims 64w + 32dt + 8q + 4hh + (0..3) in registers 4q .. 4q+3.
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int hl = 32 * j + (lane & 31);
+    const float inv = 1.f / (l_lds[hl] + l_lds[kXHeads + hl]);
+    const int h = h0 + hl;
+    if (nsplit == 1) {
+      uint16_t* op = a.out + ((size_t)t * a.H + h) * kLatent + 64 * w + 4 * hh;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          *(u32x2*)(op + 32 * dt + 8 * qd) =
+              u32x2{pack_bf16x2(o[dt][j][4 * qd] * inv, o[dt][j][4 * qd + 1] * inv),
+                    pack_bf16x2(o[dt][j][4 * qd + 2] * inv, o[dt][j][4 * qd + 3] * inv)};
+    } else {
+      // Partial of split `split`, read by the combine kernel after this launch.
+      float* wp = a.ws_o + (((size_t)split * a.T + t) * a.H + h) * kLatent + 64 * w + 4 * hh;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          *(f32x4*)(wp + 32 * dt + 8 * qd) = f32x4{o[dt][j][4 * qd] * inv, o[dt][j][4 * qd + 1] * inv,
+                                                   o[dt][j][4 * qd + 2] * inv, o[dt][j][4 * qd + 3] * inv};
+    }
+  }
+}
+
+// Merge of the fixed-size splits of the rows that were split (exact LSE-weighted
+// combine, splits in index order).  Workgroup (token t, dim quarter qd, head
+// group hg): thread (head 16hg + tid / 16, dims 128qd + 8(tid % 16) .. +8).
+__global__ __launch_bounds__(256) void combine_fixed_kernel(const DecodeParams a) {
+  const int t = blockIdx.x;
+  const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r);
+  const int np = num_splits_of(ri.L, a.chunk, a.max_splits);
+  if (np <= 1) return;
+  const int h = 16 * blockIdx.z + (threadIdx.x >> 4);
+  if (h >= a.H) return;
+  const int d0 = 128 * blockIdx.y + 8 * (threadIdx.x & 15);
+  float m = -INFINITY, ssum = 0.f;
+  f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  for (int sp0 = 0; sp0 < np; sp0 += 8) {
+    float l[8];
+    f32x4 x0[8], x1[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sp = min(sp0 + u, np - 1);
+      const size_t srow = ((size_t)sp * a.T + t) * a.H + h;
+      l[u] = a.ws_lse[srow];
+      const f32x4* src = (const f32x4*)(a.ws_o + srow * kLatent + d0);
+      x0[u] = src[0];
+      x1[u] = src[1];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float mn = fmaxf(m, l[u]);
+      if (sp0 + u < np && mn > -INFINITY) {
+        const float c_old = m == -INFINITY ? 0.f : fast_exp2((m - mn) * kLog2e);
+        const float c_new = fast_exp2((l[u] - mn) * kLog2e);
+        acc0 = acc0 * c_old + x0[u] * c_new;
+        acc1 = acc1 * c_old + x1[u] * c_new;
+        ssum = ssum * c_old + c_new;
+        m = mn;
+      }
+    }
+  }
+  const float inv = ssum > 0.f ? 1.f / ssum : 0.f;
+  const size_t row = (size_t)t * a.H + h;
+  *(u32x4*)(a.out + row * kLatent + d0) =
+      u32x4{pack_bf16x2(acc0[0] * inv, acc0[1] * inv), pack_bf16x2(acc0[2] * inv, acc0[3] * inv),
+            pack_bf16x2(acc1[0] * inv, acc1[1] * inv), pack_bf16x2(acc1[2] * inv, acc1[3] * inv)};
+  if (blockIdx.y == 0 && (threadIdx.x & 15) == 0)
+    a.lse[row] = ssum > 0.f ? m + fast_log2(ssum) * kLn2 : -INFINITY;
+}
+
+hipError_t launch_decode_h128(const DecodeParams& p, hipStream_t stream) {
+  const int items = p.T * (p.H / kXHeads) * p.max_splits;
+  const unsigned grid = (unsigned)(((items + 7) / 8) * 8);
+  if (p.P % 32 == 0) hipLaunchKernelGGL((decode_kernel_h128<true>), dim3(grid), dim3(512), 0, stream, p);
+  else hipLaunchKernelGGL((decode_kernel_h128<false>), dim3(grid), dim3(512), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.max_splits <= 1) return e;
+  hipLaunchKernelGGL(combine_fixed_kernel, dim3((unsigned)p.T, 4, (unsigned)((p.H + 15) / 16)), dim3(256), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla

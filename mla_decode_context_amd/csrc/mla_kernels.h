@@ -45,6 +45,8 @@ struct MergeParams {
 // The balanced launch is followed by a combine launch that merges the pieces
 // of the rows it split.
 hipError_t launch_decode(const DecodeParams& p, int mtiles, int max_splits, int workers, hipStream_t stream);
+// 128 heads: one workgroup per (token, split), splits merged by a second launch.
+hipError_t launch_decode_h128(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_local_seqlens(const int32_t* seq_lens, const int32_t* qsl, int B, int T, int W,
                                 int r, int32_t* row_seqlen, int32_t* shard_len, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeParams& p, hipStream_t stream);

@@ -156,6 +156,7 @@ EDGE = [
     ("h48_w4_p33", [130, 64, 5], [2, 0, 5], 48, 4, 33),
     ("h128_w1_p64", [300, 65], [2, 1], 128, 1, 64),
     ("h128_w8_ragged", [2, 3, 5, 7, 200], [2, 3, 1, 2, 4], 128, 8, 64),
+    ("h128_w2_p48", [500, 90, 33], [1, 3, 2], 128, 2, 48),
     ("h16_long_tail", [1100, 31, 33], [1, 1, 1], 16, 1, 64),
 ]
 
