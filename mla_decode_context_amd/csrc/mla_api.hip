@@ -39,6 +39,7 @@ constexpr int kWorkers = 256;
 // workgroups and never cut a row below kH128MinChunk keys.
 constexpr int kH128Groups = 256;
 constexpr int kH128MinChunk = 512;
+constexpr int kH128Stage = 64;
 
 // Launch plan: heads per workgroup and how keys are split.  Depends only on
 // host integers so that the workspace size can be computed in advance.
@@ -64,16 +65,17 @@ Plan make_plan(int T, int H, int max_seq_len, int W, int num_splits, bool split_
   int64_t chunk = lr;
   if (p.h128) {
     // A split's partial is 256 KiB (128 heads x 512 fp32): split only when
-    // there are fewer tokens than CUs, or when asked to.
+    // there are fewer tokens than CUs, or when asked to.  Splits are multiples
+    // of the kernel's 64-key stage.
     if (split_ok && lmax > 0 && num_splits != 1) {
       if (num_splits > 1) {
-        chunk = round_up(ceil_div(lmax, num_splits), kStep);
+        chunk = round_up(ceil_div(lmax, num_splits), kH128Stage);
       } else {
         const int64_t want = ceil_div(kH128Groups, T > 0 ? T : 1);
-        if (want > 1) chunk = round_up(ceil_div(lmax, want), kStep);
+        if (want > 1) chunk = round_up(ceil_div(lmax, want), kH128Stage);
         if (chunk < kH128MinChunk) chunk = kH128MinChunk;
       }
-      if (chunk > lr) chunk = lr;
+      if (chunk >= lmax) chunk = lr;
     }
   } else if (split_ok && num_splits == 0 && p.mtiles == 1) {
     p.workers = kWorkers;

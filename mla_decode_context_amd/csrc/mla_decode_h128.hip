@@ -8,23 +8,24 @@
 //
 // Work decomposition.  A workgroup of 8 waves (two per SIMD) owns one query
 // token, a block of 64 heads and one split of the row's visible keys.  Per
-// 32-key stage:
+// 64-key stage:
 //   scores  wave w computes S^T[key][head] = K Q^T for heads 16(w & 3) ..+16
-//           and keys 16(w >> 2) .. +16 of the stage (MFMA 16x16x32, keys on M,
-//           heads on N; K straight from LDS, Q^T resident in VGPRs); the two
-//           waves holding a head exchange their maxima through LDS, run the
-//           online softmax (base 2, fp32) and write P (bf16, [head][key]) and
-//           the heads' rescale factors to LDS;
-//   PV      wave w accumulates O^T[dim][head] += V^T P^T for latent dims
-//           64w .. 64w+63 and all 64 heads (MFMA 32x32x16, V^T from transposed
-//           LDS reads, P^T from LDS).
-// Each wave's accumulators are 64 registers (64 heads x 64 dims), which leaves
-// room for two waves per SIMD.  The softmax keeps a lazy reference maximum
-// (it only moves when a stage's maximum exceeds it by more than 2^16), so the
-// accumulators are rescaled almost never.  Stages of 32 rows (36 KiB) arrive
-// by direct-to-LDS loads into a 4-slot ring, three stages ahead.  The two head
-// blocks of a token, and those of the next token (the other query row of an
-// MTP request), are consecutive work items placed on the same XCD and
+//           and keys 32(w >> 2) .. +32 of the stage (MFMA 16x16x32, keys on M,
+//           heads on N; K straight from LDS, Q^T resident in VGPRs), then
+//           writes P = 2^(s - m) (bf16, [head][key]) to LDS;
+//   PV      after one barrier, wave w accumulates O^T[dim][head] += V^T P^T for
+//           latent dims 64w .. 64w+63 and all 64 heads (MFMA 32x32x16, V^T from
+//           transposed LDS reads, P^T from LDS).
+// The softmax reference m of a head is lazy: it stays put unless a stage's
+// maximum exceeds it by more than 2^16 (always on the first stage), so
+// p <= 2^16.  Both waves holding a head know m; a stage that moves it for any
+// head (rare after the first) takes a second round: the waves agree on the new
+// m through LDS, rewrite P from the scores still in registers, and the PV waves
+// rescale their accumulators.  Each wave's accumulators are 64 registers (64
+// heads x 64 dims), leaving room for two waves per SIMD.  Stages of 64 rows
+// (72 KiB) arrive by direct-to-LDS loads into a 2-slot ring, one stage ahead.
+// The two head blocks of a token, and those of the next token (the other query
+// row of an MTP request), are consecutive work items placed on the same XCD and
 // dispatched back to back, so they share that XCD's L2 for the cache rows.  A
 // row split over several workgroups writes fp32 partials that
 // combine_fixed_kernel merges afterwards.
@@ -36,45 +37,31 @@ namespace mla {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kXStep = 32;                          // keys per stage
-constexpr int kXStageBytes = kXStep * kRowBytes;    // 36 KiB
-constexpr int kXBlocks = kXStageBytes / 1024;       // 36 load instructions per stage
+constexpr int kXStep = 64;                          // keys per stage
+constexpr int kXStageBytes = kXStep * kRowBytes;    // 72 KiB
+constexpr int kXBlocks = kXStageBytes / 1024;       // 72 load instructions per stage
 constexpr int kXWaves = 8;
-constexpr int kXSlots = 4;                          // ring slots: three stages ahead
-constexpr int kXAhead = kXSlots - 1;
+constexpr int kXWaveBlocks = kXBlocks / kXWaves;    // 9 issued by each wave
+constexpr int kXSlots = 2;                          // ring slots: one stage ahead
 constexpr int kXHeads = 64;                         // heads per workgroup
-constexpr int kPRow = 80;                           // LDS bytes per head row of P (64 + 16 pad)
+constexpr int kPRow = 144;                          // LDS bytes per head row of P (128 + 16 pad)
 constexpr float kLazyLog2 = 16.f;                   // softmax reference moves past this margin
 
 __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Waits until this wave has at most `later` stages of loads outstanding; waves
-// 0..3 issue 5 loads per stage, waves 4..7 issue 4.
-__device__ __forceinline__ void wait_stages(bool five, int later) {
-  if (five) {
-    if (later >= 2) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(10));
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(5));
-    else __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
-  } else {
-    if (later >= 2) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(8));
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(4));
-    else __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
-  }
-}
-
 // LDS writes done, then a workgroup barrier.  (A plain __syncthreads would also
 // wait for the ring's loads still in flight.)
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <bool kPage32>
+template <bool kPage64>
 __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[kXSlots * kXStageBytes];   // 144 KiB
   __shared__ __attribute__((aligned(16))) uint8_t p_lds[kXHeads * kPRow];        // P, [head][key] bf16
   __shared__ float mx_lds[2][kXHeads];      // per key half: stage max of each head
   __shared__ float alpha_lds[kXHeads];
-  __shared__ int rescale_lds[kXWaves];
+  __shared__ int bump_lds[kXWaves];
 
   // Item = (split, token, head block), head block fastest.  The hardware deals
   // workgroups to the 8 XCDs round-robin by blockIdx; item x*per_xcd + k goes to
@@ -109,10 +96,10 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
   const int j_end = split == nsplit - 1 ? L : j_begin + a.chunk;
   const int n_steps = (j_end - j_begin + kXStep - 1) / kXStep;
 
-  // Scores role: head group sg = w & 3, key half kt = w >> 2; lane (head qh =
-  // lane % 16, group g = lane / 16).
+  // Scores role: head group sg = w & 3, key half kp = w >> 2 (32 keys: tiles
+  // kt = 0, 1 of 16); lane (head qh = lane % 16, group g = lane / 16).
   const int sg = w & 3;
-  const int kt = w >> 2;
+  const int kp = w >> 2;
   const int qh = lane & 15;
   const int g = lane >> 4;
   const int hl_s = 16 * sg + qh;             // this lane's score head within the block
@@ -138,27 +125,26 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
   const uint8_t* kv_bytes = (const uint8_t*)a.kv;
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring);
-  const bool five = w < 4;                   // blocks w, w+8, .., below 36
 
   // Stage layout as in the 16-head kernel: byte o of a stage is row o / 1152,
   // 16-byte chunk c = (o % 1152) / 16, holding chunk c ^ (row & 7) of the row.
-  // Keys at or past j_end (a ragged last stage) are clamped to key j_end - 1, a
-  // real cached row masked to probability 0.
+  // Wave w issues blocks w, w + 8, ..., w + 64 (1 KiB each).  Keys at or past
+  // j_end (a ragged last stage) are clamped to key j_end - 1, a real cached row
+  // masked to probability 0.
   auto issue = [&](int i, int slot) {
     const int j0 = j_begin + kXStep * i;
     const uint32_t ldst = ring_lds + slot * kXStageBytes;
-    const bool fast = kPage32 && j0 + kXStep <= j_end;
+    const bool fast = kPage64 && j0 + kXStep <= j_end;
     const uint8_t* base = nullptr;
     if (fast) {
-      // page_size % 32 == 0: the stage's 32 rows are consecutive slots of one page.
+      // page_size % 64 == 0: the stage's 64 rows are consecutive slots of one page.
       const int pg = a.page_shift >= 0 ? j0 >> a.page_shift : j0 / a.P;
       const int blk = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pg];
       base = kv_bytes + ((int64_t)blk * a.kv_bs + (int64_t)(j0 - pg * a.P) * kRow) * 2;
     }
 #pragma unroll
-    for (int u = 0; u < 5; ++u) {
+    for (int u = 0; u < kXWaveBlocks; ++u) {
       const int blkno = w + kXWaves * u;
-      if (u == 4 && !five) break;
       const int o = 1024 * blkno + 16 * lane;
       const int row = o / kRowBytes;
       const int cpos = (o - row * kRowBytes) >> 4;
@@ -179,14 +165,14 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
     }
   };
 
-  // Score reads: lane (key qh of key half kt, group g) reads chunk 4s + g of
-  // row 16kt + qh: byte (16kt + qh)*1152 + 128*(s >> 1) + 16*((4*(s & 1) + g) ^ (qh & 7)).
-  const uint32_t kbase0 = (16 * kt + qh) * kRowBytes + 16 * (g ^ (qh & 7));
-  const uint32_t kbase1 = (16 * kt + qh) * kRowBytes + 16 * ((4 + g) ^ (qh & 7));
+  // Score reads: lane (key qh of tile kt, group g) reads chunk 4s + g of row
+  // 32kp + 16kt + qh: byte row*1152 + 128*(s >> 1) + 16*((4*(s & 1) + g) ^ (qh & 7)).
+  const uint32_t kbase0 = (32 * kp + qh) * kRowBytes + 16 * (g ^ (qh & 7));
+  const uint32_t kbase1 = (32 * kp + qh) * kRowBytes + 16 * ((4 + g) ^ (qh & 7));
   // PV: lane (dim row lane % 32 of a 32-dim tile, half hh = lane / 32) needs
-  // keys 16m + 8hh + (0..7) of its dim (MFMA m; keys in natural order, as P^T
-  // is stored).  V^T comes from two transposed reads per MFMA: within lane group
-  // G = lane / 16 (hh = G >> 1), source lane j of read r addresses key
+  // keys 16m + 8hh + (0..7) of its dim (MFMA m = 0..3; keys in natural order, as
+  // P^T is stored).  V^T comes from two transposed reads per MFMA: within lane
+  // group G = lane / 16 (hh = G >> 1), source lane j of read r addresses key
   // 16m + 8hh + 4r + (j >> 2) and dims 64w + 32dt + 16(G & 1) + 4(j & 3):
   // chunk 8w + 4dt + 2(G & 1) + ((j & 3) >> 1), byte 8(j & 1).  The key's low
   // three bits are 4r + (j >> 2).
@@ -204,8 +190,9 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
   // P^T operand (B of O^T = V^T P^T): lane (head 32j + (lane % 32), half hh)
   // reads keys 16m + 8hh .. +8 of that head's P row.
   const uint32_t pbase = (uint32_t)((lane & 31) * kPRow + 16 * hh);
+  uint8_t* prow = p_lds + hl_s * kPRow + 64 * kp + 8 * g;   // this lane's P writes
 
-  float m_run = -INFINITY, l_run = 0.f;     // score head hl_s; l_run over this wave's keys
+  float m_ref = -INFINITY, l_run = 0.f;     // score head hl_s; l_run over this wave's keys
   f32x16 o[2][2];                           // O^T tiles [dim tile][head tile]
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
@@ -214,69 +201,86 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[dt][j][r] = 0.f;
 
-  for (int i = 0; i < kXAhead && i < n_steps; ++i) issue(i, i);
+  issue(0, 0);
   for (int i = 0; i < n_steps; ++i) {
-    // This wave's loads of stage i are done once at most the later stages'
-    // loads are outstanding; the barrier makes every wave's part visible, and
-    // every wave is past stage i - 1 (its ring slot, P and factors are free).
-    wait_stages(five, min(kXAhead - 1, n_steps - 1 - i));
+    // This wave's loads of stage i have landed; the barrier makes every wave's
+    // part visible and tells that every wave is past stage i - 1 (its ring slot
+    // and P are free), so stage i + 1 can go into that slot.
+    __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
     asm volatile("s_barrier" ::: "memory");
-    if (i + kXAhead < n_steps) issue(i + kXAhead, (i + kXAhead) % kXSlots);
-    const uint8_t* sb = ring + (i % kXSlots) * kXStageBytes;
-    const int j0 = j_begin + kXStep * i + 16 * kt;      // first key of this wave's half
+    if (i + 1 < n_steps) issue(i + 1, (i + 1) & 1);
+    const uint8_t* sb = ring + (i & 1) * kXStageBytes;
+    const int j0 = j_begin + kXStep * i + 32 * kp;      // first key of this wave's half
 
-    // ---- scores: 16 keys x 16 heads over 576 dims, two accumulation chains ----
-    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+    // ---- scores: 32 keys x 16 heads over 576 dims ----
+    f32x4 sc[2];
 #pragma unroll
-    for (int s = 0; s < 18; s += 2) {
-      const bf16x8 k0 = *(const bf16x8*)(sb + kbase0 + 128 * (s >> 1));
-      const bf16x8 k1 = *(const bf16x8*)(sb + kbase1 + 128 * (s >> 1));
-      s0 = mfma_16x16x32(k0, q[s], s0);
-      s1 = mfma_16x16x32(k1, q[s + 1], s1);
+    for (int kt = 0; kt < 2; ++kt) {
+      const uint8_t* kpp = sb + kt * 16 * kRowBytes;
+      f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+      for (int s = 0; s < 18; s += 2) {
+        const bf16x8 k0 = *(const bf16x8*)(kpp + kbase0 + 128 * (s >> 1));
+        const bf16x8 k1 = *(const bf16x8*)(kpp + kbase1 + 128 * (s >> 1));
+        s0 = mfma_16x16x32(k0, q[s], s0);
+        s1 = mfma_16x16x32(k1, q[s + 1], s1);
+      }
+      sc[kt] = s0 + s1;
     }
-    const f32x4 sc = s0 + s1;
-    // Lane (head qh, group g) holds keys j0 + 4g + r.
-    float v[4];
+    // Lane (head qh, group g) holds keys j0 + 16kt + 4g + r.
+    float v[8];
     float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      v[r] = (j0 + 4 * g + r < j_end) ? sc[r] * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, v[r]);
-    }
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = (j0 + 16 * kt + 4 * g + r < j_end) ? sc[kt][r] * a.scale_log2 : -INFINITY;
+        v[4 * kt + r] = x;
+        mx = fmaxf(mx, x);
+      }
     mx = col_max(mx);
-    if (g == 0) mx_lds[kt][hl_s] = mx;
-    lds_barrier();
-    mx = fmaxf(mx_lds[0][hl_s], mx_lds[1][hl_s]);   // both halves: the same value
-    // Lazy reference: m_run only moves when the stage max exceeds it by more
-    // than kLazyLog2 (or on the first stage), so p = 2^(s - m_run) <= 2^16.
-    float alpha = 1.f;
-    bool bump = false;
-    if (mx > m_run + kLazyLog2) {
-      bump = m_run > -INFINITY;               // O holds something to rescale
-      alpha = bump ? fast_exp2(m_run - mx) : 0.f;
-      m_run = mx;
-    }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float pe[4];
-    float psum = 0.f;
+    // P with the current reference; a stage whose max runs past it is redone below.
+    const bool need = mx > m_ref + kLazyLog2;
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    auto write_p = [&](float base, float& psum) {
+      psum = 0.f;
+      uint32_t pk[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pe[r] = fast_exp2(v[r] - m_use);
-      psum += pe[r];
-    }
-    l_run = l_run * alpha + psum;
-    // P row of head hl_s: keys 16kt + 4g .. +4 at byte 2*(16kt + 4g).
-    *(u32x2*)(p_lds + hl_s * kPRow + 32 * kt + 8 * g) = u32x2{pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3])};
-    if (kt == 0 && g == 0) alpha_lds[hl_s] = alpha;
-    const bool moved = (__builtin_amdgcn_read_exec() & __builtin_amdgcn_ballot_w64(bump)) != 0;
-    if (lane == 0) rescale_lds[w] = moved ? 1 : 0;
-    lds_barrier();
-
-    // ---- PV for dims 64w .. 64w+63, all 64 heads ----
-    int any = 0;
+      for (int kt = 0; kt < 2; ++kt) {
+        float pe[4];
 #pragma unroll
-    for (int u = 0; u < kXWaves; ++u) any |= rescale_lds[u];
-    if (any) {
+        for (int r = 0; r < 4; ++r) {
+          pe[r] = fast_exp2(v[4 * kt + r] - base);
+          psum += pe[r];
+        }
+        pk[2 * kt] = pack_bf16x2(pe[0], pe[1]);
+        pk[2 * kt + 1] = pack_bf16x2(pe[2], pe[3]);
+      }
+      *(u32x2*)(prow) = u32x2{pk[0], pk[1]};
+      *(u32x2*)(prow + 32) = u32x2{pk[2], pk[3]};
+    };
+    float psum;
+    if (!need) write_p(m_use, psum);
+    if (g == 0) mx_lds[kp][hl_s] = mx;
+    const bool wave_need = (__builtin_amdgcn_read_exec() & __builtin_amdgcn_ballot_w64(need)) != 0;
+    if (lane == 0) bump_lds[w] = wave_need ? 1 : 0;
+    lds_barrier();
+    int bump = 0;
+#pragma unroll
+    for (int u = 0; u < kXWaves; ++u) bump |= bump_lds[u];
+    if (bump) {
+      // Some head's max ran past its reference: both waves of every head take the
+      // same new reference from the two halves' maxima and rewrite P.
+      const float mboth = fmaxf(mx_lds[0][hl_s], mx_lds[1][hl_s]);
+      float alpha = 1.f;
+      if (mboth > m_ref + kLazyLog2) {
+        alpha = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - mboth);
+        m_ref = mboth;
+      }
+      write_p(m_ref, psum);
+      l_run *= alpha;
+      if (kp == 0 && g == 0) alpha_lds[hl_s] = alpha;
+      lds_barrier();
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const float al = alpha_lds[32 * j + (lane & 31)];
@@ -284,21 +288,22 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
         for (int dt = 0; dt < 2; ++dt) o[dt][j] *= al;
       }
     }
-    bf16x8 pbv[2][2];                        // [head tile][key half]
+    l_run += psum;
+
+    // ---- PV for dims 64w .. 64w+63, all 64 heads, 64 keys ----
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int m = 0; m < 4; ++m) {
+      bf16x8 pbv[2];
 #pragma unroll
-      for (int m = 0; m < 2; ++m) pbv[j][m] = *(const bf16x8*)(p_lds + pbase + 32 * j * kPRow + 32 * m);
+      for (int j = 0; j < 2; ++j) pbv[j] = *(const bf16x8*)(p_lds + pbase + 32 * j * kPRow + 32 * m);
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt) {
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
+      for (int dt = 0; dt < 2; ++dt) {
         const uint8_t* vp = sb + 16 * m * kRowBytes;
         const s16x4 lo = lds_read_tr16_at(vp + vb[dt][0]);
         const s16x4 hi = lds_read_tr16_at(vp + vb[dt][1]);
         const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-        for (int j = 0; j < 2; ++j) o[dt][j] = mfma_32x32x16(va, pbv[j][m], o[dt][j]);
+        for (int j = 0; j < 2; ++j) o[dt][j] = mfma_32x32x16(va, pbv[j], o[dt][j]);
       }
     }
   }
@@ -307,15 +312,11 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
   // Normalisers of all 64 heads through LDS (the P area is free after a barrier).
   __syncthreads();
   float* l_lds = (float*)p_lds;              // [key half][head]
-  float* m_lds = l_lds + 2 * kXHeads;
-  if (g == 0) {
-    l_lds[kt * kXHeads + hl_s] = l_run;
-    if (kt == 0) m_lds[hl_s] = m_run;
-  }
+  if (g == 0) l_lds[kp * kXHeads + hl_s] = l_run;
   __syncthreads();
-  if (kt == 0 && g == 0) {
+  if (kp == 0 && g == 0) {
     const float lsum = l_lds[hl_s] + l_lds[kXHeads + hl_s];
-    const float lse_v = (m_run + fast_log2(lsum)) * kLn2;
+    const float lse_v = (m_ref + fast_log2(lsum)) * kLn2;
     const int hs = h0 + hl_s;
     if (nsplit == 1) a.lse[(size_t)t * a.H + hs] = lse_v;
     else a.ws_lse[((size_t)split * a.T + t) * a.H + hs] = lse_v;
@@ -399,7 +400,7 @@ __global__ __launch_bounds__(256) void combine_fixed_kernel(const DecodeParams a
 hipError_t launch_decode_h128(const DecodeParams& p, hipStream_t stream) {
   const int items = p.T * (p.H / kXHeads) * p.max_splits;
   const unsigned grid = (unsigned)(((items + 7) / 8) * 8);
-  if (p.P % 32 == 0) hipLaunchKernelGGL((decode_kernel_h128<true>), dim3(grid), dim3(512), 0, stream, p);
+  if (p.P % 64 == 0) hipLaunchKernelGGL((decode_kernel_h128<true>), dim3(grid), dim3(512), 0, stream, p);
   else hipLaunchKernelGGL((decode_kernel_h128<false>), dim3(grid), dim3(512), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.max_splits <= 1) return e;
