@@ -39,7 +39,7 @@ constexpr int kWorkers = 256;
 // workgroups and never cut a row below kH128MinChunk keys.
 constexpr int kH128Groups = 256;
 constexpr int kH128MinChunk = 512;
-constexpr int kH128Stage = 64;
+constexpr int kH128Stage = 32;
 
 // Launch plan: heads per workgroup and how keys are split.  Depends only on
 // host integers so that the workspace size can be computed in advance.
@@ -66,7 +66,7 @@ Plan make_plan(int T, int H, int max_seq_len, int W, int num_splits, bool split_
   if (p.h128) {
     // A split's partial is 256 KiB (128 heads x 512 fp32): split only when
     // there are fewer tokens than CUs, or when asked to.  Splits are multiples
-    // of the kernel's 64-key stage.
+    // of the kernel's 32-key stage.
     if (split_ok && lmax > 0 && num_splits != 1) {
       if (num_splits > 1) {
         chunk = round_up(ceil_div(lmax, num_splits), kH128Stage);

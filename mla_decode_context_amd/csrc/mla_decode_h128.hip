@@ -6,26 +6,29 @@
 // used by 128 heads of every query row and the contraction dominates (about
 // 240 flop per cache byte per query row).
 //
-// Work decomposition.  A workgroup of 8 waves (two per SIMD) owns one query
-// token, a block of 64 heads and one split of the row's visible keys.  Per
-// 64-key stage:
-//   scores  wave w computes S^T[key][head] = K Q^T for heads 16(w & 3) ..+16
-//           and keys 32(w >> 2) .. +32 of the stage (MFMA 16x16x32, keys on M,
-//           heads on N; K straight from LDS, Q^T resident in VGPRs), then
-//           writes P = 2^(s - m) (bf16, [head][key]) to LDS;
-//   PV      after one barrier, wave w accumulates O^T[dim][head] += V^T P^T for
-//           latent dims 64w .. 64w+63 and all 64 heads (MFMA 32x32x16, V^T from
-//           transposed LDS reads, P^T from LDS).
-// The softmax reference m of a head is lazy: it stays put unless a stage's
-// maximum exceeds it by more than 2^16 (always on the first stage), so
-// p <= 2^16.  Both waves holding a head know m; a stage that moves it for any
-// head (rare after the first) takes a second round: the waves agree on the new
-// m through LDS, rewrite P from the scores still in registers, and the PV waves
-// rescale their accumulators.  Each wave's accumulators are 64 registers (64
-// heads x 64 dims), leaving room for two waves per SIMD.  Stages of 64 rows
-// (72 KiB) arrive by direct-to-LDS loads into a 2-slot ring, one stage ahead.
-// The two head blocks of a token, and those of the next token (the other query
-// row of an MTP request), are consecutive work items placed on the same XCD and
+// Work decomposition.  A workgroup of 8 waves owns one query token, a block of
+// 64 heads and one split of the row's visible keys, in 32-key stages.  The
+// waves specialise, one of each kind per SIMD:
+//   score waves 0..3   wave w computes S^T[key][head] = K Q^T for keys
+//                      16(w >> 1) .. +16 of stage k and heads 32(w & 1) .. +32
+//                      (MFMA 16x16x32, keys on M, heads on N: one K operand
+//                      read from LDS feeds two MFMAs; Q^T resident in VGPRs),
+//                      then writes P = 2^(s - m) (bf16, [head][key]) to LDS;
+//   PV waves 4..7      wave w accumulates O^T[dim][head] += V^T P^T of stage
+//                      k - 1 for latent dims 128(w - 4) .. +128 and all 64
+//                      heads (MFMA 32x32x16, V^T from transposed LDS reads,
+//                      P^T from LDS).
+// So on every SIMD a score wave and a PV wave run side by side, one stage
+// apart, with one barrier per stage; P is double-buffered.  The softmax
+// reference m of a head is lazy: it only moves when a stage's maximum exceeds
+// it by more than 2^16 (always on the first stage), so p <= 2^16.  A stage that
+// moves it for any head takes an extra round before its PV: the two score
+// waves holding a head agree on the new m through LDS and rewrite P from the
+// scores still in their registers, and the PV waves rescale their
+// accumulators.  Stages of 32 rows (36 KiB) arrive by direct-to-LDS loads into
+// a 4-slot ring (stages k - 1 and k in use, k + 1 and k + 2 in flight).  The
+// two head blocks of a token, and those of the next token (the other query row
+// of an MTP request), are consecutive work items placed on the same XCD and
 // dispatched back to back, so they share that XCD's L2 for the cache rows.  A
 // row split over several workgroups writes fp32 partials that
 // combine_fixed_kernel merges afterwards.
@@ -37,31 +40,39 @@ namespace mla {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kXStep = 64;                          // keys per stage
-constexpr int kXStageBytes = kXStep * kRowBytes;    // 72 KiB
-constexpr int kXBlocks = kXStageBytes / 1024;       // 72 load instructions per stage
+constexpr int kXStep = 32;                          // keys per stage
+constexpr int kXStageBytes = kXStep * kRowBytes;    // 36 KiB
+constexpr int kXBlocks = kXStageBytes / 1024;       // 36 load instructions per stage
 constexpr int kXWaves = 8;
-constexpr int kXWaveBlocks = kXBlocks / kXWaves;    // 9 issued by each wave
-constexpr int kXSlots = 2;                          // ring slots: one stage ahead
+constexpr int kXSlots = 4;                          // ring slots
 constexpr int kXHeads = 64;                         // heads per workgroup
-constexpr int kPRow = 144;                          // LDS bytes per head row of P (128 + 16 pad)
+constexpr int kPRow = 80;                           // LDS bytes per head row of P (64 + 16 pad)
+constexpr int kPBuf = kXHeads * kPRow;              // one P buffer
 constexpr float kLazyLog2 = 16.f;                   // softmax reference moves past this margin
 
 __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Waits for this wave's loads of stage k: issued after them are, unless k is
+// the last stage, the next stage's loads (5 for waves 0..3, 4 for waves 4..7).
+__device__ __forceinline__ void wait_stage(bool five, bool more) {
+  if (!more) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+  else if (five) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(5));
+  else __builtin_amdgcn_s_waitcnt(MLA_VMCNT(4));
+}
+
 // LDS writes done, then a workgroup barrier.  (A plain __syncthreads would also
 // wait for the ring's loads still in flight.)
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <bool kPage64>
+template <bool kPage32>
 __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[kXSlots * kXStageBytes];   // 144 KiB
-  __shared__ __attribute__((aligned(16))) uint8_t p_lds[kXHeads * kPRow];        // P, [head][key] bf16
+  __shared__ __attribute__((aligned(16))) uint8_t p_lds[2 * kPBuf];              // P, [buf][head][key] bf16
   __shared__ float mx_lds[2][kXHeads];      // per key half: stage max of each head
   __shared__ float alpha_lds[kXHeads];
-  __shared__ int bump_lds[kXWaves];
+  __shared__ int bump_lds[2][4];            // [stage parity][score wave]
 
   // Item = (split, token, head block), head block fastest.  The hardware deals
   // workgroups to the 8 XCDs round-robin by blockIdx; item x*per_xcd + k goes to
@@ -95,56 +106,34 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
   const int j_begin = split * a.chunk;
   const int j_end = split == nsplit - 1 ? L : j_begin + a.chunk;
   const int n_steps = (j_end - j_begin + kXStep - 1) / kXStep;
-
-  // Scores role: head group sg = w & 3, key half kp = w >> 2 (32 keys: tiles
-  // kt = 0, 1 of 16); lane (head qh = lane % 16, group g = lane / 16).
-  const int sg = w & 3;
-  const int kp = w >> 2;
-  const int qh = lane & 15;
-  const int g = lane >> 4;
-  const int hl_s = 16 * sg + qh;             // this lane's score head within the block
-  // Q^T operand (B of S^T = K Q^T): dims 32s + 8g .. +8 of the head for k-step s
-  // (s < 16: q_nope, s = 16, 17: q_pe).
-  bf16x8 q[18];
-  {
-    const int hs = h0 + hl_s;
-    const uint16_t* qn = a.q_nope + (int64_t)t * a.qn_st + (int64_t)hs * a.qn_sh + 8 * g;
-    const uint16_t* qr = a.q_pe + (int64_t)t * a.qp_st + (int64_t)hs * a.qp_sh + 8 * g;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) q[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qn + 32 * s));
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const u32x2 v0 = *(const u32x2*)(qr + 32 * s);
-      const u32x2 v1 = *(const u32x2*)(qr + 32 * s + 4);
-      q[16 + s] = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+  const bool scorer = w < 4;
 
   const int32_t* bt_row = a.bt + (int64_t)ri.b * a.bt_stride;
   const uint8_t* kv_bytes = (const uint8_t*)a.kv;
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring);
+  const bool five = w < 4;                   // blocks w, w+8, .., below 36
 
   // Stage layout as in the 16-head kernel: byte o of a stage is row o / 1152,
   // 16-byte chunk c = (o % 1152) / 16, holding chunk c ^ (row & 7) of the row.
-  // Wave w issues blocks w, w + 8, ..., w + 64 (1 KiB each).  Keys at or past
-  // j_end (a ragged last stage) are clamped to key j_end - 1, a real cached row
-  // masked to probability 0.
-  auto issue = [&](int i, int slot) {
+  // Keys at or past j_end (a ragged last stage) are clamped to key j_end - 1, a
+  // real cached row masked to probability 0.
+  auto issue = [&](int i) {
     const int j0 = j_begin + kXStep * i;
+    const int slot = i & (kXSlots - 1);
     const uint32_t ldst = ring_lds + slot * kXStageBytes;
-    const bool fast = kPage64 && j0 + kXStep <= j_end;
+    const bool fast = kPage32 && j0 + kXStep <= j_end;
     const uint8_t* base = nullptr;
     if (fast) {
-      // page_size % 64 == 0: the stage's 64 rows are consecutive slots of one page.
+      // page_size % 32 == 0: the stage's 32 rows are consecutive slots of one page.
       const int pg = a.page_shift >= 0 ? j0 >> a.page_shift : j0 / a.P;
       const int blk = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pg];
       base = kv_bytes + ((int64_t)blk * a.kv_bs + (int64_t)(j0 - pg * a.P) * kRow) * 2;
     }
 #pragma unroll
-    for (int u = 0; u < kXWaveBlocks; ++u) {
+    for (int u = 0; u < 5; ++u) {
       const int blkno = w + kXWaves * u;
+      if (u == 4 && !five) break;
       const int o = 1024 * blkno + 16 * lane;
       const int row = o / kRowBytes;
       const int cpos = (o - row * kRowBytes) >> 4;
@@ -165,173 +154,221 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
     }
   };
 
-  // Score reads: lane (key qh of tile kt, group g) reads chunk 4s + g of row
-  // 32kp + 16kt + qh: byte row*1152 + 128*(s >> 1) + 16*((4*(s & 1) + g) ^ (qh & 7)).
-  const uint32_t kbase0 = (32 * kp + qh) * kRowBytes + 16 * (g ^ (qh & 7));
-  const uint32_t kbase1 = (32 * kp + qh) * kRowBytes + 16 * ((4 + g) ^ (qh & 7));
-  // PV: lane (dim row lane % 32 of a 32-dim tile, half hh = lane / 32) needs
-  // keys 16m + 8hh + (0..7) of its dim (MFMA m = 0..3; keys in natural order, as
-  // P^T is stored).  V^T comes from two transposed reads per MFMA: within lane
-  // group G = lane / 16 (hh = G >> 1), source lane j of read r addresses key
-  // 16m + 8hh + 4r + (j >> 2) and dims 64w + 32dt + 16(G & 1) + 4(j & 3):
-  // chunk 8w + 4dt + 2(G & 1) + ((j & 3) >> 1), byte 8(j & 1).  The key's low
-  // three bits are 4r + (j >> 2).
+  // Both roles run the same sequence of barriers: per iteration k the stage
+  // barrier, plus a second one when stage k - 1 moved a softmax reference.
+  auto stage_barrier = [&](int k) {
+    // Stage k's loads have landed (stage k + 1's may be outstanding); the
+    // barrier publishes them, the P and maxima of stage k - 1, and tells that
+    // every wave is past iteration k - 1, so stage k - 2's slot can take stage
+    // k + 2.
+    if (k < n_steps) wait_stage(five, k + 1 < n_steps);
+    asm volatile("s_barrier" ::: "memory");
+    if (k + 2 < n_steps) issue(k + 2);
+    // Flags of stage k - 1 (double-buffered: stage k's are written meanwhile).
+    const int* f = bump_lds[(k - 1) & 1];
+    return k >= 1 ? (f[0] | f[1] | f[2] | f[3]) : 0;
+  };
+  float* l_lds = (float*)p_lds;              // after the loop: [key half][head] sums
+  issue(0);
+  if (n_steps > 1) issue(1);
+
+  if (scorer) {
+    // ---- score waves: heads 32sg .. +32 (two tiles of 16), keys 16kq .. +16 ----
+    const int sg = w & 1;
+    const int kq = w >> 1;
+    const int qh = lane & 15;
+    const int g = lane >> 4;
+    bf16x8 q[2][18];                          // Q^T operand per head tile: dims 32s + 8g .. +8
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const int hs = h0 + 32 * sg + 16 * ht + qh;
+      const uint16_t* qn = a.q_nope + (int64_t)t * a.qn_st + (int64_t)hs * a.qn_sh + 8 * g;
+      const uint16_t* qr = a.q_pe + (int64_t)t * a.qp_st + (int64_t)hs * a.qp_sh + 8 * g;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) q[ht][s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qn + 32 * s));
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const u32x2 v0 = *(const u32x2*)(qr + 32 * s);
+        const u32x2 v1 = *(const u32x2*)(qr + 32 * s + 4);
+        q[ht][16 + s] = __builtin_bit_cast(bf16x8, u32x4{v0[0], v0[1], v1[0], v1[1]});
+      }
+    }
+    // Score reads: lane (key qh, group g) reads chunk 4s + g of row 16kq + qh:
+    // byte row*1152 + 128*(s >> 1) + 16*((4*(s & 1) + g) ^ (qh & 7)).
+    const uint32_t kbase0 = (16 * kq + qh) * kRowBytes + 16 * (g ^ (qh & 7));
+    const uint32_t kbase1 = (16 * kq + qh) * kRowBytes + 16 * ((4 + g) ^ (qh & 7));
+    float m_ref[2] = {-INFINITY, -INFINITY};  // per head tile, of head 32sg + 16ht + qh
+    float l_run[2] = {0.f, 0.f};
+    float v[2][4];                            // this stage's scaled scores (kept for a redo)
+    float psum[2] = {0.f, 0.f};
+    auto write_p = [&](int buf) {
+      // P rows of heads 32sg + 16ht + qh, keys 16kq + 4g .. +4.
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+        const float base = m_ref[ht] == -INFINITY ? 0.f : m_ref[ht];
+        float pe[4];
+        psum[ht] = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pe[r] = fast_exp2(v[ht][r] - base);
+          psum[ht] += pe[r];
+        }
+        uint8_t* prow = p_lds + buf * kPBuf + (32 * sg + 16 * ht + qh) * kPRow + 32 * kq + 8 * g;
+        *(u32x2*)prow = u32x2{pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3])};
+      }
+    };
+    // The query loads are done before the first wait counts stage loads only.
+    __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+    for (int k = 0; k <= n_steps; ++k) {
+      if (stage_barrier(k)) {
+        // Stage k - 1 moved some head's reference: both score waves of each head
+        // take the new one from the two halves' maxima and rewrite P.
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+          const int hl = 32 * sg + 16 * ht + qh;
+          const float mboth = fmaxf(mx_lds[0][hl], mx_lds[1][hl]);
+          float alpha = 1.f;
+          if (mboth > m_ref[ht] + kLazyLog2) {
+            alpha = m_ref[ht] == -INFINITY ? 0.f : fast_exp2(m_ref[ht] - mboth);
+            m_ref[ht] = mboth;
+          }
+          l_run[ht] *= alpha;
+          if (kq == 0 && g == 0) alpha_lds[hl] = alpha;
+        }
+        write_p((k - 1) & 1);
+        lds_barrier();
+      }
+      if (k >= 1) {
+        l_run[0] += psum[0];
+        l_run[1] += psum[1];
+      }
+      if (k < n_steps) {
+        const uint8_t* sb = ring + (k & (kXSlots - 1)) * kXStageBytes;
+        const int j0 = j_begin + kXStep * k + 16 * kq;     // first key of this wave's half
+        f32x4 sc0 = f32x4{0.f, 0.f, 0.f, 0.f}, sc1 = sc0;
+#pragma unroll
+        for (int s = 0; s < 18; ++s) {
+          const bf16x8 kk = *(const bf16x8*)(sb + ((s & 1) ? kbase1 : kbase0) + 128 * (s >> 1));
+          sc0 = mfma_16x16x32(kk, q[0][s], sc0);
+          sc1 = mfma_16x16x32(kk, q[1][s], sc1);
+        }
+        // Lane (head qh of tile ht, group g) holds keys j0 + 4g + r.
+        bool need = false;
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+          const f32x4 sc = ht ? sc1 : sc0;
+          float mx = -INFINITY;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            v[ht][r] = (j0 + 4 * g + r < j_end) ? sc[r] * a.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, v[ht][r]);
+          }
+          mx = col_max(mx);
+          if (g == 0) mx_lds[kq][32 * sg + 16 * ht + qh] = mx;
+          need |= mx > m_ref[ht] + kLazyLog2;
+        }
+        write_p(k & 1);
+        const bool wave_need = (__builtin_amdgcn_read_exec() & __builtin_amdgcn_ballot_w64(need)) != 0;
+        if (lane == 0) bump_lds[k & 1][w] = wave_need ? 1 : 0;
+      } else if (lane == 0) {
+        bump_lds[k & 1][w] = 0;
+      }
+      // P, maxima and flags of stage k are written before the next barrier.
+      __builtin_amdgcn_s_waitcnt(MLA_LGKMCNT0);
+    }
+    // Normalisers through LDS (the P area is free after the barrier).
+    __syncthreads();
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const float lsum = col_sum(l_run[ht]);
+      if (g == 0) l_lds[kq * kXHeads + 32 * sg + 16 * ht + qh] = lsum;
+    }
+    __syncthreads();
+    if (kq == 0 && g == 0) {
+#pragma unroll
+      for (int ht = 0; ht < 2; ++ht) {
+        const int hl = 32 * sg + 16 * ht + qh;
+        const float lse_v = (m_ref[ht] + fast_log2(l_lds[hl] + l_lds[kXHeads + hl])) * kLn2;
+        const int hs = h0 + hl;
+        if (nsplit == 1) a.lse[(size_t)t * a.H + hs] = lse_v;
+        else a.ws_lse[((size_t)split * a.T + t) * a.H + hs] = lse_v;
+      }
+    }
+    return;
+  }
+
+  // ---- PV waves: dims 128pw .. +128 (four tiles of 32), heads 0..63 ----
+  const int pw = w & 3;
   const int hh = lane >> 5;
   const int G = lane >> 4;
   const int jj = lane & 15;
-  uint32_t vb[2][2];                        // [dt][r]
+  // V^T (A of O^T = V^T P^T): lane (dim row lane % 32, half hh) needs keys
+  // 16m + 8hh + (0..7) of its dim (MFMA m; keys in natural order, as P^T is
+  // stored), from two transposed reads per MFMA: within lane group G (hh = G >> 1),
+  // source lane j of read r addresses key 16m + 8hh + 4r + (j >> 2) and dims
+  // 128pw + 32dt + 16(G & 1) + 4(j & 3): chunk 16pw + 4dt + 2(G & 1) + ((j & 3) >> 1),
+  // byte 8(j & 1); the key's low three bits are 4r + (j >> 2).
+  uint32_t vb[2][2];                        // [dt & 1][r]; add 128*(dt >> 1)
 #pragma unroll
-  for (int dt = 0; dt < 2; ++dt)
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int key = 8 * hh + 4 * r + (jj >> 2);
-      vb[dt][r] = key * kRowBytes + 128 * w + 16 * ((4 * dt + 2 * (G & 1) + ((jj & 3) >> 1)) ^ (key & 7)) + 8 * (jj & 1);
+      vb[x][r] = key * kRowBytes + 256 * pw + 16 * ((4 * x + 2 * (G & 1) + ((jj & 3) >> 1)) ^ (key & 7)) + 8 * (jj & 1);
     }
-  // P^T operand (B of O^T = V^T P^T): lane (head 32j + (lane % 32), half hh)
-  // reads keys 16m + 8hh .. +8 of that head's P row.
+  // P^T (B): lane (head 32j + (lane % 32), half hh) reads keys 16m + 8hh .. +8.
   const uint32_t pbase = (uint32_t)((lane & 31) * kPRow + 16 * hh);
-  uint8_t* prow = p_lds + hl_s * kPRow + 64 * kp + 8 * g;   // this lane's P writes
-
-  float m_ref = -INFINITY, l_run = 0.f;     // score head hl_s; l_run over this wave's keys
-  f32x16 o[2][2];                           // O^T tiles [dim tile][head tile]
+  f32x16 o[4][2];                           // O^T tiles [dim tile][head tile]
 #pragma unroll
-  for (int dt = 0; dt < 2; ++dt)
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[dt][j][r] = 0.f;
-
-  issue(0, 0);
-  for (int i = 0; i < n_steps; ++i) {
-    // This wave's loads of stage i have landed; the barrier makes every wave's
-    // part visible and tells that every wave is past stage i - 1 (its ring slot
-    // and P are free), so stage i + 1 can go into that slot.
-    __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
-    asm volatile("s_barrier" ::: "memory");
-    if (i + 1 < n_steps) issue(i + 1, (i + 1) & 1);
-    const uint8_t* sb = ring + (i & 1) * kXStageBytes;
-    const int j0 = j_begin + kXStep * i + 32 * kp;      // first key of this wave's half
-
-    // ---- scores: 32 keys x 16 heads over 576 dims ----
-    f32x4 sc[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const uint8_t* kpp = sb + kt * 16 * kRowBytes;
-      f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-#pragma unroll
-      for (int s = 0; s < 18; s += 2) {
-        const bf16x8 k0 = *(const bf16x8*)(kpp + kbase0 + 128 * (s >> 1));
-        const bf16x8 k1 = *(const bf16x8*)(kpp + kbase1 + 128 * (s >> 1));
-        s0 = mfma_16x16x32(k0, q[s], s0);
-        s1 = mfma_16x16x32(k1, q[s + 1], s1);
-      }
-      sc[kt] = s0 + s1;
-    }
-    // Lane (head qh, group g) holds keys j0 + 16kt + 4g + r.
-    float v[8];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float x = (j0 + 16 * kt + 4 * g + r < j_end) ? sc[kt][r] * a.scale_log2 : -INFINITY;
-        v[4 * kt + r] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = col_max(mx);
-    // P with the current reference; a stage whose max runs past it is redone below.
-    const bool need = mx > m_ref + kLazyLog2;
-    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-    auto write_p = [&](float base, float& psum) {
-      psum = 0.f;
-      uint32_t pk[4];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        float pe[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pe[r] = fast_exp2(v[4 * kt + r] - base);
-          psum += pe[r];
-        }
-        pk[2 * kt] = pack_bf16x2(pe[0], pe[1]);
-        pk[2 * kt + 1] = pack_bf16x2(pe[2], pe[3]);
-      }
-      *(u32x2*)(prow) = u32x2{pk[0], pk[1]};
-      *(u32x2*)(prow + 32) = u32x2{pk[2], pk[3]};
-    };
-    float psum;
-    if (!need) write_p(m_use, psum);
-    if (g == 0) mx_lds[kp][hl_s] = mx;
-    const bool wave_need = (__builtin_amdgcn_read_exec() & __builtin_amdgcn_ballot_w64(need)) != 0;
-    if (lane == 0) bump_lds[w] = wave_need ? 1 : 0;
-    lds_barrier();
-    int bump = 0;
-#pragma unroll
-    for (int u = 0; u < kXWaves; ++u) bump |= bump_lds[u];
-    if (bump) {
-      // Some head's max ran past its reference: both waves of every head take the
-      // same new reference from the two halves' maxima and rewrite P.
-      const float mboth = fmaxf(mx_lds[0][hl_s], mx_lds[1][hl_s]);
-      float alpha = 1.f;
-      if (mboth > m_ref + kLazyLog2) {
-        alpha = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - mboth);
-        m_ref = mboth;
-      }
-      write_p(m_ref, psum);
-      l_run *= alpha;
-      if (kp == 0 && g == 0) alpha_lds[hl_s] = alpha;
-      lds_barrier();
+  for (int k = 0; k <= n_steps; ++k) {
+    if (stage_barrier(k)) {
+      lds_barrier();                          // the score waves' new P and factors
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const float al = alpha_lds[32 * j + (lane & 31)];
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) o[dt][j] *= al;
+        for (int dt = 0; dt < 4; ++dt) o[dt][j] *= al;
       }
     }
-    l_run += psum;
-
-    // ---- PV for dims 64w .. 64w+63, all 64 heads, 64 keys ----
+    if (k >= 1) {
+      // PV of stage k - 1: dims 128pw .. +128, all 64 heads, 32 keys.
+      const uint8_t* sb = ring + ((k - 1) & (kXSlots - 1)) * kXStageBytes;
+      const uint8_t* pb = p_lds + ((k - 1) & 1) * kPBuf + pbase;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      bf16x8 pbv[2];
+      for (int m = 0; m < 2; ++m) {
+        bf16x8 pbv[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) pbv[j] = *(const bf16x8*)(p_lds + pbase + 32 * j * kPRow + 32 * m);
+        for (int j = 0; j < 2; ++j) pbv[j] = *(const bf16x8*)(pb + 32 * j * kPRow + 32 * m);
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        const uint8_t* vp = sb + 16 * m * kRowBytes;
-        const s16x4 lo = lds_read_tr16_at(vp + vb[dt][0]);
-        const s16x4 hi = lds_read_tr16_at(vp + vb[dt][1]);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        for (int dt = 0; dt < 4; ++dt) {
+          const uint8_t* vp = sb + 128 * (dt >> 1) + 16 * m * kRowBytes;
+          const s16x4 lo = lds_read_tr16_at(vp + vb[dt & 1][0]);
+          const s16x4 hi = lds_read_tr16_at(vp + vb[dt & 1][1]);
+          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-        for (int j = 0; j < 2; ++j) o[dt][j] = mfma_32x32x16(va, pbv[j], o[dt][j]);
+          for (int j = 0; j < 2; ++j) o[dt][j] = mfma_32x32x16(va, pbv[j], o[dt][j]);
+        }
       }
     }
   }
-  l_run = col_sum(l_run);
-
-  // Normalisers of all 64 heads through LDS (the P area is free after a barrier).
   __syncthreads();
-  float* l_lds = (float*)p_lds;              // [key half][head]
-  if (g == 0) l_lds[kp * kXHeads + hl_s] = l_run;
-  __syncthreads();
-  if (kp == 0 && g == 0) {
-    const float lsum = l_lds[hl_s] + l_lds[kXHeads + hl_s];
-    const float lse_v = (m_ref + fast_log2(lsum)) * kLn2;
-    const int hs = h0 + hl_s;
-    if (nsplit == 1) a.lse[(size_t)t * a.H + hs] = lse_v;
-    else a.ws_lse[((size_t)split * a.T + t) * a.H + hs] = lse_v;
-  }
+  __syncthreads();                            // the score waves' sums are in LDS
   // Lane (dim row, half hh) of tile (dt, j) holds head 32j + (lane % 32) and
-  // dims 64w + 32dt + 8q + 4hh + (0..3) in registers 4q .. 4q+3.
+  // dims 128pw + 32dt + 8q + 4hh + (0..3) in registers 4q .. 4q+3.
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int hl = 32 * j + (lane & 31);
     const float inv = 1.f / (l_lds[hl] + l_lds[kXHeads + hl]);
     const int h = h0 + hl;
     if (nsplit == 1) {
-      uint16_t* op = a.out + ((size_t)t * a.H + h) * kLatent + 64 * w + 4 * hh;
+      uint16_t* op = a.out + ((size_t)t * a.H + h) * kLatent + 128 * pw + 4 * hh;
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd)
           *(u32x2*)(op + 32 * dt + 8 * qd) =
@@ -339,9 +376,9 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
                     pack_bf16x2(o[dt][j][4 * qd + 2] * inv, o[dt][j][4 * qd + 3] * inv)};
     } else {
       // Partial of split `split`, read by the combine kernel after this launch.
-      float* wp = a.ws_o + (((size_t)split * a.T + t) * a.H + h) * kLatent + 64 * w + 4 * hh;
+      float* wp = a.ws_o + (((size_t)split * a.T + t) * a.H + h) * kLatent + 128 * pw + 4 * hh;
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd)
           *(f32x4*)(wp + 32 * dt + 8 * qd) = f32x4{o[dt][j][4 * qd] * inv, o[dt][j][4 * qd + 1] * inv,
@@ -400,7 +437,7 @@ __global__ __launch_bounds__(256) void combine_fixed_kernel(const DecodeParams a
 hipError_t launch_decode_h128(const DecodeParams& p, hipStream_t stream) {
   const int items = p.T * (p.H / kXHeads) * p.max_splits;
   const unsigned grid = (unsigned)(((items + 7) / 8) * 8);
-  if (p.P % 64 == 0) hipLaunchKernelGGL((decode_kernel_h128<true>), dim3(grid), dim3(512), 0, stream, p);
+  if (p.P % 32 == 0) hipLaunchKernelGGL((decode_kernel_h128<true>), dim3(grid), dim3(512), 0, stream, p);
   else hipLaunchKernelGGL((decode_kernel_h128<false>), dim3(grid), dim3(512), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.max_splits <= 1) return e;
