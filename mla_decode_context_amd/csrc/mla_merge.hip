@@ -50,47 +50,72 @@ __device__ __forceinline__ bool merge_lse(const MergeParams& a, int t, int h, fl
   return true;
 }
 
-// One wave per (t, h) row; lane l owns latent dims 8l .. 8l+7.  Partials are
-// fetched eight ranks at a time so their loads are in flight together.
+// Workgroup = (token t, 16 heads); thread (head 16*blockIdx.y + tid / 16, dims
+// 32*(tid % 16) .. +32).  Whether rank w takes part in row t is the same for
+// every thread of the workgroup, so valid[w, t] comes through scalar loads;
+// the LSEs and partials of up to eight participating ranks are then loaded
+// together and combined online (running max, rescaled sum), ranks in order.
 __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t rowi = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (rowi >= (int64_t)a.T * a.H) return;
-  const int t = (int)(rowi / a.H);
-  const int h = (int)(rowi - (int64_t)t * a.H);
+  const int t = blockIdx.x;
+  const int h = 16 * blockIdx.y + (threadIdx.x >> 4);
+  const int d0 = 32 * (threadIdx.x & 15);
+  const bool hok = h < a.H;
+  const int hc = hok ? h : a.H - 1;
   const size_t plane = (size_t)a.T * a.H;
-  float lse_tot;
-  const bool any = merge_lse(a, t, h, lse_tot);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (any) {
-    for (int w0 = 0; w0 < a.W; w0 += 8) {
-      u32x4 v[8];
-      float wgt[8];
+  const size_t row = (size_t)t * a.H + hc;
+  const int32_t* vcol = a.valid;
+  float m = -INFINITY, ssum = 0.f;
+  f32x4 acc[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int w = w0 + k;
-        wgt[k] = 0.f;
-        v[k] = u32x4{0u, 0u, 0u, 0u};
-        float l;
-        if (w < a.W && takes_part(a, w, t, w * plane + rowi, l)) {
-          wgt[k] = fast_exp2((l - lse_tot) * kLog2e);
-          v[k] = *(const u32x4*)(a.outs + (w * plane + rowi) * kLatent + lane * 8);
-        }
-      }
+  for (int k = 0; k < 8; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int w0 = 0; w0 < a.W; w0 += 8) {
+    float l[8];
+    u32x4 x[8][4];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+    for (int u = 0; u < 8; ++u) {
+      const int w = w0 + u;
+      bool take = w < a.W;
+      if (take && vcol)
+        take = ((const __attribute__((address_space(4))) int32_t*)vcol)[(size_t)w * a.T + t] > 0;
+      l[u] = -INFINITY;
+      if (take) {
+        l[u] = a.lses[w * plane + row];
+        const u32x4* src = (const u32x4*)(a.outs + (w * plane + row) * kLatent + d0);
+        if (vcol || l[u] > -INFINITY) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += wgt[k] * bf16_lo(v[k][e]);
-          acc[2 * e + 1] += wgt[k] * bf16_hi(v[k][e]);
+          for (int k = 0; k < 4; ++k) x[u][k] = src[k];
         }
       }
     }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      // A rank whose LSE is -inf (or NaN, without counts) adds nothing.
+      const float mn = fmaxf(m, l[u]);
+      if (l[u] > -INFINITY && mn > -INFINITY) {
+        const float c_old = m == -INFINITY ? 0.f : fast_exp2((m - mn) * kLog2e);
+        const float c_new = fast_exp2((l[u] - mn) * kLog2e);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[2 * k] = acc[2 * k] * c_old + f32x4{bf16_lo(x[u][k][0]), bf16_hi(x[u][k][0]),
+                                                  bf16_lo(x[u][k][1]), bf16_hi(x[u][k][1])} * c_new;
+          acc[2 * k + 1] = acc[2 * k + 1] * c_old + f32x4{bf16_lo(x[u][k][2]), bf16_hi(x[u][k][2]),
+                                                          bf16_lo(x[u][k][3]), bf16_hi(x[u][k][3])} * c_new;
+        }
+        ssum = ssum * c_old + c_new;
+        m = mn;
+      }
+    }
   }
-  *(u32x4*)(a.out + (size_t)rowi * kLatent + lane * 8) =
-      u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-            pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
-  if (a.out_lse && lane == 0) a.out_lse[rowi] = lse_tot;
+  if (!hok) return;
+  const float inv = ssum > 0.f ? 1.f / ssum : 0.f;
+  uint16_t* op = a.out + row * kLatent + d0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    *(u32x4*)(op + 8 * k) = u32x4{pack_bf16x2(acc[2 * k][0] * inv, acc[2 * k][1] * inv),
+                                  pack_bf16x2(acc[2 * k][2] * inv, acc[2 * k][3] * inv),
+                                  pack_bf16x2(acc[2 * k + 1][0] * inv, acc[2 * k + 1][1] * inv),
+                                  pack_bf16x2(acc[2 * k + 1][2] * inv, acc[2 * k + 1][3] * inv)};
+  if (a.out_lse && (threadIdx.x & 15) == 0) a.out_lse[row] = ssum > 0.f ? m + fast_log2(ssum) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -185,9 +210,8 @@ __global__ __launch_bounds__(256) void merge_v_up_kernel(const MergeParams a) {
 }
 
 hipError_t launch_lse_merge(const MergeParams& p, hipStream_t stream) {
-  const int64_t rows = (int64_t)p.T * p.H;
-  if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p);
+  if (p.T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)p.T, (unsigned)((p.H + 15) / 16)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
