@@ -10,6 +10,7 @@
 // Both kernels stream the partials once from HBM (the merge is bandwidth-bound:
 // about W*1 KiB read per (token, head) against 1 KiB or 256 B written).
 #include "mla_common.h"
+#include "mla_device.h"
 #include "mla_kernels.h"
 
 namespace mla {
@@ -119,93 +120,169 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams a) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge fused with W_UV.  Workgroup = (head h, 64 tokens); wave w owns tokens
-// 16w .. 16w+15 of the block.  For each 32-wide k-step the wave forms the
-// merged latent slice of its 16 tokens directly in the MFMA operand layout
-// (lane (token lr, group g) holds dims 32s + 8g .. +8), rounds it to bf16 and
-// multiplies it with W_UV[h]^T, which the workgroup stages in LDS transposed
-// ([n][k]) 128 k-rows at a time.  y^T[n][token] accumulates in 8 tiles of
-// 16 n x 16 tokens.
+// Merge fused with W_UV.  Workgroup = (head h, a contiguous range of tokens).
+// W_UV[h] (512 x 128 bf16, 128 KiB) is staged once into LDS; the tokens then
+// stream through in blocks of 16: the merged latent rows of a block (exact
+// LSE-weighted combine of the participating ranks, rounded to bf16) go to LDS,
+// and y[tok][n] = o[tok][k] W[k][n] runs on MFMA 16x16x32 (wave w: n = 32w ..
+// 32w+31), A = o from LDS, B = W through transposed LDS reads.  The next
+// block's partials are loaded while the current block is multiplied.
+//
+// LDS layouts (both swizzled so that the MFMA operand reads are conflict-free):
+//   W  row k (256 B) holds element n at byte (2n) ^ (32 * (k & 7));
+//   o  row t (1 KiB) holds 16-byte chunk c at chunk position c ^ (t & 7).
 // ---------------------------------------------------------------------------
-constexpr int kProjTok = 64;       // tokens per workgroup
-constexpr int kKChunk = 128;       // k rows of W_UV staged per pass
-constexpr int kWtStride = kKChunk + 8;   // LDS row stride (bf16) of W_UV^T: 272 B
+constexpr int kProjBlk = 16;                       // tokens per block
+constexpr int kWBytes = kLatent * kVHead * 2;      // 128 KiB
 
-__global__ __launch_bounds__(256) void merge_v_up_kernel(const MergeParams a) {
-  __shared__ __attribute__((aligned(16))) uint16_t wt[kVHead * kWtStride];
+__global__ __launch_bounds__(256, 1) void merge_v_up_kernel(const MergeParams a) {
+  __shared__ __attribute__((aligned(16))) uint8_t w_lds[kWBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t o_lds[kProjBlk * kLatent * 2];   // 16 KiB
 
+  const int h = blockIdx.x;
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int lr = lane & 15;
-  const int g = lane >> 4;
-  const int h = blockIdx.y;
-  const int t = blockIdx.x * kProjTok + 16 * w + lr;
-  const bool row_ok = t < a.T;
-  const size_t plane = (size_t)a.T * a.H;
-  const size_t rowi = (size_t)(row_ok ? t : 0) * a.H + h;
+  const int wv = threadIdx.x >> 6;
+  const int per = (a.T + (int)gridDim.y - 1) / (int)gridDim.y;
+  const int t_begin = (int)blockIdx.y * per;
+  const int t_end = min(a.T, t_begin + per);
+  if (t_begin >= t_end) return;
 
-  float lse_tot = -INFINITY;
-  const bool any = row_ok && merge_lse(a, row_ok ? t : 0, h, lse_tot);
-
-  f32x4 y[8];
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) y[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const uint16_t* wsrc = a.wuv + (size_t)h * kLatent * kVHead;
-  for (int kc = 0; kc < kLatent; kc += kKChunk) {
-    __syncthreads();
-    // Stage W_UV[h][kc .. kc+128][0 .. 128] transposed: thread takes k = idx % 128
-    // and eight consecutive n, writes them down column k of rows n .. n+7.
-#pragma unroll
-    for (int it = 0; it < (kKChunk * kVHead / 8) / 256; ++it) {
-      const int idx = it * 256 + threadIdx.x;
-      const int k = idx & (kKChunk - 1);
-      const int n0 = (idx / kKChunk) * 8;
-      const u32x4 v = *(const u32x4*)(wsrc + (size_t)(kc + k) * kVHead + n0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        wt[(n0 + 2 * e) * kWtStride + k] = (uint16_t)(v[e] & 0xFFFFu);
-        wt[(n0 + 2 * e + 1) * kWtStride + k] = (uint16_t)(v[e] >> 16);
-      }
-    }
-    __syncthreads();
-
-#pragma unroll
-    for (int s = 0; s < kKChunk / 32; ++s) {
-      const int d0 = kc + 32 * s + 8 * g;
-      float m8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (any) {
-        for (int wr = 0; wr < a.W; ++wr) {
-          float l;
-          if (takes_part(a, wr, t, wr * plane + rowi, l)) {
-            const float wgt = fast_exp2((l - lse_tot) * kLog2e);
-            const u32x4 v = *(const u32x4*)(a.outs + (wr * plane + rowi) * kLatent + d0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              m8[2 * e] += wgt * bf16_lo(v[e]);
-              m8[2 * e + 1] += wgt * bf16_hi(v[e]);
-            }
-          }
-        }
-      }
-      const u32x4 mb = u32x4{pack_bf16x2(m8[0], m8[1]), pack_bf16x2(m8[2], m8[3]),
-                             pack_bf16x2(m8[4], m8[5]), pack_bf16x2(m8[6], m8[7])};
-      const bf16x8 bop = __builtin_bit_cast(bf16x8, mb);
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const u32x4 av = *(const u32x4*)(wt + (16 * nt + lr) * kWtStride + 32 * s + 8 * g);
-        y[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), bop, y[nt], 0, 0, 0);
-      }
+  // Stage W_UV[h]: 128 loads of 1 KiB (4 rows each); wave wv issues 32 of them.
+  {
+    const uint8_t* src = (const uint8_t*)(a.wuv + (size_t)h * kLatent * kVHead);
+    const uint32_t base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)w_lds;
+#pragma unroll 4
+    for (int i = 0; i < 32; ++i) {
+      const int blk = 32 * wv + i;
+      const int o = 1024 * blk + 16 * lane;          // LDS byte
+      const int k = o >> 8;
+      const int c = o & 255;
+      dma_16B_to_lds(src + k * 256 + (c ^ (32 * (k & 7))), w_lds + 1024 * blk);
+      (void)base;
     }
   }
 
-  // y^T tile nt: lane (token lr, group g) holds n = 16nt + 4g + (0..3).
-  if (row_ok) {
-    uint16_t* op = a.out + ((size_t)t * a.H + h) * kVHead + 4 * g;
+  // Merge role: thread (token tt = tid / 16 of the block, dims 32*(tid % 16) .. +32).
+  const int tt = threadIdx.x >> 4;
+  const int d0 = 32 * (threadIdx.x & 15);
+  const size_t plane = (size_t)a.T * a.H;
+  // MFMA role: lane (row lr = lane % 16, group g = lane / 16).
+  const int lr = lane & 15;
+  const int g = lane >> 4;
+
+  // Loads of one block's first <= 4 participating ranks for this thread.
+  struct Pend {
+    u32x4 x[4][4];
+    float l[4];
+    int nr;            // ranks covered (<= 4)
+  };
+  auto load_ranks = [&](int t, int w0, Pend& p) {
+    p.nr = 0;
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-      *(u32x2*)(op + 16 * nt) = u32x2{pack_bf16x2(y[nt][0], y[nt][1]), pack_bf16x2(y[nt][2], y[nt][3])};
-    if (a.out_lse && g == 0) a.out_lse[rowi] = lse_tot;
+    for (int u = 0; u < 4; ++u) {
+      const int w = w0 + u;
+      p.l[u] = -INFINITY;
+      if (t < t_end && w < a.W) {
+        bool take = true;
+        if (a.valid) take = a.valid[(size_t)w * a.T + t] > 0;
+        if (take) {
+          const size_t row = w * plane + (size_t)t * a.H + h;
+          p.l[u] = a.lses[row];
+          if (a.valid || p.l[u] > -INFINITY) {
+            const u32x4* src = (const u32x4*)(a.outs + row * kLatent + d0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) p.x[u][k] = src[k];
+          }
+        }
+      }
+    }
+  };
+
+  Pend nxt;
+  load_ranks(t_begin + tt, 0, nxt);
+  for (int tb = t_begin; tb < t_end; tb += kProjBlk) {
+    const int t = tb + tt;
+    // ---- merge this thread's token and 32 dims over all ranks ----
+    float m = -INFINITY, ssum = 0.f;
+    f32x4 acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int w0 = 0; w0 < a.W; w0 += 4) {
+      Pend cur = nxt;
+      if (w0 + 4 < a.W) load_ranks(t, w0 + 4, nxt);          // rest of this token's ranks
+      else load_ranks(t + kProjBlk, 0, nxt);                  // the next block's first ranks
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float mn = fmaxf(m, cur.l[u]);
+        if (cur.l[u] > -INFINITY && mn > -INFINITY) {
+          const float c_old = m == -INFINITY ? 0.f : fast_exp2((m - mn) * kLog2e);
+          const float c_new = fast_exp2((cur.l[u] - mn) * kLog2e);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            acc[2 * k] = acc[2 * k] * c_old + f32x4{bf16_lo(cur.x[u][k][0]), bf16_hi(cur.x[u][k][0]),
+                                                    bf16_lo(cur.x[u][k][1]), bf16_hi(cur.x[u][k][1])} * c_new;
+            acc[2 * k + 1] = acc[2 * k + 1] * c_old + f32x4{bf16_lo(cur.x[u][k][2]), bf16_hi(cur.x[u][k][2]),
+                                                            bf16_lo(cur.x[u][k][3]), bf16_hi(cur.x[u][k][3])} * c_new;
+          }
+          ssum = ssum * c_old + c_new;
+          m = mn;
+        }
+      }
+    }
+    // Merged latent row (bf16) into o_lds; an absent token or a row with no
+    // participating rank is zero.
+    const float inv = ssum > 0.f ? 1.f / ssum : 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = (d0 >> 3) + k;
+      *(u32x4*)(o_lds + tt * 1024 + 16 * (c ^ (tt & 7))) =
+          u32x4{pack_bf16x2(acc[2 * k][0] * inv, acc[2 * k][1] * inv),
+                pack_bf16x2(acc[2 * k][2] * inv, acc[2 * k][3] * inv),
+                pack_bf16x2(acc[2 * k + 1][0] * inv, acc[2 * k + 1][1] * inv),
+                pack_bf16x2(acc[2 * k + 1][2] * inv, acc[2 * k + 1][3] * inv)};
+    }
+    if (a.out_lse && (threadIdx.x & 15) == 0 && t < t_end)
+      a.out_lse[(size_t)t * a.H + h] = ssum > 0.f ? m + fast_log2(ssum) * kLn2 : -INFINITY;
+    // W_UV staged (first block) and the block's rows written; the next block's
+    // partial loads may still be in flight (they target registers, not LDS).
+    if (tb == t_begin) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    // ---- y[tok][n] for the block's 16 tokens, n = 32wv .. 32wv+31 ----
+    f32x4 y[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < kLatent / 32; ++s) {
+      // A = o: lane (token lr, group g) takes dims 32s + 8g .. +8 (chunk 4s + g).
+      const bf16x8 av = *(const bf16x8*)(o_lds + lr * 1024 + 16 * ((4 * s + g) ^ (lr & 7)));
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        // B = W: lane (column n = 32wv + 16nt + lr, group g) takes k = 32s + 8g .. +8
+        // from two transposed reads: source lane j of read r addresses row
+        // k = 32s + 8g + 4r + (j >> 2), columns n0 + 4(j & 3) .. +4.
+        const int n0 = 32 * wv + 16 * nt;
+        s16x4 half[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int k = 32 * s + 8 * g + 4 * r + (lr >> 2);
+          const int cb = 2 * (n0 + 4 * (lr & 3));
+          half[r] = lds_read_tr16_at(w_lds + k * 256 + (cb ^ (32 * (k & 7))));
+        }
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        y[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, y[nt], 0, 0, 0);
+      }
+    }
+    // D: lane (column n = n0 + lr, group g) holds tokens 4g .. 4g+3 of the block.
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int n = 32 * wv + 16 * nt + lr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int to = tb + 4 * g + r;
+        if (to < t_end) a.out[((size_t)to * a.H + h) * kVHead + n] = __builtin_bit_cast(uint16_t, (__bf16)y[nt][r]);
+      }
+    }
+    // o_lds is rewritten by the next block.
+    asm volatile("s_barrier" ::: "memory");
   }
 }
 
@@ -217,8 +294,11 @@ hipError_t launch_lse_merge(const MergeParams& p, hipStream_t stream) {
 
 hipError_t launch_merge_v_up(const MergeParams& p, hipStream_t stream) {
   if (p.T <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((p.T + kProjTok - 1) / kProjTok), (unsigned)p.H);
-  hipLaunchKernelGGL(merge_v_up_kernel, grid, dim3(256), 0, stream, p);
+  // About 256 workgroups (one per CU): heads x token ranges.
+  int groups = (256 + p.H - 1) / p.H;
+  const int max_groups = (p.T + kProjBlk - 1) / kProjBlk;
+  if (groups > max_groups) groups = max_groups;
+  hipLaunchKernelGGL(merge_v_up_kernel, dim3((unsigned)p.H, (unsigned)groups), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
