@@ -151,6 +151,7 @@ def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True
         res["query_tokens_per_s_one_rank"] = wl.T / ((dec_avg.max() + mg_ms) * 1e-3)
     if headline:
         res["_alg_bytes_per_launch"] = float(alg_bytes.mean())
+        res["_alg_flops_per_launch"] = float(alg_flops.mean())
         res["_decode_avg_ms"] = float(dec_avg.mean())
         res["_kernel"] = dw.decode_kernel_name()
         res["_cold_kv_GBps"] = cold_kv(dw, wl, per_shard, torch) if cold else None
@@ -270,7 +271,20 @@ def main():
         print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl)
     achieved = head["_alg_bytes_per_launch"] / (head["_decode_avg_ms"] * 1e-3) / 1e9
-    traffic = load_traffic(args.workload)
+    # The bound is whichever roofline time is longer at peak: bytes at 8 TB/s or
+    # flops at the dense bf16 MFMA peak.
+    t_mem = head["_alg_bytes_per_launch"] / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = head["_alg_flops_per_launch"] / (BF16_PEAK_TFLOPS * 1e12)
+    if t_mfma > t_mem:
+        tflops = head["_alg_flops_per_launch"] / (head["_decode_avg_ms"] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": load_traffic(args.workload)}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(args.workload)}
+    roofline.update({"kernel": head["_kernel"], "avg_launch_ms": round(head["_decode_avg_ms"], 5),
+                     "alg_bytes_per_launch": int(head["_alg_bytes_per_launch"]),
+                     "alg_flops_per_launch": int(head["_alg_flops_per_launch"])})
     cfg = WL.CONFIGS[args.workload]
     line = {
         "metric": METRIC,
@@ -290,10 +304,7 @@ def main():
         "pct_hbm_peak": round(100.0 * head["kv_GBps"] / HBM_PEAK_GBPS, 2),
         "query_tokens_per_s": round(head["query_tokens_per_s"], 1),
         "kv_GBps_cold_llc": None if head["_cold_kv_GBps"] is None else round(head["_cold_kv_GBps"], 2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": head["_kernel"], "avg_launch_ms": round(head["_decode_avg_ms"], 5),
-                     "alg_bytes_per_launch": int(head["_alg_bytes_per_launch"])},
+        "roofline": roofline,
         "merge_GBps": configs.get("mtp_dcp4", {}).get("merge_GBps"),
         "cpu_baseline": cpu,
         "configs": configs,

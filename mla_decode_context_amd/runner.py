@@ -59,6 +59,10 @@ class DeviceWorkload:
     def decode_kernel_name(self) -> str:
         """Kernels one mla_decode_partial call launches for this shape (with the
         automatic split plan), joined by "+"."""
+        if self.H == 128:
+            page32 = "true" if self.wl.P % 32 == 0 else "false"
+            name = f"decode_kernel_h128<{page32}>"
+            return name + "+combine_fixed_kernel" if self.workspace is not None else name
         page16 = "true" if self.wl.P % 16 == 0 else "false"
         if self.H <= 16:
             if self.num_splits == 0 and self.workspace is not None:
