@@ -115,15 +115,26 @@ def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    ev_sets = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(wl.W + 1)] for _ in range(steps)]
+    # Timed region: the steps back to back, as a serving loop issues them, with
+    # one pair of events around the whole region (on the launch stream).
+    ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev_a.record()
     for k in range(steps):
-        step(ev_sets[k])
+        step()
+    ev_b.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / steps
+    ev_ms_step = ev_a.elapsed_time(ev_b) / steps
+    # Breakdown pass: the same steps with events around every call (the markers
+    # add a little time per call, so these feed only the per-shard figures).
+    ev_sets = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(wl.W + 1)] for _ in range(steps)]
+    for k in range(steps):
+        step(ev_sets[k])
+    torch.cuda.synchronize()
     dec_ms = np.array([[ev_sets[k][r][0].elapsed_time(ev_sets[k][r][1]) for r in range(wl.W)]
                        for k in range(steps)])                      # [steps, W]
     res = dict(workload=name, T=wl.T, B=wl.B, H=wl.H, W=wl.W, ms_per_step=ms_step)
@@ -149,10 +160,15 @@ def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True
         res["merge_GBps"] = mbytes / (mg_ms * 1e-3) / 1e9
         res["merge_pct_hbm_peak"] = 100.0 * res["merge_GBps"] / HBM_PEAK_GBPS
         res["query_tokens_per_s_one_rank"] = wl.T / ((dec_avg.max() + mg_ms) * 1e-3)
+    res["ms_per_step_events"] = float(ev_ms_step)
     if headline:
         res["_alg_bytes_per_launch"] = float(alg_bytes.mean())
         res["_alg_flops_per_launch"] = float(alg_flops.mean())
-        res["_decode_avg_ms"] = float(dec_avg.mean())
+        # Average duration of one decode call (its decode kernel and, when rows
+        # were split, the combine kernel): with one rank and no merge a step is
+        # exactly one call, so the timed region's events divided by the steps;
+        # otherwise the per-call events of the breakdown pass.
+        res["_decode_avg_ms"] = float(ev_ms_step) if wl.W == 1 else float(dec_avg.mean())
         res["_kernel"] = dw.decode_kernel_name()
         res["_cold_kv_GBps"] = cold_kv(dw, wl, per_shard, torch) if cold else None
     del dw
@@ -160,12 +176,15 @@ def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True
     return res, wl
 
 
-def cold_kv(dw, wl, per_shard, torch, reps=5):
-    """KV GB/s with the 256 MB last-level cache flushed (1 GiB write) before each step."""
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dw.device)
+def cold_kv(dw, wl, per_shard, torch, reps=7):
+    """KV GB/s of one step started from an idle GPU whose 256 MB last-level
+    cache was just flushed by reading 1 GiB (a read leaves no dirty lines whose
+    write-back would compete with the decode)."""
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dw.device)
     times = []
     for _ in range(reps):
-        flush.fill_(1.0)
+        float(flush.sum())
+        torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
@@ -233,7 +252,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first (the GPU's clocks settle over a few thousand microseconds of work)")
     ap.add_argument("--workload", default="plain")
     ap.add_argument("--configs", default="mtp_dcp4,long_dcp8,mixed_wuv",
                     help="comma-separated secondary workloads ('' for none)")
