@@ -27,6 +27,10 @@
 // scores still in their registers, and the PV waves rescale their
 // accumulators.  Stages of 32 rows (36 KiB) arrive by direct-to-LDS loads into
 // a 4-slot ring (stages k - 1 and k in use, k + 1 and k + 2 in flight).  The
+// PV waves issue and await all stage loads, and the score waves run at a
+// higher issue priority: the score waves' chain (K reads, scores, softmax, P
+// writes) is the critical path of a stage, so everything else is kept off it.
+// The
 // two head blocks of a token, and those of the next token (the other query row
 // of an MTP request), are consecutive work items placed on the same XCD and
 // dispatched back to back, so they share that XCD's L2 for the cache rows.  A
@@ -55,11 +59,10 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 // Waits for this wave's loads of stage k: issued after them are, unless k is
-// the last stage, the next stage's loads (5 for waves 0..3, 4 for waves 4..7).
-__device__ __forceinline__ void wait_stage(bool five, bool more) {
+// the last stage, the next stage's nine loads.  Only the PV waves load stages.
+__device__ __forceinline__ void wait_stage(bool more) {
   if (!more) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
-  else if (five) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(5));
-  else __builtin_amdgcn_s_waitcnt(MLA_VMCNT(4));
+  else __builtin_amdgcn_s_waitcnt(MLA_VMCNT(9));
 }
 
 // LDS writes done, then a workgroup barrier.  (A plain __syncthreads would also
@@ -112,7 +115,6 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
   const uint8_t* kv_bytes = (const uint8_t*)a.kv;
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring);
-  const bool five = w < 4;                   // blocks w, w+8, .., below 36
 
   // Stage layout as in the 16-head kernel: byte o of a stage is row o / 1152,
   // 16-byte chunk c = (o % 1152) / 16, holding chunk c ^ (row & 7) of the row.
@@ -131,9 +133,9 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
       base = kv_bytes + ((int64_t)blk * a.kv_bs + (int64_t)(j0 - pg * a.P) * kRow) * 2;
     }
 #pragma unroll
-    for (int u = 0; u < 5; ++u) {
-      const int blkno = w + kXWaves * u;
-      if (u == 4 && !five) break;
+    for (int u = 0; u < 9; ++u) {
+      if (w < 4) break;                          // PV wave pw loads blocks pw, pw+4, .., pw+32
+      const int blkno = (w - 4) + 4 * u;
       const int o = 1024 * blkno + 16 * lane;
       const int row = o / kRowBytes;
       const int cpos = (o - row * kRowBytes) >> 4;
@@ -161,10 +163,12 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
     // barrier publishes them, the P and maxima of stage k - 1, and tells that
     // every wave is past iteration k - 1, so stage k - 2's slot can take stage
     // k + 2.
-    if (k < n_steps) wait_stage(five, k + 1 < n_steps);
+    if (w >= 4 && k < n_steps) wait_stage(k + 1 < n_steps);
     asm volatile("s_barrier" ::: "memory");
     if (k + 2 < n_steps) issue(k + 2);
-    // Flags of stage k - 1 (double-buffered: stage k's are written meanwhile).
+  };
+  // Flags of stage k - 1 (double-buffered: stage k's are written meanwhile).
+  auto read_flags = [&](int k) {
     const int* f = bump_lds[(k - 1) & 1];
     return k >= 1 ? (f[0] | f[1] | f[2] | f[3]) : 0;
   };
@@ -174,6 +178,9 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
 
   if (scorer) {
     // ---- score waves: heads 32sg .. +32 (two tiles of 16), keys 16kq .. +16 ----
+    // The score waves' chain (scores, softmax, P) sets the pace of a stage;
+    // they win issue arbitration over the PV wave on their SIMD.
+    __builtin_amdgcn_s_setprio(2);
     const int sg = w & 1;
     const int kq = w >> 1;
     const int qh = lane & 15;
@@ -220,7 +227,21 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
     // The query loads are done before the first wait counts stage loads only.
     __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
     for (int k = 0; k <= n_steps; ++k) {
-      if (stage_barrier(k)) {
+      stage_barrier(k);
+      // The scores of stage k go out first; the flags of stage k - 1 are read
+      // while the MFMAs run.
+      const uint8_t* sb = ring + (k & (kXSlots - 1)) * kXStageBytes;
+      const int j0 = j_begin + kXStep * k + 16 * kq;     // first key of this wave's half
+      f32x4 sc0 = f32x4{0.f, 0.f, 0.f, 0.f}, sc1 = sc0;
+      if (k < n_steps) {
+#pragma unroll
+        for (int s = 0; s < 18; ++s) {
+          const bf16x8 kk = *(const bf16x8*)(sb + ((s & 1) ? kbase1 : kbase0) + 128 * (s >> 1));
+          sc0 = mfma_16x16x32(kk, q[0][s], sc0);
+          sc1 = mfma_16x16x32(kk, q[1][s], sc1);
+        }
+      }
+      if (read_flags(k)) {
         // Stage k - 1 moved some head's reference: both score waves of each head
         // take the new one from the two halves' maxima and rewrite P.
 #pragma unroll
@@ -243,15 +264,6 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
         l_run[1] += psum[1];
       }
       if (k < n_steps) {
-        const uint8_t* sb = ring + (k & (kXSlots - 1)) * kXStageBytes;
-        const int j0 = j_begin + kXStep * k + 16 * kq;     // first key of this wave's half
-        f32x4 sc0 = f32x4{0.f, 0.f, 0.f, 0.f}, sc1 = sc0;
-#pragma unroll
-        for (int s = 0; s < 18; ++s) {
-          const bf16x8 kk = *(const bf16x8*)(sb + ((s & 1) ? kbase1 : kbase0) + 128 * (s >> 1));
-          sc0 = mfma_16x16x32(kk, q[0][s], sc0);
-          sc1 = mfma_16x16x32(kk, q[1][s], sc1);
-        }
         // Lane (head qh of tile ht, group g) holds keys j0 + 4g + r.
         bool need = false;
 #pragma unroll
@@ -326,7 +338,8 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[dt][j][r] = 0.f;
   for (int k = 0; k <= n_steps; ++k) {
-    if (stage_barrier(k)) {
+    stage_barrier(k);
+    if (read_flags(k)) {
       lds_barrier();                          // the score waves' new P and factors
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
