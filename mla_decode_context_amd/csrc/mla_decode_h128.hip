@@ -234,12 +234,23 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
       const int j0 = j_begin + kXStep * k + 16 * kq;     // first key of this wave's half
       f32x4 sc0 = f32x4{0.f, 0.f, 0.f, 0.f}, sc1 = sc0;
       if (k < n_steps) {
+        bf16x8 kk[18];
+#pragma unroll
+        for (int s = 0; s < 18; ++s) kk[s] = *(const bf16x8*)(sb + ((s & 1) ? kbase1 : kbase0) + 128 * (s >> 1));
 #pragma unroll
         for (int s = 0; s < 18; ++s) {
-          const bf16x8 kk = *(const bf16x8*)(sb + ((s & 1) ? kbase1 : kbase0) + 128 * (s >> 1));
-          sc0 = mfma_16x16x32(kk, q[0][s], sc0);
-          sc1 = mfma_16x16x32(kk, q[1][s], sc1);
+          sc0 = mfma_16x16x32(kk[s], q[0][s], sc0);
+          sc1 = mfma_16x16x32(kk[s], q[1][s], sc1);
         }
+        // Issue order: four K reads ahead, then one further read per two MFMAs
+        // (the compiler would otherwise keep only about two reads in flight).
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // LDS reads
+#pragma unroll
+        for (int i = 0; i < 14; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       }
       if (read_flags(k)) {
         // Stage k - 1 moved some head's reference: both score waves of each head
@@ -270,11 +281,15 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
         for (int ht = 0; ht < 2; ++ht) {
           const f32x4 sc = ht ? sc1 : sc0;
           float mx = -INFINITY;
+          if (j0 + 16 <= j_end) {                 // all 16 keys of the half are visible
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            v[ht][r] = (j0 + 4 * g + r < j_end) ? sc[r] * a.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, v[ht][r]);
+            for (int r = 0; r < 4; ++r) v[ht][r] = sc[r] * a.scale_log2;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[ht][r] = (j0 + 4 * g + r < j_end) ? sc[r] * a.scale_log2 : -INFINITY;
           }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, v[ht][r]);
           mx = col_max(mx);
           if (g == 0) mx_lds[kq][32 * sg + 16 * ht + qh] = mx;
           need |= mx > m_ref[ht] + kLazyLog2;
