@@ -21,10 +21,11 @@
 // So on every SIMD a score wave and a PV wave run side by side, one stage
 // apart, with one barrier per stage; P is double-buffered.  The softmax
 // reference m of a head is lazy: it only moves when a stage's maximum exceeds
-// it by more than 2^16 (always on the first stage), so p <= 2^16.  A stage that
-// moves it for any head takes an extra round before its PV: the two score
-// waves holding a head agree on the new m through LDS and rewrite P from the
-// scores still in their registers, and the PV waves rescale their
+// it by more than 2^16 (always on the first stage), so p <= 2^16.  Every stage
+// only tests its scores against m + 16; a stage that fails the test for any
+// head takes an extra round before its PV: the two score waves holding a head
+// form their halves' maxima from the scores still in their registers, agree
+// on the new m through LDS and rewrite P, and the PV waves rescale their
 // accumulators.  Stages of 32 rows (36 KiB) arrive by direct-to-LDS loads into
 // a 4-slot ring (stages k - 1 and k in use, k + 1 and k + 2 in flight).  The
 // PV waves issue and await all stage loads, and the score waves run at a
@@ -253,8 +254,16 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       }
       if (read_flags(k)) {
-        // Stage k - 1 moved some head's reference: both score waves of each head
-        // take the new one from the two halves' maxima and rewrite P.
+        // A score of stage k - 1 passed its head's reference by more than the
+        // margin: the two score waves holding each head publish their halves'
+        // maxima of that stage (still in registers), agree on the new reference
+        // and rewrite P.
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) {
+          const float mx = col_max(fmaxf(fmaxf(v[ht][0], v[ht][1]), fmaxf(v[ht][2], v[ht][3])));
+          if (g == 0) mx_lds[kq][32 * sg + 16 * ht + qh] = mx;
+        }
+        lds_barrier();
 #pragma unroll
         for (int ht = 0; ht < 2; ++ht) {
           const int hl = 32 * sg + 16 * ht + qh;
@@ -275,12 +284,13 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
         l_run[1] += psum[1];
       }
       if (k < n_steps) {
-        // Lane (head qh of tile ht, group g) holds keys j0 + 4g + r.
+        // Lane (head qh of tile ht, group g) holds keys j0 + 4g + r.  Only the
+        // test against the reference runs every stage; the maxima are formed in
+        // the (rare) round that moves a reference.
         bool need = false;
 #pragma unroll
         for (int ht = 0; ht < 2; ++ht) {
           const f32x4 sc = ht ? sc1 : sc0;
-          float mx = -INFINITY;
           if (j0 + 16 <= j_end) {                 // all 16 keys of the half are visible
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[ht][r] = sc[r] * a.scale_log2;
@@ -288,11 +298,9 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[ht][r] = (j0 + 4 * g + r < j_end) ? sc[r] * a.scale_log2 : -INFINITY;
           }
+          const float thr = m_ref[ht] + kLazyLog2;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, v[ht][r]);
-          mx = col_max(mx);
-          if (g == 0) mx_lds[kq][32 * sg + 16 * ht + qh] = mx;
-          need |= mx > m_ref[ht] + kLazyLog2;
+          for (int r = 0; r < 4; ++r) need |= v[ht][r] > thr;
         }
         write_p(k & 1);
         const bool wave_need = (__builtin_amdgcn_read_exec() & __builtin_amdgcn_ballot_w64(need)) != 0;
@@ -300,7 +308,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
       } else if (lane == 0) {
         bump_lds[k & 1][w] = 0;
       }
-      // P, maxima and flags of stage k are written before the next barrier.
+      // P and flags of stage k are written before the next barrier.
       __builtin_amdgcn_s_waitcnt(MLA_LGKMCNT0);
     }
     // Normalisers through LDS (the P area is free after the barrier).
@@ -355,6 +363,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
   for (int k = 0; k <= n_steps; ++k) {
     stage_barrier(k);
     if (read_flags(k)) {
+      lds_barrier();                          // the score waves' maxima
       lds_barrier();                          // the score waves' new P and factors
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
