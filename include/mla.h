@@ -103,7 +103,7 @@ const char* mla_status_string(mla_status status);
  *
  * Returns MLA_OK, or MLA_ERR_NULL / MLA_ERR_SHAPE (B<0, T<0, H outside
  * [1,128], page_size<1, cp_world<1, cp_rank outside [0,cp_world), strides
- * smaller than the data, scale not finite) / MLA_ERR_WORKSPACE /
+ * smaller than the data, scale not finite or not positive) / MLA_ERR_WORKSPACE /
  * MLA_ERR_UNSUPPORTED / MLA_ERR_HIP.  B == 0 or T == 0 enqueues nothing and
  * returns MLA_OK (the grid is sized from host ints and may be empty).
  * Device-side contract: Q_b <= S_b <= max_seq_len, Q_b <= max_query_len,

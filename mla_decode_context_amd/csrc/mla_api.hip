@@ -157,7 +157,7 @@ mla_status mla_decode_partial(
     void* workspace, size_t workspace_bytes, void* hip_stream) {
   if (B < 0 || T < 0 || H < 1 || H > MLA_MAX_HEADS || page_size < 1 || cp_world < 1 ||
       cp_rank < 0 || cp_rank >= cp_world || max_query_len < 0 || max_seq_len < 0 ||
-      num_splits < 0 || !isfinite(scale))
+      num_splits < 0 || !isfinite(scale) || !(scale > 0.f))
     return MLA_ERR_SHAPE;
   if (B == 0 && T > 0) return MLA_ERR_SHAPE;   // tokens without requests
   if (B == 0 || T == 0) return MLA_OK;

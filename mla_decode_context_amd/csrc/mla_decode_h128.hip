@@ -207,7 +207,8 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
     const uint32_t kbase1 = (16 * kq + qh) * kRowBytes + 16 * ((4 + g) ^ (qh & 7));
     float m_ref[2] = {-INFINITY, -INFINITY};  // per head tile, of head 32sg + 16ht + qh
     float l_run[2] = {0.f, 0.f};
-    float v[2][4];                            // this stage's scaled scores (kept for a redo)
+    float v[2][4];                            // this stage's raw scores, -inf if masked (kept for a redo)
+    float thr[2] = {-INFINITY, -INFINITY};    // raw-score test value: (m_ref + margin) / scale
     float psum[2] = {0.f, 0.f};
     auto write_p = [&](int buf) {
       // P rows of heads 32sg + 16ht + qh, keys 16kq + 4g .. +4.
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
         psum[ht] = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          pe[r] = fast_exp2(v[ht][r] - base);
+          pe[r] = fast_exp2(fmaf(v[ht][r], a.scale_log2, -base));
           psum[ht] += pe[r];
         }
         uint8_t* prow = p_lds + buf * kPBuf + (32 * sg + 16 * ht + qh) * kPRow + 32 * kq + 8 * g;
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
         // and rewrite P.
 #pragma unroll
         for (int ht = 0; ht < 2; ++ht) {
-          const float mx = col_max(fmaxf(fmaxf(v[ht][0], v[ht][1]), fmaxf(v[ht][2], v[ht][3])));
+          const float mx = col_max(fmaxf(fmaxf(v[ht][0], v[ht][1]), fmaxf(v[ht][2], v[ht][3]))) * a.scale_log2;
           if (g == 0) mx_lds[kq][32 * sg + 16 * ht + qh] = mx;
         }
         lds_barrier();
@@ -272,6 +273,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
           if (mboth > m_ref[ht] + kLazyLog2) {
             alpha = m_ref[ht] == -INFINITY ? 0.f : fast_exp2(m_ref[ht] - mboth);
             m_ref[ht] = mboth;
+            thr[ht] = (mboth + kLazyLog2) / a.scale_log2;
           }
           l_run[ht] *= alpha;
           if (kq == 0 && g == 0) alpha_lds[hl] = alpha;
@@ -293,14 +295,13 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
           const f32x4 sc = ht ? sc1 : sc0;
           if (j0 + 16 <= j_end) {                 // all 16 keys of the half are visible
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[ht][r] = sc[r] * a.scale_log2;
+            for (int r = 0; r < 4; ++r) v[ht][r] = sc[r];
           } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[ht][r] = (j0 + 4 * g + r < j_end) ? sc[r] * a.scale_log2 : -INFINITY;
+            for (int r = 0; r < 4; ++r) v[ht][r] = (j0 + 4 * g + r < j_end) ? sc[r] : -INFINITY;
           }
-          const float thr = m_ref[ht] + kLazyLog2;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) need |= v[ht][r] > thr;
+          for (int r = 0; r < 4; ++r) need |= v[ht][r] > thr[ht];
         }
         write_p(k & 1);
         const bool wave_need = (__builtin_amdgcn_read_exec() & __builtin_amdgcn_ballot_w64(need)) != 0;

@@ -43,6 +43,7 @@ def _decode(**kw):
     (dict(H=0), SHAPE), (dict(H=129), SHAPE), (dict(B=-1), SHAPE), (dict(T=-1), SHAPE),
     (dict(W=0), SHAPE), (dict(r=2), SHAPE), (dict(r=-1), SHAPE), (dict(page=0), SHAPE),
     (dict(scale=float("nan")), SHAPE), (dict(scale=float("inf")), SHAPE), (dict(splits=-1), SHAPE),
+    (dict(scale=0.0), SHAPE), (dict(scale=-0.07), SHAPE),
     (dict(B=0, T=3), SHAPE),
     (dict(q_nope=None), NULL), (dict(kv=None), NULL), (dict(bt=None), NULL), (dict(lse=None), NULL),
     (dict(qn_h=500), SHAPE), (dict(qn_t=512), SHAPE), (dict(qp_h=60), SHAPE), (dict(kv_bs=575 * 16), SHAPE),
