@@ -126,7 +126,8 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams a) {
 // LSE-weighted combine of the participating ranks, rounded to bf16) go to LDS,
 // and y[tok][n] = o[tok][k] W[k][n] runs on MFMA 16x16x32 (wave w: n = 32w ..
 // 32w+31), A = o from LDS, B = W through transposed LDS reads.  The next
-// block's partials are loaded while the current block is multiplied.
+// block's partials are loaded while the current block is merged and
+// multiplied, and its valid counts one block earlier still.
 //
 // LDS layouts (both swizzled so that the MFMA operand reads are conflict-free):
 //   W  row k (256 B) holds element n at byte (2n) ^ (32 * (k & 7));
@@ -170,65 +171,87 @@ __global__ __launch_bounds__(256, 1) void merge_v_up_kernel(const MergeParams a)
   const int lr = lane & 15;
   const int g = lane >> 4;
 
-  // Loads of one block's first <= 4 participating ranks for this thread.
+  // The thread's work is a sequence of items (block b, ranks w0 .. w0+3) with
+  // w0 = 4j, j < ngroups.  Loads run one item ahead, and the valid counts two
+  // items ahead, so the partials of an item go out as soon as the item before
+  // it starts (no round trip for the counts first).
+  const int ngroups = (a.W + 3) >> 2;
+  const int nitems = ((t_end - t_begin + kProjBlk - 1) / kProjBlk) * ngroups;
+  auto item_t = [&](int i) { return t_begin + (i / ngroups) * kProjBlk + tt; };
+  auto item_w0 = [&](int i) { return 4 * (i % ngroups); };
   struct Pend {
     u32x4 x[4][4];
     float l[4];
-    int nr;            // ranks covered (<= 4)
   };
-  auto load_ranks = [&](int t, int w0, Pend& p) {
-    p.nr = 0;
+  // Participation of ranks w0 .. w0+3 for token t: 1, 0, or (no counts given)
+  // 1 with the decision left to the LSE.  Ranks that do not take part are not
+  // read.
+  auto load_valid = [&](int i, int (&vv)[4]) {
+    const int t = item_t(i), w0 = item_w0(i);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int w = w0 + u;
-      p.l[u] = -INFINITY;
-      if (t < t_end && w < a.W) {
-        bool take = true;
-        if (a.valid) take = a.valid[(size_t)w * a.T + t] > 0;
-        if (take) {
-          const size_t row = w * plane + (size_t)t * a.H + h;
-          p.l[u] = a.lses[row];
-          if (a.valid || p.l[u] > -INFINITY) {
-            const u32x4* src = (const u32x4*)(a.outs + row * kLatent + d0);
+      vv[u] = 0;
+      if (i < nitems && t < t_end && w < a.W) vv[u] = a.valid ? (a.valid[(size_t)w * a.T + t] > 0 ? 1 : 0) : 1;
+    }
+  };
+  auto load_data = [&](int i, const int (&vv)[4], Pend& p) {
+    const int t = item_t(i), w0 = item_w0(i);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) p.x[u][k] = src[k];
-          }
+    for (int u = 0; u < 4; ++u) {
+      p.l[u] = -INFINITY;
+      if (vv[u]) {
+        const size_t row = (w0 + u) * plane + (size_t)t * a.H + h;
+        p.l[u] = a.lses[row];
+        if (a.valid || p.l[u] > -INFINITY) {
+          const u32x4* src = (const u32x4*)(a.outs + row * kLatent + d0);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) p.x[u][k] = src[k];
         }
       }
     }
   };
 
   Pend nxt;
-  load_ranks(t_begin + tt, 0, nxt);
-  for (int tb = t_begin; tb < t_end; tb += kProjBlk) {
+  int vv[4];
+  load_valid(0, vv);
+  load_data(0, vv, nxt);
+  load_valid(1, vv);
+  float m = -INFINITY, ssum = 0.f;
+  f32x4 acc[8];
+  for (int i = 0; i < nitems; ++i) {
+    const int tb = t_begin + (i / ngroups) * kProjBlk;
     const int t = tb + tt;
-    // ---- merge this thread's token and 32 dims over all ranks ----
-    float m = -INFINITY, ssum = 0.f;
-    f32x4 acc[8];
+    if (i % ngroups == 0) {
+      m = -INFINITY;
+      ssum = 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int w0 = 0; w0 < a.W; w0 += 4) {
-      Pend cur = nxt;
-      if (w0 + 4 < a.W) load_ranks(t, w0 + 4, nxt);          // rest of this token's ranks
-      else load_ranks(t + kProjBlk, 0, nxt);                  // the next block's first ranks
+      for (int k = 0; k < 8; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // ---- merge ranks w0 .. w0+3 of this thread's token and 32 dims ----
+    Pend cur = nxt;
+    if (i + 1 < nitems) {
+      load_data(i + 1, vv, nxt);
+      load_valid(i + 2, vv);
+    }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float mn = fmaxf(m, cur.l[u]);
-        if (cur.l[u] > -INFINITY && mn > -INFINITY) {
-          const float c_old = m == -INFINITY ? 0.f : fast_exp2((m - mn) * kLog2e);
-          const float c_new = fast_exp2((cur.l[u] - mn) * kLog2e);
+    for (int u = 0; u < 4; ++u) {
+      const float mn = fmaxf(m, cur.l[u]);
+      if (cur.l[u] > -INFINITY && mn > -INFINITY) {
+        const float c_old = m == -INFINITY ? 0.f : fast_exp2((m - mn) * kLog2e);
+        const float c_new = fast_exp2((cur.l[u] - mn) * kLog2e);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            acc[2 * k] = acc[2 * k] * c_old + f32x4{bf16_lo(cur.x[u][k][0]), bf16_hi(cur.x[u][k][0]),
-                                                    bf16_lo(cur.x[u][k][1]), bf16_hi(cur.x[u][k][1])} * c_new;
-            acc[2 * k + 1] = acc[2 * k + 1] * c_old + f32x4{bf16_lo(cur.x[u][k][2]), bf16_hi(cur.x[u][k][2]),
-                                                            bf16_lo(cur.x[u][k][3]), bf16_hi(cur.x[u][k][3])} * c_new;
-          }
-          ssum = ssum * c_old + c_new;
-          m = mn;
+        for (int k = 0; k < 4; ++k) {
+          acc[2 * k] = acc[2 * k] * c_old + f32x4{bf16_lo(cur.x[u][k][0]), bf16_hi(cur.x[u][k][0]),
+                                                  bf16_lo(cur.x[u][k][1]), bf16_hi(cur.x[u][k][1])} * c_new;
+          acc[2 * k + 1] = acc[2 * k + 1] * c_old + f32x4{bf16_lo(cur.x[u][k][2]), bf16_hi(cur.x[u][k][2]),
+                                                          bf16_lo(cur.x[u][k][3]), bf16_hi(cur.x[u][k][3])} * c_new;
         }
+        ssum = ssum * c_old + c_new;
+        m = mn;
       }
     }
+    if (i % ngroups != ngroups - 1) continue;     // more ranks of this block to come
     // Merged latent row (bf16) into o_lds; an absent token or a row with no
     // participating rank is zero.
     const float inv = ssum > 0.f ? 1.f / ssum : 0.f;
@@ -245,7 +268,7 @@ __global__ __launch_bounds__(256, 1) void merge_v_up_kernel(const MergeParams a)
       a.out_lse[(size_t)t * a.H + h] = ssum > 0.f ? m + fast_log2(ssum) * kLn2 : -INFINITY;
     // W_UV staged (first block) and the block's rows written; the next block's
     // partial loads may still be in flight (they target registers, not LDS).
-    if (tb == t_begin) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+    if (tb == t_begin) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));   // W_UV staged
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
     // ---- y[tok][n] for the block's 16 tokens, n = 32wv .. 32wv+31 ----
