@@ -54,8 +54,10 @@ __device__ __forceinline__ bool merge_lse(const MergeParams& a, int t, int h, fl
 // Workgroup = (token t, 16 heads); thread (head 16*blockIdx.y + tid / 16, dims
 // 32*(tid % 16) .. +32).  Whether rank w takes part in row t is the same for
 // every thread of the workgroup, so valid[w, t] comes through scalar loads;
-// the LSEs and partials of up to eight participating ranks are then loaded
+// the LSEs and partials of up to R participating ranks are then loaded
 // together and combined online (running max, rescaled sum), ranks in order.
+// R = 4 when W <= 4 (fewer registers, more workgroups per CU), else 8.
+template <int R>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams a) {
   const int t = blockIdx.x;
   const int h = 16 * blockIdx.y + (threadIdx.x >> 4);
@@ -69,11 +71,11 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams a) {
   f32x4 acc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int w0 = 0; w0 < a.W; w0 += 8) {
-    float l[8];
-    u32x4 x[8][4];
+  for (int w0 = 0; w0 < a.W; w0 += R) {
+    float l[R];
+    u32x4 x[R][4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < R; ++u) {
       const int w = w0 + u;
       bool take = w < a.W;
       if (take && vcol)
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams a) {
       }
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < R; ++u) {
       // A rank whose LSE is -inf (or NaN, without counts) adds nothing.
       const float mn = fmaxf(m, l[u]);
       if (l[u] > -INFINITY && mn > -INFINITY) {
@@ -311,7 +313,9 @@ __global__ __launch_bounds__(256, 1) void merge_v_up_kernel(const MergeParams a)
 
 hipError_t launch_lse_merge(const MergeParams& p, hipStream_t stream) {
   if (p.T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)p.T, (unsigned)((p.H + 15) / 16)), dim3(256), 0, stream, p);
+  const dim3 grid((unsigned)p.T, (unsigned)((p.H + 15) / 16));
+  if (p.W <= 4) hipLaunchKernelGGL(lse_merge_kernel<4>, grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(lse_merge_kernel<8>, grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
