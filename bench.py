@@ -65,10 +65,18 @@ def merge_bytes(wl, valid, proj: bool):
     return read + write + wuv, flops
 
 
-def kernel_source_hash() -> str:
+# Sources that build the 16-head decode and its combine kernel (the headline
+# workload's kernels): a traffic record stays valid while these are unchanged.
+DECODE16_SOURCES = ["mla_api.hip", "mla_common.h", "mla_decode.hip", "mla_device.h", "mla_kernels.h"]
+
+
+def kernel_source_hash(files=None) -> str:
+    """Hash of the given kernel sources (file names under the package's csrc/;
+    all of them when None)."""
+    csrc = os.path.join(ROOT, "mla_decode_context_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "mla_decode_context_amd", "csrc"))):
-        with open(os.path.join(ROOT, "mla_decode_context_amd", "csrc", f), "rb") as fh:
+    for f in sorted(files if files is not None else os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -80,7 +88,7 @@ def load_traffic(workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(rec.get("kernel_sources")):
         return None
     return rec.get("bytes_per_launch")
 
@@ -128,20 +136,28 @@ def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / steps
     ev_ms_step = ev_a.elapsed_time(ev_b) / steps
-    # Breakdown pass: the same steps with events around every call (the markers
-    # add a little time per call, so these feed only the per-shard figures).
-    ev_sets = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(wl.W + 1)] for _ in range(steps)]
-    for k in range(steps):
-        step(ev_sets[k])
-    torch.cuda.synchronize()
-    dec_ms = np.array([[ev_sets[k][r][0].elapsed_time(ev_sets[k][r][1]) for r in range(wl.W)]
-                       for k in range(steps)])                      # [steps, W]
+    # Breakdown: each operation of a step on its own, `steps` calls back to back
+    # between two events (markers around every single call would add a few
+    # microseconds to each): every shard's decode, then the merge.
+    def loop_ms(op):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        op()
+        a.record()
+        for _ in range(steps):
+            op()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    dec_avg = np.array([loop_ms(lambda r=r: dw.partial(r)) for r in range(wl.W)])   # per shard, ms
+    mg_ms = None
+    if merging:
+        dw.valid_counts()
+        mg_ms = loop_ms(dw.merge_v_up if proj else dw.merge)
     res = dict(workload=name, T=wl.T, B=wl.B, H=wl.H, W=wl.W, ms_per_step=ms_step)
     kv_total = sum(p["kv"] for p in per_shard)
     res["kv_GBps"] = kv_total / (ms_step * 1e-3) / 1e9
     res["query_tokens_per_s"] = wl.T / (ms_step * 1e-3)
-    dec_avg = dec_ms.mean(axis=0)                                   # per shard, ms
     res["decode_ms_per_shard"] = [round(float(x), 4) for x in dec_avg]
     alg_bytes = np.array([p["total"] for p in per_shard], dtype=np.float64)
     alg_flops = np.array([p["flops"] for p in per_shard], dtype=np.float64)
@@ -152,7 +168,6 @@ def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True
     res["decode_pct_hbm_peak"] = 100.0 * res["decode_alg_GBps"] / HBM_PEAK_GBPS
     # one-rank view: the slowest rank's partial plus the merge (excludes the exchange)
     if merging:
-        mg_ms = np.array([ev_sets[k][wl.W][0].elapsed_time(ev_sets[k][wl.W][1]) for k in range(steps)]).mean()
         valid = dw.valid.cpu().numpy()
         mbytes, mflops = merge_bytes(wl, valid, proj)
         res["merge_kind"] = "merge+W_UV" if proj else "lse_merge"
@@ -167,7 +182,7 @@ def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True
         # Average duration of one decode call (its decode kernel and, when rows
         # were split, the combine kernel): with one rank and no merge a step is
         # exactly one call, so the timed region's events divided by the steps;
-        # otherwise the per-call events of the breakdown pass.
+        # otherwise the breakdown's back-to-back timing of each shard's calls.
         res["_decode_avg_ms"] = float(ev_ms_step) if wl.W == 1 else float(dec_avg.mean())
         res["_kernel"] = dw.decode_kernel_name()
         res["_cold_kv_GBps"] = cold_kv(dw, wl, per_shard, torch) if cold else None

@@ -12,8 +12,8 @@ Two subcommands:
       then WRITE_SIZE, both in KiB per dispatch), each scaled by what the same
       counter reads for the plain N-MiB copy that ``bench.py --copy-probe-mib N``
       runs first (the largest ``__amd_rocclr_copyBuffer`` dispatch).  The record
-      carries the hash of the kernel sources it was measured on; bench.py only
-      reports it while that hash still matches.
+      carries the hash of the 16-head decode path's sources it was measured on;
+      bench.py only reports it while that hash still matches.
 
 Only reads CSV files; it touches no GPU.
 """
@@ -76,7 +76,7 @@ def copy_reading(rows, expect_bytes):
 
 
 def cmd_traffic(a):
-    from bench import kernel_source_hash
+    from bench import DECODE16_SOURCES, kernel_source_hash
 
     copy_bytes = a.copy_mib * (1 << 20)
     fetch = counter_per_dispatch(a.fetch, "FETCH_SIZE")
@@ -92,7 +92,8 @@ def cmd_traffic(a):
     rec = {
         "kernel": a.kernel,
         "workload": a.workload,
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_sources": DECODE16_SOURCES,
+        "kernel_source_hash": kernel_source_hash(DECODE16_SOURCES),
         "bytes_per_launch": round(fetch_b + write_b),
         "fetch_bytes_per_launch": round(fetch_b),
         "write_bytes_per_launch": round(write_b),
