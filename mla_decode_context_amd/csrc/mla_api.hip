@@ -50,15 +50,21 @@ struct Plan {
   int chunk;        // keys per split (fixed-split grid)
   int max_splits;   // grid extent along splits (fixed-split grid)
   int workers;      // > 0: balanced schedule over this many workgroups
+  bool ordered;     // 128 heads: longest-first dispatch order in the workspace
 };
 
-Plan make_plan(int T, int H, int max_seq_len, int W, int num_splits, bool split_ok) {
+// The 128-head kernel's dispatch order sorts (split, request) units in one
+// workgroup's LDS; more units than this run in token order.
+constexpr int64_t kH128MaxOrderUnits = 8192;
+
+Plan make_plan(int B, int T, int H, int max_seq_len, int W, int num_splits, bool split_ok) {
   Plan p;
   const int ht = (H + 15) / 16;
   p.mtiles = ht >= 2 ? 2 : 1;
   p.hblocks = (int)ceil_div(ht, p.mtiles);
   p.workers = 0;
   p.h128 = H == 128;
+  if (p.h128) p.hblocks = 2;      // 64-head blocks of the 128-head kernel
   // A row's visible local keys never exceed ceil(max_seq_len / W).
   const int64_t lmax = max_seq_len > 0 ? ceil_div(max_seq_len, W) : 0;
   const int64_t lr = round_up(lmax > 0 ? lmax : 1, kStep);
@@ -95,26 +101,37 @@ Plan make_plan(int T, int H, int max_seq_len, int W, int num_splits, bool split_
   }
   p.chunk = (int)chunk;
   p.max_splits = (int)ceil_div(lr, chunk);
+  p.ordered = p.h128 && split_ok && (int64_t)B * p.max_splits <= kH128MaxOrderUnits;
   return p;
 }
 
 // Workspace layout (offsets from the 256-byte aligned base):
+//   int32 item_map[T * hblocks * max_splits]  128 heads only: dispatch order
 //   int32 counters[T * hblocks]          split tickets, zero between calls
 //   int4  row_desc[T]                    balanced schedule only: pieces per row
 //   fp32  lse[slots][H]                  split LSEs
 //   fp32  o[slots][H][512]               normalised split partials
 // with slots = max_splits * T (fixed splits; slot split*T + t) or 2 * workers
-// (balanced schedule; two per workgroup).
-bool uses_workspace(const Plan& p) { return p.workers > 0 || p.max_splits > 1; }
+// (balanced schedule; two per workgroup).  The split regions exist only when
+// the plan splits.
+bool splits_ws(const Plan& p) { return p.workers > 0 || p.max_splits > 1; }
+bool uses_workspace(const Plan& p) { return splits_ws(p) || p.ordered; }
 int64_t slots_of(const Plan& p, int T) { return p.workers > 0 ? 2 * (int64_t)p.workers : (int64_t)p.max_splits * T; }
+size_t map_bytes(const Plan& p, int T) {
+  return p.ordered ? (size_t)round_up((int64_t)T * p.hblocks * p.max_splits * 4, 256) : 0;
+}
 size_t counters_bytes(const Plan& p, int T) { return (size_t)round_up((int64_t)T * p.hblocks * 4, 256); }
 size_t desc_bytes(const Plan& p, int T) { return p.workers > 0 ? (size_t)round_up((int64_t)T * 16, 256) : 0; }
 size_t lse_bytes(const Plan& p, int T, int H) { return (size_t)round_up(slots_of(p, T) * H * 4, 256); }
 
 size_t workspace_bytes_for(const Plan& p, int T, int H) {
   if (!uses_workspace(p)) return 0;
-  const size_t rows = (size_t)slots_of(p, T) * H;
-  return counters_bytes(p, T) + desc_bytes(p, T) + lse_bytes(p, T, H) + rows * MLA_D_LATENT * sizeof(float) + 256;
+  size_t n = map_bytes(p, T) + 256;
+  if (splits_ws(p)) {
+    const size_t rows = (size_t)slots_of(p, T) * H;
+    n += counters_bytes(p, T) + desc_bytes(p, T) + lse_bytes(p, T, H) + rows * MLA_D_LATENT * sizeof(float);
+  }
+  return n;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -141,7 +158,7 @@ size_t mla_decode_workspace_size(int32_t B, int32_t T, int32_t H, int32_t max_qu
       cp_world < 1 || num_splits < 0)
     return (size_t)-1;
   if (B == 0 || T == 0) return 0;
-  const Plan p = make_plan(T, H, max_seq_len, cp_world, num_splits, true);
+  const Plan p = make_plan(B, T, H, max_seq_len, cp_world, num_splits, true);
   return workspace_bytes_for(p, T, H);
 }
 
@@ -176,7 +193,7 @@ mla_status mla_decode_partial(
   mla_status st = check_device();
   if (st != MLA_OK) return st;
 
-  const Plan plan = make_plan(T, H, max_seq_len, cp_world, num_splits, workspace != nullptr);
+  const Plan plan = make_plan(B, T, H, max_seq_len, cp_world, num_splits, workspace != nullptr);
   const size_t need = workspace_bytes_for(plan, T, H);
   if (need > 0 && workspace_bytes < need) return MLA_ERR_WORKSPACE;
 
@@ -191,9 +208,11 @@ mla_status mla_decode_partial(
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   p.chunk = plan.chunk; p.hblocks = plan.hblocks; p.max_splits = plan.max_splits;
   p.out = (uint16_t*)out; p.lse = lse;
-  p.ws_o = nullptr; p.ws_lse = nullptr; p.counters = nullptr; p.row_desc = nullptr;
-  if (uses_workspace(plan)) {
-    char* base = (char*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+  p.ws_o = nullptr; p.ws_lse = nullptr; p.counters = nullptr; p.row_desc = nullptr; p.item_map = nullptr;
+  char* ws_base = (char*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
+  if (plan.ordered) p.item_map = (int32_t*)ws_base;
+  if (splits_ws(plan)) {
+    char* base = ws_base + map_bytes(plan, T);
     const size_t c_end = counters_bytes(plan, T);
     const size_t d_end = c_end + desc_bytes(plan, T);
     p.counters = (int32_t*)base;

@@ -79,13 +79,28 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
   __shared__ int bump_lds[2][4];            // [stage parity][score wave]
 
   // Item = (split, token, head block), head block fastest.  The hardware deals
-  // workgroups to the 8 XCDs round-robin by blockIdx; item x*per_xcd + k goes to
-  // blockIdx 8k + x, so consecutive items share an XCD and are dispatched one
-  // after the other.
+  // workgroups to the 8 XCDs round-robin by blockIdx and each XCD starts its
+  // own in blockIdx order.
   const int hblocks = a.H / kXHeads;
-  const int per_xcd = (int)(gridDim.x >> 3);
-  const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (item >= a.T * hblocks * a.max_splits) return;
+  int item;
+  if (a.item_map) {
+    // Ordered dispatch: grid position p holds the p-th item of the longest-first
+    // order.  Groups of four consecutive positions (one request's rows and head
+    // blocks) go to one XCD, group g to XCD g mod 8, so every XCD runs its share
+    // longest first and a request's workgroups read its cache rows through the
+    // same L2.
+    const int x = (int)(blockIdx.x & 7), k = (int)(blockIdx.x >> 3);
+    const int pos = 4 * (8 * (k >> 2) + x) + (k & 3);
+    if (pos >= a.T * hblocks * a.max_splits) return;
+    item = a.item_map[pos];
+    if (item < 0) return;
+  } else {
+    // Item x*per_xcd + k goes to blockIdx 8k + x: consecutive items share an
+    // XCD and are dispatched one after the other.
+    const int per_xcd = (int)(gridDim.x >> 3);
+    item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+    if (item >= a.T * hblocks * a.max_splits) return;
+  }
   const int hb = item % hblocks;
   const int t = (item / hblocks) % a.T;
   const int split = item / (hblocks * a.T);
@@ -472,9 +487,135 @@ __global__ __launch_bounds__(256) void combine_fixed_kernel(const DecodeParams a
     a.lse[row] = ssum > 0.f ? m + fast_log2(ssum) * kLn2 : -INFINITY;
 }
 
+// ---- Longest-first dispatch order ----
+//
+// Workgroups of the decode grid start in blockIdx order as CUs free up, so the
+// order of the items is a list schedule; rows differ several-fold in length
+// (and a prefill chunk's rows all belong to one request), so in token order a
+// few CUs end up with the longest rows at the end.  Dispatching longest first
+// (LPT) bounds the finish spread by the shortest items instead.
+//
+// Unit = (split s, request b): the rows of b that have keys in split s, with
+// both head blocks.  Its length is the number of 32-key stages of its longest
+// row (the last one, which sees all Lc_b local keys) in that split.  Units are
+// counting-sorted by that length, longest first (equal lengths in any order:
+// the order changes only timing, never a result), and expanded into items, a
+// unit's rows last row first.  Position p >= the item count maps to -1.
+constexpr int kOrdThreads = 1024;
+constexpr int kOrdBuckets = 1024;                  // stage counts >= 1023 share the top bucket
+constexpr int kOrdMaxUnits = 8192;                 // more units: the decode runs unordered
+
+struct UnitInfo {
+  int q0, rows, first;   // first token, rows with work in this split, index of the first of them
+  int stages;            // sort key
+};
+
+__device__ __forceinline__ UnitInfo unit_info(const DecodeParams& a, int u) {
+  const int s = u / a.B, b = u - s * a.B;
+  UnitInfo ui;
+  ui.q0 = a.qsl[b];
+  const int Q = a.qsl[b + 1] - ui.q0;
+  const int S = a.seq_lens[b];
+  const int c = s * a.chunk;
+  // Row i sees ceil((S - Q + i + 1 - r) / W) local keys, more than c exactly when
+  // i >= cW - S + Q + r.  Split 0 also keeps the rows without keys (they write
+  // their empty result).
+  ui.first = s == 0 ? 0 : max(0, c * a.W - S + Q + a.r);
+  ui.rows = max(0, Q - ui.first);
+  const int cnt = min(ceil_div_pos(S - a.r, a.W) - c, a.chunk);
+  ui.stages = ui.rows > 0 && cnt > 0 ? (cnt + kXStep - 1) / kXStep : 0;
+  return ui;
+}
+
+__device__ __forceinline__ int block_excl_scan(int v, int* wsum) {
+  // Exclusive prefix sum over the 1024 threads of the workgroup.
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[wv] = x;
+  __syncthreads();
+  int carry = 0;
+  for (int i = 0; i < wv; ++i) carry += wsum[i];
+  __syncthreads();
+  return carry + x - v;
+}
+
+__global__ __launch_bounds__(kOrdThreads) void h128_order_kernel(const DecodeParams a) {
+  __shared__ int start[kOrdBuckets];
+  __shared__ int ord[kOrdMaxUnits];      // sorted units
+  __shared__ int first_item[kOrdMaxUnits + 1];
+  __shared__ int wsum[kOrdThreads / 64];
+  const int tid = threadIdx.x;
+  const int U = a.B * a.max_splits;
+  const int hblocks = a.H / kXHeads;
+  const int n_map = a.T * hblocks * a.max_splits;
+  start[tid] = 0;
+  __syncthreads();
+  for (int u = tid; u < U; u += kOrdThreads) atomicAdd(&start[min(unit_info(a, u).stages, kOrdBuckets - 1)], 1);
+  __syncthreads();
+  // Longest first: bucket k starts after every unit of the buckets above it.
+  const int kb = kOrdBuckets - 1 - tid;
+  const int cnt = start[kb];
+  const int before = block_excl_scan(cnt, wsum);
+  start[kb] = before;
+  __syncthreads();
+  for (int u = tid; u < U; u += kOrdThreads) {
+    const int k = min(unit_info(a, u).stages, kOrdBuckets - 1);
+    ord[atomicAdd(&start[k], 1)] = u;
+  }
+  __syncthreads();
+  // Item offsets of the sorted units: thread tid sums positions tid*per .. +per.
+  const int per = (U + kOrdThreads - 1) / kOrdThreads;
+  int local = 0;
+  for (int i = 0; i < per; ++i) {
+    const int pos = tid * per + i;
+    if (pos < U) local += unit_info(a, ord[pos]).rows * hblocks;
+  }
+  int run = block_excl_scan(local, wsum);
+  for (int i = 0; i < per; ++i) {
+    const int pos = tid * per + i;
+    if (pos < U) {
+      first_item[pos] = run;
+      run += unit_info(a, ord[pos]).rows * hblocks;
+    }
+  }
+  if (tid == kOrdThreads - 1) first_item[U] = run;   // the last thread's range ends the sequence
+  __syncthreads();
+  const int n_items = first_item[U];
+  for (int p = tid; p < n_map; p += kOrdThreads) {
+    int item = -1;
+    if (p < n_items) {
+      // The unit holding item p: the last position whose first item is <= p.
+      int lo = 0, hi = U - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (first_item[mid] <= p) lo = mid; else hi = mid - 1;
+      }
+      const int u = ord[lo];
+      const int s = u / a.B;
+      const UnitInfo ui = unit_info(a, u);
+      const int o = p - first_item[lo];
+      const int row = ui.first + ui.rows - 1 - o / hblocks;      // last row first
+      item = (s * a.T + ui.q0 + row) * hblocks + o % hblocks;
+    }
+    a.item_map[p] = item;
+  }
+}
+
 hipError_t launch_decode_h128(const DecodeParams& p, hipStream_t stream) {
   const int items = p.T * (p.H / kXHeads) * p.max_splits;
-  const unsigned grid = (unsigned)(((items + 7) / 8) * 8);
+  unsigned grid = (unsigned)(((items + 7) / 8) * 8);
+  if (p.item_map) {
+    if (p.B * p.max_splits > kOrdMaxUnits) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(h128_order_kernel, dim3(1), dim3(kOrdThreads), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    grid = (unsigned)(((items + 31) / 32) * 32);
+  }
   if (p.P % 32 == 0) hipLaunchKernelGGL((decode_kernel_h128<true>), dim3(grid), dim3(512), 0, stream, p);
   else hipLaunchKernelGGL((decode_kernel_h128<false>), dim3(grid), dim3(512), 0, stream, p);
   hipError_t e = hipGetLastError();

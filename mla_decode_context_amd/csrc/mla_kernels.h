@@ -26,6 +26,7 @@ struct DecodeParams {
   float* ws_lse;           // fp32 [slots,H]
   int32_t* counters;       // int32 [T*hblocks] split tickets; zero between calls
   int4* row_desc;          // balanced schedule: per token {pieces, first slot, slot-0 offset, 0}
+  int32_t* item_map;       // 128 heads: dispatch order, item of each grid position (-1: none); or null
 };
 
 struct MergeParams {
@@ -45,7 +46,9 @@ struct MergeParams {
 // The balanced launch is followed by a combine launch that merges the pieces
 // of the rows it split.
 hipError_t launch_decode(const DecodeParams& p, int mtiles, int max_splits, int workers, hipStream_t stream);
-// 128 heads: one workgroup per (token, split), splits merged by a second launch.
+// 128 heads: one workgroup per (token, 64-head block, split), splits merged by
+// a second launch.  With p.item_map set, a first one-workgroup launch orders the
+// items longest first (the decode grid then runs them in that order).
 hipError_t launch_decode_h128(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_local_seqlens(const int32_t* seq_lens, const int32_t* qsl, int B, int T, int W,
                                 int r, int32_t* row_seqlen, int32_t* shard_len, hipStream_t stream);

@@ -122,128 +122,141 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams a) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge fused with W_UV.  Workgroup = (head h, a contiguous range of tokens).
-// W_UV[h] (512 x 128 bf16, 128 KiB) is staged once into LDS; the tokens then
-// stream through in blocks of 16: the merged latent rows of a block (exact
-// LSE-weighted combine of the participating ranks, rounded to bf16) go to LDS,
-// and y[tok][n] = o[tok][k] W[k][n] runs on MFMA 16x16x32 (wave w: n = 32w ..
-// 32w+31), A = o from LDS, B = W through transposed LDS reads.  The next
-// block's partials are loaded while the current block is merged and
-// multiplied, and its valid counts one block earlier still.
+// Merge fused with W_UV.  Workgroup = (head h, a contiguous range of tokens),
+// 512 threads.  W_UV[h] (512 x 128 bf16, 128 KiB) is staged once into LDS; the
+// tokens then stream through in blocks of 16: the merged latent rows of a
+// block (exact LSE-weighted combine of the participating ranks, rounded to
+// bf16) go to LDS, and y[tok][n] = o[tok][k] W[k][n] runs on MFMA 16x16x32
+// (wave w: n = 16w .. 16w+15), A = o from LDS, B = W through transposed LDS
+// reads.  Each thread merges one token's 16 dims, so three items' partials fit
+// in its registers: two items are always in flight while one is merged and
+// projected, and their valid counts come one item earlier through scalar
+// loads (a wait for a count never waits for partials).
 //
 // LDS layouts (both swizzled so that the MFMA operand reads are conflict-free):
 //   W  row k (256 B) holds element n at byte (2n) ^ (32 * (k & 7));
 //   o  row t (1 KiB) holds 16-byte chunk c at chunk position c ^ (t & 7).
 // ---------------------------------------------------------------------------
 constexpr int kProjBlk = 16;                       // tokens per block
+constexpr int kProjThreads = 512;
 constexpr int kWBytes = kLatent * kVHead * 2;      // 128 KiB
+constexpr int kBufFlags = 0x00020000;              // buffer resource word 3 (raw 32-bit data)
 
-__global__ __launch_bounds__(256, 1) void merge_v_up_kernel(const MergeParams a) {
+template <bool kValid>
+__global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const MergeParams a) {
   __shared__ __attribute__((aligned(16))) uint8_t w_lds[kWBytes];
   __shared__ __attribute__((aligned(16))) uint8_t o_lds[kProjBlk * kLatent * 2];   // 16 KiB
 
   const int h = blockIdx.x;
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int per = (a.T + (int)gridDim.y - 1) / (int)gridDim.y;
   const int t_begin = (int)blockIdx.y * per;
   const int t_end = min(a.T, t_begin + per);
   if (t_begin >= t_end) return;
 
-  // Stage W_UV[h]: 128 loads of 1 KiB (4 rows each); wave wv issues 32 of them.
+  // Stage W_UV[h]: 128 loads of 1 KiB (4 rows each); wave wv issues 16 of them.
   {
     const uint8_t* src = (const uint8_t*)(a.wuv + (size_t)h * kLatent * kVHead);
-    const uint32_t base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)w_lds;
 #pragma unroll 4
-    for (int i = 0; i < 32; ++i) {
-      const int blk = 32 * wv + i;
+    for (int i = 0; i < 16; ++i) {
+      const int blk = 16 * wv + i;
       const int o = 1024 * blk + 16 * lane;          // LDS byte
       const int k = o >> 8;
       const int c = o & 255;
       dma_16B_to_lds(src + k * 256 + (c ^ (32 * (k & 7))), w_lds + 1024 * blk);
-      (void)base;
     }
   }
 
-  // Merge role: thread (token tt = tid / 16 of the block, dims 32*(tid % 16) .. +32).
-  const int tt = threadIdx.x >> 4;
-  const int d0 = 32 * (threadIdx.x & 15);
+  // Merge role: thread (token tt = tid / 32 of the block, dims 16*(tid % 32) .. +16);
+  // wave wv holds tokens 2wv and 2wv + 1.
+  const int tt = threadIdx.x >> 5;
+  const int d0 = 16 * (threadIdx.x & 31);
   const size_t plane = (size_t)a.T * a.H;
   // MFMA role: lane (row lr = lane % 16, group g = lane / 16).
   const int lr = lane & 15;
   const int g = lane >> 4;
 
   // The thread's work is a sequence of items (block b, ranks w0 .. w0+3) with
-  // w0 = 4j, j < ngroups.  Loads run one item ahead, and the valid counts two
-  // items ahead, so the partials of an item go out as soon as the item before
-  // it starts (no round trip for the counts first).
+  // w0 = 4j, j < ngroups.
   const int ngroups = (a.W + 3) >> 2;
   const int nitems = ((t_end - t_begin + kProjBlk - 1) / kProjBlk) * ngroups;
-  auto item_t = [&](int i) { return t_begin + (i / ngroups) * kProjBlk + tt; };
+  auto item_tb = [&](int i) { return t_begin + (i / ngroups) * kProjBlk; };
   auto item_w0 = [&](int i) { return 4 * (i % ngroups); };
   struct Pend {
-    u32x4 x[4][4];
+    u32x4 x[4][2];
     float l[4];
+    int part;          // bit u: rank w0 + u was read for this lane
   };
-  // Participation of ranks w0 .. w0+3 for token t: 1, 0, or (no counts given)
-  // 1 with the decision left to the LSE.  Ranks that do not take part are not
-  // read.
+  // Participation of ranks w0 .. w0+3 for the thread's token.  With counts, the
+  // counts of the wave's two tokens come through scalar loads and ranks that do
+  // not take part are not read; without counts every rank's row is read and
+  // its LSE decides.
   auto load_valid = [&](int i, int (&vv)[4]) {
-    const int t = item_t(i), w0 = item_w0(i);
+    const int tb = item_tb(i), w0 = item_w0(i);
+    const int t = tb + tt;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int w = w0 + u;
-      vv[u] = 0;
-      if (i < nitems && t < t_end && w < a.W) vv[u] = a.valid ? (a.valid[(size_t)w * a.T + t] > 0 ? 1 : 0) : 1;
+      const int w = min(w0 + u, a.W - 1);
+      if (kValid) {
+        const __attribute__((address_space(4))) int32_t* vrow =
+            (const __attribute__((address_space(4))) int32_t*)a.valid + (size_t)w * a.T;
+        const int c0 = vrow[min(tb + 2 * wv, a.T - 1)];
+        const int c1 = vrow[min(tb + 2 * wv + 1, a.T - 1)];
+        vv[u] = (lane < 32 ? c0 : c1) > 0 ? 1 : 0;
+      } else {
+        vv[u] = 1;
+      }
+      vv[u] &= (i < nitems && w0 + u < a.W && t < t_end) ? 1 : 0;
     }
   };
+  // Every load of an item is issued whether or not the item exists or its lane
+  // takes part: buffer loads whose offset lies past the buffer's range return
+  // zero without touching memory.  So the number of loads in flight never
+  // depends on the data and the compiler's waits stay exact.
+  constexpr uint32_t kOff = 0x40000000u;          // past every range below
   auto load_data = [&](int i, const int (&vv)[4], Pend& p) {
-    const int t = item_t(i), w0 = item_w0(i);
+    const int tb = min(item_tb(i), a.T - 1), w0 = item_w0(i);
+    p.part = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      p.l[u] = -INFINITY;
-      if (vv[u]) {
-        const size_t row = (w0 + u) * plane + (size_t)t * a.H + h;
-        p.l[u] = a.lses[row];
-        if (a.valid || p.l[u] > -INFINITY) {
-          const u32x4* src = (const u32x4*)(a.outs + row * kLatent + d0);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) p.x[u][k] = src[k];
-        }
-      }
+      const int w = min(w0 + u, a.W - 1);
+      const size_t row0 = w * plane + (size_t)tb * a.H + h;     // the block's first token
+      const __amdgpu_buffer_rsrc_t ro =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(a.outs + row0 * kLatent), (short)0, kProjBlk * a.H * 1024, kBufFlags);
+      const __amdgpu_buffer_rsrc_t rl =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(a.lses + row0), (short)0, kProjBlk * a.H * 4, kBufFlags);
+      const uint32_t oo = vv[u] ? (uint32_t)(tt * a.H * 1024 + 2 * d0) : kOff;
+      const uint32_t ol = vv[u] ? (uint32_t)(tt * a.H * 4) : kOff;
+      p.l[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, ol, 0, 0));
+      p.x[u][0] = __builtin_amdgcn_raw_buffer_load_b128(ro, oo, 0, 0);
+      p.x[u][1] = __builtin_amdgcn_raw_buffer_load_b128(ro, oo + 16, 0, 0);
+      p.part |= vv[u] << u;
     }
   };
 
-  Pend nxt;
-  int vv[4];
-  load_valid(0, vv);
-  load_data(0, vv, nxt);
-  load_valid(1, vv);
   float m = -INFINITY, ssum = 0.f;
-  f32x4 acc[8];
-  for (int i = 0; i < nitems; ++i) {
-    const int tb = t_begin + (i / ngroups) * kProjBlk;
+  f32x4 acc[4];
+  // One item: merge its ranks into the running (m, ssum, acc); after the last
+  // rank group of a block, project the block's merged rows.
+  auto process = [&](int i, const Pend& cur) {
+    const int tb = item_tb(i);
     const int t = tb + tt;
     if (i % ngroups == 0) {
       m = -INFINITY;
       ssum = 0.f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    // ---- merge ranks w0 .. w0+3 of this thread's token and 32 dims ----
-    Pend cur = nxt;
-    if (i + 1 < nitems) {
-      load_data(i + 1, vv, nxt);
-      load_valid(i + 2, vv);
+      for (int k = 0; k < 4; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float mn = fmaxf(m, cur.l[u]);
-      if (cur.l[u] > -INFINITY && mn > -INFINITY) {
+      const float lu = (cur.part >> u) & 1 ? cur.l[u] : -INFINITY;
+      const float mn = fmaxf(m, lu);
+      if (lu > -INFINITY && mn > -INFINITY) {
         const float c_old = m == -INFINITY ? 0.f : fast_exp2((m - mn) * kLog2e);
-        const float c_new = fast_exp2((cur.l[u] - mn) * kLog2e);
+        const float c_new = fast_exp2((lu - mn) * kLog2e);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < 2; ++k) {
           acc[2 * k] = acc[2 * k] * c_old + f32x4{bf16_lo(cur.x[u][k][0]), bf16_hi(cur.x[u][k][0]),
                                                   bf16_lo(cur.x[u][k][1]), bf16_hi(cur.x[u][k][1])} * c_new;
           acc[2 * k + 1] = acc[2 * k + 1] * c_old + f32x4{bf16_lo(cur.x[u][k][2]), bf16_hi(cur.x[u][k][2]),
@@ -253,12 +266,12 @@ __global__ __launch_bounds__(256, 1) void merge_v_up_kernel(const MergeParams a)
         m = mn;
       }
     }
-    if (i % ngroups != ngroups - 1) continue;     // more ranks of this block to come
+    if (i % ngroups != ngroups - 1) return;     // more ranks of this block to come
     // Merged latent row (bf16) into o_lds; an absent token or a row with no
     // participating rank is zero.
     const float inv = ssum > 0.f ? 1.f / ssum : 0.f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 2; ++k) {
       const int c = (d0 >> 3) + k;
       *(u32x4*)(o_lds + tt * 1024 + 16 * (c ^ (tt & 7))) =
           u32x4{pack_bf16x2(acc[2 * k][0] * inv, acc[2 * k][1] * inv),
@@ -266,48 +279,74 @@ __global__ __launch_bounds__(256, 1) void merge_v_up_kernel(const MergeParams a)
                 pack_bf16x2(acc[2 * k + 1][0] * inv, acc[2 * k + 1][1] * inv),
                 pack_bf16x2(acc[2 * k + 1][2] * inv, acc[2 * k + 1][3] * inv)};
     }
-    if (a.out_lse && (threadIdx.x & 15) == 0 && t < t_end)
-      a.out_lse[(size_t)t * a.H + h] = ssum > 0.f ? m + fast_log2(ssum) * kLn2 : -INFINITY;
-    // W_UV staged (first block) and the block's rows written; the next block's
-    // partial loads may still be in flight (they target registers, not LDS).
-    if (tb == t_begin) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));   // W_UV staged
+    if (a.out_lse) {
+      // (uniform branch: a kernel argument)
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.out_lse + (size_t)tb * a.H + h), (short)0, kProjBlk * a.H * 4, kBufFlags);
+      const float lse_v = ssum > 0.f ? m + fast_log2(ssum) * kLn2 : -INFINITY;
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse_v), rs,
+                                            (threadIdx.x & 31) == 0 && t < t_end ? (uint32_t)(tt * a.H * 4) : kOff, 0, 0);
+    }
+    // W_UV staged (first block: every load issued so far has landed) and the
+    // block's rows written; later items' partial loads may still be in flight
+    // (they target registers, not LDS).
+    if (tb == t_begin) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    // ---- y[tok][n] for the block's 16 tokens, n = 32wv .. 32wv+31 ----
-    f32x4 y[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // ---- y[tok][n] for the block's 16 tokens, n = 16wv .. 16wv+15 ----
+    f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int n0 = 16 * wv;
 #pragma unroll
     for (int s = 0; s < kLatent / 32; ++s) {
       // A = o: lane (token lr, group g) takes dims 32s + 8g .. +8 (chunk 4s + g).
       const bf16x8 av = *(const bf16x8*)(o_lds + lr * 1024 + 16 * ((4 * s + g) ^ (lr & 7)));
+      // B = W: lane (column n = n0 + lr, group g) takes k = 32s + 8g .. +8 from
+      // two transposed reads: source lane j of read r addresses row
+      // k = 32s + 8g + 4r + (j >> 2), columns n0 + 4(j & 3) .. +4.
+      s16x4 half[2];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        // B = W: lane (column n = 32wv + 16nt + lr, group g) takes k = 32s + 8g .. +8
-        // from two transposed reads: source lane j of read r addresses row
-        // k = 32s + 8g + 4r + (j >> 2), columns n0 + 4(j & 3) .. +4.
-        const int n0 = 32 * wv + 16 * nt;
-        s16x4 half[2];
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int k = 32 * s + 8 * g + 4 * r + (lr >> 2);
-          const int cb = 2 * (n0 + 4 * (lr & 3));
-          half[r] = lds_read_tr16_at(w_lds + k * 256 + (cb ^ (32 * (k & 7))));
-        }
-        const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        y[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, y[nt], 0, 0, 0);
+      for (int r = 0; r < 2; ++r) {
+        const int k = 32 * s + 8 * g + 4 * r + (lr >> 2);
+        const int cb = 2 * (n0 + 4 * (lr & 3));
+        half[r] = lds_read_tr16_at(w_lds + k * 256 + (cb ^ (32 * (k & 7))));
       }
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, y, 0, 0, 0);
     }
     // D: lane (column n = n0 + lr, group g) holds tokens 4g .. 4g+3 of the block.
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.out + ((size_t)tb * a.H + h) * kVHead), (short)0, kProjBlk * a.H * kVHead * 2, kBufFlags);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int n = 32 * wv + 16 * nt + lr;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int to = tb + 4 * g + r;
-        if (to < t_end) a.out[((size_t)to * a.H + h) * kVHead + n] = __builtin_bit_cast(uint16_t, (__bf16)y[nt][r]);
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int tk = 4 * g + r;
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)y[r]), ry,
+                                            tb + tk < t_end ? (uint32_t)((tk * a.H * kVHead + n0 + lr) * 2) : kOff, 0, 0);
     }
     // o_lds is rewritten by the next block.
     asm volatile("s_barrier" ::: "memory");
+  };
+
+  // Three register buffers in rotation: while item i is merged, the partials of
+  // items i + 1 and i + 2 are in flight (and the counts of item i + 3).  The
+  // buffers are never copied (a copy would wait for its loads).
+  Pend b0, b1, b2;
+  int vv[4];
+  load_valid(0, vv);
+  load_data(0, vv, b0);
+  load_valid(1, vv);
+  load_data(1, vv, b1);
+  load_valid(2, vv);
+  auto step = [&](int i, const Pend& cur, Pend& dst) {
+    load_data(i + 2, vv, dst);        // past the last item: no lane reads anything
+    load_valid(i + 3, vv);
+    process(i, cur);
+  };
+  for (int i = 0; i < nitems; i += 3) {
+    step(i, b0, b2);
+    if (i + 1 >= nitems) break;
+    step(i + 1, b1, b0);
+    if (i + 2 >= nitems) break;
+    step(i + 2, b2, b1);
   }
 }
 
@@ -325,7 +364,9 @@ hipError_t launch_merge_v_up(const MergeParams& p, hipStream_t stream) {
   int groups = (256 + p.H - 1) / p.H;
   const int max_groups = (p.T + kProjBlk - 1) / kProjBlk;
   if (groups > max_groups) groups = max_groups;
-  hipLaunchKernelGGL(merge_v_up_kernel, dim3((unsigned)p.H, (unsigned)groups), dim3(256), 0, stream, p);
+  const dim3 grid((unsigned)p.H, (unsigned)groups);
+  if (p.valid) hipLaunchKernelGGL(merge_v_up_kernel<true>, grid, dim3(kProjThreads), 0, stream, p);
+  else hipLaunchKernelGGL(merge_v_up_kernel<false>, grid, dim3(kProjThreads), 0, stream, p);
   return hipGetLastError();
 }
 

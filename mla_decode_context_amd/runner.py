@@ -62,7 +62,13 @@ class DeviceWorkload:
         if self.H == 128:
             page32 = "true" if self.wl.P % 32 == 0 else "false"
             name = f"decode_kernel_h128<{page32}>"
-            return name + "+combine_fixed_kernel" if self.workspace is not None else name
+            if self.workspace is None:
+                return name
+            # the workspace holds the dispatch order (one int32 per token and
+            # 64-head block, 256-byte aligned) and, when rows are split, the partials
+            order_only = -(-self.T * 2 * 4 // 256) * 256 + 256
+            name = "h128_order_kernel+" + name
+            return name + "+combine_fixed_kernel" if self.workspace.numel() > order_only else name
         page16 = "true" if self.wl.P % 16 == 0 else "false"
         if self.H <= 16:
             if self.num_splits == 0 and self.workspace is not None:

@@ -224,3 +224,83 @@ def test_hip_graph_replay_matches_eager(tiny):
         torch.cuda.synchronize()
         assert torch.equal(dw.outs, ref[0]) and torch.equal(dw.lses, ref[1])
         assert torch.equal(dw.out, ref[2]) and torch.equal(dw.out_lse, ref[3])
+
+
+# ---------------------------------------------------------------------------
+# 128 heads: longest-first dispatch order
+# ---------------------------------------------------------------------------
+
+ORDER_CASES = [
+    # name, seq_lens, query_lens, W, num_splits
+    ("mtp_like", [1500, 40, 3000, 700, 2, 2200], [2, 2, 2, 1, 2, 4], 4, 0),
+    ("split_rows", [5000, 900, 3], [1, 2, 3], 2, 4),
+    ("prefill_chunk", [600, 90, 1200], [1, 64, 2], 1, 1),
+]
+
+
+def _h128_split_plan(T, max_seq_len, W, num_splits):
+    """The library's split plan for 128 heads (host arithmetic): keys per split
+    and the number of splits.  Automatic splits aim for 256 workgroups and never
+    cut below 512 keys; splits are whole 32-key stages."""
+    lmax = -(-max_seq_len // W)
+    lr = -(-max(lmax, 1) // 32) * 32
+    chunk = lr
+    if num_splits != 1 and lmax > 0:
+        if num_splits > 1:
+            chunk = -(-(-(-lmax // num_splits)) // 32) * 32
+        else:
+            want = -(-256 // T)
+            if want > 1:
+                chunk = -(-(-(-lmax // want)) // 32) * 32
+            chunk = max(chunk, 512)
+        if chunk >= lmax:
+            chunk = lr
+    return chunk, -(-lr // chunk)
+
+
+@pytest.mark.parametrize("name,S,Q,W,num_splits", ORDER_CASES, ids=[c[0] for c in ORDER_CASES])
+def test_h128_dispatch_order(name, S, Q, W, num_splits):
+    """The 128-head launch orders its work items longest first in the workspace
+    (its first region: int32 item = (split*T + token)*2 + head block per grid
+    position, -1 past the last item).
+
+    Checks, for every rank: the order holds exactly the items the split plan
+    needs, each once, then -1; the (split, request) units it visits have
+    non-increasing stage counts; results match the oracle; and with nothing
+    split they are bitwise those of the same call in token order (workspace =
+    NULL)."""
+    log(f"h128 order {name}")
+    wl = WL.make_custom(name, S, Q, H=128, W=W, P=64, seed=5)
+    dw = DeviceWorkload(wl, num_splits=num_splits)
+    dw.outs.fill_(float("nan"))
+    ref_o, ref_l = oracle_partials(wl, list(range(wl.T)))
+    qsl = np.asarray(wl.query_start_loc, dtype=np.int64)
+    req_of = np.repeat(np.arange(wl.B), np.diff(qsl))
+    chunk, max_splits = _h128_split_plan(wl.T, int(np.max(wl.seq_lens)), W, num_splits)
+    n_map = wl.T * 2 * max_splits
+    off = (-dw.workspace.data_ptr()) % 256
+    for r in range(W):
+        dw.partial(r)
+        torch.cuda.synchronize()
+        check_rows(dw.outs[r], dw.lses[r], ref_o[r], ref_l[r], f"{name} r={r}")
+        m = dw.workspace[off: off + 4 * n_map].cpu().numpy().view(np.int32)
+        L = O.row_counts(wl.seq_lens, wl.query_start_loc, W, r).astype(np.int64)
+        want = {(s * wl.T + t) * 2 + h for t in range(wl.T) for h in range(2)
+                for s in range(max(1, -(-int(L[t]) // chunk)))}
+        items = m[m >= 0]
+        assert len(items) == len(want) and set(items.tolist()) == want, f"{name} r={r}: wrong item set"
+        assert np.all(m[len(items):] == -1), f"{name} r={r}: the order's tail must be -1"
+        split = items // (2 * wl.T)
+        b = req_of[(items // 2) % wl.T]
+        Lc = O.shard_lengths(wl.seq_lens, W, r).astype(np.int64)[b]
+        cnt = np.minimum(Lc - split * chunk, chunk)
+        stages = np.minimum(np.where(cnt > 0, -(-cnt // 32), 0), 1023)
+        assert np.all(np.diff(stages) <= 0), f"{name} r={r}: not longest first"
+        if max_splits == 1:
+            out2 = torch.empty_like(dw.outs[r])
+            lse2 = torch.empty_like(dw.lses[r])
+            mla.mla_decode_partial(dw.q_nope, dw.q_pe, dw.caches[r], dw.tables[r], dw.seq_lens, dw.qsl,
+                                   W, r, wl.scale, out2, lse2, max_query_len=dw.max_query_len,
+                                   max_seq_len=dw.max_seq_len, workspace=None, num_splits=1)
+            torch.cuda.synchronize()
+            assert torch.equal(out2, dw.outs[r]) and torch.equal(lse2, dw.lses[r]), name
