@@ -96,9 +96,12 @@ const char* mla_status_string(mla_status status);
  * 0 = choose automatically, 1 = never split, k = at most k.  Splitting needs
  * `workspace` of at least mla_decode_workspace_size(...) bytes (any
  * alignment); with workspace == NULL the call runs unsplit.  The workspace
- * holds the split partials and the split tickets of the in-kernel combine:
- * it must be zero-filled before its first use, every call leaves it ready for
- * the next (tickets back at zero), and calls that overlap in time (e.g. on two
+ * holds the split partials and the split tickets of the in-kernel combine,
+ * and, for H = 128, the order in which the call dispatches its work
+ * (longest rows first, computed on the device by the call itself; without a
+ * workspace the rows run in token order, with the same results).  It must be
+ * zero-filled before its first use, every call leaves it ready for the next
+ * (tickets back at zero), and calls that overlap in time (e.g. on two
  * streams) must not share one workspace.
  *
  * Returns MLA_OK, or MLA_ERR_NULL / MLA_ERR_SHAPE (B<0, T<0, H outside
@@ -122,7 +125,8 @@ mla_status mla_decode_partial(
 
 /*
  * Bytes of workspace mla_decode_partial needs for the same host arguments
- * (0 when the plan does not split).  Pure host arithmetic, no device access.
+ * (0 when the plan neither splits nor, for H = 128, orders its work).  Pure
+ * host arithmetic, no device access.
  * Returns (size_t)-1 for invalid arguments.
  */
 size_t mla_decode_workspace_size(int32_t B, int32_t T, int32_t H, int32_t max_query_len,
@@ -135,8 +139,10 @@ size_t mla_decode_workspace_size(int32_t B, int32_t T, int32_t H, int32_t max_qu
  *   outs  bf16 [W,T,H,512] contiguous (rank r's partial at outs + r*T*H*512)
  *   lses  fp32 [W,T,H] contiguous (natural-log LSE, -inf for empty rows)
  *   valid int32 [W,T] per-row key counts, or NULL.  Rank w takes part in row t
- *         iff valid[w*T+t] > 0 (with NULL: iff its lse is > -inf).  Partials of
- *         ranks that do not take part are never read, whatever they hold.
+ *         iff valid[w*T+t] > 0 (with NULL: iff its lse is > -inf).  What a
+ *         rank that does not take part holds never reaches the result; with
+ *         counts given its partial and LSE are not even read (without counts
+ *         every rank's row is read and its LSE decides).
  *   out   bf16 [T,H,512]:  out = sum_w exp(lse_w - LSE) * outs_w
  *   out_lse fp32 [T,H] or NULL:  LSE = ln sum_w exp(lse_w)
  * A row with no participating rank gets out = 0 and LSE = -inf.

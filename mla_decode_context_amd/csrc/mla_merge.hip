@@ -15,110 +15,142 @@
 
 namespace mla {
 
-// Rank w takes part in row t iff valid[w,t] > 0, or, without counts, iff its
-// LSE is above -inf (a NaN LSE is treated as not taking part).  With counts,
-// nothing else of a rank that does not take part is read.
-__device__ __forceinline__ bool takes_part(const MergeParams& a, int w, int t, size_t lse_idx,
-                                           float& lse_w) {
-  if (a.valid && a.valid[(size_t)w * a.T + t] <= 0) return false;
-  lse_w = a.lses[lse_idx];
-  return a.valid ? true : (lse_w > -INFINITY);
-}
+// Workgroup = (8 heads, a contiguous range of tokens), 256 threads; thread
+// (head 8*blockIdx.x + tid / 32, dims 16*(tid % 32) .. +16).  The workgroup
+// walks its tokens in items of (token, R ranks): every rank's LSE and partial
+// of the item are loaded together and combined online (running max, rescaled
+// sum, ranks in order).  Three register buffers rotate so that two items'
+// loads are in flight while one is combined.  Whether rank w takes part in
+// row t is the same for the whole workgroup, so valid[w, t] comes through
+// scalar loads one item earlier still.  Every load and store is a buffer
+// operation issued whether or not its lane has work: a disabled lane carries
+// an offset past the buffer's range, which reads zero (or writes nothing)
+// without touching memory, so the compiler's waits for the loads stay exact.
+// R = 4 when W <= 8 (fewer registers, more workgroups per CU; ranks 5..8 are a
+// second item of the same token), else 8.
+constexpr int kMergeHeads = 8;
+constexpr int kBufFlags = 0x00020000;              // buffer resource word 3 (raw 32-bit data)
+constexpr uint32_t kOffNone = 0x40000000u;         // past every buffer range used here
 
-// Merge weights of row (t, h): fills LSE and returns false when no rank takes part.
-__device__ __forceinline__ bool merge_lse(const MergeParams& a, int t, int h, float& lse_tot) {
-  const size_t plane = (size_t)a.T * a.H;
-  const size_t row = (size_t)t * a.H + h;
-  float mx = -INFINITY;
-  bool any = false;
-  for (int w = 0; w < a.W; ++w) {
-    float l;
-    if (takes_part(a, w, t, w * plane + row, l)) {
-      mx = any ? fmaxf(mx, l) : l;
-      any = true;
-    }
-  }
-  if (!any) {
-    lse_tot = -INFINITY;
-    return false;
-  }
-  float sum = 0.f;
-  for (int w = 0; w < a.W; ++w) {
-    float l;
-    if (takes_part(a, w, t, w * plane + row, l)) sum += fast_exp2((l - mx) * kLog2e);
-  }
-  lse_tot = mx + fast_log2(sum) * kLn2;
-  return true;
-}
-
-// Workgroup = (token t, 16 heads); thread (head 16*blockIdx.y + tid / 16, dims
-// 32*(tid % 16) .. +32).  Whether rank w takes part in row t is the same for
-// every thread of the workgroup, so valid[w, t] comes through scalar loads;
-// the LSEs and partials of up to R participating ranks are then loaded
-// together and combined online (running max, rescaled sum), ranks in order.
-// R = 4 when W <= 4 (fewer registers, more workgroups per CU), else 8.
-template <int R>
+template <int R, bool kValid>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams a) {
-  const int t = blockIdx.x;
-  const int h = 16 * blockIdx.y + (threadIdx.x >> 4);
-  const int d0 = 32 * (threadIdx.x & 15);
-  const bool hok = h < a.H;
-  const int hc = hok ? h : a.H - 1;
+  const int lane = threadIdx.x & 63;
+  const int hl = threadIdx.x >> 5;
+  const int h0 = kMergeHeads * (int)blockIdx.x;
+  const bool hok = h0 + hl < a.H;
+  const int d0 = 16 * (threadIdx.x & 31);
+  const int per = (a.T + (int)gridDim.y - 1) / (int)gridDim.y;
+  const int t_begin = (int)blockIdx.y * per;
+  const int t_end = min(a.T, t_begin + per);
+  if (t_begin >= t_end) return;
   const size_t plane = (size_t)a.T * a.H;
-  const size_t row = (size_t)t * a.H + hc;
-  const int32_t* vcol = a.valid;
-  float m = -INFINITY, ssum = 0.f;
-  f32x4 acc[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int w0 = 0; w0 < a.W; w0 += R) {
+  const int ngroups = (a.W + R - 1) / R;
+  const int nitems = (t_end - t_begin) * ngroups;
+  struct Pend {
+    u32x4 x[R][2];
     float l[R];
-    u32x4 x[R][4];
+    int part;          // bit u: rank w0 + u was read
+  };
+  auto item_t = [&](int i) { return min(t_begin + i / ngroups, a.T - 1); };
+  auto load_valid = [&](int i, int (&vv)[R]) {
+    const int t = item_t(i), w0 = R * (i % ngroups);
 #pragma unroll
     for (int u = 0; u < R; ++u) {
-      const int w = w0 + u;
-      bool take = w < a.W;
-      if (take && vcol)
-        take = ((const __attribute__((address_space(4))) int32_t*)vcol)[(size_t)w * a.T + t] > 0;
-      l[u] = -INFINITY;
-      if (take) {
-        l[u] = a.lses[w * plane + row];
-        const u32x4* src = (const u32x4*)(a.outs + (w * plane + row) * kLatent + d0);
-        if (vcol || l[u] > -INFINITY) {
+      const int w = min(w0 + u, a.W - 1);
+      int c = 1;
+      if (kValid) c = ((const __attribute__((address_space(4))) int32_t*)a.valid)[(size_t)w * a.T + t] > 0 ? 1 : 0;
+      vv[u] = c & ((i < nitems && w0 + u < a.W && hok) ? 1 : 0);
+    }
+  };
+  auto load_data = [&](int i, const int (&vv)[R], Pend& p) {
+    const int t = item_t(i), w0 = R * (i % ngroups);
+    p.part = 0;
 #pragma unroll
-          for (int k = 0; k < 4; ++k) x[u][k] = src[k];
-        }
-      }
+    for (int u = 0; u < R; ++u) {
+      const size_t row0 = min(w0 + u, a.W - 1) * plane + (size_t)t * a.H + h0;   // the item's first head
+      const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.outs + row0 * kLatent), (short)0, kMergeHeads * kLatent * 2, kBufFlags);
+      const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.lses + row0), (short)0, kMergeHeads * 4, kBufFlags);
+      const uint32_t oo = vv[u] ? (uint32_t)(hl * kLatent * 2 + 2 * d0) : kOffNone;
+      const uint32_t ol = vv[u] ? (uint32_t)(hl * 4) : kOffNone;
+      p.l[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, ol, 0, 0));
+      p.x[u][0] = __builtin_amdgcn_raw_buffer_load_b128(ro, oo, 0, 0);
+      p.x[u][1] = __builtin_amdgcn_raw_buffer_load_b128(ro, oo + 16, 0, 0);
+      p.part |= vv[u] << u;
+    }
+  };
+  float m = -INFINITY, ssum = 0.f;
+  f32x4 acc[4];
+  auto process = [&](int i, const Pend& cur) {
+    if (i % ngroups == 0) {
+      m = -INFINITY;
+      ssum = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int u = 0; u < R; ++u) {
       // A rank whose LSE is -inf (or NaN, without counts) adds nothing.
-      const float mn = fmaxf(m, l[u]);
-      if (l[u] > -INFINITY && mn > -INFINITY) {
+      const float lu = (cur.part >> u) & 1 ? cur.l[u] : -INFINITY;
+      const float mn = fmaxf(m, lu);
+      if (lu > -INFINITY && mn > -INFINITY) {
         const float c_old = m == -INFINITY ? 0.f : fast_exp2((m - mn) * kLog2e);
-        const float c_new = fast_exp2((l[u] - mn) * kLog2e);
+        const float c_new = fast_exp2((lu - mn) * kLog2e);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          acc[2 * k] = acc[2 * k] * c_old + f32x4{bf16_lo(x[u][k][0]), bf16_hi(x[u][k][0]),
-                                                  bf16_lo(x[u][k][1]), bf16_hi(x[u][k][1])} * c_new;
-          acc[2 * k + 1] = acc[2 * k + 1] * c_old + f32x4{bf16_lo(x[u][k][2]), bf16_hi(x[u][k][2]),
-                                                          bf16_lo(x[u][k][3]), bf16_hi(x[u][k][3])} * c_new;
+        for (int k = 0; k < 2; ++k) {
+          acc[2 * k] = acc[2 * k] * c_old + f32x4{bf16_lo(cur.x[u][k][0]), bf16_hi(cur.x[u][k][0]),
+                                                  bf16_lo(cur.x[u][k][1]), bf16_hi(cur.x[u][k][1])} * c_new;
+          acc[2 * k + 1] = acc[2 * k + 1] * c_old + f32x4{bf16_lo(cur.x[u][k][2]), bf16_hi(cur.x[u][k][2]),
+                                                          bf16_lo(cur.x[u][k][3]), bf16_hi(cur.x[u][k][3])} * c_new;
         }
         ssum = ssum * c_old + c_new;
         m = mn;
       }
     }
-  }
-  if (!hok) return;
-  const float inv = ssum > 0.f ? 1.f / ssum : 0.f;
-  uint16_t* op = a.out + row * kLatent + d0;
+    if (i % ngroups != ngroups - 1) return;     // more ranks of this token to come
+    const int t = item_t(i);
+    const float inv = ssum > 0.f ? 1.f / ssum : 0.f;
+    const size_t row0 = (size_t)t * a.H + h0;
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.out + row0 * kLatent), (short)0, kMergeHeads * kLatent * 2, kBufFlags);
+    const uint32_t ow = hok ? (uint32_t)(hl * kLatent * 2 + 2 * d0) : kOffNone;
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
-    *(u32x4*)(op + 8 * k) = u32x4{pack_bf16x2(acc[2 * k][0] * inv, acc[2 * k][1] * inv),
-                                  pack_bf16x2(acc[2 * k][2] * inv, acc[2 * k][3] * inv),
-                                  pack_bf16x2(acc[2 * k + 1][0] * inv, acc[2 * k + 1][1] * inv),
-                                  pack_bf16x2(acc[2 * k + 1][2] * inv, acc[2 * k + 1][3] * inv)};
-  if (a.out_lse && (threadIdx.x & 15) == 0) a.out_lse[row] = ssum > 0.f ? m + fast_log2(ssum) * kLn2 : -INFINITY;
+    for (int k = 0; k < 2; ++k)
+      __builtin_amdgcn_raw_buffer_store_b128(
+          u32x4{pack_bf16x2(acc[2 * k][0] * inv, acc[2 * k][1] * inv),
+                pack_bf16x2(acc[2 * k][2] * inv, acc[2 * k][3] * inv),
+                pack_bf16x2(acc[2 * k + 1][0] * inv, acc[2 * k + 1][1] * inv),
+                pack_bf16x2(acc[2 * k + 1][2] * inv, acc[2 * k + 1][3] * inv)},
+          rw, ow + 16 * k, 0, 0);
+    if (a.out_lse) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(a.out_lse + row0), (short)0, kMergeHeads * 4, kBufFlags);
+      const float lse_v = ssum > 0.f ? m + fast_log2(ssum) * kLn2 : -INFINITY;
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse_v), rs,
+                                            hok && (threadIdx.x & 31) == 0 ? (uint32_t)(hl * 4) : kOffNone, 0, 0);
+    }
+  };
+  Pend b0, b1, b2;
+  int vv[R];
+  load_valid(0, vv);
+  load_data(0, vv, b0);
+  load_valid(1, vv);
+  load_data(1, vv, b1);
+  load_valid(2, vv);
+  auto step = [&](int i, const Pend& cur, Pend& dst) {
+    load_data(i + 2, vv, dst);        // past the last item: no lane reads anything
+    load_valid(i + 3, vv);
+    process(i, cur);
+  };
+  for (int i = 0; i < nitems; i += 3) {
+    step(i, b0, b2);
+    if (i + 1 >= nitems) break;
+    step(i + 1, b1, b0);
+    if (i + 2 >= nitems) break;
+    step(i + 2, b2, b1);
+  }
+  (void)lane;
 }
 
 // ---------------------------------------------------------------------------
@@ -140,7 +172,6 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams a) {
 constexpr int kProjBlk = 16;                       // tokens per block
 constexpr int kProjThreads = 512;
 constexpr int kWBytes = kLatent * kVHead * 2;      // 128 KiB
-constexpr int kBufFlags = 0x00020000;              // buffer resource word 3 (raw 32-bit data)
 
 template <bool kValid>
 __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const MergeParams a) {
@@ -214,8 +245,7 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
   // takes part: buffer loads whose offset lies past the buffer's range return
   // zero without touching memory.  So the number of loads in flight never
   // depends on the data and the compiler's waits stay exact.
-  constexpr uint32_t kOff = 0x40000000u;          // past every range below
-  auto load_data = [&](int i, const int (&vv)[4], Pend& p) {
+    auto load_data = [&](int i, const int (&vv)[4], Pend& p) {
     const int tb = min(item_tb(i), a.T - 1), w0 = item_w0(i);
     p.part = 0;
 #pragma unroll
@@ -226,8 +256,8 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
           __builtin_amdgcn_make_buffer_rsrc((void*)(a.outs + row0 * kLatent), (short)0, kProjBlk * a.H * 1024, kBufFlags);
       const __amdgpu_buffer_rsrc_t rl =
           __builtin_amdgcn_make_buffer_rsrc((void*)(a.lses + row0), (short)0, kProjBlk * a.H * 4, kBufFlags);
-      const uint32_t oo = vv[u] ? (uint32_t)(tt * a.H * 1024 + 2 * d0) : kOff;
-      const uint32_t ol = vv[u] ? (uint32_t)(tt * a.H * 4) : kOff;
+      const uint32_t oo = vv[u] ? (uint32_t)(tt * a.H * 1024 + 2 * d0) : kOffNone;
+      const uint32_t ol = vv[u] ? (uint32_t)(tt * a.H * 4) : kOffNone;
       p.l[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, ol, 0, 0));
       p.x[u][0] = __builtin_amdgcn_raw_buffer_load_b128(ro, oo, 0, 0);
       p.x[u][1] = __builtin_amdgcn_raw_buffer_load_b128(ro, oo + 16, 0, 0);
@@ -285,7 +315,7 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
           (void*)(a.out_lse + (size_t)tb * a.H + h), (short)0, kProjBlk * a.H * 4, kBufFlags);
       const float lse_v = ssum > 0.f ? m + fast_log2(ssum) * kLn2 : -INFINITY;
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse_v), rs,
-                                            (threadIdx.x & 31) == 0 && t < t_end ? (uint32_t)(tt * a.H * 4) : kOff, 0, 0);
+                                            (threadIdx.x & 31) == 0 && t < t_end ? (uint32_t)(tt * a.H * 4) : kOffNone, 0, 0);
     }
     // W_UV staged (first block: every load issued so far has landed) and the
     // block's rows written; later items' partial loads may still be in flight
@@ -320,7 +350,7 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
     for (int r = 0; r < 4; ++r) {
       const int tk = 4 * g + r;
       __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)y[r]), ry,
-                                            tb + tk < t_end ? (uint32_t)((tk * a.H * kVHead + n0 + lr) * 2) : kOff, 0, 0);
+                                            tb + tk < t_end ? (uint32_t)((tk * a.H * kVHead + n0 + lr) * 2) : kOffNone, 0, 0);
     }
     // o_lds is rewritten by the next block.
     asm volatile("s_barrier" ::: "memory");
@@ -352,9 +382,21 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
 
 hipError_t launch_lse_merge(const MergeParams& p, hipStream_t stream) {
   if (p.T <= 0) return hipSuccess;
-  const dim3 grid((unsigned)p.T, (unsigned)((p.H + 15) / 16));
-  if (p.W <= 4) hipLaunchKernelGGL(lse_merge_kernel<4>, grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL(lse_merge_kernel<8>, grid, dim3(256), 0, stream, p);
+  // Ranges of 16 tokens (measured best against 4, 8 and 32 at the DCP4 and
+  // DCP8 shapes), shorter when that leaves fewer than 256 workgroups; heads
+  // fastest.
+  const int hblocks = (p.H + kMergeHeads - 1) / kMergeHeads;
+  int ranges = (p.T + 15) / 16;
+  const int want = (256 + hblocks - 1) / hblocks;
+  if (ranges < want) ranges = want < (p.T + 3) / 4 ? want : (p.T + 3) / 4;
+  const dim3 grid((unsigned)hblocks, (unsigned)ranges);
+  if (p.W <= 8) {
+    if (p.valid) hipLaunchKernelGGL((lse_merge_kernel<4, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((lse_merge_kernel<4, false>), grid, dim3(256), 0, stream, p);
+  } else {
+    if (p.valid) hipLaunchKernelGGL((lse_merge_kernel<8, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((lse_merge_kernel<8, false>), grid, dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
