@@ -503,19 +503,23 @@ __global__ __launch_bounds__(256) void combine_fixed_kernel(const DecodeParams a
 // unit's rows last row first.  Position p >= the item count maps to -1.
 constexpr int kOrdThreads = 1024;
 constexpr int kOrdBuckets = 1024;                  // stage counts >= 1023 share the top bucket
-constexpr int kOrdMaxUnits = 8192;                 // more units: the decode runs unordered
+constexpr int kOrdMaxUnits = 8192;                 // more (split, request) units: the decode runs unordered
+constexpr int kOrdMaxRequests = 4096;              // more requests: likewise
 
 struct UnitInfo {
   int q0, rows, first;   // first token, rows with work in this split, index of the first of them
   int stages;            // sort key
 };
 
-__device__ __forceinline__ UnitInfo unit_info(const DecodeParams& a, int u) {
+// Unit u = (split u / B, request u % B), from the request's first token, rows
+// and length held in LDS.
+__device__ __forceinline__ UnitInfo unit_info(const DecodeParams& a, int u, const int* rq0, const int* rq,
+                                              const int* rs) {
   const int s = u / a.B, b = u - s * a.B;
   UnitInfo ui;
-  ui.q0 = a.qsl[b];
-  const int Q = a.qsl[b + 1] - ui.q0;
-  const int S = a.seq_lens[b];
+  ui.q0 = rq0[b];
+  const int Q = rq[b];
+  const int S = rs[b];
   const int c = s * a.chunk;
   // Row i sees ceil((S - Q + i + 1 - r) / W) local keys, more than c exactly when
   // i >= cW - S + Q + r.  Split 0 also keeps the rows without keys (they write
@@ -548,14 +552,23 @@ __global__ __launch_bounds__(kOrdThreads) void h128_order_kernel(const DecodePar
   __shared__ int start[kOrdBuckets];
   __shared__ int ord[kOrdMaxUnits];      // sorted units
   __shared__ int first_item[kOrdMaxUnits + 1];
+  __shared__ int rq0[kOrdMaxRequests], rq[kOrdMaxRequests], rs[kOrdMaxRequests];   // per request
   __shared__ int wsum[kOrdThreads / 64];
   const int tid = threadIdx.x;
   const int U = a.B * a.max_splits;
   const int hblocks = a.H / kXHeads;
   const int n_map = a.T * hblocks * a.max_splits;
+  // The only global reads: every request's first token, rows and length.
+  for (int b = tid; b < a.B; b += kOrdThreads) {
+    const int q0 = a.qsl[b];
+    rq0[b] = q0;
+    rq[b] = a.qsl[b + 1] - q0;
+    rs[b] = a.seq_lens[b];
+  }
   start[tid] = 0;
   __syncthreads();
-  for (int u = tid; u < U; u += kOrdThreads) atomicAdd(&start[min(unit_info(a, u).stages, kOrdBuckets - 1)], 1);
+  for (int u = tid; u < U; u += kOrdThreads)
+    atomicAdd(&start[min(unit_info(a, u, rq0, rq, rs).stages, kOrdBuckets - 1)], 1);
   __syncthreads();
   // Longest first: bucket k starts after every unit of the buckets above it.
   const int kb = kOrdBuckets - 1 - tid;
@@ -564,7 +577,7 @@ __global__ __launch_bounds__(kOrdThreads) void h128_order_kernel(const DecodePar
   start[kb] = before;
   __syncthreads();
   for (int u = tid; u < U; u += kOrdThreads) {
-    const int k = min(unit_info(a, u).stages, kOrdBuckets - 1);
+    const int k = min(unit_info(a, u, rq0, rq, rs).stages, kOrdBuckets - 1);
     ord[atomicAdd(&start[k], 1)] = u;
   }
   __syncthreads();
@@ -573,14 +586,14 @@ __global__ __launch_bounds__(kOrdThreads) void h128_order_kernel(const DecodePar
   int local = 0;
   for (int i = 0; i < per; ++i) {
     const int pos = tid * per + i;
-    if (pos < U) local += unit_info(a, ord[pos]).rows * hblocks;
+    if (pos < U) local += unit_info(a, ord[pos], rq0, rq, rs).rows * hblocks;
   }
   int run = block_excl_scan(local, wsum);
   for (int i = 0; i < per; ++i) {
     const int pos = tid * per + i;
     if (pos < U) {
       first_item[pos] = run;
-      run += unit_info(a, ord[pos]).rows * hblocks;
+      run += unit_info(a, ord[pos], rq0, rq, rs).rows * hblocks;
     }
   }
   if (tid == kOrdThreads - 1) first_item[U] = run;   // the last thread's range ends the sequence
@@ -597,7 +610,7 @@ __global__ __launch_bounds__(kOrdThreads) void h128_order_kernel(const DecodePar
       }
       const int u = ord[lo];
       const int s = u / a.B;
-      const UnitInfo ui = unit_info(a, u);
+      const UnitInfo ui = unit_info(a, u, rq0, rq, rs);
       const int o = p - first_item[lo];
       const int row = ui.first + ui.rows - 1 - o / hblocks;      // last row first
       item = (s * a.T + ui.q0 + row) * hblocks + o % hblocks;
@@ -609,8 +622,12 @@ __global__ __launch_bounds__(kOrdThreads) void h128_order_kernel(const DecodePar
 hipError_t launch_decode_h128(const DecodeParams& p, hipStream_t stream) {
   const int items = p.T * (p.H / kXHeads) * p.max_splits;
   unsigned grid = (unsigned)(((items + 7) / 8) * 8);
+  if (p.item_map && (p.B * p.max_splits > kOrdMaxUnits || p.B > kOrdMaxRequests)) {
+    DecodeParams q = p;                 // too many units to sort in one workgroup: token order
+    q.item_map = nullptr;
+    return launch_decode_h128(q, stream);
+  }
   if (p.item_map) {
-    if (p.B * p.max_splits > kOrdMaxUnits) return hipErrorInvalidValue;
     hipLaunchKernelGGL(h128_order_kernel, dim3(1), dim3(kOrdThreads), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -117,3 +117,12 @@ def test_merge_v_up_proj_random(W, T, H):
     assert np.all(gy[dead] == 0) and np.all(to_f64(yl)[dead] == -np.inf)
     check_proj(y[torch.from_numpy(~dead)], ref_y[~dead], f"merge_v_up W={W}")
     assert np.max(np.abs(to_f64(yl)[~dead] - ref_l[~dead])) <= 1e-3
+    # Without counts the LSE decides: ranks that do not take part carry -inf
+    # (and NaN partials, which must not reach the result).
+    lses_m = lses.copy()
+    lses_m[np.broadcast_to((valid <= 0)[:, :, None], lses.shape)] = -np.inf
+    y2 = torch.full((T, H, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    yl2 = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+    mla.mla_merge_v_up_proj(outs_p.cuda(), torch.from_numpy(lses_m).cuda(), None, wuv_t.cuda(), y2, yl2)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y) and torch.equal(yl2, yl), f"merge_v_up W={W} valid=None"
