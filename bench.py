@@ -166,6 +166,13 @@ def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True
     res["decode_TFLOPs"] = float(alg_flops.sum() / (dec_avg.sum() * 1e-3) / 1e12)
     res["decode_pct_bf16_peak"] = 100.0 * res["decode_TFLOPs"] / BF16_PEAK_TFLOPS
     res["decode_pct_hbm_peak"] = 100.0 * res["decode_alg_GBps"] / HBM_PEAK_GBPS
+    # Roofline fraction of the decode calls: the longer of the two roofline
+    # times (bytes at the HBM peak, flops at the dense bf16 peak) over the
+    # measured time, summed over the shards.
+    t_roof = np.maximum(alg_bytes / (HBM_PEAK_GBPS * 1e9), alg_flops / (BF16_PEAK_TFLOPS * 1e12))
+    res["decode_roofline_frac"] = float(t_roof.sum() / (dec_avg.sum() * 1e-3))
+    res["decode_bound"] = "mfma" if alg_flops.sum() / (BF16_PEAK_TFLOPS * 1e12) > \
+        alg_bytes.sum() / (HBM_PEAK_GBPS * 1e9) else "hbm"
     # one-rank view: the slowest rank's partial plus the merge (excludes the exchange)
     if merging:
         valid = dw.valid.cpu().numpy()
@@ -250,6 +257,24 @@ def cpu_baseline(wl, budget_s=12.0):
                 query_tokens_per_s=round(done_tokens / spent, 2))
 
 
+def hbm_read_probe(torch, gib: int = 2, reps: int = 5):
+    """Achievable streaming-read rate on this GPU: torch's sum over a gib-GiB
+    fp32 buffer (far larger than the last-level cache), best of reps.  A
+    calibration beside the 8 TB/s spec, not part of the decode path."""
+    x = torch.ones(gib * (1 << 28), dtype=torch.float32, device="cuda")
+    best = 0.0
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        x.sum()
+        b.record()
+        torch.cuda.synchronize()
+        best = max(best, x.numel() * 4 / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del x
+    torch.cuda.empty_cache()
+    return round(best, 1)
+
+
 def copy_probe(torch, mib: int):
     """One plain device-to-device copy of mib MiB: the known-size kernel that HBM
     traffic counters are scaled by."""
@@ -301,6 +326,8 @@ def main():
         res, _ = time_workload(name, args.config_steps, 3, torch)
         configs[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()}
         print(f"[bench] {name}: {json.dumps(configs[name])}", file=sys.stderr, flush=True)
+    probe = hbm_read_probe(torch)
+    print(f"[bench] HBM read probe: {probe} GB/s", file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
@@ -339,6 +366,7 @@ def main():
         "pct_hbm_peak": round(100.0 * head["kv_GBps"] / HBM_PEAK_GBPS, 2),
         "query_tokens_per_s": round(head["query_tokens_per_s"], 1),
         "kv_GBps_cold_llc": None if head["_cold_kv_GBps"] is None else round(head["_cold_kv_GBps"], 2),
+        "hbm_read_probe": {"GBps": probe, "method": "torch sum over 2 GiB fp32, best of 5"},
         "roofline": roofline,
         "merge_GBps": configs.get("mtp_dcp4", {}).get("merge_GBps"),
         "cpu_baseline": cpu,
