@@ -257,24 +257,6 @@ def cpu_baseline(wl, budget_s=12.0):
                 query_tokens_per_s=round(done_tokens / spent, 2))
 
 
-def hbm_read_probe(torch, gib: int = 2, reps: int = 5):
-    """Achievable streaming-read rate on this GPU: torch's sum over a gib-GiB
-    fp32 buffer (far larger than the last-level cache), best of reps.  A
-    calibration beside the 8 TB/s spec, not part of the decode path."""
-    x = torch.ones(gib * (1 << 28), dtype=torch.float32, device="cuda")
-    best = 0.0
-    for _ in range(reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        x.sum()
-        b.record()
-        torch.cuda.synchronize()
-        best = max(best, x.numel() * 4 / (a.elapsed_time(b) * 1e-3) / 1e9)
-    del x
-    torch.cuda.empty_cache()
-    return round(best, 1)
-
-
 def copy_probe(torch, mib: int):
     """One plain device-to-device copy of mib MiB: the known-size kernel that HBM
     traffic counters are scaled by."""
@@ -326,8 +308,6 @@ def main():
         res, _ = time_workload(name, args.config_steps, 3, torch)
         configs[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()}
         print(f"[bench] {name}: {json.dumps(configs[name])}", file=sys.stderr, flush=True)
-    probe = hbm_read_probe(torch)
-    print(f"[bench] HBM read probe: {probe} GB/s", file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
@@ -366,7 +346,6 @@ def main():
         "pct_hbm_peak": round(100.0 * head["kv_GBps"] / HBM_PEAK_GBPS, 2),
         "query_tokens_per_s": round(head["query_tokens_per_s"], 1),
         "kv_GBps_cold_llc": None if head["_cold_kv_GBps"] is None else round(head["_cold_kv_GBps"], 2),
-        "hbm_read_probe": {"GBps": probe, "method": "torch sum over 2 GiB fp32, best of 5"},
         "roofline": roofline,
         "merge_GBps": configs.get("mtp_dcp4", {}).get("merge_GBps"),
         "cpu_baseline": cpu,
