@@ -505,6 +505,7 @@ constexpr int kOrdThreads = 1024;
 constexpr int kOrdBuckets = 1024;                  // stage counts >= 1023 share the top bucket
 constexpr int kOrdMaxUnits = 8192;                 // more (split, request) units: the decode runs unordered
 constexpr int kOrdMaxRequests = 4096;              // more requests: likewise
+static_assert(kOrdThreads == kOrdBuckets, "one bucket per thread in the order kernel's scan");
 
 struct UnitInfo {
   int q0, rows, first;   // first token, rows with work in this split, index of the first of them

@@ -304,3 +304,30 @@ def test_h128_dispatch_order(name, S, Q, W, num_splits):
                                    max_seq_len=dw.max_seq_len, workspace=None, num_splits=1)
             torch.cuda.synchronize()
             assert torch.equal(out2, dw.outs[r]) and torch.equal(lse2, dw.lses[r]), name
+
+
+def test_hip_graph_replay_h128_ordered():
+    """The 128-head call (dispatch-order kernel, decode, split combine) and the
+    merge captured in one HIP graph: every replay matches the eager results."""
+    wl = WL.make_custom("graph_h128", [700, 90, 2, 1500], [2, 1, 2, 4], H=128, W=2, P=64, seed=8)
+    dw = DeviceWorkload(wl, num_splits=0)
+    dw.step()
+    torch.cuda.synchronize()
+    ref = dw.outs.clone(), dw.lses.clone(), dw.out.clone(), dw.out_lse.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dw.step(stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dw.step()
+    for _ in range(3):
+        dw.outs.zero_()
+        dw.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dw.outs, ref[0]) and torch.equal(dw.lses, ref[1])
+        assert torch.equal(dw.out, ref[2]) and torch.equal(dw.out_lse, ref[3])
