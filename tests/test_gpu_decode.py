@@ -108,11 +108,12 @@ def test_tiny_dcp_bitwise_deterministic_and_block_permutation(tiny):
 # visible-set probe: q = 0 and one-hot latents make the visible keys readable
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("H", [16, 128])
 @pytest.mark.parametrize("W", [1, 2, 3])
-def test_visible_set_probe_exact(W):
+def test_visible_set_probe_exact(W, H):
     S = np.array([6, 37, 128, 255, 3], dtype=np.int32)
     Q = np.array([4, 4, 4, 4, 3], dtype=np.int32)
-    wl = WL.make_custom("probe", S, Q, H=16, W=W, P=16, seed=5)
+    wl = WL.make_custom("probe", S, Q, H=H, W=W, P=16, seed=5)
     wl.q_nope[:] = 0
     wl.q_pe[:] = 0
     one = 0x3F80   # bf16 1.0
