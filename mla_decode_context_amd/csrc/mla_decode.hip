@@ -507,7 +507,7 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
       const int blk = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pg];
       const uint8_t* base = kv_bytes + ((int64_t)blk * a.kv_bs + (int64_t)(j0 - pg * a.P) * kRow) * 2;
 #pragma unroll
-      for (int i2 = 0; i2 < kWBlocks; ++i2) dma_16B_to_lds_sbase(ldst + 1024 * i2, doff[i2], base);
+      for (int i2 = 0; i2 < kWBlocks; ++i2) dma_16B_to_lds_sbase<true>(ldst + 1024 * i2, doff[i2], base);
     } else {
 #pragma unroll
       for (int i2 = 0; i2 < kWBlocks; ++i2) {
@@ -520,7 +520,7 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
         const int bb = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pb2];
         const int pg = j / a.P;                    // pa or pb2
         const int64_t rbase = (int64_t)(pg == pa ? ba : bb) * a.kv_bs + (int64_t)(j - pg * a.P) * kRow;
-        dma_16B_to_lds(kv_bytes + rbase * 2 + (doff[i2] - row * kRowBytes), ring + slot * kWStageBytes + 1024 * i2);
+        dma_16B_to_lds_stream(kv_bytes + rbase * 2 + (doff[i2] - row * kRowBytes), ring + slot * kWStageBytes + 1024 * i2);
       }
     }
   };

@@ -157,7 +157,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
       const int cpos = (o - row * kRowBytes) >> 4;
       const uint32_t doff = (uint32_t)(row * kRowBytes + ((cpos ^ (row & 7)) << 4));
       if (fast) {
-        dma_16B_to_lds_sbase(ldst + 1024 * blkno, doff, base);
+        dma_16B_to_lds_sbase<false>(ldst + 1024 * blkno, doff, base);
       } else {
         const int ra = (1024 * blkno) / kRowBytes;   // the block spans rows ra and ra + 1
         const int j = min(j0 + row, j_end - 1);
