@@ -716,8 +716,9 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // Balanced schedule.  The launch's work is laid out on a line of units: row by
 // row in token order, each row takes kRowUnits (its fixed cost: query load,
 // pipeline fill, the four-wave merge and the waves' uneven finish; measured, a
-// second piece costs a worker about 3.5 stage-times of each wave) followed by
-// one unit per 16-key stage.
+// second piece costs a worker about 3.5 stage-times of each wave, and timing
+// 10, 14, 18 and 24 units per row put the optimum at 18) followed by one unit
+// per 16-key stage.
 // Worker g (one workgroup) takes units [g*per, (g+1)*per) with
 // per = ceil(total / workers), so every worker streams the same number of cache
 // rows (to within one stage) whatever the length mix; a row cut by worker
@@ -728,7 +729,7 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // predecessor (or that starts exactly on its boundary) and 2g + 1 for the row
 // it hands on, so pieces never share a slot.  Every wave computes the schedule
 // itself (same inputs, same result), so no barrier is needed.
-constexpr int kRowUnits = 14;
+constexpr int kRowUnits = 18;
 constexpr int kMinUnitsPerWorker = 8;
 
 __device__ __forceinline__ int h16_stages(int L) { return (L + kWStage - 1) / kWStage; }
