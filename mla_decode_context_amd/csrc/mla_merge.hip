@@ -34,7 +34,6 @@ constexpr uint32_t kOffNone = 0x40000000u;         // past every buffer range us
 
 template <int R, bool kValid>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams a) {
-  const int lane = threadIdx.x & 63;
   const int hl = threadIdx.x >> 5;
   const int h0 = kMergeHeads * (int)blockIdx.x;
   const bool hok = h0 + hl < a.H;
@@ -150,7 +149,6 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams a) {
     if (i + 2 >= nitems) break;
     step(i + 2, b2, b1);
   }
-  (void)lane;
 }
 
 // ---------------------------------------------------------------------------

@@ -31,7 +31,8 @@ def _oracle_merge(outs_t, lses, valid):
     return O.lse_merge(to_f64(outs_t), lses.astype(np.float64), valid)
 
 
-@pytest.mark.parametrize("W,T,H", [(1, 5, 16), (2, 37, 16), (4, 19, 128), (8, 9, 128), (3, 70, 20), (13, 6, 2)])
+@pytest.mark.parametrize("W,T,H", [(1, 5, 16), (2, 37, 16), (4, 19, 128), (8, 9, 128), (3, 70, 20), (13, 6, 2),
+                                   (8, 2, 128), (2, 3, 1), (5, 41, 9)])
 def test_lse_merge_random(W, T, H):
     log(f"merge W={W} T={T} H={H}")
     outs_t, lses, valid = _random_partials(W, T, H, seed=W * 100 + T)
@@ -91,7 +92,7 @@ def test_merge_identities():
     assert np.max(np.abs(to_f64(la) - to_f64(lb))) <= 1e-5
 
 
-@pytest.mark.parametrize("W,T,H", [(4, 70, 128), (1, 16, 16), (2, 130, 24), (8, 3, 128)])
+@pytest.mark.parametrize("W,T,H", [(4, 70, 128), (1, 16, 16), (2, 130, 24), (8, 3, 128), (3, 2, 8), (12, 17, 4)])
 def test_merge_v_up_proj_random(W, T, H):
     log(f"merge_v_up W={W} T={T} H={H}")
     outs_t, lses, valid = _random_partials(W, T, H, seed=W * 7 + T)
