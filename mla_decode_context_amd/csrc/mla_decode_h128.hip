@@ -54,6 +54,8 @@ constexpr int kXHeads = 64;                         // heads per workgroup
 constexpr int kPRow = 80;                           // LDS bytes per head row of P (64 + 16 pad)
 constexpr int kPBuf = kXHeads * kPRow;              // one P buffer
 constexpr float kLazyLog2 = 16.f;                   // softmax reference moves past this margin
+constexpr int kORow = 272;                          // LDS bytes per staged output row (256 + 16 pad:
+                                                    // the 32 heads of one write spread over banks)
 
 __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -412,19 +414,23 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
   __syncthreads();
   __syncthreads();                            // the score waves' sums are in LDS
   // Lane (dim row, half hh) of tile (dt, j) holds head 32j + (lane % 32) and
-  // dims 128pw + 32dt + 8q + 4hh + (0..3) in registers 4q .. 4q+3.
+  // dims 128pw + 32dt + 8q + 4hh + (0..3) in registers 4q .. 4q+3.  A finished
+  // row goes out through LDS: stored straight from these registers, a store
+  // instruction would touch 32 heads' rows 8 bytes each (measured 8 % slower
+  // per call at the MTP shape).
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int hl = 32 * j + (lane & 31);
     const float inv = 1.f / (l_lds[hl] + l_lds[kXHeads + hl]);
     const int h = h0 + hl;
     if (nsplit == 1) {
-      uint16_t* op = a.out + ((size_t)t * a.H + h) * kLatent + 128 * pw + 4 * hh;
+      // bf16 row of head hl, this wave's 128 dims, into the (now idle) ring.
+      uint8_t* st = ring + pw * (kXHeads * kORow) + hl * kORow + 8 * hh;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd)
-          *(u32x2*)(op + 32 * dt + 8 * qd) =
+          *(u32x2*)(st + 2 * (32 * dt + 8 * qd)) =
               u32x2{pack_bf16x2(o[dt][j][4 * qd] * inv, o[dt][j][4 * qd + 1] * inv),
                     pack_bf16x2(o[dt][j][4 * qd + 2] * inv, o[dt][j][4 * qd + 3] * inv)};
     } else {
@@ -436,6 +442,19 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
         for (int qd = 0; qd < 4; ++qd)
           *(f32x4*)(wp + 32 * dt + 8 * qd) = f32x4{o[dt][j][4 * qd] * inv, o[dt][j][4 * qd + 1] * inv,
                                                    o[dt][j][4 * qd + 2] * inv, o[dt][j][4 * qd + 3] * inv};
+    }
+  }
+  if (nsplit == 1) {
+    // Each wave reads back its own rows (its LDS writes are complete after the
+    // wait) and stores them 256 contiguous bytes per head: lane l takes 16 bytes
+    // l % 16 of head 4i + l / 16.
+    __builtin_amdgcn_s_waitcnt(MLA_LGKMCNT0);
+    const uint8_t* sb = ring + pw * (kXHeads * kORow);
+#pragma unroll
+    for (int i = 0; i < kXHeads / 4; ++i) {
+      const int hr = 4 * i + (lane >> 4);
+      const u32x4 v = *(const u32x4*)(sb + hr * kORow + 16 * (lane & 15));
+      *(u32x4*)(a.out + ((size_t)t * a.H + h0 + hr) * kLatent + 128 * pw + 8 * (lane & 15)) = v;
     }
   }
 }
