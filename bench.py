@@ -180,6 +180,10 @@ def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True
         return a.elapsed_time(b) / steps
 
     dec_avg = np.array([loop_ms(lambda r=r: dw.partial(r)) for r in range(wl.W)])   # per shard, ms
+    # Every shard's decode back to back, as a step issues them (consecutive
+    # calls read different shards' caches, so a shard whose cache fits in the
+    # last-level cache gains nothing from the previous call): ms per shard.
+    dec_step = loop_ms(lambda: [dw.partial(r) for r in range(wl.W)]) / wl.W
     mg_ms = None
     if merging:
         dw.valid_counts()
@@ -188,19 +192,21 @@ def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True
     kv_total = sum(p["kv"] for p in per_shard)
     res["kv_GBps"] = kv_total / (ms_step * 1e-3) / 1e9
     res["query_tokens_per_s"] = wl.T / (ms_step * 1e-3)
-    res["decode_ms_per_shard"] = [round(float(x), 4) for x in dec_avg]
+    res["decode_ms_per_shard"] = [round(float(x), 4) for x in dec_avg]   # one shard's calls repeated
+    res["decode_ms_per_shard_in_step"] = round(float(dec_step), 4)
     alg_bytes = np.array([p["total"] for p in per_shard], dtype=np.float64)
     alg_flops = np.array([p["flops"] for p in per_shard], dtype=np.float64)
-    res["decode_alg_GBps"] = float((alg_bytes / (dec_avg * 1e-3)).sum() / len(dec_avg) / 1e9)
-    res["decode_kv_GBps"] = float(sum(p["kv"] for p in per_shard) / (dec_avg.sum() * 1e-3) / 1e9)
-    res["decode_TFLOPs"] = float(alg_flops.sum() / (dec_avg.sum() * 1e-3) / 1e12)
+    dec_all = dec_step * wl.W        # ms for every shard's decode of one step
+    res["decode_alg_GBps"] = float(alg_bytes.sum() / (dec_all * 1e-3) / 1e9)
+    res["decode_kv_GBps"] = float(sum(p["kv"] for p in per_shard) / (dec_all * 1e-3) / 1e9)
+    res["decode_TFLOPs"] = float(alg_flops.sum() / (dec_all * 1e-3) / 1e12)
     res["decode_pct_bf16_peak"] = 100.0 * res["decode_TFLOPs"] / BF16_PEAK_TFLOPS
     res["decode_pct_hbm_peak"] = 100.0 * res["decode_alg_GBps"] / HBM_PEAK_GBPS
     # Roofline fraction of the decode calls: the longer of the two roofline
     # times (bytes at the HBM peak, flops at the dense bf16 peak) over the
     # measured time, summed over the shards.
     t_roof = np.maximum(alg_bytes / (HBM_PEAK_GBPS * 1e9), alg_flops / (BF16_PEAK_TFLOPS * 1e12))
-    res["decode_roofline_frac"] = float(t_roof.sum() / (dec_avg.sum() * 1e-3))
+    res["decode_roofline_frac"] = float(t_roof.sum() / (dec_all * 1e-3))
     res["decode_bound"] = "mfma" if alg_flops.sum() / (BF16_PEAK_TFLOPS * 1e12) > \
         alg_bytes.sum() / (HBM_PEAK_GBPS * 1e9) else "hbm"
     # one-rank view: the slowest rank's partial plus the merge (excludes the exchange)
@@ -221,8 +227,8 @@ def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True
         # Average duration of one decode call (its decode kernel and, when rows
         # were split, the combine kernel): with one rank and no merge a step is
         # exactly one call, so the timed region's events divided by the steps;
-        # otherwise the breakdown's back-to-back timing of each shard's calls.
-        res["_decode_avg_ms"] = float(ev_ms_step) if wl.W == 1 else float(dec_avg.mean())
+        # otherwise every shard's decode back to back, divided by the shards.
+        res["_decode_avg_ms"] = float(ev_ms_step) if wl.W == 1 else float(dec_step)
         res["_kernel"] = dw.decode_kernel_name()
         res["_cold_kv_GBps"] = cold_kv(dw, wl, per_shard, torch) if cold else None
     del dw
