@@ -70,6 +70,14 @@ __device__ __forceinline__ void wait_stage(bool more) {
 
 // LDS writes done, then a workgroup barrier.  (A plain __syncthreads would also
 // wait for the ring's loads still in flight.)
+// Chunk c of stage row `row` sits at chunk c ^ chunk_swizzle(row) (the low three
+// bits only, so a chunk stays in its 128-byte block).  Against the plain row & 7
+// this also flips bit 2 when bit 1 of the row is set: the PV waves' transposed
+// reads touch four consecutive rows per 16 lanes at two chunk pairs, and with
+// row & 7 rows 2i and 2i + 1 of lanes 0..31 land on the same banks (two passes
+// instead of one, measured with SQ_LDS_BANK_CONFLICT); the score waves' 16-byte
+// reads stay conflict-free either way.
+__device__ __forceinline__ int chunk_swizzle(int row) { return (row & 7) ^ ((row << 1) & 4); }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <bool kPage32>
@@ -134,8 +142,8 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring);
 
-  // Stage layout as in the 16-head kernel: byte o of a stage is row o / 1152,
-  // 16-byte chunk c = (o % 1152) / 16, holding chunk c ^ (row & 7) of the row.
+  // Stage layout: byte o of a stage is row o / 1152, 16-byte chunk
+  // c = (o % 1152) / 16, holding chunk c ^ chunk_swizzle(row) of the row.
   // Keys at or past j_end (a ragged last stage) are clamped to key j_end - 1, a
   // real cached row masked to probability 0.
   auto issue = [&](int i) {
@@ -157,7 +165,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
       const int o = 1024 * blkno + 16 * lane;
       const int row = o / kRowBytes;
       const int cpos = (o - row * kRowBytes) >> 4;
-      const uint32_t doff = (uint32_t)(row * kRowBytes + ((cpos ^ (row & 7)) << 4));
+      const uint32_t doff = (uint32_t)(row * kRowBytes + ((cpos ^ chunk_swizzle(row)) << 4));
       if (fast) {
         dma_16B_to_lds_sbase<false>(ldst + 1024 * blkno, doff, base);
       } else {
@@ -219,9 +227,9 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
       }
     }
     // Score reads: lane (key qh, group g) reads chunk 4s + g of row 16kq + qh:
-    // byte row*1152 + 128*(s >> 1) + 16*((4*(s & 1) + g) ^ (qh & 7)).
-    const uint32_t kbase0 = (16 * kq + qh) * kRowBytes + 16 * (g ^ (qh & 7));
-    const uint32_t kbase1 = (16 * kq + qh) * kRowBytes + 16 * ((4 + g) ^ (qh & 7));
+    // byte row*1152 + 128*(s >> 1) + 16*((4*(s & 1) + g) ^ chunk_swizzle(qh)).
+    const uint32_t kbase0 = (16 * kq + qh) * kRowBytes + 16 * (g ^ chunk_swizzle(qh));
+    const uint32_t kbase1 = (16 * kq + qh) * kRowBytes + 16 * ((4 + g) ^ chunk_swizzle(qh));
     float m_ref[2] = {-INFINITY, -INFINITY};  // per head tile, of head 32sg + 16ht + qh
     float l_run[2] = {0.f, 0.f};
     float v[2][4];                            // this stage's raw scores, -inf if masked (kept for a redo)
@@ -367,7 +375,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int key = 8 * hh + 4 * r + (jj >> 2);
-      vb[x][r] = key * kRowBytes + 256 * pw + 16 * ((4 * x + 2 * (G & 1) + ((jj & 3) >> 1)) ^ (key & 7)) + 8 * (jj & 1);
+      vb[x][r] = key * kRowBytes + 256 * pw + 16 * ((4 * x + 2 * (G & 1) + ((jj & 3) >> 1)) ^ chunk_swizzle(key)) + 8 * (jj & 1);
     }
   // P^T (B): lane (head 32j + (lane % 32), half hh) reads keys 16m + 8hh .. +8.
   const uint32_t pbase = (uint32_t)((lane & 31) * kPRow + 16 * hh);
