@@ -66,55 +66,79 @@ def query_rows(seq_lens, query_start_loc):
     return rows
 
 
-def visible_keys(p: int, W: int, r: int) -> list[int]:
+def holder(k: int, W: int, I: int = 1) -> int:
+    """DCP shard that stores global token k.
+
+    PR #24453 thread: with the interleaved layout token k lives on shard k mod W
+    (key A on rank 0, B on rank 1, ...).  The same thread mentions the other
+    layout, contiguous runs of tokens (whole pages) per shard; with runs of I
+    tokens dealt to the shards in turn, token k lives on shard (k div I) mod W.
+    I = 1 is the interleaved layout.
+    """
+    return (k // I) % W
+
+
+def visible_keys(p: int, W: int, r: int, I: int = 1) -> list[int]:
     """Global positions a query row at position p attends to on shard r.
 
-    PR #24453 thread, "DCP Rank 0/1" masks: shard r holds the keys with
-    position mod W == r, and the causal rule keeps those at or before p.
-    Listed in shard-local order (position p' is local index p' div W).
+    PR #24453 thread, "DCP Rank 0/1" masks: shard r holds the keys of its own
+    (holder(k) == r), and the causal rule keeps those at or before p.  Listed in
+    ascending position, which is the shard-local order.
     """
-    return [k for k in range(p + 1) if k % W == r]
+    return [k for k in range(p + 1) if holder(k, W, I) == r]
 
 
-def visible_count(p: int, W: int, r: int) -> int:
-    """Closed form of len(visible_keys(p, W, r)): the per-row, per-shard seqlen_k.
+def visible_count(p: int, W: int, r: int, I: int = 1) -> int:
+    """Closed form of len(visible_keys(p, W, r, I)): the per-row, per-shard seqlen_k.
 
-    The keys k <= p with k = r (mod W) are r, r+W, ..., so their number is
-    ceil((p + 1 - r) / W) when p >= r and 0 otherwise.
+    The n = p + 1 positions 0..p hold n div (W*I) whole rounds of the shards'
+    runs, I tokens of shard r each, and a last partial round of m = n mod (W*I)
+    positions in which shard r's run covers positions rI .. rI + I - 1, i.e.
+    min(max(m - rI, 0), I) of them.  With I = 1: ceil((p + 1 - r) / W) when
+    p >= r, else 0.
     """
-    n = p + 1 - r
-    return 0 if n <= 0 else (n + W - 1) // W
+    n = p + 1
+    if n <= 0:
+        return 0
+    rounds, m = divmod(n, W * I)
+    return rounds * I + min(max(m - r * I, 0), I)
 
 
-def shard_length(S: int, W: int, r: int) -> int:
+def local_index(k: int, W: int, I: int = 1) -> int:
+    """Shard-local index of global token k on its holder: the number of the
+    holder's tokens before k (whole rounds of I tokens, then the offset in the run)."""
+    return (k // (W * I)) * I + k % I
+
+
+def shard_length(S: int, W: int, r: int, I: int = 1) -> int:
     """Tokens of a request with S global tokens stored on shard r (= visible_count(S-1))."""
-    return visible_count(S - 1, W, r) if S > 0 else 0
+    return visible_count(S - 1, W, r, I) if S > 0 else 0
 
 
-def dense_mask(S: int, Q: int, W: int = 1, r: int = 0) -> np.ndarray:
+def dense_mask(S: int, Q: int, W: int = 1, r: int = 0, I: int = 1) -> np.ndarray:
     """Boolean [Q, S] mask over GLOBAL key positions, built entry by entry.
 
     mask[i, k] is True iff key k is causally visible to query row i (k <= S-Q+i)
-    and key k is stored on shard r (k mod W == r).  With W = 1 this is the
-    "Normal" matrix of the PR #24453 thread; its columns restricted to one shard's
-    keys give the "DCP Rank r" matrices.
+    and key k is stored on shard r ((k div I) mod W == r).  With W = 1 this is the
+    "Normal" matrix of the PR #24453 thread; with I = 1 its columns restricted to
+    one shard's keys give the "DCP Rank r" matrices.
     """
     m = np.zeros((Q, S), dtype=bool)
     for i in range(Q):
         for k in range(S):
-            m[i, k] = (k <= S - Q + i) and (k % W == r)
+            m[i, k] = (k <= S - Q + i) and ((k // I) % W == r)
     return m
 
 
-def row_counts(seq_lens, query_start_loc, W: int, r: int) -> np.ndarray:
+def row_counts(seq_lens, query_start_loc, W: int, r: int, I: int = 1) -> np.ndarray:
     """Per query token t, its seqlen_k on shard r (int32 [T])."""
-    return np.array([visible_count(p, W, r) for (_, _, p) in query_rows(seq_lens, query_start_loc)],
+    return np.array([visible_count(p, W, r, I) for (_, _, p) in query_rows(seq_lens, query_start_loc)],
                     dtype=np.int32)
 
 
-def shard_lengths(seq_lens, W: int, r: int) -> np.ndarray:
+def shard_lengths(seq_lens, W: int, r: int, I: int = 1) -> np.ndarray:
     """Per request, the number of its tokens stored on shard r (int32 [B])."""
-    return np.array([shard_length(int(s), W, r) for s in seq_lens], dtype=np.int32)
+    return np.array([shard_length(int(s), W, r, I) for s in seq_lens], dtype=np.int32)
 
 
 # ---------------------------------------------------------------------------
@@ -145,11 +169,11 @@ def attend(q_nope: np.ndarray, q_pe: np.ndarray, keys: np.ndarray, scale: float)
 
 
 def decode_partial(seq_lens, query_start_loc, q_nope_bits, q_pe_bits, global_kv, scale: float,
-                   W: int = 1, r: int = 0, tokens=None):
+                   W: int = 1, r: int = 0, tokens=None, I: int = 1):
     """Shard r's partial attention for every query token (or the listed ones).
 
     ``global_kv(b)`` returns request b's global token rows [S_b, 576] as bf16 bits.
-    Each row attends to visible_keys(p, W, r).  Returns out [n,H,512], lse [n,H]
+    Each row attends to visible_keys(p, W, r, I).  Returns out [n,H,512], lse [n,H]
     (float64) for the selected tokens in the order given.
     """
     rows = query_rows(seq_lens, query_start_loc)
@@ -163,7 +187,7 @@ def decode_partial(seq_lens, query_start_loc, q_nope_bits, q_pe_bits, global_kv,
         if b not in cache:
             cache.clear()
             cache[b] = bf16_bits_to_f64(global_kv(b))
-        keys = cache[b][visible_keys(p, W, r)]
+        keys = cache[b][visible_keys(p, W, r, I)]
         outs[n_out], lses[n_out] = attend(bf16_bits_to_f64(q_nope_bits[t]),
                                           bf16_bits_to_f64(q_pe_bits[t]), keys, scale)
     return outs, lses

@@ -258,6 +258,79 @@ def check_wuv_commutes(seed=4) -> bool:
     return np.allclose(y[1, 1], outs[0, 1, 1] @ w_uv[1], atol=1e-13)
 
 
+def _dealt_holders(S: int, W: int, I: int) -> list[int]:
+    """Shard of each of the tokens 0..S-1 when runs of I consecutive tokens are
+    dealt to the shards 0, 1, .., W-1, 0, .. in turn (simulated with counters)."""
+    out, cur, used = [], 0, 0
+    for _ in range(S):
+        if used == I:
+            cur, used = (cur + 1) % W, 0
+        out.append(cur)
+        used += 1
+    return out
+
+
+def check_runs_bruteforce(max_w=5, max_i=7, max_s=70) -> bool:
+    """Run-dealt layout (runs of I tokens per shard): holder, visible keys, counts,
+    local indices and shard lengths == a simulation of the dealing; the shards
+    partition the keys; I = 1 is the interleaved p mod W layout; with I = page
+    size every page sits whole on one shard, consecutive pages on consecutive
+    shards."""
+    for W in range(1, max_w + 1):
+        for I in range(1, max_i + 1):
+            hold = _dealt_holders(max_s, W, I)
+            for k in range(max_s):
+                if O.holder(k, W, I) != hold[k]:
+                    return False
+                if O.local_index(k, W, I) != sum(1 for j in range(k) if hold[j] == hold[k]):
+                    return False
+                if I == 1 and hold[k] != k % W:
+                    return False
+            for p in range(max_s):
+                tot = 0
+                for r in range(W):
+                    keys = [k for k in range(p + 1) if hold[k] == r]
+                    if O.visible_keys(p, W, r, I) != keys or O.visible_count(p, W, r, I) != len(keys):
+                        return False
+                    if O.shard_length(p + 1, W, r, I) != len(keys):
+                        return False
+                    tot += len(keys)
+                if tot != p + 1:
+                    return False
+    for P, W in ((4, 3), (16, 2)):
+        hold = _dealt_holders(8 * P, W, P)
+        for g in range(8):
+            if set(hold[g * P:(g + 1) * P]) != {g % W}:
+                return False
+    for S, Q, W, I in ((13, 4, 2, 3), (20, 2, 3, 4), (9, 9, 4, 2)):
+        rows = O.query_rows([S], [0, Q])
+        for r in range(W):
+            dm = O.dense_mask(S, Q, W, r, I)
+            if [int(x) for x in dm.sum(axis=1)] != [O.visible_count(p, W, r, I) for (_, _, p) in rows]:
+                return False
+    return True
+
+
+def check_runs_merge_equals_unsharded(seed=5) -> bool:
+    """Run-dealt layout: the merge of the W shards' partials == attention over all keys."""
+    rng = np.random.default_rng(seed)
+    scale = 1 / math.sqrt(192)
+    for seq_lens, q_lens, H, W, I in [([7, 19], [4, 3], 2, 2, 3), ([2, 3, 40], [2, 3, 5], 2, 4, 16),
+                                      ([33], [6], 1, 3, 5), ([12, 30], [1, 6], 2, 8, 2)]:
+        qsl, kvs, qnb, qpb = _sharded_case(rng, seq_lens, q_lens, H, W)
+        full, full_lse = O.decode_partial(seq_lens, qsl, qnb, qpb, lambda b: kvs[b], scale, 1, 0)
+        parts = [O.decode_partial(seq_lens, qsl, qnb, qpb, lambda b: kvs[b], scale, W, r, I=I)
+                 for r in range(W)]
+        outs = np.stack([p[0] for p in parts])
+        lses = np.stack([p[1] for p in parts])
+        valid = np.stack([O.row_counts(seq_lens, qsl, W, r, I) for r in range(W)])
+        for v in (valid, None):
+            m, ml = O.lse_merge(outs, lses, v)
+            if not (np.allclose(m, full, atol=1e-12) and np.allclose(ml, full_lse, atol=1e-12)):
+                return False
+    return True
+
+
 ALL_CHECKS = [check_worked_masks, check_ab_example, check_counts_bruteforce, check_against_sdpa,
               check_closed_forms, check_merge_equals_unsharded, check_merge_identities,
-              check_wuv_commutes]
+              check_wuv_commutes, check_runs_bruteforce, check_runs_merge_equals_unsharded]

@@ -12,14 +12,27 @@ from oracle import mla_oracle as O
 from tests import _pins
 
 
-def _count_drop_plus_one(p, W, r):          # forgets that key p itself is visible
+def _count_drop_plus_one(p, W, r, I=1):     # forgets that key p itself is visible
     n = p - r
     return 0 if n <= 0 else (n + W - 1) // W
 
 
-def _count_floor(p, W, r):                  # floor instead of ceil
+def _count_floor(p, W, r, I=1):             # floor instead of ceil
     n = p + 1 - r
     return 0 if n <= 0 else n // W
+
+
+def _count_runs_unscaled_rank(p, W, r, I=1):  # shard r's run taken to start at position r, not rI
+    rounds, m = divmod(p + 1, W * I)
+    return rounds * I + min(max(m - r, 0), I)
+
+
+def _holder_offset_in_run(k, W, I=1):        # deals by the offset inside the run
+    return (k % I) % W if I > 1 else k % W
+
+
+def _local_index_interleaved(k, W, I=1):     # local index as if the layout were interleaved
+    return k // W
 
 
 def _rows_top_left(seq_lens, qsl):          # query rows at the first Q positions
@@ -30,7 +43,7 @@ def _rows_top_left(seq_lens, qsl):          # query rows at the first Q position
     return rows
 
 
-def _keys_wrong_residue(p, W, r):           # shard r holds p mod W == W-1-r
+def _keys_wrong_residue(p, W, r, I=1):      # shard r holds p mod W == W-1-r
     return [k for k in range(p + 1) if k % W == (W - 1 - r)]
 
 
@@ -77,6 +90,9 @@ MUTANTS = [
     ("visible_count", _count_floor),
     ("query_rows", _rows_top_left),
     ("visible_keys", _keys_wrong_residue),
+    ("visible_count", _count_runs_unscaled_rank),
+    ("holder", _holder_offset_in_run),
+    ("local_index", _local_index_interleaved),
     ("attend", _attend_no_pe),
     ("attend", _attend_double_scale),
     ("attend", _attend_log2),
@@ -88,8 +104,9 @@ MUTANTS = [
 def test_pins_catch_mutant(monkeypatch, name, fn):
     monkeypatch.setattr(O, name, fn)
     results = {c.__name__: _safe(c) for c in _pins.ALL_CHECKS
-               if c is not _pins.check_counts_bruteforce}
+               if c not in (_pins.check_counts_bruteforce, _pins.check_runs_bruteforce)}
     results["check_counts_bruteforce"] = _safe(lambda: _pins.check_counts_bruteforce(5, 30, 5))
+    results["check_runs_bruteforce"] = _safe(lambda: _pins.check_runs_bruteforce(4, 5, 40))
     assert not all(results.values()), f"no pin failed for mutant {name}:{fn.__name__}"
 
 
