@@ -332,7 +332,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200,
                     help="untimed steps first (the GPU's clocks settle over a few thousand microseconds of work)")
     ap.add_argument("--workload", default="plain")
-    ap.add_argument("--configs", default="mtp_dcp4,long_dcp8,mixed_wuv",
+    ap.add_argument("--configs", default="mtp_dcp4,long_dcp8,mixed_wuv,mtp_dcp4_pages",
                     help="comma-separated secondary workloads ('' for none)")
     ap.add_argument("--config-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -10,7 +10,9 @@
  *  - PR #24453 ("add DCP support for FLASH_ATTN_MLA backend"), review thread:
  *    global token p is stored on DCP rank p mod W, and with more than one query
  *    row per request each row gets its own per-rank seqlen_k (the interleaved
- *    causal mask; a row may see no key on a rank).
+ *    causal mask; a row may see no key on a rank).  The same thread mentions the
+ *    layout that gives each rank contiguous blocks of tokens (whole pages); the
+ *    calls take both as runs of cp_interleave tokens dealt to the ranks in turn.
  *  - PR #48196 ("DCP sparse MLA output-merge optimizations"): the exact
  *    LSE-weighted merge of per-rank partials with per-row valid counts, and the
  *    W_UV up-projection, which commutes with the merge.
@@ -65,10 +67,15 @@ const char* mla_status_string(mla_status status);
  * query_start_loc[b+1]); Q_b is their count and T = query_start_loc[B].
  * seq_lens[b] = S_b is the request's GLOBAL token count, its own Q_b query
  * tokens included; query row i of b sits at global position p = S_b - Q_b + i.
- * On rank r of W the request's tokens p = r, r+W, ... are stored in local order
- * j = p div W: local token j lives in physical block block_table[b*bt_stride +
- * j / page_size], slot j % page_size.  Row p sees the local tokens
- * j < ceil((p + 1 - r) / W) (0 if p < r) -- its per-rank seqlen_k.
+ * Shard layout: runs of I = cp_interleave consecutive tokens are dealt to the W
+ * ranks in turn, so token p is stored on rank (p div I) mod W (I = 1: rank
+ * p mod W, the interleaved layout; I = page_size: whole pages per rank).  Rank
+ * r stores its tokens in ascending position, local token j = (p div WI)*I +
+ * p mod I living in physical block block_table[b*bt_stride + j / page_size],
+ * slot j % page_size.  Row p sees the rank's first
+ *   L = (n div WI)*I + min(max(n mod WI - rI, 0), I),   n = p + 1,
+ * local tokens (its per-rank seqlen_k; with I = 1, ceil((p + 1 - r) / W), 0 if
+ * p < r).
  *
  * For every token t and head h, with the visible local keys j:
  *   s_j  = scale * (q_nope[t,h,:] . c_kv_j + q_pe[t,h,:] . k_pe_j)
@@ -105,7 +112,8 @@ const char* mla_status_string(mla_status status);
  * streams) must not share one workspace.
  *
  * Returns MLA_OK, or MLA_ERR_NULL / MLA_ERR_SHAPE (B<0, T<0, H outside
- * [1,128], page_size<1, cp_world<1, cp_rank outside [0,cp_world), strides
+ * [1,128], page_size<1, cp_world<1, cp_rank outside [0,cp_world),
+ * cp_interleave<1 or cp_world*cp_interleave > 2^30, strides
  * smaller than the data, scale not finite or not positive) / MLA_ERR_WORKSPACE /
  * MLA_ERR_UNSUPPORTED / MLA_ERR_HIP.  B == 0 or T == 0 enqueues nothing and
  * returns MLA_OK (the grid is sized from host ints and may be empty).
@@ -119,7 +127,7 @@ mla_status mla_decode_partial(
     const int32_t* block_table, int32_t bt_stride,
     const int32_t* seq_lens, const int32_t* query_start_loc,
     int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
-    int32_t cp_world, int32_t cp_rank, float scale, int32_t num_splits,
+    int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, float scale, int32_t num_splits,
     void* out, float* lse,
     void* workspace, size_t workspace_bytes, void* hip_stream);
 
@@ -130,7 +138,8 @@ mla_status mla_decode_partial(
  * Returns (size_t)-1 for invalid arguments.
  */
 size_t mla_decode_workspace_size(int32_t B, int32_t T, int32_t H, int32_t max_query_len,
-                                 int32_t max_seq_len, int32_t cp_world, int32_t num_splits);
+                                 int32_t max_seq_len, int32_t cp_world, int32_t cp_interleave,
+                                 int32_t num_splits);
 
 /*
  * mla_lse_merge -- exact LSE-weighted merge of W per-rank partials
@@ -170,9 +179,10 @@ mla_status mla_merge_v_up_proj(const void* outs, const float* lses, const int32_
                                void* out, float* out_lse, void* hip_stream);
 
 /*
- * mla_dcp_local_seqlens -- the per-row, per-rank seqlen_k of the interleaved
- * mask (PR #24453 review thread), computed on the device by the same device
- * function the decode kernel uses.  row_seqlen int32 [T] (row t's visible key
+ * mla_dcp_local_seqlens -- the per-row, per-rank seqlen_k of the DCP mask
+ * (PR #24453 review thread; shard layout with runs of cp_interleave tokens as
+ * for mla_decode_partial), computed on the device by the same device function
+ * the decode kernel uses.  row_seqlen int32 [T] (row t's visible key
  * count on rank cp_rank; usable directly as `valid[cp_rank]` of the merge) and
  * shard_len int32 [B] (request b's tokens stored on the rank), either may be
  * NULL.  Returns MLA_OK, MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED or
@@ -180,7 +190,8 @@ mla_status mla_merge_v_up_proj(const void* outs, const float* lses, const int32_
  */
 mla_status mla_dcp_local_seqlens(const int32_t* seq_lens, const int32_t* query_start_loc,
                                  int32_t B, int32_t T, int32_t cp_world, int32_t cp_rank,
-                                 int32_t* row_seqlen, int32_t* shard_len, void* hip_stream);
+                                 int32_t cp_interleave, int32_t* row_seqlen, int32_t* shard_len,
+                                 void* hip_stream);
 
 #ifdef __cplusplus
 }

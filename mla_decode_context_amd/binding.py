@@ -46,10 +46,10 @@ def load_library():
     lib.mla_decode_partial.argtypes = [
         _c_void_p, _i64, _i64, _c_void_p, _i64, _i64, _c_void_p, _i64, _i32,
         _c_void_p, _i32, _c_void_p, _c_void_p,
-        _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
+        _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
         _c_void_p, _c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p]
     lib.mla_decode_workspace_size.restype = ctypes.c_size_t
-    lib.mla_decode_workspace_size.argtypes = [_i32] * 7
+    lib.mla_decode_workspace_size.argtypes = [_i32] * 8
     lib.mla_lse_merge.restype = _i32
     lib.mla_lse_merge.argtypes = [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
                                   _c_void_p, _c_void_p, _c_void_p]
@@ -57,7 +57,7 @@ def load_library():
     lib.mla_merge_v_up_proj.argtypes = [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
                                         _c_void_p, _c_void_p, _c_void_p, _c_void_p]
     lib.mla_dcp_local_seqlens.restype = _i32
-    lib.mla_dcp_local_seqlens.argtypes = [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32,
+    lib.mla_dcp_local_seqlens.argtypes = [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32,
                                           _c_void_p, _c_void_p, _c_void_p]
     _lib = lib
     return lib
@@ -93,8 +93,9 @@ def _need(t, dtype, name, dims=None):
         raise MlaError(f"{name}: expected {dims} dims, got shape {tuple(t.shape)}")
 
 
-def workspace_size(B, T, H, max_query_len, max_seq_len, cp_world, num_splits=0) -> int:
-    n = load_library().mla_decode_workspace_size(B, T, H, max_query_len, max_seq_len, cp_world, num_splits)
+def workspace_size(B, T, H, max_query_len, max_seq_len, cp_world, num_splits=0, cp_interleave=1) -> int:
+    n = load_library().mla_decode_workspace_size(B, T, H, max_query_len, max_seq_len, cp_world,
+                                                 cp_interleave, num_splits)
     if n == ctypes.c_size_t(-1).value:
         raise MlaError("mla_decode_workspace_size: invalid arguments")
     return int(n)
@@ -102,8 +103,9 @@ def workspace_size(B, T, H, max_query_len, max_seq_len, cp_world, num_splits=0) 
 
 def mla_decode_partial(q_nope, q_pe, kv_cache, block_table, seq_lens, query_start_loc,
                        cp_world, cp_rank, scale, out, lse, *, max_query_len, max_seq_len,
-                       workspace=None, num_splits=0, stream=None):
-    """One DCP rank's partial attention; writes ``out`` [T,H,512] bf16 and ``lse`` [T,H] fp32."""
+                       workspace=None, num_splits=0, stream=None, cp_interleave=1):
+    """One DCP rank's partial attention; writes ``out`` [T,H,512] bf16 and ``lse`` [T,H] fp32.
+    ``cp_interleave``: tokens per run of the shard layout (1 = token p on rank p mod W)."""
     lib = load_library()
     _need(q_nope, torch.bfloat16, "q_nope", 3)
     _need(q_pe, torch.bfloat16, "q_pe", 3)
@@ -142,7 +144,8 @@ def mla_decode_partial(q_nope, q_pe, kv_cache, block_table, seq_lens, query_star
         _ptr(kv_cache), kv_cache.stride(0), page,
         _ptr(block_table), block_table.stride(0),
         _ptr(seq_lens), _ptr(query_start_loc),
-        B, T, H, int(max_query_len), int(max_seq_len), int(cp_world), int(cp_rank), float(scale),
+        B, T, H, int(max_query_len), int(max_seq_len), int(cp_world), int(cp_rank), int(cp_interleave),
+        float(scale),
         int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "mla_decode_partial")
 
@@ -199,7 +202,7 @@ def mla_merge_v_up_proj(outs, lses, valid, W_UV, out, out_lse=None, stream=None)
 
 
 def mla_dcp_local_seqlens(seq_lens, query_start_loc, T, cp_world, cp_rank, row_seqlen=None,
-                          shard_len=None, stream=None):
+                          shard_len=None, stream=None, cp_interleave=1):
     """Per-row visible key counts [T] and per-request stored token counts [B] on rank cp_rank."""
     lib = load_library()
     _need(seq_lens, torch.int32, "seq_lens", 1)
@@ -214,5 +217,6 @@ def mla_dcp_local_seqlens(seq_lens, query_start_loc, T, cp_world, cp_rank, row_s
         if shard_len.shape[0] != B:
             raise MlaError("shard_len: expected [B]")
     st = lib.mla_dcp_local_seqlens(_ptr(seq_lens), _ptr(query_start_loc), B, int(T), int(cp_world),
-                                   int(cp_rank), _ptr(row_seqlen), _ptr(shard_len), _stream(stream))
+                                   int(cp_rank), int(cp_interleave), _ptr(row_seqlen), _ptr(shard_len),
+                                   _stream(stream))
     _check(st, "mla_dcp_local_seqlens")

@@ -57,7 +57,19 @@ struct Plan {
 // workgroup's LDS; more units than this run in token order.
 constexpr int64_t kH128MaxOrderUnits = 8192;
 
-Plan make_plan(int B, int T, int H, int max_seq_len, int W, int num_splits, bool split_ok) {
+// Of the positions 0..n-1, the tokens that runs of I dealt to W ranks in turn
+// put on rank r (the device's shard_count, on the host).
+int64_t host_shard_count(int64_t n, int64_t W, int64_t r, int64_t I) {
+  if (n <= 0) return 0;
+  const int64_t rounds = n / (W * I);
+  const int64_t m = n - rounds * W * I - r * I;
+  return rounds * I + (m < 0 ? 0 : m > I ? I : m);
+}
+
+// A shard layout the kernels can index: W ranks, runs of I tokens, W * I in int.
+bool layout_ok(int32_t W, int32_t I) { return W >= 1 && I >= 1 && (int64_t)W * I <= (int64_t(1) << 30); }
+
+Plan make_plan(int B, int T, int H, int max_seq_len, int W, int I, int num_splits, bool split_ok) {
   Plan p;
   const int ht = (H + 15) / 16;
   p.mtiles = ht >= 2 ? 2 : 1;
@@ -65,8 +77,9 @@ Plan make_plan(int B, int T, int H, int max_seq_len, int W, int num_splits, bool
   p.workers = 0;
   p.h128 = H == 128;
   if (p.h128) p.hblocks = 2;      // 64-head blocks of the 128-head kernel
-  // A row's visible local keys never exceed ceil(max_seq_len / W).
-  const int64_t lmax = max_seq_len > 0 ? ceil_div(max_seq_len, W) : 0;
+  // A row's visible local keys never exceed what rank 0 (the first run of every
+  // round) holds of max_seq_len tokens: ceil(max_seq_len / W) when I = 1.
+  const int64_t lmax = host_shard_count(max_seq_len, W, 0, I);
   const int64_t lr = round_up(lmax > 0 ? lmax : 1, kStep);
   int64_t chunk = lr;
   if (p.h128) {
@@ -153,12 +166,13 @@ const char* mla_status_string(mla_status status) {
 }
 
 size_t mla_decode_workspace_size(int32_t B, int32_t T, int32_t H, int32_t max_query_len,
-                                 int32_t max_seq_len, int32_t cp_world, int32_t num_splits) {
+                                 int32_t max_seq_len, int32_t cp_world, int32_t cp_interleave,
+                                 int32_t num_splits) {
   if (B < 0 || T < 0 || H < 1 || H > MLA_MAX_HEADS || max_query_len < 0 || max_seq_len < 0 ||
-      cp_world < 1 || num_splits < 0)
+      !layout_ok(cp_world, cp_interleave) || num_splits < 0)
     return (size_t)-1;
   if (B == 0 || T == 0) return 0;
-  const Plan p = make_plan(B, T, H, max_seq_len, cp_world, num_splits, true);
+  const Plan p = make_plan(B, T, H, max_seq_len, cp_world, cp_interleave, num_splits, true);
   return workspace_bytes_for(p, T, H);
 }
 
@@ -169,10 +183,10 @@ mla_status mla_decode_partial(
     const int32_t* block_table, int32_t bt_stride,
     const int32_t* seq_lens, const int32_t* query_start_loc,
     int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
-    int32_t cp_world, int32_t cp_rank, float scale, int32_t num_splits,
+    int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, float scale, int32_t num_splits,
     void* out, float* lse,
     void* workspace, size_t workspace_bytes, void* hip_stream) {
-  if (B < 0 || T < 0 || H < 1 || H > MLA_MAX_HEADS || page_size < 1 || cp_world < 1 ||
+  if (B < 0 || T < 0 || H < 1 || H > MLA_MAX_HEADS || page_size < 1 || !layout_ok(cp_world, cp_interleave) ||
       cp_rank < 0 || cp_rank >= cp_world || max_query_len < 0 || max_seq_len < 0 ||
       num_splits < 0 || !isfinite(scale) || !(scale > 0.f))
     return MLA_ERR_SHAPE;
@@ -193,7 +207,7 @@ mla_status mla_decode_partial(
   mla_status st = check_device();
   if (st != MLA_OK) return st;
 
-  const Plan plan = make_plan(B, T, H, max_seq_len, cp_world, num_splits, workspace != nullptr);
+  const Plan plan = make_plan(B, T, H, max_seq_len, cp_world, cp_interleave, num_splits, workspace != nullptr);
   const size_t need = workspace_bytes_for(plan, T, H);
   if (need > 0 && workspace_bytes < need) return MLA_ERR_WORKSPACE;
 
@@ -204,7 +218,7 @@ mla_status mla_decode_partial(
   p.page_shift = (page_size & (page_size - 1)) == 0 ? __builtin_ctz((unsigned)page_size) : -1;
   p.bt = block_table; p.bt_stride = bt_stride;
   p.seq_lens = seq_lens; p.qsl = query_start_loc;
-  p.B = B; p.T = T; p.H = H; p.W = cp_world; p.r = cp_rank;
+  p.B = B; p.T = T; p.H = H; p.W = cp_world; p.r = cp_rank; p.I = cp_interleave;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   p.chunk = plan.chunk; p.hblocks = plan.hblocks; p.max_splits = plan.max_splits;
   p.out = (uint16_t*)out; p.lse = lse;
@@ -257,15 +271,17 @@ mla_status mla_merge_v_up_proj(const void* outs, const float* lses, const int32_
 
 mla_status mla_dcp_local_seqlens(const int32_t* seq_lens, const int32_t* query_start_loc,
                                  int32_t B, int32_t T, int32_t cp_world, int32_t cp_rank,
-                                 int32_t* row_seqlen, int32_t* shard_len, void* hip_stream) {
-  if (B < 0 || T < 0 || cp_world < 1 || cp_rank < 0 || cp_rank >= cp_world) return MLA_ERR_SHAPE;
+                                 int32_t cp_interleave, int32_t* row_seqlen, int32_t* shard_len,
+                                 void* hip_stream) {
+  if (B < 0 || T < 0 || !layout_ok(cp_world, cp_interleave) || cp_rank < 0 || cp_rank >= cp_world)
+    return MLA_ERR_SHAPE;
   if (B == 0 && T > 0) return MLA_ERR_SHAPE;
   if (B == 0 && T == 0) return MLA_OK;
   if (!seq_lens || !query_start_loc) return MLA_ERR_NULL;
   mla_status st = check_device();
   if (st != MLA_OK) return st;
   hipError_t e = mla::launch_local_seqlens(seq_lens, query_start_loc, B, T, cp_world, cp_rank,
-                                           row_seqlen, shard_len, (hipStream_t)hip_stream);
+                                           cp_interleave, row_seqlen, shard_len, (hipStream_t)hip_stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

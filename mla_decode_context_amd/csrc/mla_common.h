@@ -52,9 +52,30 @@ struct RowInfo {
 
 __device__ __forceinline__ int ceil_div_pos(int n, int W) { return n > 0 ? (n + W - 1) / W : 0; }
 
+// Shard layout: runs of I consecutive tokens of a request are dealt to the W
+// ranks in turn, so global token p lives on rank (p div I) mod W -- I = 1 is the
+// interleaved layout (token p on rank p mod W), I = page size gives each rank
+// whole pages.  Of the positions 0..n-1 rank r holds
+//   (n div WI) * I + min(max(n mod WI - rI, 0), I),
+// and they are the first ones of its local order (ascending position).
+__device__ __forceinline__ int shard_count(int n, int W, int r, int I) {
+  if (n <= 0) return 0;
+  if (I == 1) return ceil_div_pos(n - r, W);
+  const int span = W * I;
+  const int rounds = n / span;
+  return rounds * I + min(max(n - rounds * span - r * I, 0), I);
+}
+
+// Global position of rank r's local token j (the inverse of the layout above).
+__device__ __forceinline__ int shard_position(int j, int W, int r, int I) {
+  if (I == 1) return j * W + r;
+  const int run = j / I;
+  return (run * W + r) * I + (j - run * I);
+}
+
 __device__ __forceinline__ RowInfo locate_row(const int32_t* __restrict__ qsl,
                                               const int32_t* __restrict__ seq_lens,
-                                              int B, int t, int W, int r) {
+                                              int B, int t, int W, int r, int I) {
   // last b with qsl[b] <= t; it has qsl[b+1] > t because t < qsl[B]
   int lo = 0, hi = B - 1;
   while (lo < hi) {
@@ -67,8 +88,8 @@ __device__ __forceinline__ RowInfo locate_row(const int32_t* __restrict__ qsl,
   const int p = S - q + (t - q0);
   RowInfo ri;
   ri.b = lo;
-  ri.L = ceil_div_pos(p + 1 - r, W);
-  ri.Lc = ceil_div_pos(S - r, W);
+  ri.L = shard_count(p + 1, W, r, I);
+  ri.Lc = shard_count(S, W, r, I);
   return ri;
 }
 

@@ -131,7 +131,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams a) {
   const int t = blockIdx.x / a.hblocks;
   const int hb = blockIdx.x - t * a.hblocks;
   const int split = blockIdx.y;
-  const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r);
+  const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r, a.I);
   const int L = ri.L;
   const int nsplit = num_splits_of(L, a.chunk, (int)gridDim.y);
   if (split >= nsplit) return;
@@ -397,11 +397,11 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams a) {
 }
 
 __global__ __launch_bounds__(256) void local_seqlens_kernel(const int32_t* seq_lens, const int32_t* qsl,
-                                                            int B, int T, int W, int r,
+                                                            int B, int T, int W, int r, int I,
                                                             int32_t* row_seqlen, int32_t* shard_len) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (row_seqlen && i < T) row_seqlen[i] = locate_row(qsl, seq_lens, B, i, W, r).L;
-  if (shard_len && i < B) shard_len[i] = ceil_div_pos(seq_lens[i] - r, W);
+  if (row_seqlen && i < T) row_seqlen[i] = locate_row(qsl, seq_lens, B, i, W, r, I).L;
+  if (shard_len && i < B) shard_len[i] = shard_count(seq_lens[i], W, r, I);
 }
 
 
@@ -735,17 +735,20 @@ constexpr int kMinUnitsPerWorker = 8;
 __device__ __forceinline__ int h16_stages(int L) { return (L + kWStage - 1) / kWStage; }
 
 // Units of request b; also returns its first token q0, rows Q and length S.
-__device__ __forceinline__ int request_units(const DecodeParams& a, int b, int& q0, int& Q, int& S) {
+__device__ __forceinline__ int request_units(const DecodeParams& a, int I, int b, int& q0, int& Q, int& S) {
   q0 = a.qsl[b];
   Q = a.qsl[b + 1] - q0;
   S = a.seq_lens[b];
   int u = 0;
-  for (int i = 0; i < Q; ++i) u += kRowUnits + h16_stages(ceil_div_pos(S - Q + i + 1 - a.r, a.W));
+  for (int i = 0; i < Q; ++i) u += kRowUnits + h16_stages(shard_count(S - Q + i + 1, a.W, a.r, I));
   return u;
 }
 
-template <bool kPage16, bool kBalanced>
+// kRuns: the shard layout has runs longer than one token (cp_interleave > 1);
+// without it the run length is the constant 1 and the layout arithmetic folds.
+template <bool kPage16, bool kBalanced, bool kRuns>
 __global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a) {
+  const int I = kRuns ? a.I : 1;
   // Four wave rings of two 18 KiB slots; reused for the four-wave merge.
   __shared__ __attribute__((aligned(16))) uint8_t lds_block[kWLdsBytes];
 
@@ -753,7 +756,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a
     // Grid (token, split): split s takes keys [s*chunk, (s+1)*chunk) of the row.
     const int t = blockIdx.x;
     const int split = blockIdx.y;
-    const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r);
+    const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r, I);
     const int nsplit = num_splits_of(ri.L, a.chunk, (int)gridDim.y);
     if (split >= nsplit) return;
     if (ri.L == 0) {
@@ -771,13 +774,13 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a
     // Every lane holds one request of the chunk [b0c, b0c + 64): its first
     // token, rows, length and units.  Chunk 0 is kept; the total runs over all.
     int lq0 = 0, lQ = 0, lS = 0;
-    const int u_first = lane < a.B ? request_units(a, lane, lq0, lQ, lS) : 0;
+    const int u_first = lane < a.B ? request_units(a, I, lane, lq0, lQ, lS) : 0;
     const int inc_first = wave_incl_scan(u_first);
     int total = __shfl(inc_first, 63, 64);
     for (int b0 = 64; b0 < a.B; b0 += 64) {
       const int bb = b0 + lane;
       int x, y, z;
-      total += __shfl(wave_incl_scan(bb < a.B ? request_units(a, bb, x, y, z) : 0), 63, 64);
+      total += __shfl(wave_incl_scan(bb < a.B ? request_units(a, I, bb, x, y, z) : 0), 63, 64);
     }
     int per = (total + G - 1) / G;
     if (per < kMinUnitsPerWorker) per = kMinUnitsPerWorker;
@@ -790,7 +793,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a
       const int bb = b0 + lane;
       int u = u_first, inc = inc_first;
       if (b0 > 0) {
-        u = bb < a.B ? request_units(a, bb, lq0, lQ, lS) : 0;
+        u = bb < a.B ? request_units(a, I, bb, lq0, lQ, lS) : 0;
         inc = wave_incl_scan(u);
       }
       const bool hit = bb < a.B && carry + inc - u <= x0 && x0 < carry + inc;
@@ -829,7 +832,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a
         i = 0;
         continue;
       }
-      const int L = ceil_div_pos(S - Q + i + 1 - a.r, a.W);
+      const int L = shard_count(S - Q + i + 1, a.W, a.r, I);
       const int n = h16_stages(L);
       const int t = q0 + i;
       if (pos + kRowUnits + n > x0) {
@@ -914,8 +917,11 @@ hipError_t launch_decode(const DecodeParams& p, int mtiles, int max_splits, int 
   const bool page16 = p.P % 16 == 0;
   if (mtiles == 1 && workers > 0) {
     const dim3 grid((unsigned)workers);
-    if (page16) hipLaunchKernelGGL((decode_kernel_h16<true, true>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((decode_kernel_h16<false, true>), grid, dim3(256), 0, stream, p);
+    const bool runs = p.I != 1;
+    if (page16 && !runs) hipLaunchKernelGGL((decode_kernel_h16<true, true, false>), grid, dim3(256), 0, stream, p);
+    else if (page16) hipLaunchKernelGGL((decode_kernel_h16<true, true, true>), grid, dim3(256), 0, stream, p);
+    else if (!runs) hipLaunchKernelGGL((decode_kernel_h16<false, true, false>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((decode_kernel_h16<false, true, true>), grid, dim3(256), 0, stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(split_combine_kernel, dim3((unsigned)p.T, 4), dim3(256), 0, stream, p);
@@ -923,8 +929,8 @@ hipError_t launch_decode(const DecodeParams& p, int mtiles, int max_splits, int 
   }
   const dim3 grid((unsigned)(p.T * p.hblocks), (unsigned)max_splits);
   if (mtiles == 1) {
-    if (page16) hipLaunchKernelGGL((decode_kernel_h16<true, false>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((decode_kernel_h16<false, false>), grid, dim3(256), 0, stream, p);
+    if (page16) hipLaunchKernelGGL((decode_kernel_h16<true, false, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((decode_kernel_h16<false, false, true>), grid, dim3(256), 0, stream, p);
   } else {
     if (page16) hipLaunchKernelGGL((decode_kernel<2, kStages, true>), grid, dim3(256), 0, stream, p);
     else hipLaunchKernelGGL((decode_kernel<2, kStages, false>), grid, dim3(256), 0, stream, p);
@@ -933,11 +939,11 @@ hipError_t launch_decode(const DecodeParams& p, int mtiles, int max_splits, int 
 }
 
 hipError_t launch_local_seqlens(const int32_t* seq_lens, const int32_t* qsl, int B, int T, int W,
-                                int r, int32_t* row_seqlen, int32_t* shard_len, hipStream_t stream) {
+                                int r, int I, int32_t* row_seqlen, int32_t* shard_len, hipStream_t stream) {
   const int n = T > B ? T : B;
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(local_seqlens_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, seq_lens, qsl,
-                     B, T, W, r, row_seqlen, shard_len);
+                     B, T, W, r, I, row_seqlen, shard_len);
   return hipGetLastError();
 }
 

@@ -80,7 +80,8 @@ __device__ __forceinline__ void wait_stage(bool more) {
 __device__ __forceinline__ int chunk_swizzle(int row) { return (row & 7) ^ ((row << 1) & 4); }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <bool kPage32>
+// kRuns: the shard layout has runs longer than one token (cp_interleave > 1).
+template <bool kPage32, bool kRuns>
 __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams a) {
   __shared__ __attribute__((aligned(16))) uint8_t ring[kXSlots * kXStageBytes];   // 144 KiB
   __shared__ __attribute__((aligned(16))) uint8_t p_lds[2 * kPBuf];              // P, [buf][head][key] bf16
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
   const int hb = item % hblocks;
   const int t = (item / hblocks) % a.T;
   const int split = item / (hblocks * a.T);
-  const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r);
+  const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r, kRuns ? a.I : 1);
   const int L = ri.L;
   const int nsplit = num_splits_of(L, a.chunk, a.max_splits);
   if (split >= nsplit) return;
@@ -472,7 +473,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
 // group hg): thread (head 16hg + tid / 16, dims 128qd + 8(tid % 16) .. +8).
 __global__ __launch_bounds__(256) void combine_fixed_kernel(const DecodeParams a) {
   const int t = blockIdx.x;
-  const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r);
+  const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r, a.I);
   const int np = num_splits_of(ri.L, a.chunk, a.max_splits);
   if (np <= 1) return;
   const int h = 16 * blockIdx.z + (threadIdx.x >> 4);
@@ -549,12 +550,12 @@ __device__ __forceinline__ UnitInfo unit_info(const DecodeParams& a, int u, cons
   const int Q = rq[b];
   const int S = rs[b];
   const int c = s * a.chunk;
-  // Row i sees ceil((S - Q + i + 1 - r) / W) local keys, more than c exactly when
-  // i >= cW - S + Q + r.  Split 0 also keeps the rows without keys (they write
-  // their empty result).
-  ui.first = s == 0 ? 0 : max(0, c * a.W - S + Q + a.r);
+  // Row i (global position S - Q + i) sees more than c local keys exactly when
+  // it sits past the position of local key c, i.e. i >= pos(c) - S + Q.  Split 0
+  // also keeps the rows without keys (they write their empty result).
+  ui.first = s == 0 ? 0 : max(0, shard_position(c, a.W, a.r, a.I) - S + Q);
   ui.rows = max(0, Q - ui.first);
-  const int cnt = min(ceil_div_pos(S - a.r, a.W) - c, a.chunk);
+  const int cnt = min(shard_count(S, a.W, a.r, a.I) - c, a.chunk);
   ui.stages = ui.rows > 0 && cnt > 0 ? (cnt + kXStep - 1) / kXStep : 0;
   return ui;
 }
@@ -661,8 +662,11 @@ hipError_t launch_decode_h128(const DecodeParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     grid = (unsigned)(((items + 31) / 32) * 32);
   }
-  if (p.P % 32 == 0) hipLaunchKernelGGL((decode_kernel_h128<true>), dim3(grid), dim3(512), 0, stream, p);
-  else hipLaunchKernelGGL((decode_kernel_h128<false>), dim3(grid), dim3(512), 0, stream, p);
+  const bool runs = p.I != 1;
+  if (p.P % 32 == 0 && !runs) hipLaunchKernelGGL((decode_kernel_h128<true, false>), dim3(grid), dim3(512), 0, stream, p);
+  else if (p.P % 32 == 0) hipLaunchKernelGGL((decode_kernel_h128<true, true>), dim3(grid), dim3(512), 0, stream, p);
+  else if (!runs) hipLaunchKernelGGL((decode_kernel_h128<false, false>), dim3(grid), dim3(512), 0, stream, p);
+  else hipLaunchKernelGGL((decode_kernel_h128<false, true>), dim3(grid), dim3(512), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.max_splits <= 1) return e;
   hipLaunchKernelGGL(combine_fixed_kernel, dim3((unsigned)p.T, 4, (unsigned)((p.H + 15) / 16)), dim3(256), 0,

@@ -30,6 +30,7 @@ class DeviceWorkload:
         self.device = torch.device(device)
         dev = self.device
         self.B, self.T, self.H, self.W = wl.B, wl.T, wl.H, wl.W
+        self.I = wl.I                  # shard run length of the layout
         self.scale = wl.scale
         self.max_query_len = wl.max_query_len
         self.max_seq_len = wl.max_seq_len
@@ -52,7 +53,8 @@ class DeviceWorkload:
 
     def alloc_workspace(self, num_splits: int):
         self.num_splits = num_splits
-        n = mla.workspace_size(self.B, self.T, self.H, self.max_query_len, self.max_seq_len, self.W, num_splits)
+        n = mla.workspace_size(self.B, self.T, self.H, self.max_query_len, self.max_seq_len, self.W, num_splits,
+                               cp_interleave=self.I)
         # zero-filled once: the split tickets must start at zero (calls reset them)
         self.workspace = torch.zeros(n, dtype=torch.uint8, device=self.device) if n else None
 
@@ -61,7 +63,8 @@ class DeviceWorkload:
         automatic split plan), joined by "+"."""
         if self.H == 128:
             page32 = "true" if self.wl.P % 32 == 0 else "false"
-            name = f"decode_kernel_h128<{page32}>"
+            runs = "true" if self.I != 1 else "false"
+            name = f"decode_kernel_h128<{page32}, {runs}>"
             if self.workspace is None:
                 return name
             # the workspace holds the dispatch order (one int32 per token and
@@ -72,8 +75,9 @@ class DeviceWorkload:
         page16 = "true" if self.wl.P % 16 == 0 else "false"
         if self.H <= 16:
             if self.num_splits == 0 and self.workspace is not None:
-                return f"decode_kernel_h16<{page16}, true>+split_combine_kernel"
-            return f"decode_kernel_h16<{page16}, false>"
+                runs = "true" if self.I != 1 else "false"
+                return f"decode_kernel_h16<{page16}, true, {runs}>+split_combine_kernel"
+            return f"decode_kernel_h16<{page16}, false, true>"
         return f"decode_kernel<2, 3, {page16}>"
 
     def partial(self, r: int, stream=None):
@@ -81,12 +85,12 @@ class DeviceWorkload:
             self.q_nope, self.q_pe, self.caches[r], self.tables[r], self.seq_lens, self.qsl,
             self.W, r, self.scale, self.outs[r], self.lses[r],
             max_query_len=self.max_query_len, max_seq_len=self.max_seq_len,
-            workspace=self.workspace, num_splits=self.num_splits, stream=stream)
+            workspace=self.workspace, num_splits=self.num_splits, stream=stream, cp_interleave=self.I)
 
     def valid_counts(self, stream=None):
         for r in range(self.W):
             mla.mla_dcp_local_seqlens(self.seq_lens, self.qsl, self.T, self.W, r,
-                                      row_seqlen=self.valid[r], stream=stream)
+                                      row_seqlen=self.valid[r], stream=stream, cp_interleave=self.I)
 
     def merge(self, stream=None):
         mla.mla_lse_merge(self.outs, self.lses, self.valid, self.out, self.out_lse, stream=stream)

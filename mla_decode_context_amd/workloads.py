@@ -17,8 +17,11 @@ Shapes follow the workload the pages describe:
   passed to the varlen kernel);
 * under DCP the global token ``p`` of a request is stored on shard ``p mod W`` at
   shard-local index ``p div W`` (PR #24453 review thread: with dcp=2 key A lives on
-  rank 0 and key B on rank 1).  Each shard owns a separate paged cache with its
-  own randomly permuted physical block ids.
+  rank 0 and key B on rank 1).  With a run length ``I`` > 1 (the same thread's
+  mention of contiguous whole pages per shard), runs of ``I`` consecutive tokens
+  go to the shards in turn: token ``p`` on shard ``(p div I) mod W``, each shard
+  keeping its tokens in ascending position.  Each shard owns a separate paged
+  cache with its own randomly permuted physical block ids.
 
 Random streams (NumPy PCG64), one per purpose so that any request's tokens can be
 regenerated on demand without replaying the others:
@@ -72,8 +75,12 @@ CONFIGS = {
              "W=4, context 512..16384, page 64, W_UV [128,512,128] ~ 0.02*N(0,1)",
         B=98, n_decode=96, decode_q=(1, 2, 4), chunk_q=512, seq_range=(512, 16384),
         H=128, W=4, P=64, seed=4, w_uv=True),
+    "mtp_dcp4_pages": dict(
+        desc="mtp_dcp4 with whole pages per shard: runs of 64 tokens (one page) "
+             "dealt to the 4 shards in turn",
+        B=128, seq_range=(1024, 4096), q_len=2, H=128, W=4, P=64, seed=2, I=64),
 }
-CONFIG_ORDER = ["tiny_dcp", "plain", "mtp_dcp4", "long_dcp8", "mixed_wuv"]
+CONFIG_ORDER = ["tiny_dcp", "plain", "mtp_dcp4", "long_dcp8", "mixed_wuv", "mtp_dcp4_pages"]
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -90,13 +97,20 @@ def _normal_bf16(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarra
     return f32_to_bf16_bits(x)
 
 
-def shard_token_count(S: int, W: int, r: int) -> int:
-    """How many of the tokens 0..S-1 land on shard r under p -> p mod W placement.
+def shard_token_rows(S: int, W: int, r: int, I: int = 1) -> np.ndarray:
+    """Positions among 0..S-1 that shard r stores, ascending (its local order),
+    when runs of I tokens go to the shards in turn (I = 1: p mod W == r).
 
-    This is storage bookkeeping for building the caches (how many rows shard r
+    This is storage bookkeeping for building the caches (which rows shard r
     holds), not the per-query-row mask.
     """
-    return len(range(r, S, W))
+    pos = np.arange(S, dtype=np.int64)
+    return pos[(pos // I) % W == r]
+
+
+def shard_token_count(S: int, W: int, r: int, I: int = 1) -> int:
+    """How many of the tokens 0..S-1 shard r stores."""
+    return int(shard_token_rows(S, W, r, I).shape[0])
 
 
 @dataclass
@@ -123,6 +137,7 @@ class Workload:
     q_pe: np.ndarray           # uint16 [T,H,64]
     shards: list = field(default_factory=list)
     w_uv: np.ndarray | None = None   # uint16 [H,512,128]
+    I: int = 1                       # shard run length: token p on shard (p div I) mod W
 
     @property
     def T(self) -> int:
@@ -168,15 +183,15 @@ def _draw_lengths(cfg: dict, seed: int):
 
 
 def build_shard(seed: int, r: int, W: int, P: int, seq_lens: np.ndarray,
-                kv_rows_of, spare_frac: float = 0.05) -> Shard:
-    """Lay the tokens p = r, r+W, r+2W, ... of every request into shard r's pages.
+                kv_rows_of, spare_frac: float = 0.05, I: int = 1) -> Shard:
+    """Lay shard r's tokens of every request (p = r, r+W, ... when I = 1) into its pages.
 
     ``kv_rows_of(b)`` returns the shard-local rows of request b ([n, 576] bf16 bits)
     in local order.  Logical blocks are numbered request by request; physical ids
     are a random permutation of the pool, which has ``spare_frac`` extra blocks.
     """
     B = len(seq_lens)
-    counts = np.array([shard_token_count(int(s), W, r) for s in seq_lens], dtype=np.int32)
+    counts = np.array([shard_token_count(int(s), W, r, I) for s in seq_lens], dtype=np.int32)
     nblk = np.array([math.ceil(int(c) / P) for c in counts], dtype=np.int64)
     n_logical = int(nblk.sum())
     pool = n_logical + max(1, int(math.ceil(spare_frac * n_logical)))
@@ -204,7 +219,7 @@ def build_shard(seed: int, r: int, W: int, P: int, seq_lens: np.ndarray,
 
 def make_workload(name: str, *, threads: int = 8, seed: int | None = None,
                   seq_lens=None, query_lens=None, H: int | None = None,
-                  W: int | None = None, P: int | None = None) -> Workload:
+                  W: int | None = None, P: int | None = None, I: int | None = None) -> Workload:
     """Build one of the named workloads (or a variant with some fields replaced)."""
     cfg = dict(CONFIGS[name])
     seed = cfg["seed"] if seed is None else seed
@@ -217,12 +232,13 @@ def make_workload(name: str, *, threads: int = 8, seed: int | None = None,
     H = cfg["H"] if H is None else H
     W = cfg["W"] if W is None else W
     P = cfg["P"] if P is None else P
+    I = cfg.get("I", 1) if I is None else I
     return make_custom(name, S, Q, H=H, W=W, P=P, seed=seed,
-                       w_uv=cfg.get("w_uv", False), threads=threads)
+                       w_uv=cfg.get("w_uv", False), threads=threads, I=I)
 
 
 def make_custom(name: str, seq_lens, query_lens, *, H: int, W: int, P: int, seed: int,
-                w_uv: bool = False, threads: int = 8, scale: float | None = None) -> Workload:
+                w_uv: bool = False, threads: int = 8, scale: float | None = None, I: int = 1) -> Workload:
     """Build a workload from explicit per-request lengths."""
     S = np.asarray(seq_lens, dtype=np.int32)
     Q = np.asarray(query_lens, dtype=np.int32)
@@ -234,7 +250,7 @@ def make_custom(name: str, seq_lens, query_lens, *, H: int, W: int, P: int, seed
     rq = np.random.default_rng([seed, 1])
     q_nope = _normal_bf16(rq, (T, H, D_LATENT))
     q_pe = _normal_bf16(rq, (T, H, D_ROPE))
-    wl = Workload(name=name, B=B, H=H, W=W, P=P, seed=seed,
+    wl = Workload(name=name, B=B, H=H, W=W, P=P, seed=seed, I=I,
                   scale=(1.0 / math.sqrt(D_V + D_ROPE)) if scale is None else scale,
                   seq_lens=S, query_lens=Q, query_start_loc=qsl, q_nope=q_nope, q_pe=q_pe)
     # Global KV is generated per request (in parallel: each request has its own
@@ -242,7 +258,8 @@ def make_custom(name: str, seq_lens, query_lens, *, H: int, W: int, P: int, seed
     with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
         kv = list(ex.map(lambda b: _request_kv(seed, b, int(S[b])), range(B)))
         wl.shards = list(ex.map(
-            lambda r: build_shard(seed, r, W, P, S, lambda b: kv[b][r::W]), range(W)))
+            lambda r: build_shard(seed, r, W, P, S, lambda b: kv[b][shard_token_rows(int(S[b]), W, r, I)], I=I),
+            range(W)))
     del kv
     if w_uv:
         wl.w_uv = _normal_bf16(np.random.default_rng([seed, 4]), (H, D_LATENT, D_V), std=0.02)

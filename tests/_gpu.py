@@ -70,7 +70,7 @@ def oracle_partials(wl, tokens, kv_bits=None):
         return kv[b]
 
     parts = [O.decode_partial(wl.seq_lens, wl.query_start_loc, wl.q_nope, wl.q_pe, gkv, wl.scale,
-                              wl.W, r, tokens=tokens) for r in range(wl.W)]
+                              wl.W, r, tokens=tokens, I=wl.I) for r in range(wl.W)]
     return np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts])
 
 
@@ -87,7 +87,7 @@ def oracle_unsharded(wl, tokens, kv_bits=None):
 
 
 def oracle_valid(wl, tokens):
-    return np.stack([O.row_counts(wl.seq_lens, wl.query_start_loc, wl.W, r)[tokens] for r in range(wl.W)])
+    return np.stack([O.row_counts(wl.seq_lens, wl.query_start_loc, wl.W, r, wl.I)[tokens] for r in range(wl.W)])
 
 
 def sample_tokens(wl, n_random=12, seed=123, extra_requests=()):

@@ -30,12 +30,12 @@ def test_status_strings():
 
 def _decode(**kw):
     a = dict(q_nope=P, qn_t=16 * 512, qn_h=512, q_pe=P, qp_t=16 * 64, qp_h=64, kv=P, kv_bs=16 * 576, page=16,
-             bt=P, bt_stride=4, seq=P, qsl=P, B=2, T=4, H=16, mq=2, ms=100, W=2, r=0, scale=0.07,
+             bt=P, bt_stride=4, seq=P, qsl=P, B=2, T=4, H=16, mq=2, ms=100, W=2, r=0, I=1, scale=0.07,
              splits=0, out=P, lse=P, ws=None, ws_bytes=0)
     a.update(kw)
     return lib.mla_decode_partial(a["q_nope"], a["qn_t"], a["qn_h"], a["q_pe"], a["qp_t"], a["qp_h"], a["kv"],
                                   a["kv_bs"], a["page"], a["bt"], a["bt_stride"], a["seq"], a["qsl"], a["B"],
-                                  a["T"], a["H"], a["mq"], a["ms"], a["W"], a["r"], a["scale"], a["splits"],
+                                  a["T"], a["H"], a["mq"], a["ms"], a["W"], a["r"], a["I"], a["scale"], a["splits"],
                                   a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
 
 
@@ -49,13 +49,19 @@ def _decode(**kw):
     (dict(qn_h=500), SHAPE), (dict(qn_t=512), SHAPE), (dict(qp_h=60), SHAPE), (dict(kv_bs=575 * 16), SHAPE),
     (dict(q_nope=ctypes.c_void_p(16 * 1024 + 2)), SHAPE), (dict(bt_stride=0), SHAPE),
     (dict(T=0), OK), (dict(B=0, T=0), OK), (dict(T=0, q_nope=None), OK),
+    (dict(I=0), SHAPE), (dict(I=-3), SHAPE), (dict(W=4, I=1 << 29), SHAPE),
+    (dict(W=2, I=1 << 28, T=0), OK),
 ])
 def test_decode_argument_checks(kw, code):
     assert _decode(**kw) == code
 
 
+def _ws(B, T, H, mq, ms, W, splits, I=1):
+    return lib.mla_decode_workspace_size(B, T, H, mq, ms, W, I, splits)
+
+
 def test_workspace_size_host_logic():
-    ws = lib.mla_decode_workspace_size
+    ws = _ws
     bad = ctypes.c_size_t(-1).value
     assert ws(2, 4, 0, 1, 100, 1, 0) == bad
     assert ws(2, 4, 16, 1, 100, 0, 0) == bad
@@ -72,6 +78,13 @@ def test_workspace_size_host_logic():
     assert ws(300, 600, 128, 2, 4000, 4, 1) == 4864 + 256     # 600 * 2 * 4 bytes, rounded up
     # more (split, request) units than the order kernel sorts: no order, no workspace
     assert ws(9000, 9000, 128, 1, 4000, 4, 1) == 0
+    # run layout: invalid run lengths are rejected; the split plan follows the
+    # longest shard (rank 0 holds a whole first run of every round): 100 tokens
+    # in runs of 64 over 2 ranks put 64 on rank 0, more than ceil(100 / 2) = 50
+    assert ws(2, 4, 16, 1, 100, 2, 0, I=0) == bad
+    assert ws(2, 4, 16, 1, 100, 4, 0, I=1 << 29) == bad          # W * I above 2^30
+    assert ws(1, 1, 16, 1, 8192, 4, 4, I=64) == ws(1, 1, 16, 1, 8192, 4, 4, I=1)
+    assert ws(1, 1, 128, 1, 100, 2, 0, I=64) >= ws(1, 1, 128, 1, 100, 2, 0, I=1)
 
 
 def test_merge_argument_checks():
@@ -84,6 +97,7 @@ def test_merge_argument_checks():
     assert v(P, P, None, 2, 4, 16, None, P, None, None) == NULL
     assert v(P, P, None, 2, -1, 16, P, P, None, None) == SHAPE
     s = lib.mla_dcp_local_seqlens
-    assert s(P, P, 2, 4, 2, 2, P, P, None) == SHAPE
-    assert s(None, P, 2, 4, 2, 1, P, P, None) == NULL
-    assert s(P, P, 0, 0, 2, 1, P, P, None) == OK
+    assert s(P, P, 2, 4, 2, 2, 1, P, P, None) == SHAPE
+    assert s(P, P, 2, 4, 2, 1, 0, P, P, None) == SHAPE
+    assert s(None, P, 2, 4, 2, 1, 1, P, P, None) == NULL
+    assert s(P, P, 0, 0, 2, 1, 16, P, P, None) == OK

@@ -23,7 +23,7 @@ pytestmark = [pytest.mark.gpu, needs_gpu]
 SHORT = {"long_dcp8": (0, 64, 128, 192), "mixed_wuv": (96, 97)}
 
 
-@pytest.mark.parametrize("name", ["plain", "mtp_dcp4", "long_dcp8", "mixed_wuv"])
+@pytest.mark.parametrize("name", ["plain", "mtp_dcp4", "long_dcp8", "mixed_wuv", "mtp_dcp4_pages"])
 def test_full_config_sampled_rows(name):
     log(f"[{name}] generating inputs")
     wl = WL.make_workload(name, threads=16)
@@ -42,7 +42,7 @@ def test_full_config_sampled_rows(name):
         log(f"[{name}] rank {r}: {st}")
     assert np.array_equal(dw.valid.cpu().numpy()[:, toks], oracle_valid(wl, toks))
     assert np.array_equal(dw.valid.cpu().numpy(), np.stack(
-        [O.row_counts(wl.seq_lens, wl.query_start_loc, wl.W, r) for r in range(wl.W)]))
+        [O.row_counts(wl.seq_lens, wl.query_start_loc, wl.W, r, wl.I) for r in range(wl.W)]))
     if wl.w_uv is None:
         if wl.W > 1:
             full_o, full_l = oracle_unsharded(wl, toks, kv)

@@ -37,11 +37,25 @@ def _length_cases():
     Q = np.minimum(rng.integers(0, 9, size=40), S)
     for W in (1, 3, 5, 8):
         cases.append((f"ragged_W{W}", S, Q, W))
+    return [c + (1,) for c in cases] + _run_length_cases()
+
+
+def _run_length_cases():
+    # runs of I tokens per shard: whole pages (I = 16, 64), odd runs, runs longer
+    # than most requests
+    rng = np.random.default_rng(8)
+    S = rng.integers(1, 300, size=50)
+    Q = np.minimum(rng.integers(0, 9, size=50), S)
+    cases = []
+    for W, I in ((2, 16), (3, 5), (4, 64), (8, 3), (1, 7), (5, 200)):
+        cases.append((f"runs_W{W}_I{I}", S, Q, W, I))
+    S, Q = WL._draw_lengths(WL.CONFIGS["mtp_dcp4_pages"], 2)
+    cases.append(("mtp_dcp4_pages", S, Q, 4, 64))
     return cases
 
 
-@pytest.mark.parametrize("name,S,Q,W", _length_cases(), ids=lambda x: x if isinstance(x, str) else "")
-def test_local_seqlens_bit_exact(name, S, Q, W):
+@pytest.mark.parametrize("name,S,Q,W,I", _length_cases(), ids=lambda x: x if isinstance(x, str) else "")
+def test_local_seqlens_bit_exact(name, S, Q, W, I):
     S = np.asarray(S, dtype=np.int32)
     Q = np.asarray(Q, dtype=np.int32)
     qsl = np.concatenate([[0], np.cumsum(Q)]).astype(np.int32)
@@ -50,10 +64,10 @@ def test_local_seqlens_bit_exact(name, S, Q, W):
     for r in range(W):
         rows = torch.full((T,), -7, dtype=torch.int32, device="cuda")
         shard = torch.full((len(S),), -7, dtype=torch.int32, device="cuda")
-        mla.mla_dcp_local_seqlens(seq_d, qsl_d, T, W, r, row_seqlen=rows, shard_len=shard)
+        mla.mla_dcp_local_seqlens(seq_d, qsl_d, T, W, r, row_seqlen=rows, shard_len=shard, cp_interleave=I)
         torch.cuda.synchronize()
-        assert np.array_equal(rows.cpu().numpy(), O.row_counts(S, qsl, W, r)), (name, r)
-        assert np.array_equal(shard.cpu().numpy(), O.shard_lengths(S, W, r)), (name, r)
+        assert np.array_equal(rows.cpu().numpy(), O.row_counts(S, qsl, W, r, I)), (name, r)
+        assert np.array_equal(shard.cpu().numpy(), O.shard_lengths(S, W, r, I)), (name, r)
 
 
 # ---------------------------------------------------------------------------
@@ -109,18 +123,19 @@ def test_tiny_dcp_bitwise_deterministic_and_block_permutation(tiny):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("H", [16, 128])
-@pytest.mark.parametrize("W", [1, 2, 3])
-def test_visible_set_probe_exact(W, H):
+@pytest.mark.parametrize("W,I", [(1, 1), (2, 1), (3, 1), (2, 16), (3, 5)])
+def test_visible_set_probe_exact(W, I, H):
     S = np.array([6, 37, 128, 255, 3], dtype=np.int32)
     Q = np.array([4, 4, 4, 4, 3], dtype=np.int32)
-    wl = WL.make_custom("probe", S, Q, H=H, W=W, P=16, seed=5)
+    wl = WL.make_custom("probe", S, Q, H=H, W=W, P=16, seed=5, I=I)
     wl.q_nope[:] = 0
     wl.q_pe[:] = 0
     one = 0x3F80   # bf16 1.0
     for r, sh in enumerate(wl.shards):
         for b in range(wl.B):
+            held = WL.shard_token_rows(int(S[b]), W, r, I)     # the generator's placement
             for j in range(int(sh.token_counts[b])):
-                p = j * W + r
+                p = int(held[j])
                 row = sh.cache[sh.block_table[b, j // wl.P], j % wl.P]
                 row[:] = 0
                 row[p % 512] = one
@@ -133,7 +148,7 @@ def test_visible_set_probe_exact(W, H):
         out = to_f64(dw.outs[r])
         lse = to_f64(dw.lses[r])
         for t, (b, i, p) in enumerate(rows):
-            keys = O.visible_keys(p, W, r)
+            keys = O.visible_keys(p, W, r, I)
             n = len(keys)
             if n == 0:
                 assert np.all(out[t] == 0) and np.all(lse[t] == -np.inf)
@@ -173,6 +188,39 @@ def test_edge_shapes(name, S, Q, H, W, P, num_splits):
     dw.outs.fill_(float("nan"))
     dw.step()
     torch.cuda.synchronize()
+    for r in range(W):
+        check_rows(dw.outs[r], dw.lses[r], ref_o[r], ref_l[r], f"{name} r={r}")
+    full_o, full_l = oracle_unsharded(wl, toks)
+    check_rows(dw.out, dw.out_lse, full_o, full_l, f"{name} merged")
+
+
+RUN_EDGE = [
+    # name, seq_lens, query_lens, H, W, P, I
+    ("runs_h16_w2_page", [300, 17, 64], [1, 3, 2], 16, 2, 16, 16),
+    ("runs_h16_w3_i5", [100, 9, 41], [4, 2, 1], 16, 3, 16, 5),
+    ("runs_h8_w2_p7", [50, 20], [2, 5], 8, 2, 7, 7),
+    ("runs_h48_w3_i4", [90, 31], [2, 1], 48, 3, 33, 4),
+    ("runs_h128_w4_page", [700, 64, 129, 5], [2, 2, 1, 3], 128, 4, 64, 64),
+    ("runs_h128_w2_i3_p48", [200, 33], [3, 2], 128, 2, 48, 3),
+    ("runs_h128_w3_long_run", [2100, 40], [4, 2], 128, 3, 64, 512),
+]
+
+
+@pytest.mark.parametrize("name,S,Q,H,W,P,I", RUN_EDGE, ids=[e[0] for e in RUN_EDGE])
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_run_layout_shapes(name, S, Q, H, W, P, I, num_splits):
+    """Shards holding runs of I tokens (whole pages when I = P): every rank's
+    partial against the oracle's run-layout partial, and the merge against
+    unsharded attention."""
+    log(f"run layout {name} num_splits={num_splits}")
+    wl = WL.make_custom(name, S, Q, H=H, W=W, P=P, seed=13, I=I)
+    toks = list(range(wl.T))
+    ref_o, ref_l = oracle_partials(wl, toks)
+    dw = DeviceWorkload(wl, num_splits=num_splits)
+    dw.outs.fill_(float("nan"))
+    dw.step()
+    torch.cuda.synchronize()
+    assert np.array_equal(dw.valid.cpu().numpy(), oracle_valid(wl, toks))
     for r in range(W):
         check_rows(dw.outs[r], dw.lses[r], ref_o[r], ref_l[r], f"{name} r={r}")
     full_o, full_l = oracle_unsharded(wl, toks)

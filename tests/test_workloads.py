@@ -55,3 +55,22 @@ def test_mixed_lengths():
     assert S.min() >= 512 and S.max() <= 16384
     S4, Q4 = WL._draw_lengths(WL.CONFIGS["long_dcp8"], 3)
     assert [S4[0], S4[64], S4[128], S4[192]] == [2, 3, 5, 7] and np.all(Q4 == 2)
+
+
+def test_run_layout_places_runs_of_tokens():
+    # Runs of I tokens dealt to the shards in turn: shard r's local token j is the
+    # global token at position ((j div I) * W + r) * I + j mod I (written out
+    # here on its own; the GPU parity tests hold the kernels to the same layout).
+    for I, P in ((5, 16), (16, 16), (1, 7)):
+        wl = WL.make_custom("runs", [6, 37, 128, 255], [4, 4, 4, 4], H=16, W=3, P=P, seed=0, I=I)
+        assert wl.I == I
+        for r, sh in enumerate(wl.shards):
+            for b in range(wl.B):
+                g = wl.global_kv(b)
+                S = int(wl.seq_lens[b])
+                n = int(sh.token_counts[b])
+                pos = [((j // I) * wl.W + r) * I + j % I for j in range(n)]
+                assert all(p < S for p in pos) and (n == 0 or ((n // I) * wl.W + r) * I + n % I >= S)
+                for j, p in enumerate(pos):
+                    assert np.array_equal(sh.cache[sh.block_table[b, j // P], j % P], g[p])
+        assert sum(int(sh.token_counts[b]) for sh in wl.shards for b in range(wl.B)) == int(wl.seq_lens.sum())
