@@ -240,3 +240,46 @@ def project_then_merge(outs, lses, valid, w_uv):
     outs = np.asarray(outs, dtype=np.float64)
     proj = np.stack([v_up_proj(outs[w], w_uv) for w in range(outs.shape[0])])
     return lse_merge(proj, lses, valid)
+
+
+# ---------------------------------------------------------------------------
+# The exchange layout of the projected merge (one GPU's share of it)
+# ---------------------------------------------------------------------------
+
+def a2a_pack(o_r: np.ndarray, lse_r: np.ndarray, valid_r, w_uv: np.ndarray, W: int):
+    """Rank r's send buffers for the all-to-all of the projected merge.
+
+    PR #48196: each rank projects its partial through W_UV before the exchange
+    (the payload per head shrinks from 512 to 128 values), and empty rows are
+    handled in the pack from the per-row valid counts.  Reading (the pages name
+    no layout): destination q owns the contiguous head slice q*Hs .. q*Hs+Hs-1,
+    Hs = H / W, and receives y[t, h] = o_r[t, h] @ W_UV[h] with its LSE for those
+    heads; a row whose valid count is 0 (or, without counts, whose LSE is -inf)
+    is sent as y = 0, LSE = -inf, and its partial is never read.
+
+    o_r [T,H,512], lse_r [T,H], valid_r [T] or None, w_uv [H,512,128].
+    Returns send_y [W,T,Hs,128] and send_lse [W,T,Hs] (float64).
+    """
+    o_r = np.asarray(o_r, dtype=np.float64)
+    lse_r = np.asarray(lse_r, dtype=np.float64)
+    T, H = lse_r.shape
+    assert H % W == 0
+    Hs = H // W
+    send_y = np.zeros((W, T, Hs, w_uv.shape[2]))
+    send_lse = np.full((W, T, Hs), -np.inf)
+    for t in range(T):
+        for h in range(H):
+            used = valid_r[t] > 0 if valid_r is not None else np.isfinite(lse_r[t, h])
+            if not used:
+                continue
+            q, hh = divmod(h, Hs)
+            send_y[q, t, hh] = o_r[t, h] @ w_uv[h]
+            send_lse[q, t, hh] = lse_r[t, h]
+    return send_y, send_lse
+
+
+def a2a_combine(recv_y: np.ndarray, recv_lse: np.ndarray):
+    """Receiver side: merge the W ranks' slices [W,T,Hs,128] / [W,T,Hs] of one
+    destination; an empty row arrives as LSE -inf and takes no part (the same
+    LSE-weighted merge as lse_merge, over the projected rows)."""
+    return lse_merge(recv_y, recv_lse, None)

@@ -331,6 +331,43 @@ def check_runs_merge_equals_unsharded(seed=5) -> bool:
     return True
 
 
+def check_a2a_pack_combine(seed=6) -> bool:
+    """Projected exchange: every rank packs, the all-to-all hands destination q
+    the slice q of every rank, and q's combine == the head slice q of
+    project-then-merge (itself pinned to merge-then-project); rows with valid
+    count 0 hold NaN and never reach the result."""
+    rng = np.random.default_rng(seed)
+    for W, T, H in ((4, 5, 8), (2, 3, 4), (8, 2, 16)):
+        outs = rng.standard_normal((W, T, H, 512))
+        lses = rng.standard_normal((W, T, H)) * 3
+        valid = rng.integers(0, 3, size=(W, T))
+        valid[:, 0] = 0                      # a row no rank takes part in
+        valid[0, 1] = 5
+        for w in range(W):
+            for t in range(T):
+                if valid[w, t] == 0:
+                    outs[w, t] = np.nan
+                    lses[w, t] = np.nan
+        wuv = rng.standard_normal((H, 512, 128)) * 0.02
+        Hs = H // W
+        sends = [O.a2a_pack(outs[r], lses[r], valid[r], wuv, W) for r in range(W)]
+        ref_y, ref_l = O.project_then_merge(np.nan_to_num(outs), np.nan_to_num(lses), valid, wuv)
+        for q in range(W):
+            recv_y = np.stack([sends[r][0][q] for r in range(W)])
+            recv_l = np.stack([sends[r][1][q] for r in range(W)])
+            y, l = O.a2a_combine(recv_y, recv_l)
+            if not (np.allclose(y, ref_y[:, q * Hs:(q + 1) * Hs], atol=1e-12)
+                    and np.array_equal(np.isinf(l), np.isinf(ref_l[:, q * Hs:(q + 1) * Hs]))
+                    and np.allclose(l[np.isfinite(l)], ref_l[:, q * Hs:(q + 1) * Hs][np.isfinite(l)], atol=1e-12)):
+                return False
+        # one rank, one slice: the pack is the plain projection of the valid rows
+        y0, l0 = O.a2a_pack(np.nan_to_num(outs[0]), np.nan_to_num(lses[0]), None, wuv, 1)
+        if not np.allclose(y0[0], np.einsum("thk,hkn->thn", np.nan_to_num(outs[0]), wuv), atol=1e-12):
+            return False
+    return True
+
+
 ALL_CHECKS = [check_worked_masks, check_ab_example, check_counts_bruteforce, check_against_sdpa,
               check_closed_forms, check_merge_equals_unsharded, check_merge_identities,
-              check_wuv_commutes, check_runs_bruteforce, check_runs_merge_equals_unsharded]
+              check_wuv_commutes, check_runs_bruteforce, check_runs_merge_equals_unsharded,
+              check_a2a_pack_combine]

@@ -35,6 +35,19 @@ def _local_index_interleaved(k, W, I=1):     # local index as if the layout were
     return k // W
 
 
+_real_pack = O.a2a_pack
+
+
+def _pack_interleaved_heads(o_r, lse_r, valid_r, w_uv, W):   # destination q gets heads q, q+W, ...
+    y, l = _real_pack(o_r, lse_r, valid_r, w_uv, W)
+    T, H = np.asarray(lse_r).shape
+    Hs = H // W
+    perm = [h for q in range(W) for h in range(q, H, W)]     # head order the mutant sends
+    flat_y = y.transpose(1, 0, 2, 3).reshape(T, H, -1)[:, np.argsort(perm)]
+    flat_l = l.transpose(1, 0, 2).reshape(T, H)[:, np.argsort(perm)]
+    return (flat_y.reshape(T, W, Hs, -1).transpose(1, 0, 2, 3), flat_l.reshape(T, W, Hs).transpose(1, 0, 2))
+
+
 def _rows_top_left(seq_lens, qsl):          # query rows at the first Q positions
     rows = []
     for b in range(len(seq_lens)):
@@ -93,6 +106,7 @@ MUTANTS = [
     ("visible_count", _count_runs_unscaled_rank),
     ("holder", _holder_offset_in_run),
     ("local_index", _local_index_interleaved),
+    ("a2a_pack", _pack_interleaved_heads),
     ("attend", _attend_no_pe),
     ("attend", _attend_double_scale),
     ("attend", _attend_log2),
