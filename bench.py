@@ -12,7 +12,10 @@ ones run every rank's partial, the valid counts and the merge (or the merge
 fused with W_UV) per step.  Their merge figures time the merge where a step
 runs it, right after the shard decodes; ``merge_*_back_to_back`` repeats the
 merge alone, which for partials that fit in the 256 MB last-level cache reads
-them from there.
+them from there.  The W_UV workload also times the projected exchange's two
+kernels (``a2a_pack_*``: every rank projects and packs its partial by
+destination head slice; ``a2a_combine_*``: every destination merges the slices
+it receives).
 
 Printed: one JSON line.  ``value`` is KV-cache GB/s of the whole step (bytes of
 cache rows the method must read once, divided by the step time) with inputs
@@ -203,7 +206,10 @@ def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True
             mevs.append(evs[wl.W])
         torch.cuda.synchronize()
         mg_step_ms = float(np.median([a.elapsed_time(b) for a, b in mevs]))
+    xchg = exchange_times(dw, wl, steps, torch) if merging and proj and wl.H % wl.W == 0 else None
     res = dict(workload=name, T=wl.T, B=wl.B, H=wl.H, W=wl.W, ms_per_step=ms_step)
+    if xchg is not None:
+        res.update(xchg)
     kv_total = sum(p["kv"] for p in per_shard)
     res["kv_GBps"] = kv_total / (ms_step * 1e-3) / 1e9
     res["query_tokens_per_s"] = wl.T / (ms_step * 1e-3)
@@ -251,6 +257,46 @@ def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True
     del dw
     torch.cuda.empty_cache()
     return res, wl
+
+
+def exchange_times(dw, wl, steps, torch):
+    """The projected exchange of the merge, the part one GPU holds: every rank's
+    pack (projection by W_UV, by destination head slice), then every
+    destination's combine of the slices it would receive, addressed in place in
+    the ranks' send buffers (the transport between GPUs is not part of it).
+    Timed where a step runs them, right after the shard decodes (median over
+    `steps`, events around each phase)."""
+    from mla_decode_context_amd import binding as mla
+    W, T, H = wl.W, wl.T, wl.H
+    Hs = H // W
+    send_y = torch.empty((W, W, T, Hs, 128), dtype=torch.bfloat16, device="cuda")
+    send_l = torch.empty((W, W, T, Hs), dtype=torch.float32, device="cuda")
+    out = torch.empty((W, T, Hs, 128), dtype=torch.bfloat16, device="cuda")
+    out_l = torch.empty((W, T, Hs), dtype=torch.float32, device="cuda")
+    marks = []
+    for _ in range(steps + 1):
+        for r in range(W):
+            dw.partial(r)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record()
+        for r in range(W):
+            mla.mla_dcp_a2a_pack(dw.outs[r], dw.lses[r], dw.valid[r], dw.w_uv, send_y[r], send_l[r], W)
+        ev[1].record()
+        for q in range(W):
+            mla.mla_dcp_a2a_combine(send_y[:, q], send_l[:, q], out[q], out_l[q])
+        ev[2].record()
+        marks.append(ev)
+    torch.cuda.synchronize()
+    marks = marks[1:]
+    pack_ms = float(np.median([e[0].elapsed_time(e[1]) for e in marks])) / W
+    comb_ms = float(np.median([e[1].elapsed_time(e[2]) for e in marks])) / W
+    valid = dw.valid.cpu().numpy()
+    rows_in = float((valid > 0).sum()) / W                  # participating rows per rank
+    pack_bytes = rows_in * H * (1024 + 4) + T * H * (256 + 4) + H * 512 * 128 * 2
+    comb_bytes = W * T * Hs * (256 + 4) + T * Hs * (256 + 4)
+    return {"a2a_pack_ms_per_rank": pack_ms, "a2a_pack_GBps": pack_bytes / (pack_ms * 1e-3) / 1e9,
+            "a2a_combine_ms_per_rank": comb_ms, "a2a_combine_GBps": comb_bytes / (comb_ms * 1e-3) / 1e9,
+            "a2a_payload_bytes_per_peer": T * Hs * (256 + 4)}
 
 
 def cold_kv(dw, wl, per_shard, torch, reps=7):

@@ -179,6 +179,48 @@ mla_status mla_merge_v_up_proj(const void* outs, const float* lses, const int32_
                                void* out, float* out_lse, void* hip_stream);
 
 /*
+ * mla_dcp_a2a_pack -- one rank's side of the projected exchange before the
+ * merge (PR #48196: each rank projects its partial through W_UV before the
+ * all-to-all, and empty rows are handled in the pack from the valid counts).
+ * Destination q owns the contiguous heads q*Hs .. q*Hs+Hs-1, Hs = H / cp_world.
+ *
+ *   out_r   bf16 [T,H,512] contiguous: this rank's partial (mla_decode_partial)
+ *   lse_r   fp32 [T,H]
+ *   valid_r int32 [T] this rank's per-row counts, or NULL (then a row takes part
+ *           iff its lse is > -inf).  A row that takes no part is sent as y = 0,
+ *           lse = -inf and its partial is not read.
+ *   W_UV    bf16 [H,512,128] contiguous
+ *   send_y  bf16 [cp_world,T,Hs,128]: send_y[q,t,j] = out_r[t,qHs+j] @ W_UV[qHs+j]
+ *           (fp32 accumulation, rounded to bf16)
+ *   send_lse fp32 [cp_world,T,Hs]
+ * Requires H % cp_world == 0.  Returns MLA_OK, MLA_ERR_NULL, MLA_ERR_SHAPE,
+ * MLA_ERR_UNSUPPORTED or MLA_ERR_HIP; T == 0 is a no-op.
+ */
+mla_status mla_dcp_a2a_pack(const void* out_r, const float* lse_r, const int32_t* valid_r,
+                            int32_t T, int32_t H, int32_t cp_world, const void* W_UV,
+                            void* send_y, float* send_lse, void* hip_stream);
+
+/*
+ * mla_dcp_a2a_combine -- the receiving rank's side: the LSE-weighted merge of
+ * the cp_world projected slices it received (one from every rank, its own
+ * included), rows of 128 values.
+ *
+ *   recv_y   bf16: source s's slice [T,Hs,128] (contiguous) at
+ *            recv_y + s*recv_y_stride elements (stride >= T*Hs*128, a multiple of 8)
+ *   recv_lse fp32: source s's [T,Hs] at recv_lse + s*recv_lse_stride (>= T*Hs)
+ *   out      bf16 [T,Hs,128]:  out = sum_s exp(lse_s - LSE) * y_s over the
+ *            sources whose lse is > -inf
+ *   out_lse  fp32 [T,Hs] or NULL:  LSE = ln sum_s exp(lse_s)
+ * A row no source takes part in gets out = 0 and LSE = -inf.  The strides let
+ * the slices sit wherever the transport put them (for example every rank's
+ * send buffer in one allocation).  Returns MLA_OK, MLA_ERR_NULL, MLA_ERR_SHAPE,
+ * MLA_ERR_UNSUPPORTED or MLA_ERR_HIP; T == 0 is a no-op.
+ */
+mla_status mla_dcp_a2a_combine(const void* recv_y, int64_t recv_y_stride, const float* recv_lse,
+                               int64_t recv_lse_stride, int32_t cp_world, int32_t T, int32_t Hs,
+                               void* out, float* out_lse, void* hip_stream);
+
+/*
  * mla_dcp_local_seqlens -- the per-row, per-rank seqlen_k of the DCP mask
  * (PR #24453 review thread; shard layout with runs of cp_interleave tokens as
  * for mla_decode_partial), computed on the device by the same device function

@@ -56,6 +56,12 @@ def load_library():
     lib.mla_merge_v_up_proj.restype = _i32
     lib.mla_merge_v_up_proj.argtypes = [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
                                         _c_void_p, _c_void_p, _c_void_p, _c_void_p]
+    lib.mla_dcp_a2a_pack.restype = _i32
+    lib.mla_dcp_a2a_pack.argtypes = [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _c_void_p,
+                                     _c_void_p, _c_void_p, _c_void_p]
+    lib.mla_dcp_a2a_combine.restype = _i32
+    lib.mla_dcp_a2a_combine.argtypes = [_c_void_p, _i64, _c_void_p, _i64, _i32, _i32, _i32,
+                                        _c_void_p, _c_void_p, _c_void_p]
     lib.mla_dcp_local_seqlens.restype = _i32
     lib.mla_dcp_local_seqlens.argtypes = [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32,
                                           _c_void_p, _c_void_p, _c_void_p]
@@ -199,6 +205,53 @@ def mla_merge_v_up_proj(outs, lses, valid, W_UV, out, out_lse=None, stream=None)
     st = lib.mla_merge_v_up_proj(_ptr(outs), _ptr(lses), _ptr(valid), W, T, H, _ptr(W_UV), _ptr(out),
                                  _ptr(out_lse), _stream(stream))
     _check(st, "mla_merge_v_up_proj")
+
+
+def mla_dcp_a2a_pack(out_r, lse_r, valid_r, W_UV, send_y, send_lse, cp_world, stream=None):
+    """Rank r's projected send buffers: send_y [W,T,H/W,128] bf16, send_lse [W,T,H/W] fp32."""
+    lib = load_library()
+    _need(out_r, torch.bfloat16, "out_r", 3)
+    _need(lse_r, torch.float32, "lse_r", 2)
+    _need(W_UV, torch.bfloat16, "W_UV", 3)
+    _need(send_y, torch.bfloat16, "send_y", 4)
+    _need(send_lse, torch.float32, "send_lse", 3)
+    T, H, dn = out_r.shape
+    W = int(cp_world)
+    if dn != D_LATENT or W < 1 or H % W or tuple(lse_r.shape) != (T, H) or tuple(W_UV.shape) != (H, D_LATENT, 128):
+        raise MlaError("mla_dcp_a2a_pack: expected out_r [T,H,512], lse_r [T,H], W_UV [H,512,128], H % W == 0")
+    if tuple(send_y.shape) != (W, T, H // W, 128) or tuple(send_lse.shape) != (W, T, H // W):
+        raise MlaError("mla_dcp_a2a_pack: send_y [W,T,H/W,128] / send_lse [W,T,H/W] expected")
+    for t, n in ((out_r, "out_r"), (lse_r, "lse_r"), (W_UV, "W_UV"), (send_y, "send_y"), (send_lse, "send_lse")):
+        if T and not t.is_contiguous():
+            raise MlaError(f"{n}: must be contiguous")
+    if valid_r is not None:
+        _need(valid_r, torch.int32, "valid_r", 1)
+        if valid_r.shape[0] != T or not valid_r.is_contiguous():
+            raise MlaError("valid_r: expected contiguous [T]")
+    st = lib.mla_dcp_a2a_pack(_ptr(out_r), _ptr(lse_r), _ptr(valid_r), T, H, W, _ptr(W_UV), _ptr(send_y),
+                              _ptr(send_lse), _stream(stream))
+    _check(st, "mla_dcp_a2a_pack")
+
+
+def mla_dcp_a2a_combine(recv_y, recv_lse, out, out_lse=None, stream=None):
+    """Merge the W received slices recv_y [W,T,Hs,128] / recv_lse [W,T,Hs] (any stride
+    along W, each slice contiguous) into out [T,Hs,128] and out_lse [T,Hs]."""
+    lib = load_library()
+    _need(recv_y, torch.bfloat16, "recv_y", 4)
+    _need(recv_lse, torch.float32, "recv_lse", 3)
+    _need(out, torch.bfloat16, "out", 3)
+    W, T, Hs, dv = recv_y.shape
+    if dv != 128 or tuple(recv_lse.shape) != (W, T, Hs) or tuple(out.shape) != (T, Hs, 128):
+        raise MlaError("mla_dcp_a2a_combine: recv_y [W,T,Hs,128], recv_lse [W,T,Hs], out [T,Hs,128] expected")
+    if T and Hs and not (recv_y[0].is_contiguous() and recv_lse[0].is_contiguous() and out.is_contiguous()):
+        raise MlaError("mla_dcp_a2a_combine: every slice and out must be contiguous")
+    if out_lse is not None:
+        _need(out_lse, torch.float32, "out_lse", 2)
+        if tuple(out_lse.shape) != (T, Hs) or not out_lse.is_contiguous():
+            raise MlaError("out_lse: expected contiguous [T,Hs]")
+    st = lib.mla_dcp_a2a_combine(_ptr(recv_y), recv_y.stride(0), _ptr(recv_lse), recv_lse.stride(0), W, T, Hs,
+                                 _ptr(out), _ptr(out_lse), _stream(stream))
+    _check(st, "mla_dcp_a2a_combine")
 
 
 def mla_dcp_local_seqlens(seq_lens, query_start_loc, T, cp_world, cp_rank, row_seqlen=None,

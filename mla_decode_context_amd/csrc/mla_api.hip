@@ -251,7 +251,7 @@ static mla_status merge_common(const void* outs, const float* lses, const int32_
   mla::MergeParams p;
   p.outs = (const uint16_t*)outs; p.lses = lses; p.valid = valid;
   p.W = W; p.T = T; p.H = H;
-  p.wuv = (const uint16_t*)W_UV; p.out = (uint16_t*)out; p.out_lse = out_lse;
+  p.wuv = (const uint16_t*)W_UV; p.out = (uint16_t*)out; p.out_lse = out_lse; p.hs = H;
   hipError_t e = proj ? mla::launch_merge_v_up(p, (hipStream_t)hip_stream)
                       : mla::launch_lse_merge(p, (hipStream_t)hip_stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
@@ -267,6 +267,43 @@ mla_status mla_merge_v_up_proj(const void* outs, const float* lses, const int32_
                                int32_t W, int32_t T, int32_t H, const void* W_UV,
                                void* out, float* out_lse, void* hip_stream) {
   return merge_common(outs, lses, valid, W, T, H, W_UV, true, out, out_lse, hip_stream);
+}
+
+mla_status mla_dcp_a2a_pack(const void* out_r, const float* lse_r, const int32_t* valid_r,
+                            int32_t T, int32_t H, int32_t cp_world, const void* W_UV,
+                            void* send_y, float* send_lse, void* hip_stream) {
+  if (T < 0 || H < 1 || H > MLA_MAX_HEADS || cp_world < 1 || H % cp_world != 0) return MLA_ERR_SHAPE;
+  if (T == 0) return MLA_OK;
+  if (!out_r || !lse_r || !W_UV || !send_y || !send_lse) return MLA_ERR_NULL;
+  if (!aligned(out_r, 16) || !aligned(send_y, 16) || !aligned(W_UV, 16)) return MLA_ERR_SHAPE;
+  mla_status st = check_device();
+  if (st != MLA_OK) return st;
+  // The fused merge + projection over one partial (its merge is the identity),
+  // writing head h into destination slice h / (H / cp_world).
+  mla::MergeParams p;
+  p.outs = (const uint16_t*)out_r; p.lses = lse_r; p.valid = valid_r;
+  p.W = 1; p.T = T; p.H = H;
+  p.wuv = (const uint16_t*)W_UV; p.out = (uint16_t*)send_y; p.out_lse = send_lse; p.hs = H / cp_world;
+  return mla::launch_merge_v_up(p, (hipStream_t)hip_stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_dcp_a2a_combine(const void* recv_y, int64_t recv_y_stride, const float* recv_lse,
+                               int64_t recv_lse_stride, int32_t cp_world, int32_t T, int32_t Hs,
+                               void* out, float* out_lse, void* hip_stream) {
+  if (cp_world < 1 || T < 0 || Hs < 1 || Hs > MLA_MAX_HEADS) return MLA_ERR_SHAPE;
+  const int64_t rows = (int64_t)T * Hs;
+  if (rows == 0) return MLA_OK;
+  if (!recv_y || !recv_lse || !out) return MLA_ERR_NULL;
+  if (cp_world > 1 && (recv_y_stride < rows * MLA_D_V || recv_lse_stride < rows)) return MLA_ERR_SHAPE;
+  if (recv_y_stride % 8 != 0 || !aligned(recv_y, 16) || !aligned(out, 16)) return MLA_ERR_SHAPE;
+  mla_status st = check_device();
+  if (st != MLA_OK) return st;
+  mla::SliceParams p;
+  p.y = (const uint16_t*)recv_y; p.y_stride = recv_y_stride;
+  p.lse = recv_lse; p.lse_stride = recv_lse_stride;
+  p.W = cp_world; p.rows = (int32_t)rows;
+  p.out = (uint16_t*)out; p.out_lse = out_lse;
+  return mla::launch_slice_combine(p, (hipStream_t)hip_stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 mla_status mla_dcp_local_seqlens(const int32_t* seq_lens, const int32_t* query_start_loc,

@@ -38,6 +38,18 @@ struct MergeParams {
   const uint16_t* wuv;     // bf16 [H,512,128] (merge + projection only)
   uint16_t* out;           // bf16 [T,H,512] or [T,H,128]
   float* out_lse;          // fp32 [T,H] or null
+  int32_t hs;              // merge + projection: heads per output slice; head h goes to
+                           // slice h / hs, laid out [H/hs][T][hs][128] (hs = H: [T][H][128])
+};
+
+// Combine of the projected slices one rank receives in the exchange: source s's
+// rows [rows][128] at y + s*y_stride, their LSEs at lse + s*lse_stride.
+struct SliceParams {
+  const uint16_t* y;       int64_t y_stride;       // elements between sources
+  const float* lse;        int64_t lse_stride;
+  int32_t W, rows;         // sources; rows = T * heads of the slice
+  uint16_t* out;           // bf16 [rows][128]
+  float* out_lse;          // fp32 [rows] or null
 };
 
 // Heads handled by one decode workgroup: 16 * mtiles, mtiles in {1,2}.  With
@@ -55,5 +67,6 @@ hipError_t launch_local_seqlens(const int32_t* seq_lens, const int32_t* qsl, int
                                 int r, int I, int32_t* row_seqlen, int32_t* shard_len, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_merge_v_up(const MergeParams& p, hipStream_t stream);
+hipError_t launch_slice_combine(const SliceParams& p, hipStream_t stream);
 
 }  // namespace mla

@@ -270,6 +270,8 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
   auto process = [&](int i, const Pend& cur) {
     const int tb = item_tb(i);
     const int t = tb + tt;
+    // Output row of (token tb, head h): slice h / hs holds [T][hs] rows.
+    const size_t out_row0 = ((size_t)(h / a.hs) * a.T + tb) * a.hs + h % a.hs;
     if (i % ngroups == 0) {
       m = -INFINITY;
       ssum = 0.f;
@@ -310,10 +312,10 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
     if (a.out_lse) {
       // (uniform branch: a kernel argument)
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(a.out_lse + (size_t)tb * a.H + h), (short)0, kProjBlk * a.H * 4, kBufFlags);
+          (void*)(a.out_lse + out_row0), (short)0, kProjBlk * a.hs * 4, kBufFlags);
       const float lse_v = ssum > 0.f ? m + fast_log2(ssum) * kLn2 : -INFINITY;
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse_v), rs,
-                                            (threadIdx.x & 31) == 0 && t < t_end ? (uint32_t)(tt * a.H * 4) : kOffNone, 0, 0);
+                                            (threadIdx.x & 31) == 0 && t < t_end ? (uint32_t)(tt * a.hs * 4) : kOffNone, 0, 0);
     }
     // W_UV staged (first block: every load issued so far has landed) and the
     // block's rows written; later items' partial loads may still be in flight
@@ -343,12 +345,12 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
     }
     // D: lane (column n = n0 + lr, group g) holds tokens 4g .. 4g+3 of the block.
     const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.out + ((size_t)tb * a.H + h) * kVHead), (short)0, kProjBlk * a.H * kVHead * 2, kBufFlags);
+        (void*)(a.out + out_row0 * kVHead), (short)0, kProjBlk * a.hs * kVHead * 2, kBufFlags);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tk = 4 * g + r;
       __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)y[r]), ry,
-                                            tb + tk < t_end ? (uint32_t)((tk * a.H * kVHead + n0 + lr) * 2) : kOffNone, 0, 0);
+                                            tb + tk < t_end ? (uint32_t)((tk * a.hs * kVHead + n0 + lr) * 2) : kOffNone, 0, 0);
     }
     // o_lds is rewritten by the next block.
     asm volatile("s_barrier" ::: "memory");
@@ -407,6 +409,55 @@ hipError_t launch_merge_v_up(const MergeParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)p.H, (unsigned)groups);
   if (p.valid) hipLaunchKernelGGL(merge_v_up_kernel<true>, grid, dim3(kProjThreads), 0, stream, p);
   else hipLaunchKernelGGL(merge_v_up_kernel<false>, grid, dim3(kProjThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+
+// Combine of the projected slices a rank receives in the exchange of the merge:
+// for every row (token, head of the slice) the W sources' 128-value rows are
+// merged by their LSEs (online, sources in order); a source whose LSE is -inf
+// (an empty row, as the pack sends it) takes no part.  Thread = (row, 8 values):
+// 16 threads per row, 16 rows per workgroup; the sources' loads go out together,
+// eight at a time.
+__global__ __launch_bounds__(256) void slice_combine_kernel(const SliceParams a) {
+  const int row = (int)blockIdx.x * 16 + (int)(threadIdx.x >> 4);
+  if (row >= a.rows) return;
+  const int d0 = 8 * (threadIdx.x & 15);
+  float m = -INFINITY, ssum = 0.f;
+  f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+  for (int w0 = 0; w0 < a.W; w0 += 8) {
+    float l[8];
+    u32x4 x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int w = min(w0 + u, a.W - 1);
+      l[u] = a.lse[(int64_t)w * a.lse_stride + row];
+      x[u] = *(const u32x4*)(a.y + (int64_t)w * a.y_stride + (int64_t)row * kVHead + d0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float lu = w0 + u < a.W ? l[u] : -INFINITY;
+      if (lu > -INFINITY) {
+        const float mn = fmaxf(m, lu);
+        const float c_old = m == -INFINITY ? 0.f : fast_exp2((m - mn) * kLog2e);
+        const float c_new = fast_exp2((lu - mn) * kLog2e);
+        acc0 = acc0 * c_old + f32x4{bf16_lo(x[u][0]), bf16_hi(x[u][0]), bf16_lo(x[u][1]), bf16_hi(x[u][1])} * c_new;
+        acc1 = acc1 * c_old + f32x4{bf16_lo(x[u][2]), bf16_hi(x[u][2]), bf16_lo(x[u][3]), bf16_hi(x[u][3])} * c_new;
+        ssum = ssum * c_old + c_new;
+        m = mn;
+      }
+    }
+  }
+  const float inv = ssum > 0.f ? 1.f / ssum : 0.f;
+  *(u32x4*)(a.out + (int64_t)row * kVHead + d0) =
+      u32x4{pack_bf16x2(acc0[0] * inv, acc0[1] * inv), pack_bf16x2(acc0[2] * inv, acc0[3] * inv),
+            pack_bf16x2(acc1[0] * inv, acc1[1] * inv), pack_bf16x2(acc1[2] * inv, acc1[3] * inv)};
+  if (a.out_lse && (threadIdx.x & 15) == 0) a.out_lse[row] = ssum > 0.f ? m + fast_log2(ssum) * kLn2 : -INFINITY;
+}
+
+hipError_t launch_slice_combine(const SliceParams& p, hipStream_t stream) {
+  if (p.rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(slice_combine_kernel, dim3((unsigned)((p.rows + 15) / 16)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -16,7 +16,8 @@ P = ctypes.c_void_p(16 * 1024)          # a dummy, aligned non-null "device" add
 def test_exports_every_declared_symbol():
     names = binding.header_functions()
     assert set(names) == {"mla_status_string", "mla_decode_partial", "mla_decode_workspace_size",
-                          "mla_lse_merge", "mla_merge_v_up_proj", "mla_dcp_local_seqlens"}
+                          "mla_lse_merge", "mla_merge_v_up_proj", "mla_dcp_local_seqlens",
+                          "mla_dcp_a2a_pack", "mla_dcp_a2a_combine"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -101,3 +102,21 @@ def test_merge_argument_checks():
     assert s(P, P, 2, 4, 2, 1, 0, P, P, None) == SHAPE
     assert s(None, P, 2, 4, 2, 1, 1, P, P, None) == NULL
     assert s(P, P, 0, 0, 2, 1, 16, P, P, None) == OK
+
+
+def test_exchange_argument_checks():
+    pk = lib.mla_dcp_a2a_pack
+    assert pk(P, P, None, 4, 128, 3, P, P, P, None) == SHAPE       # H % W != 0
+    assert pk(P, P, None, 4, 0, 1, P, P, P, None) == SHAPE
+    assert pk(P, P, None, -1, 16, 2, P, P, P, None) == SHAPE
+    assert pk(P, P, None, 4, 16, 2, None, P, P, None) == NULL      # W_UV missing
+    assert pk(P, P, None, 4, 16, 2, P, P, None, None) == NULL      # send_lse missing
+    assert pk(P, P, None, 0, 16, 2, None, None, None, None) == OK  # T == 0
+    cb = lib.mla_dcp_a2a_combine
+    rows = 4 * 8
+    assert cb(P, rows * 128, P, rows, 0, 4, 8, P, None, None) == SHAPE
+    assert cb(P, rows * 128 - 8, P, rows, 2, 4, 8, P, None, None) == SHAPE    # slices overlap
+    assert cb(P, rows * 128, P, rows - 1, 2, 4, 8, P, None, None) == SHAPE
+    assert cb(P, rows * 128 + 4, P, rows, 2, 4, 8, P, None, None) == SHAPE    # not 16-byte aligned
+    assert cb(None, rows * 128, P, rows, 2, 4, 8, P, None, None) == NULL
+    assert cb(P, rows * 128, P, rows, 2, 0, 8, P, None, None) == OK
