@@ -171,7 +171,10 @@ constexpr int kProjBlk = 16;                       // tokens per block
 constexpr int kProjThreads = 512;
 constexpr int kWBytes = kLatent * kVHead * 2;      // 128 KiB
 
-template <bool kValid>
+// kOne (W = 1): the merge is the identity, and an item's four slots are four
+// consecutive token blocks of the one partial instead of four ranks of one
+// block, so that four times the bytes are in flight per item.
+template <bool kValid, bool kOne>
 __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const MergeParams a) {
   __shared__ __attribute__((aligned(16))) uint8_t w_lds[kWBytes];
   __shared__ __attribute__((aligned(16))) uint8_t o_lds[kProjBlk * kLatent * 2];   // 16 KiB
@@ -208,10 +211,15 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
 
   // The thread's work is a sequence of items (block b, ranks w0 .. w0+3) with
   // w0 = 4j, j < ngroups.
-  const int ngroups = (a.W + 3) >> 2;
-  const int nitems = ((t_end - t_begin + kProjBlk - 1) / kProjBlk) * ngroups;
+  const int ngroups = kOne ? 1 : (a.W + 3) >> 2;
+  const int nblocks = (t_end - t_begin + kProjBlk - 1) / kProjBlk;
+  const int nitems = kOne ? (nblocks + 3) / 4 : nblocks * ngroups;
   auto item_tb = [&](int i) { return t_begin + (i / ngroups) * kProjBlk; };
   auto item_w0 = [&](int i) { return 4 * (i % ngroups); };
+  // Slot u of item i: its first token, its rank and whether it exists.
+  auto slot_tb = [&](int i, int u) { return kOne ? t_begin + (4 * i + u) * kProjBlk : item_tb(i); };
+  auto slot_w = [&](int i, int u) { return kOne ? 0 : min(item_w0(i) + u, a.W - 1); };
+  auto slot_ok = [&](int i, int u) { return kOne ? slot_tb(i, u) < t_end : item_w0(i) + u < a.W; };
   struct Pend {
     u32x4 x[4][2];
     float l[4];
@@ -222,11 +230,11 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
   // not take part are not read; without counts every rank's row is read and
   // its LSE decides.
   auto load_valid = [&](int i, int (&vv)[4]) {
-    const int tb = item_tb(i), w0 = item_w0(i);
-    const int t = tb + tt;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int w = min(w0 + u, a.W - 1);
+      const int tb = slot_tb(i, u);
+      const int t = tb + tt;
+      const int w = slot_w(i, u);
       if (kValid) {
         const __attribute__((address_space(4))) int32_t* vrow =
             (const __attribute__((address_space(4))) int32_t*)a.valid + (size_t)w * a.T;
@@ -236,19 +244,19 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
       } else {
         vv[u] = 1;
       }
-      vv[u] &= (i < nitems && w0 + u < a.W && t < t_end) ? 1 : 0;
+      vv[u] &= (i < nitems && slot_ok(i, u) && t < t_end) ? 1 : 0;
     }
   };
   // Every load of an item is issued whether or not the item exists or its lane
   // takes part: buffer loads whose offset lies past the buffer's range return
   // zero without touching memory.  So the number of loads in flight never
   // depends on the data and the compiler's waits stay exact.
-    auto load_data = [&](int i, const int (&vv)[4], Pend& p) {
-    const int tb = min(item_tb(i), a.T - 1), w0 = item_w0(i);
+  auto load_data = [&](int i, const int (&vv)[4], Pend& p) {
     p.part = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int w = min(w0 + u, a.W - 1);
+      const int tb = min(slot_tb(i, u), a.T - 1);
+      const int w = slot_w(i, u);
       const size_t row0 = w * plane + (size_t)tb * a.H + h;     // the block's first token
       const __amdgpu_buffer_rsrc_t ro =
           __builtin_amdgcn_make_buffer_rsrc((void*)(a.outs + row0 * kLatent), (short)0, kProjBlk * a.H * 1024, kBufFlags);
@@ -267,36 +275,11 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
   f32x4 acc[4];
   // One item: merge its ranks into the running (m, ssum, acc); after the last
   // rank group of a block, project the block's merged rows.
-  auto process = [&](int i, const Pend& cur) {
-    const int tb = item_tb(i);
+  // Project the block starting at token tb from the merged rows (acc, m, ssum).
+  auto emit = [&](int tb) {
     const int t = tb + tt;
     // Output row of (token tb, head h): slice h / hs holds [T][hs] rows.
     const size_t out_row0 = ((size_t)(h / a.hs) * a.T + tb) * a.hs + h % a.hs;
-    if (i % ngroups == 0) {
-      m = -INFINITY;
-      ssum = 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float lu = (cur.part >> u) & 1 ? cur.l[u] : -INFINITY;
-      const float mn = fmaxf(m, lu);
-      if (lu > -INFINITY && mn > -INFINITY) {
-        const float c_old = m == -INFINITY ? 0.f : fast_exp2((m - mn) * kLog2e);
-        const float c_new = fast_exp2((lu - mn) * kLog2e);
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          acc[2 * k] = acc[2 * k] * c_old + f32x4{bf16_lo(cur.x[u][k][0]), bf16_hi(cur.x[u][k][0]),
-                                                  bf16_lo(cur.x[u][k][1]), bf16_hi(cur.x[u][k][1])} * c_new;
-          acc[2 * k + 1] = acc[2 * k + 1] * c_old + f32x4{bf16_lo(cur.x[u][k][2]), bf16_hi(cur.x[u][k][2]),
-                                                          bf16_lo(cur.x[u][k][3]), bf16_hi(cur.x[u][k][3])} * c_new;
-        }
-        ssum = ssum * c_old + c_new;
-        m = mn;
-      }
-    }
-    if (i % ngroups != ngroups - 1) return;     // more ranks of this block to come
     // Merged latent row (bf16) into o_lds; an absent token or a row with no
     // participating rank is zero.
     const float inv = ssum > 0.f ? 1.f / ssum : 0.f;
@@ -355,6 +338,56 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
     // o_lds is rewritten by the next block.
     asm volatile("s_barrier" ::: "memory");
   };
+  auto process = [&](int i, const Pend& cur) {
+    if constexpr (kOne) {
+      // Each slot is a block of its own; the one partial is its merged row
+      // (weight exp(lse - lse) = 1), or zero with LSE -inf if it takes no part.
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int tb = slot_tb(i, u);
+        if (tb >= t_end) break;                       // uniform: depends on i and u only
+        const bool in = ((cur.part >> u) & 1) && cur.l[u] > -INFINITY;
+        m = in ? cur.l[u] : -INFINITY;
+        ssum = in ? 1.f : 0.f;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          acc[2 * k] = in ? f32x4{bf16_lo(cur.x[u][k][0]), bf16_hi(cur.x[u][k][0]),
+                                  bf16_lo(cur.x[u][k][1]), bf16_hi(cur.x[u][k][1])} : f32x4{0.f, 0.f, 0.f, 0.f};
+          acc[2 * k + 1] = in ? f32x4{bf16_lo(cur.x[u][k][2]), bf16_hi(cur.x[u][k][2]),
+                                      bf16_lo(cur.x[u][k][3]), bf16_hi(cur.x[u][k][3])} : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        emit(tb);
+      }
+      return;
+    } else {
+    if (i % ngroups == 0) {
+        m = -INFINITY;
+        ssum = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float lu = (cur.part >> u) & 1 ? cur.l[u] : -INFINITY;
+        const float mn = fmaxf(m, lu);
+        if (lu > -INFINITY && mn > -INFINITY) {
+          const float c_old = m == -INFINITY ? 0.f : fast_exp2((m - mn) * kLog2e);
+          const float c_new = fast_exp2((lu - mn) * kLog2e);
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            acc[2 * k] = acc[2 * k] * c_old + f32x4{bf16_lo(cur.x[u][k][0]), bf16_hi(cur.x[u][k][0]),
+                                                    bf16_lo(cur.x[u][k][1]), bf16_hi(cur.x[u][k][1])} * c_new;
+            acc[2 * k + 1] = acc[2 * k + 1] * c_old + f32x4{bf16_lo(cur.x[u][k][2]), bf16_hi(cur.x[u][k][2]),
+                                                            bf16_lo(cur.x[u][k][3]), bf16_hi(cur.x[u][k][3])} * c_new;
+          }
+          ssum = ssum * c_old + c_new;
+          m = mn;
+        }
+      }
+      if (i % ngroups != ngroups - 1) return;     // more ranks of this block to come
+      emit(item_tb(i));
+    }
+  };
 
   // Three register buffers in rotation: while item i is merged, the partials of
   // items i + 1 and i + 2 are in flight (and the counts of item i + 3).  The
@@ -407,8 +440,13 @@ hipError_t launch_merge_v_up(const MergeParams& p, hipStream_t stream) {
   const int max_groups = (p.T + kProjBlk - 1) / kProjBlk;
   if (groups > max_groups) groups = max_groups;
   const dim3 grid((unsigned)p.H, (unsigned)groups);
-  if (p.valid) hipLaunchKernelGGL(merge_v_up_kernel<true>, grid, dim3(kProjThreads), 0, stream, p);
-  else hipLaunchKernelGGL(merge_v_up_kernel<false>, grid, dim3(kProjThreads), 0, stream, p);
+  if (p.W == 1) {
+    if (p.valid) hipLaunchKernelGGL((merge_v_up_kernel<true, true>), grid, dim3(kProjThreads), 0, stream, p);
+    else hipLaunchKernelGGL((merge_v_up_kernel<false, true>), grid, dim3(kProjThreads), 0, stream, p);
+  } else {
+    if (p.valid) hipLaunchKernelGGL((merge_v_up_kernel<true, false>), grid, dim3(kProjThreads), 0, stream, p);
+    else hipLaunchKernelGGL((merge_v_up_kernel<false, false>), grid, dim3(kProjThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
