@@ -177,7 +177,8 @@ constexpr int kWBytes = kLatent * kVHead * 2;      // 128 KiB
 template <bool kValid, bool kOne>
 __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const MergeParams a) {
   __shared__ __attribute__((aligned(16))) uint8_t w_lds[kWBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t o_lds[kProjBlk * kLatent * 2];   // 16 KiB
+  // Merged rows of a block, two buffers in turn (W_UV and both fill the 160 KiB).
+  __shared__ __attribute__((aligned(16))) uint8_t o_buf[2][kProjBlk * kLatent * 2];
 
   const int h = blockIdx.x;
   const int lane = threadIdx.x & 63;
@@ -276,8 +277,13 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
   // One item: merge its ranks into the running (m, ssum, acc); after the last
   // rank group of a block, project the block's merged rows.
   // Project the block starting at token tb from the merged rows (acc, m, ssum).
+  int nemit = 0;                      // blocks emitted so far (uniform)
   auto emit = [&](int tb) {
     const int t = tb + tt;
+    // Buffer nemit & 1: the barrier below, which every wave passes only after
+    // its reads of the previous block, makes the buffer of two blocks ago free.
+    uint8_t* o_lds = o_buf[nemit & 1];
+    ++nemit;
     // Output row of (token tb, head h): slice h / hs holds [T][hs] rows.
     const size_t out_row0 = ((size_t)(h / a.hs) * a.T + tb) * a.hs + h % a.hs;
     // Merged latent row (bf16) into o_lds; an absent token or a row with no
@@ -335,8 +341,6 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
       __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)y[r]), ry,
                                             tb + tk < t_end ? (uint32_t)((tk * a.hs * kVHead + n0 + lr) * 2) : kOffNone, 0, 0);
     }
-    // o_lds is rewritten by the next block.
-    asm volatile("s_barrier" ::: "memory");
   };
   auto process = [&](int i, const Pend& cur) {
     if constexpr (kOne) {
