@@ -103,3 +103,31 @@ def test_pack_without_counts_and_combine_identity():
     fin = torch.isfinite(send_l[1, 0])
     assert torch.equal(one[fin], send_y[1, 0][fin]) and torch.equal(one_l[fin], send_l[1, 0][fin])
     assert torch.all(one[~fin] == 0) and torch.all(torch.isinf(one_l[~fin]))
+
+
+@pytest.mark.parametrize("W,T,Hs", [(13, 37, 3), (9, 5, 16), (1, 20, 7)])
+def test_combine_many_sources_padded(W, T, Hs):
+    # More sources than one load batch (8), odd slice sizes, sources padded
+    # apart in one allocation, and rows that some or all sources leave empty.
+    rng = np.random.default_rng(W * 100 + T)
+    pad = 3 * 128                                     # elements between a slice's end and the next
+    buf = torch.full((W, T * Hs * 128 + pad), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lbuf = torch.full((W, T * Hs + 5), float("nan"), dtype=torch.float32, device="cuda")
+    y = (rng.standard_normal((W, T, Hs, 128)) * 0.5).astype(np.float32)
+    l = (rng.standard_normal((W, T, Hs)) * 4).astype(np.float32)
+    l[rng.random((W, T, Hs)) < 0.3] = -np.inf
+    l[:, 0, 0] = -np.inf                              # a row no source takes part in
+    buf[:, :T * Hs * 128] = torch.tensor(y.reshape(W, -1)).to(torch.bfloat16).cuda()
+    lbuf[:, :T * Hs] = torch.tensor(l.reshape(W, -1)).cuda()
+    recv_y = buf[:, :T * Hs * 128].view(W, T, Hs, 128)
+    recv_l = lbuf[:, :T * Hs].view(W, T, Hs)
+    out = torch.empty((T, Hs, 128), dtype=torch.bfloat16, device="cuda")
+    out_l = torch.empty((T, Hs), dtype=torch.float32, device="cuda")
+    mla.mla_dcp_a2a_combine(recv_y, recv_l, out, out_l)
+    torch.cuda.synchronize()
+    ref_y, ref_l = O.a2a_combine(to_f64(recv_y), l.astype(np.float64))
+    got_l = to_f64(out_l)
+    assert np.array_equal(np.isinf(got_l), np.isinf(ref_l))
+    assert np.max(np.abs(got_l[np.isfinite(got_l)] - ref_l[np.isfinite(ref_l)]), initial=0.0) <= 1e-4
+    check_proj(out, ref_y, f"combine W={W}")
+    assert torch.all(out[0, 0] == 0)
