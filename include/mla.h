@@ -14,8 +14,11 @@
  *    layout that gives each rank contiguous blocks of tokens (whole pages); the
  *    calls take both as runs of cp_interleave tokens dealt to the ranks in turn.
  *  - PR #48196 ("DCP sparse MLA output-merge optimizations"): the exact
- *    LSE-weighted merge of per-rank partials with per-row valid counts, and the
- *    W_UV up-projection, which commutes with the merge.
+ *    LSE-weighted merge of per-rank partials with per-row valid counts, the
+ *    W_UV up-projection, which commutes with the merge, and the exchange that
+ *    projects each rank's partial before the all-to-all (the pack by
+ *    destination head slice and the receiving rank's combine; the transport
+ *    between GPUs is the caller's).
  *
  * Conventions for every call:
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
