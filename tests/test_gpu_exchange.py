@@ -131,3 +131,48 @@ def test_combine_many_sources_padded(W, T, Hs):
     assert np.max(np.abs(got_l[np.isfinite(got_l)] - ref_l[np.isfinite(ref_l)]), initial=0.0) <= 1e-4
     check_proj(out, ref_y, f"combine W={W}")
     assert torch.all(out[0, 0] == 0)
+
+
+def test_hip_graph_replay_exchange():
+    # Pack of every rank and combine of every destination captured in one HIP
+    # graph; every replay (with eager work and synchronisation in between)
+    # reproduces the eager result bit for bit.
+    W = 4
+    wl = WL.make_custom("graph", [300, 17, 64, 2, 129], [2, 3, 1, 2, 4], H=128, W=W, P=16, seed=23, w_uv=True)
+    dw = DeviceWorkload(wl)
+    for r in range(W):
+        dw.partial(r)
+    dw.valid_counts()
+    torch.cuda.synchronize()
+    T, Hs = dw.T, dw.H // W
+    send_y = torch.zeros((W, W, T, Hs, 128), dtype=torch.bfloat16, device="cuda")
+    send_l = torch.zeros((W, W, T, Hs), dtype=torch.float32, device="cuda")
+    out = torch.zeros((W, T, Hs, 128), dtype=torch.bfloat16, device="cuda")
+    out_l = torch.zeros((W, T, Hs), dtype=torch.float32, device="cuda")
+
+    def exchange():
+        for r in range(W):
+            mla.mla_dcp_a2a_pack(dw.outs[r], dw.lses[r], dw.valid[r], dw.w_uv, send_y[r], send_l[r], W)
+        for q in range(W):
+            mla.mla_dcp_a2a_combine(send_y[:, q], send_l[:, q], out[q], out_l[q])
+
+    exchange()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (send_y, send_l, out, out_l)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        exchange()             # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        exchange()
+    for _ in range(3):
+        for x in (send_y, send_l, out, out_l):
+            x.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for x, y in zip((send_y, send_l, out, out_l), ref):
+            assert torch.equal(x, y)
