@@ -375,8 +375,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed steps first (the GPU's clocks settle over a few thousand microseconds of work)")
+    ap.add_argument("--warmup", type=int, default=3000,
+                    help="untimed steps first (the GPU's clocks settle over a few thousand calls; "
+                         "3000 plain steps are about 0.2 s)")
     ap.add_argument("--workload", default="plain")
     ap.add_argument("--configs", default="mtp_dcp4,long_dcp8,mixed_wuv,mtp_dcp4_pages",
                     help="comma-separated secondary workloads ('' for none)")
