@@ -428,3 +428,40 @@ def test_many_short_requests(H, W):
             assert np.all(np.abs(go - ref) <= 2e-2 * scale), f"many_short H={H} short rows"
             assert np.linalg.norm(go - ref) <= 5e-3 * np.linalg.norm(ref), f"many_short H={H} short rows rel-L2"
             assert np.max(np.abs(to_f64(dw.out_lse)[short_rows] - np.asarray(full_l)[short_rows])) <= 1e-3
+
+
+def _random_cases(n=16, seed=29):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(n):
+        B = int(rng.integers(1, 7))
+        S = [int(x) for x in rng.integers(1, 300, size=B)]
+        Q = [int(min(s, rng.integers(0, 6))) for s in S]
+        if sum(Q) == 0:
+            Q[0] = 1
+        H = int(rng.choice([8, 16, 32, 128]))
+        W = int(rng.integers(1, 6))
+        I = int(rng.choice([1, 1, 2, 7, 16]))
+        P = int(rng.choice([7, 16, 32, 64]))
+        splits = int(rng.choice([0, 1, 3]))
+        cases.append((f"rand{k}_h{H}_w{W}_i{I}_p{P}_s{splits}", S, Q, H, W, P, I, splits))
+    return cases
+
+
+@pytest.mark.parametrize("name,S,Q,H,W,P,I,splits", _random_cases(), ids=[c[0] for c in _random_cases()])
+def test_random_shapes(name, S, Q, H, W, P, I, splits):
+    """Seeded random shapes (requests, query rows, lengths, heads, ranks, run
+    length, page size, split count): every rank's partial and the merge
+    against the oracle."""
+    log(f"random {name}")
+    wl = WL.make_custom(name, S, Q, H=H, W=W, P=P, seed=31, I=I)
+    toks = list(range(wl.T))
+    ref_o, ref_l = oracle_partials(wl, toks)
+    dw = DeviceWorkload(wl, num_splits=splits)
+    dw.outs.fill_(float("nan"))
+    dw.step()
+    torch.cuda.synchronize()
+    for r in range(W):
+        check_rows(dw.outs[r], dw.lses[r], ref_o[r], ref_l[r], f"{name} r={r}")
+    full_o, full_l = oracle_unsharded(wl, toks)
+    check_rows(dw.out, dw.out_lse, full_o, full_l, f"{name} merged")
