@@ -33,8 +33,9 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-_NOISE = ("is not a recognized feature for this target", "inline asm clobber list contains reserved",
-          "Reserved registers on the clobber list", "asm volatile(", "generated when compiling", "^")
+# The host pass does not know the packed-fp32 feature flag; that warning (and
+# the count line after it) is expected and dropped.  Nothing else is filtered.
+_NOISE = ("is not a recognized feature for this target", "generated when compiling")
 
 
 def _run(cmd, verbose):

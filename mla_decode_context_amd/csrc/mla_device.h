@@ -35,14 +35,17 @@ __device__ __forceinline__ s16x4 lds_read_tr16_at(const uint8_t* p) {
 // that the compiler adds no wait of its own: the kernel orders these loads with
 // explicit vmcnt waits and barriers.  The asm is volatile with a memory clobber,
 // so no other memory access moves across it.  A write of M0 needs one wait state
-// before an LDS-DMA instruction reads it, hence the s_nop.
+// before an LDS-DMA instruction reads it, hence the s_nop.  M0 is not named as
+// a clobber: LLVM reserves it and ignores it in clobber lists, so it is this
+// asm's to use only because the compiled kernels read M0 nowhere else (a CPU
+// test scans the gfx950 assembly of every kernel source for that).
 __device__ __forceinline__ void dma_16B_to_lds(const void* src, const uint8_t* lds_block) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds_block);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :
                : "s"(lds), "v"(src)
-               : "memory", "m0");
+               : "memory");
 }
 
 // The same load with the non-temporal hint, for cache rows (see below).
@@ -52,7 +55,7 @@ __device__ __forceinline__ void dma_16B_to_lds_stream(const void* src, const uin
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
                :
                : "s"(lds), "v"(src)
-               : "memory", "m0");
+               : "memory");
 }
 
 // Empty asm that "uses" a pointer, extending its registers' live range.
@@ -109,16 +112,20 @@ __device__ __forceinline__ void dma_16B_to_lds_sbase(uint32_t lds_off, uint32_t 
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
   const uint64_t sbase = ((uint64_t)hi << 32) | (uint64_t)lo;
+  // The readfirstlanes above are VALU writes of the base SGPRs, and a VMEM
+  // instruction may read an SGPR only five wait states after a VALU wrote it;
+  // the compiler inserts no wait states inside inline asm and may place the
+  // readfirstlanes right before it.  s_mov (one) + s_nop 4 (five) cover that.
   if (kNT)
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2 nt"
                  :
                  : "s"(lds_off), "v"(voff), "s"(sbase)
-                 : "memory", "m0");
+                 : "memory");
   else
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
                  : "s"(lds_off), "v"(voff), "s"(sbase)
-                 : "memory", "m0");
+                 : "memory");
 }
 
 // max / sum over the four lanes l, l^16, l^32, l^48 (one MFMA column) with the
