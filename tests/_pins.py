@@ -23,6 +23,88 @@ def _bits(x):
     return (u >> 16).astype(np.uint16)
 
 
+def _torch_widen(bits) -> np.ndarray:
+    """bf16 storage bits -> float64 through torch's bfloat16 dtype (a library
+    route independent of the oracle's own widening)."""
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+# bf16 bit patterns and the values the binary32 format gives them (bf16 is the
+# upper half of an IEEE-754 binary32: sign, 8 exponent bits with bias 127, 7
+# fraction bits): 1.0, -2.5, pi rounded to 8 significant bits, the smallest
+# subnormal 2^-133, the smallest normal 2^-126, the largest finite
+# (2 - 2^-7) * 2^127, +0, -0, +inf and -inf.
+BF16_FIXED = [
+    (0x3F80, 1.0), (0xC020, -2.5), (0x4049, 3.140625), (0x0001, 2.0 ** -133), (0x0080, 2.0 ** -126),
+    (0x7F7F, (2.0 - 2.0 ** -7) * 2.0 ** 127), (0x0000, 0.0), (0x8000, -0.0), (0x7F80, math.inf),
+    (0xFF80, -math.inf), (0x3C00, 2.0 ** -7), (0x4300, 128.0), (0xBF81, -(1.0 + 2.0 ** -7)), (0xBF01, -0.50390625),
+]
+
+
+def check_bf16_widening() -> bool:
+    """The oracle's exact widening of bf16 bits against fixed patterns whose
+    values follow from the binary32 format (signs of zero included), NaN
+    patterns staying NaN, and torch's bf16 dtype on every one of the 65536
+    patterns."""
+    bits = np.array([b for b, _ in BF16_FIXED], dtype=np.uint16)
+    got = O.bf16_bits_to_f64(bits)
+    for g, (b, want) in zip(got, BF16_FIXED):
+        if not (g == want and np.signbit(g) == np.signbit(want)):
+            return False
+    if not np.all(np.isnan(O.bf16_bits_to_f64(np.array([0x7FC0, 0xFFC1, 0x7F81], dtype=np.uint16)))):
+        return False
+    every = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    a, b = O.bf16_bits_to_f64(every), _torch_widen(every)
+    same = (a == b) | (np.isnan(a) & np.isnan(b))
+    return bool(np.all(same) and np.array_equal(np.signbit(a), np.signbit(b)))
+
+
+def check_v_up_proj_closed_forms(seed=7) -> bool:
+    """y[t,h,:] = o[t,h,:] @ W_UV[h] against projections whose result is known
+    without a matrix product: (i) W_UV[h] picks latent dim sel(h,n) into column
+    n with a factor c_h of its own, so y[t,h,n] = c_h * o[t,h,sel(h,n)];
+    (ii) two picks per column add; (iii) a rank-one W_UV[h] = u_h v_h^T gives
+    y[t,h,:] = (sum_k o[t,h,k] u_h[k]) * v_h, the inner sum taken term by term."""
+    rng = np.random.default_rng(seed)
+    T, H, K, N = 3, 4, 512, 128
+    o = rng.standard_normal((T, H, K))
+    c = np.array([1.0, -2.0, 0.5, 3.0])
+    sel = np.array([[(7 * n + 61 * h + 3) % K for n in range(N)] for h in range(H)])
+    w = np.zeros((H, K, N))
+    for h in range(H):
+        for n in range(N):
+            w[h, sel[h, n], n] = c[h]
+    y = O.v_up_proj(o, w)
+    if y.shape != (T, H, N):
+        return False
+    for t in range(T):
+        for h in range(H):
+            for n in range(N):
+                if y[t, h, n] != c[h] * o[t, h, sel[h, n]]:
+                    return False
+    sel2 = (sel + 100) % K
+    w2 = w.copy()
+    for h in range(H):
+        for n in range(N):
+            w2[h, sel2[h, n], n] = 0.25
+    y2 = O.v_up_proj(o, w2)
+    for t in range(T):
+        for h in range(H):
+            for n in range(N):
+                if abs(y2[t, h, n] - (c[h] * o[t, h, sel[h, n]] + 0.25 * o[t, h, sel2[h, n]])) > 1e-14:
+                    return False
+    u = rng.standard_normal((H, K))
+    v = rng.standard_normal((H, N))
+    y3 = O.v_up_proj(o, u[:, :, None] * v[:, None, :])
+    for t in range(T):
+        for h in range(H):
+            dot = math.fsum(o[t, h, k] * u[h, k] for k in range(K))
+            if not np.allclose(y3[t, h], dot * v[h], rtol=1e-12, atol=1e-12):
+                return False
+    return True
+
+
 def load_worked_masks():
     out = []
     with open(os.path.join(GOLDEN, "pr24453_worked_masks.txt")) as f:
@@ -113,8 +195,9 @@ def check_against_sdpa(seed=0) -> bool:
     scale = 1 / math.sqrt(192)
     for (S, Q, H, W) in [(6, 4, 3, 1), (9, 3, 2, 2), (13, 5, 4, 3), (31, 1, 2, 1), (40, 7, 2, 4)]:
         kvb, qnb, qpb = _rand_case(rng, S, Q, H)
-        kv = O.bf16_bits_to_f64(kvb)
-        q = np.concatenate([O.bf16_bits_to_f64(qnb), O.bf16_bits_to_f64(qpb)], axis=-1)  # [Q,H,576]
+        # inputs widened by torch's own bf16 dtype, not by the oracle's widening
+        kv = _torch_widen(kvb)
+        q = np.concatenate([_torch_widen(qnb), _torch_widen(qpb)], axis=-1)  # [Q,H,576]
         for r in range(W):
             out, lse = O.decode_partial([S], [0, Q], qnb, qpb, lambda b: kvb, scale, W, r)
             mask = torch.from_numpy(O.dense_mask(S, Q, W, r))  # [Q, S]
@@ -149,7 +232,7 @@ def check_closed_forms(seed=1) -> bool:
     scale = 1 / math.sqrt(192)
     S, Q, H, W = 23, 4, 2, 3
     kvb, qnb, qpb = _rand_case(rng, S, Q, H, zero_q=True)
-    kv = O.bf16_bits_to_f64(kvb)
+    kv = _torch_widen(kvb)
     for r in range(W):
         out, lse = O.decode_partial([S], [0, Q], qnb, qpb, lambda b: kvb, scale, W, r)
         for i in range(Q):
@@ -162,8 +245,8 @@ def check_closed_forms(seed=1) -> bool:
     # one visible key: out is that key's latent exactly, lse its scaled score
     kvb, qnb, qpb = _rand_case(rng, 1, 1, H)
     out, lse = O.decode_partial([1], [0, 1], qnb, qpb, lambda b: kvb, scale, 1, 0)
-    kv = O.bf16_bits_to_f64(kvb)
-    s0 = scale * (O.bf16_bits_to_f64(qnb[0]) @ kv[0, :512] + O.bf16_bits_to_f64(qpb[0]) @ kv[0, 512:])
+    kv = _torch_widen(kvb)
+    s0 = scale * (_torch_widen(qnb[0]) @ kv[0, :512] + _torch_widen(qpb[0]) @ kv[0, 512:])
     return np.array_equal(out[0], np.repeat(kv[:1, :512], H, axis=0)) and np.allclose(lse[0], s0, atol=1e-13)
 
 
@@ -367,7 +450,7 @@ def check_a2a_pack_combine(seed=6) -> bool:
     return True
 
 
-ALL_CHECKS = [check_worked_masks, check_ab_example, check_counts_bruteforce, check_against_sdpa,
-              check_closed_forms, check_merge_equals_unsharded, check_merge_identities,
-              check_wuv_commutes, check_runs_bruteforce, check_runs_merge_equals_unsharded,
-              check_a2a_pack_combine]
+ALL_CHECKS = [check_bf16_widening, check_worked_masks, check_ab_example, check_counts_bruteforce,
+              check_against_sdpa, check_closed_forms, check_merge_equals_unsharded, check_merge_identities,
+              check_wuv_commutes, check_v_up_proj_closed_forms, check_runs_bruteforce,
+              check_runs_merge_equals_unsharded, check_a2a_pack_combine]

@@ -98,6 +98,35 @@ def _vup_transposed(o, w_uv):               # uses W_UV[h]^T-like indexing
     return np.einsum("thk,hkn->thn", o, w_uv[:, :, ::-1])
 
 
+def _vup_heads_swapped(o, w_uv):            # head h projected by W_UV of head H-1-h
+    return np.einsum("thk,hkn->thn", o, w_uv[::-1])
+
+
+def _vup_k_misindexed(o, w_uv):             # latent dim k paired with row 511-k of W_UV[h]
+    return np.einsum("thk,hkn->thn", o, w_uv[:, ::-1, :])
+
+
+def _vup_heads_rolled(o, w_uv):             # off by one head
+    return np.einsum("thk,hkn->thn", o, np.roll(w_uv, 1, axis=0))
+
+
+def _widen_as_fp16(bits):                   # reads the bits as IEEE half
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def _widen_shift15(bits):                   # one bit too few in the shift
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(15)
+    return b.view(np.float32).astype(np.float64)
+
+
+def _widen_flush_subnormals(bits):          # flushes subnormals to zero
+    x = _real_widen(bits)
+    return np.where(np.abs(x) < 2.0 ** -126, 0.0 * x, x)
+
+
+_real_widen = O.bf16_bits_to_f64
+
+
 MUTANTS = [
     ("visible_count", _count_drop_plus_one),
     ("visible_count", _count_floor),
@@ -111,6 +140,13 @@ MUTANTS = [
     ("attend", _attend_double_scale),
     ("attend", _attend_log2),
     ("lse_merge", _merge_wrong_sign),
+    ("v_up_proj", _vup_transposed),
+    ("v_up_proj", _vup_heads_swapped),
+    ("v_up_proj", _vup_k_misindexed),
+    ("v_up_proj", _vup_heads_rolled),
+    ("bf16_bits_to_f64", _widen_as_fp16),
+    ("bf16_bits_to_f64", _widen_shift15),
+    ("bf16_bits_to_f64", _widen_flush_subnormals),
 ]
 
 
