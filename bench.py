@@ -1,31 +1,31 @@
 """Benchmark of the absorbed-MLA DCP decode path on one MI355X.
 
-Default workload (the headline line): plain decode, batch 64, one query row per
-request, 16 heads, W = 1, contexts drawn uniformly from 1024..8192 tokens, page
-64 with permuted physical blocks.  One step = one pass of the whole path over
-that batch: the decode kernel (row seqlens, paged gather, scores, masked online
-softmax, PV, split-K with the in-kernel combine, finalise).  With W = 1 the
-merge is the identity and is not run.
+Default workload (the headline line): long-context DCP decode, batch 256, two
+query rows per request (MTP), 128 heads, W = 8 shards simulated on the one GPU,
+contexts drawn uniformly from 8192..32768 tokens (four requests shortened so
+that some shards hold empty rows), page 64 with permuted physical blocks.  One
+step = one pass of the whole path over that batch: every shard's
+mla_decode_partial (row seqlens, paged gather, scores, masked online softmax,
+PV, split-K where the plan splits, finalise), the per-row valid counts of every
+shard, and the LSE merge of the eight partials.
 
-Other workloads (reported under "configs", not in the headline value): the DCP
-ones run every rank's partial, the valid counts and the merge (or the merge
-fused with W_UV) per step.  Their merge figures time the merge where a step
-runs it, right after the shard decodes; ``merge_*_back_to_back`` repeats the
-merge alone, which for partials that fit in the 256 MB last-level cache reads
-them from there.  The W_UV workload also times the projected exchange's two
-kernels (``a2a_pack_*``: every rank projects and packs its partial by
-destination head slice; ``a2a_combine_*``: every destination merges the slices
-it receives).
+Other workloads (reported under "configs", not in the headline value): the
+plain 16-head decode (W = 1, no merge), the MTP DCP4 step, the mixed batch
+whose merge is fused with W_UV, and the whole-page DCP4 layout.  Merge figures
+time the merge where a step runs it, right after the shard decodes;
+``merge_*_back_to_back`` repeats the merge alone, which for partials that fit
+in the 256 MB last-level cache reads them from there.  The W_UV workload also
+times the projected exchange's two kernels.
 
 Printed: one JSON line.  ``value`` is KV-cache GB/s of the whole step (bytes of
 cache rows the method must read once, divided by the step time) with inputs
-already resident in HBM; the timed steps alternate between two copies of the
-cache, so no call finds the previous call's rows in the last-level cache
-(``kv_GBps_same_cache`` repeats the steps on one copy, ``kv_GBps_cold_llc``
-times single steps after a flush).  ``roofline`` is the dominant kernel's
-algorithmic bytes per launch over its average launch duration (one pair of HIP
-events on the launch stream around the timed steps); ``cpu_baseline`` times
-the fp64 oracle on the host for the same workload.
+already resident in HBM.  ``roofline`` is the dominant kernel's algorithmic
+flops (or bytes, for an HBM-bound workload) per call over its average call
+duration, measured with HIP events on the launch stream around every step's
+decode calls inside the timed region; ``calibration`` holds what a streaming
+read and a register-resident MFMA loop reach on the same GPU (the roofline is
+also given as a fraction of those); ``cpu_baseline`` times the fp64 oracle on
+the host for a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -74,9 +74,11 @@ def merge_bytes(wl, valid, proj: bool):
     return read + write + wuv, flops
 
 
-# Sources that build the 16-head decode and its combine kernel (the headline
-# workload's kernels): a traffic record stays valid while these are unchanged.
+# Sources that build each measured kernel: a traffic record stays valid while
+# the sources it names are unchanged.
 DECODE16_SOURCES = ["mla_api.hip", "mla_common.h", "mla_decode.hip", "mla_device.h", "mla_kernels.h"]
+H128_SOURCES = ["mla_api.hip", "mla_common.h", "mla_decode_h128.hip", "mla_device.h", "mla_kernels.h"]
+MERGE_SOURCES = ["mla_api.hip", "mla_common.h", "mla_merge.hip", "mla_device.h", "mla_kernels.h"]
 
 
 def kernel_source_hash(files=None) -> str:
@@ -102,7 +104,7 @@ def load_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
-def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True):
+def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True, alternate=False):
     from mla_decode_context_amd import workloads as WL
     from mla_decode_context_amd.runner import DeviceWorkload
 
@@ -129,11 +131,12 @@ def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True
             if evs is not None:
                 evs[wl.W][1].record()
 
-    # For the headline workload a second copy of every shard's cache: the timed
-    # steps alternate between the two copies, so no call can find the rows that
-    # the previous call read still in the 256 MB last-level cache (the copies
-    # hold the same rows under the same block tables, so results are identical).
-    spare = [dw.caches[r].clone() for r in range(wl.W)] if headline else None
+    # With `alternate`, a second copy of every shard's cache: the timed steps
+    # alternate between the two copies, so no call can find the rows that the
+    # previous call read still in the 256 MB last-level cache (the copies hold
+    # the same rows under the same block tables, so results are identical).
+    # Workloads whose shards together exceed that cache need no copy.
+    spare = [dw.caches[r].clone() for r in range(wl.W)] if alternate else None
 
     def swap():
         if spare is not None:
@@ -145,7 +148,10 @@ def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True
         swap()
     torch.cuda.synchronize()
     # Timed region: the steps back to back, as a serving loop issues them, with
-    # one pair of events around the whole region (on the launch stream).
+    # one pair of events around the whole region (on the launch stream, the
+    # current stream).  Events between the steps' calls are left out: each one
+    # costs the GPU a few microseconds of idle time (measured 12 us per 70 us
+    # plain step).
     ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -244,15 +250,17 @@ def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True
     res["ms_per_step_events"] = float(ev_ms_step)
     if same_cache_ms is not None:
         res["kv_GBps_same_cache"] = sum(p["kv"] for p in per_shard) / (same_cache_ms * 1e-3) / 1e9
+    # Roofline of the decode calls (the dominant kernels): algorithmic bytes
+    # and flops of the average call over its average duration (a call launches
+    # the kernels decode_kernel_name() lists).  The duration: with one rank and
+    # no merge a step is exactly one call, so the timed region's events over
+    # the steps; otherwise a timed loop of `steps` passes over every shard's
+    # decode, back to back as a step issues them, between one pair of events.
+    res["_alg_bytes_per_launch"] = float(alg_bytes.mean())
+    res["_alg_flops_per_launch"] = float(alg_flops.mean())
+    res["_decode_avg_ms"] = float(ev_ms_step) if not merging else float(dec_step)
+    res["_kernel"] = dw.decode_kernel_name()
     if headline:
-        res["_alg_bytes_per_launch"] = float(alg_bytes.mean())
-        res["_alg_flops_per_launch"] = float(alg_flops.mean())
-        # Average duration of one decode call (its decode kernel and, when rows
-        # were split, the combine kernel): with one rank and no merge a step is
-        # exactly one call, so the timed region's events divided by the steps;
-        # otherwise every shard's decode back to back, divided by the shards.
-        res["_decode_avg_ms"] = float(ev_ms_step) if wl.W == 1 else float(dec_step)
-        res["_kernel"] = dw.decode_kernel_name()
         res["_cold_kv_GBps"] = cold_kv(dw, wl, per_shard, torch) if cold else None
     del dw
     torch.cuda.empty_cache()
@@ -352,10 +360,96 @@ def cpu_baseline(wl, budget_s=12.0):
             if spent >= budget_s:
                 break
     return dict(value=round(done_kv / spent / 1e9, 4), unit="GB/s", cores=int(threads), kind="oracle",
+                cpu_model=cpu_model(),
                 sample=f"fp64 oracle over {reqs} requests ({reqs / wl.B:.2f} passes over the {wl.B}-request "
                        f"batch, {done_tokens} query rows, every rank) in {spent:.1f} s; "
                        f"query-tokens/s {done_tokens / spent:.3g}",
                 query_tokens_per_s=round(done_tokens / spent, 2))
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def calibrate(torch, reps=5):
+    """KO5: what this GPU reaches for a streaming read of 4 GiB (plain and
+    non-temporal loads; 16x the last-level cache) and for a register-resident
+    bf16 MFMA loop.  Best of `reps` timed calls after one untimed call."""
+    from mla_decode_context_amd import binding as mla
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(mla.SINK_WORDS, dtype=torch.int32, device="cuda")
+
+    def best_ms(op):
+        op()
+        times = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            op()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        return min(times), float(np.median(times))
+
+    rd, rd_med = best_ms(lambda: mla.calib_hbm_read(buf, sink, nontemporal=False))
+    rn, rn_med = best_ms(lambda: mla.calib_hbm_read(buf, sink, nontemporal=True))
+    del buf
+    iters = 40000
+    flops = mla.calib_mfma_bf16(iters, sink)
+    mf, mf_med = best_ms(lambda: mla.calib_mfma_bf16(iters, sink))
+    del sink
+    torch.cuda.empty_cache()
+    return {"hbm_read_GBps": round(nbytes / (rd * 1e-3) / 1e9, 1),
+            "hbm_read_GBps_median": round(nbytes / (rd_med * 1e-3) / 1e9, 1),
+            "hbm_read_nt_GBps": round(nbytes / (rn * 1e-3) / 1e9, 1),
+            "hbm_read_nt_GBps_median": round(nbytes / (rn_med * 1e-3) / 1e9, 1),
+            "mfma_bf16_TFLOPs": round(flops / (mf * 1e-3) / 1e12, 1),
+            "mfma_bf16_TFLOPs_median": round(flops / (mf_med * 1e-3) / 1e12, 1),
+            "method": "mla_calib_hbm_read over 4 GiB (plain / non-temporal loads), mla_calib_mfma_bf16 "
+                      f"({iters} rounds of 8 chains of v_mfma_f32_16x16x32_bf16, 2 waves per SIMD); "
+                      f"best of {reps} event-timed calls"}
+
+
+def make_roofline(res, workload, calib=None):
+    """Roofline object of a workload's decode calls: MFMA-bound when its flops
+    at the bf16 peak take longer than its bytes at the HBM peak."""
+    t_mem = res["_alg_bytes_per_launch"] / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = res["_alg_flops_per_launch"] / (BF16_PEAK_TFLOPS * 1e12)
+    sec = res["_decode_avg_ms"] * 1e-3
+    if t_mfma > t_mem:
+        ach = res["_alg_flops_per_launch"] / sec / 1e12
+        rl = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+              "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": load_traffic(workload)}
+        meas = calib.get("mfma_bf16_TFLOPs") if calib else None
+    else:
+        ach = res["_alg_bytes_per_launch"] / sec / 1e9
+        rl = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+              "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": load_traffic(workload)}
+        meas = calib.get("hbm_read_nt_GBps") if calib else None
+    if meas:
+        rl["achievable"] = meas
+        rl["frac_of_achievable"] = round(ach / meas, 4)
+    rl.update({"kernel": res["_kernel"], "avg_launch_ms": round(res["_decode_avg_ms"], 5),
+               "alg_bytes_per_launch": int(res["_alg_bytes_per_launch"]),
+               "alg_flops_per_launch": int(res["_alg_flops_per_launch"])})
+    return rl
 
 
 def copy_probe(torch, mib: int):
@@ -375,15 +469,16 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=3000,
-                    help="untimed steps first (the GPU's clocks settle over a few thousand calls; "
-                         "3000 plain steps are about 0.2 s)")
-    ap.add_argument("--workload", default="plain")
-    ap.add_argument("--configs", default="mtp_dcp4,long_dcp8,mixed_wuv,mtp_dcp4_pages",
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps first (the GPU's clocks settle over the first few thousand calls; "
+                         "300 long_dcp8 steps are about 1 s)")
+    ap.add_argument("--workload", default="long_dcp8")
+    ap.add_argument("--configs", default="plain,mtp_dcp4,mixed_wuv,mtp_dcp4_pages",
                     help="comma-separated secondary workloads ('' for none)")
     ap.add_argument("--config-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true", help="skip the flushed-cache (cold) decode timing")
+    ap.add_argument("--no-calib", action="store_true", help="skip the HBM / MFMA calibration kernels")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run one plain copy of this many MiB (scale for traffic counters)")
     args = ap.parse_args()
@@ -401,34 +496,28 @@ def main():
         copy_probe(torch, args.copy_probe_mib)
     print(f"[bench] {args.workload}: generating inputs", file=sys.stderr, flush=True)
     head, wl = time_workload(args.workload, args.steps, args.warmup, torch, headline=True,
-                             cold=not args.no_cold)
+                             cold=not args.no_cold, alternate=args.workload == "plain")
     print(f"[bench] {args.workload}: {head['ms_per_step']:.4f} ms/step, {head['kv_GBps']:.1f} GB/s",
           file=sys.stderr, flush=True)
+    calib = None
+    if not args.no_calib:
+        print("[bench] calibration: streaming read and MFMA loop", file=sys.stderr, flush=True)
+        calib = calibrate(torch)
+        print(f"[bench] calibration: {json.dumps(calib)}", file=sys.stderr, flush=True)
     configs = {}
-    for name in [c for c in args.configs.split(",") if c]:
+    for name in [c for c in args.configs.split(",") if c and c != args.workload]:
         print(f"[bench] {name}: generating inputs", file=sys.stderr, flush=True)
-        res, _ = time_workload(name, args.config_steps, 3, torch)
-        configs[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()}
+        res, _ = time_workload(name, args.config_steps, 3 if name != "plain" else 300, torch,
+                               alternate=name == "plain")
+        res["roofline"] = make_roofline(res, name, calib)
+        configs[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()
+                         if not k.startswith("_")}
         print(f"[bench] {name}: {json.dumps(configs[name])}", file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on the host", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl)
-    achieved = head["_alg_bytes_per_launch"] / (head["_decode_avg_ms"] * 1e-3) / 1e9
-    # The bound is whichever roofline time is longer at peak: bytes at 8 TB/s or
-    # flops at the dense bf16 MFMA peak.
-    t_mem = head["_alg_bytes_per_launch"] / (HBM_PEAK_GBPS * 1e9)
-    t_mfma = head["_alg_flops_per_launch"] / (BF16_PEAK_TFLOPS * 1e12)
-    if t_mfma > t_mem:
-        tflops = head["_alg_flops_per_launch"] / (head["_decode_avg_ms"] * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": load_traffic(args.workload)}
-    else:
-        roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(args.workload)}
-    roofline.update({"kernel": head["_kernel"], "avg_launch_ms": round(head["_decode_avg_ms"], 5),
-                     "alg_bytes_per_launch": int(head["_alg_bytes_per_launch"]),
-                     "alg_flops_per_launch": int(head["_alg_flops_per_launch"])})
+    roofline = make_roofline(head, args.workload, calib)
     cfg = WL.CONFIGS[args.workload]
     line = {
         "metric": METRIC,
@@ -447,13 +536,20 @@ def main():
                    "heads": wl.H, "dcp_world": wl.W, "page_size": wl.P, "seed": wl.seed},
         "pct_hbm_peak": round(100.0 * head["kv_GBps"] / HBM_PEAK_GBPS, 2),
         "query_tokens_per_s": round(head["query_tokens_per_s"], 1),
-        "kv_GBps_cold_llc": None if head["_cold_kv_GBps"] is None else round(head["_cold_kv_GBps"], 2),
-        "kv_GBps_same_cache": round(head["kv_GBps_same_cache"], 2),
+        "decode_ms_per_shard_in_step": head["decode_ms_per_shard_in_step"],
+        "decode_pct_bf16_peak": round(head["decode_pct_bf16_peak"], 2),
+        "kv_GBps_cold_llc": None if head.get("_cold_kv_GBps") is None else round(head["_cold_kv_GBps"], 2),
         "roofline": roofline,
-        "merge_GBps": configs.get("mtp_dcp4", {}).get("merge_GBps"),
+        "merge_kind": head.get("merge_kind"),
+        "merge_ms": None if head.get("merge_ms") is None else round(head["merge_ms"], 5),
+        "merge_GBps": None if head.get("merge_GBps") is None else round(head["merge_GBps"], 1),
+        "merge_pct_hbm_peak": None if head.get("merge_pct_hbm_peak") is None else round(head["merge_pct_hbm_peak"], 2),
+        "calibration": calib,
         "cpu_baseline": cpu,
         "configs": configs,
     }
+    if "kv_GBps_same_cache" in head:
+        line["kv_GBps_same_cache"] = round(head["kv_GBps_same_cache"], 2)
     print(json.dumps(line))
 
 

@@ -26,7 +26,8 @@
  *    keeps no state between calls except a per-device "is this gfx950" flag.
  *  - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream)
  *    and the call returns without waiting.  No call reads device memory on the
- *    host, so all calls can be captured in a HIP graph.
+ *    host (except mla_decode_partial in the MLA_DEBUG=1 mode described with
+ *    it), so all calls can be captured in a HIP graph.
  *  - bf16 tensors are passed as `const void*` holding IEEE bfloat16 bits.
  *  - Errors are returned as mla_status codes; the library never aborts.  Host-
  *    visible argument errors are detected before anything is enqueued.
@@ -50,6 +51,7 @@ typedef int32_t mla_status;
 #define MLA_ERR_UNSUPPORTED -3  /* current device is not gfx950                     */
 #define MLA_ERR_WORKSPACE   -4  /* workspace too small for the requested splits      */
 #define MLA_ERR_HIP         -5  /* a HIP runtime call or kernel launch failed        */
+#define MLA_ERR_CAPTURE     -6  /* MLA_DEBUG checks asked for on a capturing stream  */
 
 /* Fixed head dimensions of the absorbed form. */
 #define MLA_D_LATENT 512   /* kv_lora_rank: c_kv, q_nope and output width */
@@ -122,6 +124,15 @@ const char* mla_status_string(mla_status status);
  * returns MLA_OK (the grid is sized from host ints and may be empty).
  * Device-side contract: Q_b <= S_b <= max_seq_len, Q_b <= max_query_len,
  * block ids valid for every stored local token.
+ *
+ * Debug mode: with the environment variable MLA_DEBUG=1 the call first copies
+ * seq_lens, query_start_loc and block_table to host memory on hip_stream,
+ * waits for the stream, and checks the device-side contract with
+ * mla_check_decode_metadata (block ids against the device allocation that
+ * holds kv_cache).  A violation is reported on stderr and the call returns
+ * MLA_ERR_SHAPE with nothing enqueued.  The wait makes debug mode unusable
+ * inside HIP graph capture: on a capturing stream the call returns
+ * MLA_ERR_CAPTURE.  Without MLA_DEBUG=1 nothing is read back.
  */
 mla_status mla_decode_partial(
     const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
@@ -133,6 +144,26 @@ mla_status mla_decode_partial(
     int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, float scale, int32_t num_splits,
     void* out, float* lse,
     void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * mla_check_decode_metadata -- the device-side contract of mla_decode_partial,
+ * checked on HOST copies of its metadata (what MLA_DEBUG=1 runs).  All
+ * pointers are host pointers: seq_lens [B], query_start_loc [B+1],
+ * block_table [B * bt_stride].  Checks, in order:
+ *   query_start_loc[0] == 0, nondecreasing, query_start_loc[B] == T;
+ *   per request: 0 <= Q_b <= max_query_len, Q_b <= S_b <= max_seq_len;
+ *   the ceil(Lc_b / page_size) blocks that hold rank cp_rank's Lc_b stored
+ *   tokens fit in the row (<= bt_stride) and have ids in [0, num_blocks)
+ *   (num_blocks < 0: only ids >= 0 are required).
+ * Returns MLA_OK, MLA_ERR_NULL, or MLA_ERR_SHAPE for the first violation,
+ * whose description goes to `reason` (NUL-terminated, truncated to
+ * reason_len; may be NULL).  Pure host code: no device access.
+ */
+mla_status mla_check_decode_metadata(const int32_t* seq_lens, const int32_t* query_start_loc,
+                                     const int32_t* block_table, int32_t bt_stride, int32_t B, int32_t T,
+                                     int32_t max_query_len, int32_t max_seq_len, int32_t page_size,
+                                     int32_t cp_world, int32_t cp_rank, int32_t cp_interleave,
+                                     int64_t num_blocks, char* reason, size_t reason_len);
 
 /*
  * Bytes of workspace mla_decode_partial needs for the same host arguments

@@ -16,7 +16,8 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmla.so")
-HEADER = os.path.join(os.path.dirname(_PKG), "include", "mla.h")
+INCLUDE = os.path.join(os.path.dirname(_PKG), "include")
+HEADER = os.path.join(INCLUDE, "mla.h")
 
 MLA_OK = 0
 D_LATENT, D_ROPE, D_ROW, D_V = 512, 64, 576, 128
@@ -65,14 +66,27 @@ def load_library():
     lib.mla_dcp_local_seqlens.restype = _i32
     lib.mla_dcp_local_seqlens.argtypes = [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32,
                                           _c_void_p, _c_void_p, _c_void_p]
+    lib.mla_check_decode_metadata.restype = _i32
+    lib.mla_check_decode_metadata.argtypes = [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32,
+                                              _i32, _i32, _i32, _i32, _i64, ctypes.c_char_p, ctypes.c_size_t]
+    lib.mla_calib_hbm_read.restype = _i32
+    lib.mla_calib_hbm_read.argtypes = [_c_void_p, ctypes.c_size_t, _i32, _c_void_p, _c_void_p]
+    lib.mla_calib_mfma_bf16.restype = _i32
+    lib.mla_calib_mfma_bf16.argtypes = [_i32, _c_void_p, _c_void_p]
+    lib.mla_calib_mfma_flops.restype = ctypes.c_double
+    lib.mla_calib_mfma_flops.argtypes = [_i32]
     _lib = lib
     return lib
 
 
 def header_functions() -> list[str]:
-    """Names of the functions declared in include/mla.h."""
-    text = open(HEADER).read()
-    return re.findall(r"^\s*(?:mla_status|size_t|const char\*)\s+(mla_\w+)\s*\(", text, re.M)
+    """Names of the functions declared in the headers under include/."""
+    names = []
+    for f in sorted(os.listdir(INCLUDE)):
+        if f.endswith(".h"):
+            text = open(os.path.join(INCLUDE, f)).read()
+            names += re.findall(r"^\s*(?:mla_status|size_t|double|const char\*)\s+(mla_\w+)\s*\(", text, re.M)
+    return names
 
 
 def _check(status: int, what: str):
@@ -252,6 +266,28 @@ def mla_dcp_a2a_combine(recv_y, recv_lse, out, out_lse=None, stream=None):
     st = lib.mla_dcp_a2a_combine(_ptr(recv_y), recv_y.stride(0), _ptr(recv_lse), recv_lse.stride(0), W, T, Hs,
                                  _ptr(out), _ptr(out_lse), _stream(stream))
     _check(st, "mla_dcp_a2a_combine")
+
+
+SINK_WORDS = 1 << 20          # MLA_CALIB_SINK_WORDS
+
+
+def calib_hbm_read(buf, sink, nontemporal=False, stream=None):
+    """Read every byte of the GPU tensor ``buf`` once (calibration of the HBM
+    read rate); ``sink`` is an int32/uint32 GPU tensor of at least 2^20 words."""
+    lib = load_library()
+    if not buf.is_cuda or not buf.is_contiguous() or not sink.is_cuda or sink.numel() * sink.element_size() < 4 * SINK_WORDS:
+        raise MlaError("calib_hbm_read: contiguous GPU buffer and a 2^20-word GPU sink expected")
+    _check(lib.mla_calib_hbm_read(_ptr(buf), buf.numel() * buf.element_size(), int(bool(nontemporal)), _ptr(sink),
+                                  _stream(stream)), "mla_calib_hbm_read")
+
+
+def calib_mfma_bf16(iters, sink, stream=None) -> float:
+    """Enqueue the register-resident bf16 MFMA loop; returns the flops it performs."""
+    lib = load_library()
+    if not sink.is_cuda or sink.numel() * sink.element_size() < 4 * SINK_WORDS:
+        raise MlaError("calib_mfma_bf16: a 2^20-word GPU sink expected")
+    _check(lib.mla_calib_mfma_bf16(int(iters), _ptr(sink), _stream(stream)), "mla_calib_mfma_bf16")
+    return float(lib.mla_calib_mfma_flops(int(iters)))
 
 
 def mla_dcp_local_seqlens(seq_lens, query_start_loc, T, cp_world, cp_rank, row_seqlen=None,

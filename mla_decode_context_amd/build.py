@@ -18,6 +18,7 @@ SOURCES = [
     ("mla_decode.hip", _VGPR_FORM),
     ("mla_merge.hip", _VGPR_FORM),
     ("mla_decode_h128.hip", _VGPR_FORM),
+    ("mla_calib.hip", _VGPR_FORM),
 ]
 
 HIPCC_FLAGS = [

@@ -1,7 +1,12 @@
 // C ABI of libmla: argument validation, launch planning and kernel launches.
 // The call contracts are documented in include/mla.h.
 #include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
+
+#include <vector>
 
 #include "mla.h"
 #include "mla_kernels.h"
@@ -149,6 +154,36 @@ size_t workspace_bytes_for(const Plan& p, int T, int H) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+mla_status fail(char* reason, size_t len, const char* fmt, ...) {
+  if (reason && len > 0) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(reason, len, fmt, ap);
+    va_end(ap);
+  }
+  return MLA_ERR_SHAPE;
+}
+
+bool debug_mode() {
+  const char* v = getenv("MLA_DEBUG");
+  return v && v[0] == '1' && v[1] == 0;
+}
+
+// Blocks of the allocation that holds kv_cache, from kv_cache on (a block k is
+// usable when its page_size rows end inside the allocation); -1 if unknown.
+int64_t blocks_in_allocation(const void* kv_cache, int64_t kv_block_stride, int32_t page_size) {
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)kv_cache) != hipSuccess || !base) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  const int64_t avail = (int64_t)((uintptr_t)base + size - (uintptr_t)kv_cache);
+  const int64_t block = (int64_t)page_size * MLA_D_ROW * 2;
+  if (avail < block) return 0;
+  return (avail - block) / (kv_block_stride * 2) + 1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -161,8 +196,50 @@ const char* mla_status_string(mla_status status) {
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: the current device is not gfx950";
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace too small for the split plan";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP runtime call or kernel launch failed";
+    case MLA_ERR_CAPTURE: return "MLA_ERR_CAPTURE: MLA_DEBUG checks cannot run on a capturing stream";
     default: return "unknown mla_status";
   }
+}
+
+mla_status mla_check_decode_metadata(const int32_t* seq_lens, const int32_t* query_start_loc,
+                                     const int32_t* block_table, int32_t bt_stride, int32_t B, int32_t T,
+                                     int32_t max_query_len, int32_t max_seq_len, int32_t page_size,
+                                     int32_t cp_world, int32_t cp_rank, int32_t cp_interleave,
+                                     int64_t num_blocks, char* reason, size_t reason_len) {
+  if (reason && reason_len) reason[0] = 0;
+  if (B < 0 || T < 0 || page_size < 1 || !layout_ok(cp_world, cp_interleave) || cp_rank < 0 ||
+      cp_rank >= cp_world || bt_stride < 1)
+    return fail(reason, reason_len, "invalid sizes");
+  if (B == 0) return T == 0 ? MLA_OK : fail(reason, reason_len, "T = %d tokens without requests", T);
+  if (!seq_lens || !query_start_loc || !block_table) return MLA_ERR_NULL;
+  if (query_start_loc[0] != 0)
+    return fail(reason, reason_len, "query_start_loc[0] = %d, not 0", query_start_loc[0]);
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t q = query_start_loc[b + 1] - query_start_loc[b];
+    if (q < 0)
+      return fail(reason, reason_len, "query_start_loc decreases at request %d (%d -> %d)", b,
+                  query_start_loc[b], query_start_loc[b + 1]);
+    if (q > max_query_len)
+      return fail(reason, reason_len, "request %d has %d query rows > max_query_len %d", b, q, max_query_len);
+    const int32_t S = seq_lens[b];
+    if (S < q) return fail(reason, reason_len, "request %d: seq_len %d < its %d query rows", b, S, q);
+    if (S > max_seq_len)
+      return fail(reason, reason_len, "request %d: seq_len %d > max_seq_len %d", b, S, max_seq_len);
+    const int64_t lc = host_shard_count(S, cp_world, cp_rank, cp_interleave);
+    const int64_t nb = ceil_div(lc, page_size);
+    if (nb > bt_stride)
+      return fail(reason, reason_len, "request %d needs %lld blocks on rank %d, the block table row has %d", b,
+                  (long long)nb, cp_rank, bt_stride);
+    for (int64_t i = 0; i < nb; ++i) {
+      const int32_t id = block_table[(int64_t)b * bt_stride + i];
+      if (id < 0 || (num_blocks >= 0 && id >= num_blocks))
+        return fail(reason, reason_len, "request %d: block_table entry %lld = %d outside [0, %lld)", b,
+                    (long long)i, id, (long long)(num_blocks >= 0 ? num_blocks : (int64_t)1 << 31));
+    }
+  }
+  if (query_start_loc[B] != T)
+    return fail(reason, reason_len, "query_start_loc[B] = %d, not T = %d", query_start_loc[B], T);
+  return MLA_OK;
 }
 
 size_t mla_decode_workspace_size(int32_t B, int32_t T, int32_t H, int32_t max_query_len,
@@ -206,6 +283,28 @@ mla_status mla_decode_partial(
   if (bt_stride < 1 || !aligned(out, 16)) return MLA_ERR_SHAPE;
   mla_status st = check_device();
   if (st != MLA_OK) return st;
+  if (debug_mode()) {
+    // Host copies of the metadata, one wait, the contract checked before
+    // anything is enqueued.  Not valid inside capture.
+    hipStream_t s = (hipStream_t)hip_stream;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) return MLA_ERR_HIP;
+    if (cs != hipStreamCaptureStatusNone) return MLA_ERR_CAPTURE;
+    std::vector<int32_t> hs(B), hq(B + 1), hb((size_t)B * bt_stride);
+    if (hipMemcpyAsync(hs.data(), seq_lens, hs.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipMemcpyAsync(hq.data(), query_start_loc, hq.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipMemcpyAsync(hb.data(), block_table, hb.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return MLA_ERR_HIP;
+    char why[256];
+    const mla_status cst = mla_check_decode_metadata(
+        hs.data(), hq.data(), hb.data(), bt_stride, B, T, max_query_len, max_seq_len, page_size, cp_world, cp_rank,
+        cp_interleave, blocks_in_allocation(kv_cache, kv_block_stride, page_size), why, sizeof(why));
+    if (cst != MLA_OK) {
+      fprintf(stderr, "mla_decode_partial (MLA_DEBUG): %s\n", why);
+      return cst;
+    }
+  }
 
   const Plan plan = make_plan(B, T, H, max_seq_len, cp_world, cp_interleave, num_splits, workspace != nullptr);
   const size_t need = workspace_bytes_for(plan, T, H);

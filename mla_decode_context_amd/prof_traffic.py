@@ -12,8 +12,9 @@ Two subcommands:
       then WRITE_SIZE, both in KiB per dispatch), each scaled by what the same
       counter reads for the plain N-MiB copy that ``bench.py --copy-probe-mib N``
       runs first (the largest ``__amd_rocclr_copyBuffer`` dispatch).  The record
-      carries the hash of the 16-head decode path's sources it was measured on;
-      bench.py only reports it while that hash still matches.
+      carries the hash of the sources that build the kernel (``--sources``:
+      decode16, h128 or merge); bench.py only reports it while that hash still
+      matches.
 
 Only reads CSV files; it touches no GPU.
 """
@@ -76,7 +77,9 @@ def copy_reading(rows, expect_bytes):
 
 
 def cmd_traffic(a):
-    from bench import DECODE16_SOURCES, kernel_source_hash
+    from bench import DECODE16_SOURCES, H128_SOURCES, MERGE_SOURCES, kernel_source_hash
+
+    sources = {"decode16": DECODE16_SOURCES, "h128": H128_SOURCES, "merge": MERGE_SOURCES}[a.sources]
 
     copy_bytes = a.copy_mib * (1 << 20)
     fetch = counter_per_dispatch(a.fetch, "FETCH_SIZE")
@@ -92,8 +95,8 @@ def cmd_traffic(a):
     rec = {
         "kernel": a.kernel,
         "workload": a.workload,
-        "kernel_sources": DECODE16_SOURCES,
-        "kernel_source_hash": kernel_source_hash(DECODE16_SOURCES),
+        "kernel_sources": sources,
+        "kernel_source_hash": kernel_source_hash(sources),
         "bytes_per_launch": round(fetch_b + write_b),
         "fetch_bytes_per_launch": round(fetch_b),
         "write_bytes_per_launch": round(write_b),
@@ -160,6 +163,7 @@ def main():
     t.add_argument("--copy-mib", type=int, required=True)
     t.add_argument("--kernel", required=True)
     t.add_argument("--workload", required=True)
+    t.add_argument("--sources", choices=["decode16", "h128", "merge"], default="decode16")
     t.add_argument("--alg-bytes", type=float, required=True)
     t.add_argument("--cmd-fetch", required=True)
     t.add_argument("--cmd-write", required=True)

@@ -9,7 +9,7 @@ from mla_decode_context_amd import binding
 
 lib = binding.load_library()
 
-OK, NULL, SHAPE, UNSUP, WS, HIP = 0, -1, -2, -3, -4, -5
+OK, NULL, SHAPE, UNSUP, WS, HIP, CAPTURE = 0, -1, -2, -3, -4, -5, -6
 P = ctypes.c_void_p(16 * 1024)          # a dummy, aligned non-null "device" address (never dereferenced)
 
 
@@ -17,13 +17,14 @@ def test_exports_every_declared_symbol():
     names = binding.header_functions()
     assert set(names) == {"mla_status_string", "mla_decode_partial", "mla_decode_workspace_size",
                           "mla_lse_merge", "mla_merge_v_up_proj", "mla_dcp_local_seqlens",
-                          "mla_dcp_a2a_pack", "mla_dcp_a2a_combine"}
+                          "mla_dcp_a2a_pack", "mla_dcp_a2a_combine", "mla_check_decode_metadata",
+                          "mla_calib_hbm_read", "mla_calib_mfma_bf16", "mla_calib_mfma_flops"}
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_status_strings():
-    for code in (OK, NULL, SHAPE, UNSUP, WS, HIP):
+    for code in (OK, NULL, SHAPE, UNSUP, WS, HIP, CAPTURE):
         s = lib.mla_status_string(code).decode()
         assert s.startswith("MLA_")
     assert "unknown" in lib.mla_status_string(7).decode()
@@ -120,3 +121,70 @@ def test_exchange_argument_checks():
     assert cb(P, rows * 128 + 4, P, rows, 2, 4, 8, P, None, None) == SHAPE    # not 16-byte aligned
     assert cb(None, rows * 128, P, rows, 2, 4, 8, P, None, None) == NULL
     assert cb(P, rows * 128, P, rows, 2, 0, 8, P, None, None) == OK
+
+
+def test_calibration_argument_checks():
+    assert lib.mla_calib_hbm_read(P, 0, 0, None, None) == OK           # nothing to read
+    assert lib.mla_calib_hbm_read(None, 1024, 0, P, None) == NULL
+    assert lib.mla_calib_hbm_read(P, 1000, 0, P, None) == SHAPE        # not whole 16-byte words
+    assert lib.mla_calib_hbm_read(ctypes.c_void_p(16 * 1024 + 4), 1024, 0, P, None) == SHAPE
+    assert lib.mla_calib_mfma_bf16(-1, P, None) == SHAPE
+    assert lib.mla_calib_mfma_bf16(10, None, None) == NULL
+    # 512 workgroups x 4 waves x iters x 8 chains x 16384 flop per MFMA
+    assert lib.mla_calib_mfma_flops(10) == 512 * 4 * 10 * 8 * 16384.0
+    assert lib.mla_calib_mfma_flops(-1) == -1.0
+
+
+# ---------------------------------------------------------------------------
+# mla_check_decode_metadata: the device-side contract on host copies (what
+# MLA_DEBUG=1 checks before a decode call launches anything)
+# ---------------------------------------------------------------------------
+
+def _meta(**kw):
+    """A valid metadata set: 3 requests, W = 2, rank 1, page 4, 40 blocks."""
+    m = dict(S=[9, 2, 17], qsl=[0, 2, 3, 7], bt=None, bt_stride=3, T=7, mq=4, ms=17, P=4, W=2, r=1, I=1, nblk=40)
+    m.update(kw)
+    if m["bt"] is None:
+        m["bt"] = [0, 1, -1, 2, -1, -1, 3, 4, 5]     # rank 1 holds 4, 1, 8 tokens -> 1, 1, 2 blocks
+    return m
+
+
+def _check_meta(m):
+    S = (ctypes.c_int32 * len(m["S"]))(*m["S"])
+    q = (ctypes.c_int32 * len(m["qsl"]))(*m["qsl"])
+    bt = (ctypes.c_int32 * len(m["bt"]))(*m["bt"])
+    why = ctypes.create_string_buffer(256)
+    st = lib.mla_check_decode_metadata(S, q, bt, m["bt_stride"], len(m["S"]), m["T"], m["mq"], m["ms"], m["P"],
+                                       m["W"], m["r"], m["I"], m["nblk"], why, 256)
+    return st, why.value.decode()
+
+
+@pytest.mark.parametrize("kw,fragment", [
+    (dict(qsl=[1, 2, 3, 7]), "query_start_loc[0]"),
+    (dict(qsl=[0, 3, 2, 7]), "decreases"),
+    (dict(qsl=[0, 2, 3, 6]), "not T"),
+    (dict(mq=3), "max_query_len"),
+    (dict(S=[9, 0, 17]), "query rows"),                 # Q_b > S_b
+    (dict(ms=16), "max_seq_len"),
+    (dict(bt=[0, 1, -1, 2, -1, -1, 3, -1, 5]), "block_table entry 1 = -1"),
+    (dict(bt=[0, 1, -1, 40, -1, -1, 3, 4, 5]), "block_table entry 0 = 40"),
+    (dict(bt=[0, 1, 2, 3, 4, 5], bt_stride=2, S=[9, 2, 33], ms=33), "blocks on rank"),
+])
+def test_check_metadata_violations(kw, fragment):
+    st, why = _check_meta(_meta(**kw))
+    assert st == SHAPE and fragment in why, (st, why)
+
+
+def test_check_metadata_accepts_valid_sets():
+    assert _check_meta(_meta()) == (OK, "")
+    # unused entries past a request's blocks are never looked at, whatever they hold
+    assert _check_meta(_meta(bt=[0, 1, -99, 2, 12345, -7, 3, 4, 5]))[0] == OK
+    # unknown pool size: ids only need to be >= 0
+    assert _check_meta(_meta(bt=[0, 10 ** 6, -1, 2, -1, -1, 3, 4, 5], nblk=-1))[0] == OK
+    # whole-page runs (I = 4): rank 1 holds 4, 0, 8 tokens; request 1 needs no block
+    assert _check_meta(_meta(I=4, bt=[0, -1, -1, -1, -1, -1, 3, 4, -1]))[0] == OK
+    # rank 0 of W = 1 holds everything: 9, 2, 17 tokens -> 3, 1, 5 blocks (stride 5)
+    bt = [0, 1, 2, -1, -1, 3, -1, -1, -1, -1, 4, 5, 6, 7, 8]
+    assert _check_meta(_meta(W=1, r=0, bt=bt, bt_stride=5))[0] == OK
+    assert _check_meta(_meta(S=[], qsl=[0], bt=[0], T=0))[0] == OK
+    assert _check_meta(_meta(S=[], qsl=[0], bt=[0], T=2))[0] == SHAPE
