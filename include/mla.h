@@ -53,6 +53,13 @@ typedef int32_t mla_status;
 #define MLA_ERR_HIP         -5  /* a HIP runtime call or kernel launch failed        */
 #define MLA_ERR_CAPTURE     -6  /* MLA_DEBUG checks asked for on a capturing stream  */
 
+/* Element types of the per-rank partial outputs (mla_decode_partial's out,
+ * the merges' outs).  bf16 is the default path; fp32 partials keep the merge's
+ * inputs unrounded, so a merged row carries one bf16 rounding instead of two
+ * (at twice the partials' bytes). */
+#define MLA_DTYPE_BF16 0
+#define MLA_DTYPE_F32  1
+
 /* Fixed head dimensions of the absorbed form. */
 #define MLA_D_LATENT 512   /* kv_lora_rank: c_kv, q_nope and output width */
 #define MLA_D_ROPE    64   /* qk_rope_head_dim: k_pe and q_pe width       */
@@ -99,7 +106,9 @@ const char* mla_status_string(mla_status status);
  *            never read (may be -1)
  *   seq_lens int32 [B]; query_start_loc int32 [B+1], query_start_loc[0] = 0,
  *            nondecreasing
- *   out      bf16 [T,H,512] contiguous;  lse fp32 [T,H] contiguous
+ *   out      [T,H,512] contiguous, bf16 (out_dtype = MLA_DTYPE_BF16, rounded
+ *            to nearest even) or fp32 (MLA_DTYPE_F32, the normalised fp32
+ *            accumulator);  lse fp32 [T,H] contiguous
  *
  * Host integers: max_query_len >= every Q_b and max_seq_len >= every S_b are
  * upper bounds that size the launch grid (nothing is read back from the
@@ -119,7 +128,8 @@ const char* mla_status_string(mla_status status);
  * Returns MLA_OK, or MLA_ERR_NULL / MLA_ERR_SHAPE (B<0, T<0, H outside
  * [1,128], page_size<1, cp_world<1, cp_rank outside [0,cp_world),
  * cp_interleave<1 or cp_world*cp_interleave > 2^30, strides
- * smaller than the data, scale not finite or not positive) / MLA_ERR_WORKSPACE /
+ * smaller than the data, scale not finite or not positive, out_dtype not one
+ * of the two) / MLA_ERR_WORKSPACE /
  * MLA_ERR_UNSUPPORTED / MLA_ERR_HIP.  B == 0 or T == 0 enqueues nothing and
  * returns MLA_OK (the grid is sized from host ints and may be empty).
  * Device-side contract: Q_b <= S_b <= max_seq_len, Q_b <= max_query_len,
@@ -142,7 +152,7 @@ mla_status mla_decode_partial(
     const int32_t* seq_lens, const int32_t* query_start_loc,
     int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
     int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, float scale, int32_t num_splits,
-    void* out, float* lse,
+    void* out, int32_t out_dtype, float* lse,
     void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
@@ -179,7 +189,8 @@ size_t mla_decode_workspace_size(int32_t B, int32_t T, int32_t H, int32_t max_qu
  * mla_lse_merge -- exact LSE-weighted merge of W per-rank partials
  * (PR #48196, _dcp_lse_merge, with per-row valid counts).
  *
- *   outs  bf16 [W,T,H,512] contiguous (rank r's partial at outs + r*T*H*512)
+ *   outs  [W,T,H,512] contiguous (rank r's partial at outs + r*T*H*512), of
+ *         element type outs_dtype (MLA_DTYPE_BF16 or MLA_DTYPE_F32)
  *   lses  fp32 [W,T,H] contiguous (natural-log LSE, -inf for empty rows)
  *   valid int32 [W,T] per-row key counts, or NULL.  Rank w takes part in row t
  *         iff valid[w*T+t] > 0 (with NULL: iff its lse is > -inf).  What a
@@ -189,10 +200,11 @@ size_t mla_decode_workspace_size(int32_t B, int32_t T, int32_t H, int32_t max_qu
  *   out   bf16 [T,H,512]:  out = sum_w exp(lse_w - LSE) * outs_w
  *   out_lse fp32 [T,H] or NULL:  LSE = ln sum_w exp(lse_w)
  * A row with no participating rank gets out = 0 and LSE = -inf.
- * Returns MLA_OK, MLA_ERR_NULL, MLA_ERR_SHAPE (W<1, T<0, H outside [1,128]),
- * MLA_ERR_UNSUPPORTED or MLA_ERR_HIP; T == 0 is a no-op.
+ * Returns MLA_OK, MLA_ERR_NULL, MLA_ERR_SHAPE (W<1, T<0, H outside [1,128],
+ * outs_dtype not one of the two), MLA_ERR_UNSUPPORTED or MLA_ERR_HIP; T == 0
+ * is a no-op.
  */
-mla_status mla_lse_merge(const void* outs, const float* lses, const int32_t* valid,
+mla_status mla_lse_merge(const void* outs, int32_t outs_dtype, const float* lses, const int32_t* valid,
                          int32_t W, int32_t T, int32_t H,
                          void* out, float* out_lse, void* hip_stream);
 
@@ -201,14 +213,14 @@ mla_status mla_lse_merge(const void* outs, const float* lses, const int32_t* val
  * (PR #48196, _dcp_merge_and_v_up_proj; exact because the merge is linear in
  * the partials and the projection is linear).
  *
- *   outs, lses, valid, W, T, H   as in mla_lse_merge
+ *   outs, outs_dtype, lses, valid, W, T, H   as in mla_lse_merge
  *   W_UV  bf16 [H,512,128] contiguous:  y[t,h,:] = merged_out[t,h,:] @ W_UV[h]
  *   out   bf16 [T,H,128] contiguous
  *   out_lse fp32 [T,H] or NULL
  * The merged latent row is rounded to bf16 before the projection (fp32
  * accumulation).  Returns as mla_lse_merge.
  */
-mla_status mla_merge_v_up_proj(const void* outs, const float* lses, const int32_t* valid,
+mla_status mla_merge_v_up_proj(const void* outs, int32_t outs_dtype, const float* lses, const int32_t* valid,
                                int32_t W, int32_t T, int32_t H, const void* W_UV,
                                void* out, float* out_lse, void* hip_stream);
 
@@ -218,7 +230,8 @@ mla_status mla_merge_v_up_proj(const void* outs, const float* lses, const int32_
  * all-to-all, and empty rows are handled in the pack from the valid counts).
  * Destination q owns the contiguous heads q*Hs .. q*Hs+Hs-1, Hs = H / cp_world.
  *
- *   out_r   bf16 [T,H,512] contiguous: this rank's partial (mla_decode_partial)
+ *   out_r   [T,H,512] contiguous: this rank's partial (mla_decode_partial), of
+ *           element type out_dtype (MLA_DTYPE_BF16 or MLA_DTYPE_F32)
  *   lse_r   fp32 [T,H]
  *   valid_r int32 [T] this rank's per-row counts, or NULL (then a row takes part
  *           iff its lse is > -inf).  A row that takes no part is sent as y = 0,
@@ -230,7 +243,7 @@ mla_status mla_merge_v_up_proj(const void* outs, const float* lses, const int32_
  * Requires H % cp_world == 0.  Returns MLA_OK, MLA_ERR_NULL, MLA_ERR_SHAPE,
  * MLA_ERR_UNSUPPORTED or MLA_ERR_HIP; T == 0 is a no-op.
  */
-mla_status mla_dcp_a2a_pack(const void* out_r, const float* lse_r, const int32_t* valid_r,
+mla_status mla_dcp_a2a_pack(const void* out_r, int32_t out_dtype, const float* lse_r, const int32_t* valid_r,
                             int32_t T, int32_t H, int32_t cp_world, const void* W_UV,
                             void* send_y, float* send_lse, void* hip_stream);
 

@@ -21,6 +21,7 @@ HEADER = os.path.join(INCLUDE, "mla.h")
 
 MLA_OK = 0
 D_LATENT, D_ROPE, D_ROW, D_V = 512, 64, 576, 128
+DTYPE_BF16, DTYPE_F32 = 0, 1          # MLA_DTYPE_BF16 / MLA_DTYPE_F32
 
 _lib = None
 
@@ -48,17 +49,17 @@ def load_library():
         _c_void_p, _i64, _i64, _c_void_p, _i64, _i64, _c_void_p, _i64, _i32,
         _c_void_p, _i32, _c_void_p, _c_void_p,
         _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
-        _c_void_p, _c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p]
+        _c_void_p, _i32, _c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p]
     lib.mla_decode_workspace_size.restype = ctypes.c_size_t
     lib.mla_decode_workspace_size.argtypes = [_i32] * 8
     lib.mla_lse_merge.restype = _i32
-    lib.mla_lse_merge.argtypes = [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
+    lib.mla_lse_merge.argtypes = [_c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i32, _i32,
                                   _c_void_p, _c_void_p, _c_void_p]
     lib.mla_merge_v_up_proj.restype = _i32
-    lib.mla_merge_v_up_proj.argtypes = [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
+    lib.mla_merge_v_up_proj.argtypes = [_c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i32, _i32,
                                         _c_void_p, _c_void_p, _c_void_p, _c_void_p]
     lib.mla_dcp_a2a_pack.restype = _i32
-    lib.mla_dcp_a2a_pack.argtypes = [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _c_void_p,
+    lib.mla_dcp_a2a_pack.argtypes = [_c_void_p, _i32, _c_void_p, _c_void_p, _i32, _i32, _i32, _c_void_p,
                                      _c_void_p, _c_void_p, _c_void_p]
     lib.mla_dcp_a2a_combine.restype = _i32
     lib.mla_dcp_a2a_combine.argtypes = [_c_void_p, _i64, _c_void_p, _i64, _i32, _i32, _i32,
@@ -113,6 +114,15 @@ def _need(t, dtype, name, dims=None):
         raise MlaError(f"{name}: expected {dims} dims, got shape {tuple(t.shape)}")
 
 
+def _partial_dtype(t, name):
+    """ABI code of a partial-output tensor's element type (bf16 or fp32)."""
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise MlaError(f"{name}: expected bfloat16 or float32 partials, got {t.dtype}")
+
+
 def workspace_size(B, T, H, max_query_len, max_seq_len, cp_world, num_splits=0, cp_interleave=1) -> int:
     n = load_library().mla_decode_workspace_size(B, T, H, max_query_len, max_seq_len, cp_world,
                                                  cp_interleave, num_splits)
@@ -124,7 +134,8 @@ def workspace_size(B, T, H, max_query_len, max_seq_len, cp_world, num_splits=0, 
 def mla_decode_partial(q_nope, q_pe, kv_cache, block_table, seq_lens, query_start_loc,
                        cp_world, cp_rank, scale, out, lse, *, max_query_len, max_seq_len,
                        workspace=None, num_splits=0, stream=None, cp_interleave=1):
-    """One DCP rank's partial attention; writes ``out`` [T,H,512] bf16 and ``lse`` [T,H] fp32.
+    """One DCP rank's partial attention; writes ``out`` [T,H,512] (bf16, or fp32
+    partials when ``out`` is a float32 tensor) and ``lse`` [T,H] fp32.
     ``cp_interleave``: tokens per run of the shard layout (1 = token p on rank p mod W)."""
     lib = load_library()
     _need(q_nope, torch.bfloat16, "q_nope", 3)
@@ -133,7 +144,8 @@ def mla_decode_partial(q_nope, q_pe, kv_cache, block_table, seq_lens, query_star
     _need(block_table, torch.int32, "block_table", 2)
     _need(seq_lens, torch.int32, "seq_lens", 1)
     _need(query_start_loc, torch.int32, "query_start_loc", 1)
-    _need(out, torch.bfloat16, "out", 3)
+    out_dtype = _partial_dtype(out, "out")
+    _need(out, out.dtype, "out", 3)
     _need(lse, torch.float32, "lse", 2)
     T, H, dn = q_nope.shape
     if dn != D_LATENT or tuple(q_pe.shape) != (T, H, D_ROPE):
@@ -166,14 +178,15 @@ def mla_decode_partial(q_nope, q_pe, kv_cache, block_table, seq_lens, query_star
         _ptr(seq_lens), _ptr(query_start_loc),
         B, T, H, int(max_query_len), int(max_seq_len), int(cp_world), int(cp_rank), int(cp_interleave),
         float(scale),
-        int(num_splits), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream))
+        int(num_splits), _ptr(out), out_dtype, _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "mla_decode_partial")
 
 
 def mla_lse_merge(outs, lses, valid, out, out_lse=None, stream=None):
-    """Merge W partials: outs [W,T,H,512] bf16, lses [W,T,H] fp32, valid [W,T] int32 or None."""
+    """Merge W partials: outs [W,T,H,512] bf16 or fp32, lses [W,T,H] fp32, valid [W,T] int32 or None."""
     lib = load_library()
-    _need(outs, torch.bfloat16, "outs", 4)
+    outs_dtype = _partial_dtype(outs, "outs")
+    _need(outs, outs.dtype, "outs", 4)
     _need(lses, torch.float32, "lses", 3)
     W, T, H, d = outs.shape
     if d != D_LATENT or tuple(lses.shape) != (W, T, H) or (T and not (outs.is_contiguous() and lses.is_contiguous())):
@@ -189,15 +202,16 @@ def mla_lse_merge(outs, lses, valid, out, out_lse=None, stream=None):
         _need(out_lse, torch.float32, "out_lse", 2)
         if tuple(out_lse.shape) != (T, H) or not out_lse.is_contiguous():
             raise MlaError("out_lse: expected contiguous [T,H]")
-    st = lib.mla_lse_merge(_ptr(outs), _ptr(lses), _ptr(valid), W, T, H, _ptr(out), _ptr(out_lse),
+    st = lib.mla_lse_merge(_ptr(outs), outs_dtype, _ptr(lses), _ptr(valid), W, T, H, _ptr(out), _ptr(out_lse),
                            _stream(stream))
     _check(st, "mla_lse_merge")
 
 
 def mla_merge_v_up_proj(outs, lses, valid, W_UV, out, out_lse=None, stream=None):
-    """Merge W partials and project by W_UV [H,512,128]: out [T,H,128] bf16."""
+    """Merge W partials (bf16 or fp32) and project by W_UV [H,512,128]: out [T,H,128] bf16."""
     lib = load_library()
-    _need(outs, torch.bfloat16, "outs", 4)
+    outs_dtype = _partial_dtype(outs, "outs")
+    _need(outs, outs.dtype, "outs", 4)
     _need(lses, torch.float32, "lses", 3)
     _need(W_UV, torch.bfloat16, "W_UV", 3)
     W, T, H, d = outs.shape
@@ -216,7 +230,7 @@ def mla_merge_v_up_proj(outs, lses, valid, W_UV, out, out_lse=None, stream=None)
         _need(out_lse, torch.float32, "out_lse", 2)
         if tuple(out_lse.shape) != (T, H) or not out_lse.is_contiguous():
             raise MlaError("out_lse: expected contiguous [T,H]")
-    st = lib.mla_merge_v_up_proj(_ptr(outs), _ptr(lses), _ptr(valid), W, T, H, _ptr(W_UV), _ptr(out),
+    st = lib.mla_merge_v_up_proj(_ptr(outs), outs_dtype, _ptr(lses), _ptr(valid), W, T, H, _ptr(W_UV), _ptr(out),
                                  _ptr(out_lse), _stream(stream))
     _check(st, "mla_merge_v_up_proj")
 
@@ -224,7 +238,8 @@ def mla_merge_v_up_proj(outs, lses, valid, W_UV, out, out_lse=None, stream=None)
 def mla_dcp_a2a_pack(out_r, lse_r, valid_r, W_UV, send_y, send_lse, cp_world, stream=None):
     """Rank r's projected send buffers: send_y [W,T,H/W,128] bf16, send_lse [W,T,H/W] fp32."""
     lib = load_library()
-    _need(out_r, torch.bfloat16, "out_r", 3)
+    out_dtype = _partial_dtype(out_r, "out_r")
+    _need(out_r, out_r.dtype, "out_r", 3)
     _need(lse_r, torch.float32, "lse_r", 2)
     _need(W_UV, torch.bfloat16, "W_UV", 3)
     _need(send_y, torch.bfloat16, "send_y", 4)
@@ -242,7 +257,7 @@ def mla_dcp_a2a_pack(out_r, lse_r, valid_r, W_UV, send_y, send_lse, cp_world, st
         _need(valid_r, torch.int32, "valid_r", 1)
         if valid_r.shape[0] != T or not valid_r.is_contiguous():
             raise MlaError("valid_r: expected contiguous [T]")
-    st = lib.mla_dcp_a2a_pack(_ptr(out_r), _ptr(lse_r), _ptr(valid_r), T, H, W, _ptr(W_UV), _ptr(send_y),
+    st = lib.mla_dcp_a2a_pack(_ptr(out_r), out_dtype, _ptr(lse_r), _ptr(valid_r), T, H, W, _ptr(W_UV), _ptr(send_y),
                               _ptr(send_lse), _stream(stream))
     _check(st, "mla_dcp_a2a_pack")
 

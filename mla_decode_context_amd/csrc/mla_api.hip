@@ -153,6 +153,7 @@ size_t workspace_bytes_for(const Plan& p, int T, int H) {
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+bool dtype_ok(int32_t d) { return d == MLA_DTYPE_BF16 || d == MLA_DTYPE_F32; }
 
 mla_status fail(char* reason, size_t len, const char* fmt, ...) {
   if (reason && len > 0) {
@@ -261,11 +262,11 @@ mla_status mla_decode_partial(
     const int32_t* seq_lens, const int32_t* query_start_loc,
     int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
     int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, float scale, int32_t num_splits,
-    void* out, float* lse,
+    void* out, int32_t out_dtype, float* lse,
     void* workspace, size_t workspace_bytes, void* hip_stream) {
   if (B < 0 || T < 0 || H < 1 || H > MLA_MAX_HEADS || page_size < 1 || !layout_ok(cp_world, cp_interleave) ||
       cp_rank < 0 || cp_rank >= cp_world || max_query_len < 0 || max_seq_len < 0 ||
-      num_splits < 0 || !isfinite(scale) || !(scale > 0.f))
+      num_splits < 0 || !isfinite(scale) || !(scale > 0.f) || !dtype_ok(out_dtype))
     return MLA_ERR_SHAPE;
   if (B == 0 && T > 0) return MLA_ERR_SHAPE;   // tokens without requests
   if (B == 0 || T == 0) return MLA_OK;
@@ -320,7 +321,9 @@ mla_status mla_decode_partial(
   p.B = B; p.T = T; p.H = H; p.W = cp_world; p.r = cp_rank; p.I = cp_interleave;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   p.chunk = plan.chunk; p.hblocks = plan.hblocks; p.max_splits = plan.max_splits;
-  p.out = (uint16_t*)out; p.lse = lse;
+  p.out = out_dtype == MLA_DTYPE_BF16 ? (uint16_t*)out : nullptr;
+  p.out_f = out_dtype == MLA_DTYPE_F32 ? (float*)out : nullptr;
+  p.lse = lse;
   p.ws_o = nullptr; p.ws_lse = nullptr; p.counters = nullptr; p.row_desc = nullptr; p.item_map = nullptr;
   char* ws_base = (char*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
   if (plan.ordered) p.item_map = (int32_t*)ws_base;
@@ -338,17 +341,19 @@ mla_status mla_decode_partial(
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
-static mla_status merge_common(const void* outs, const float* lses, const int32_t* valid, int32_t W,
-                               int32_t T, int32_t H, const void* W_UV, bool proj, void* out,
+static mla_status merge_common(const void* outs, int32_t outs_dtype, const float* lses, const int32_t* valid,
+                               int32_t W, int32_t T, int32_t H, const void* W_UV, bool proj, void* out,
                                float* out_lse, void* hip_stream) {
-  if (W < 1 || T < 0 || H < 1 || H > MLA_MAX_HEADS) return MLA_ERR_SHAPE;
+  if (W < 1 || T < 0 || H < 1 || H > MLA_MAX_HEADS || !dtype_ok(outs_dtype)) return MLA_ERR_SHAPE;
   if (T == 0) return MLA_OK;
   if (!outs || !lses || !out || (proj && !W_UV)) return MLA_ERR_NULL;
   if (!aligned(outs, 16) || !aligned(out, 16) || (proj && !aligned(W_UV, 16))) return MLA_ERR_SHAPE;
   mla_status st = check_device();
   if (st != MLA_OK) return st;
   mla::MergeParams p;
-  p.outs = (const uint16_t*)outs; p.lses = lses; p.valid = valid;
+  p.outs = outs_dtype == MLA_DTYPE_BF16 ? (const uint16_t*)outs : nullptr;
+  p.outs_f = outs_dtype == MLA_DTYPE_F32 ? (const float*)outs : nullptr;
+  p.lses = lses; p.valid = valid;
   p.W = W; p.T = T; p.H = H;
   p.wuv = (const uint16_t*)W_UV; p.out = (uint16_t*)out; p.out_lse = out_lse; p.hs = H;
   hipError_t e = proj ? mla::launch_merge_v_up(p, (hipStream_t)hip_stream)
@@ -356,22 +361,23 @@ static mla_status merge_common(const void* outs, const float* lses, const int32_
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
-mla_status mla_lse_merge(const void* outs, const float* lses, const int32_t* valid,
+mla_status mla_lse_merge(const void* outs, int32_t outs_dtype, const float* lses, const int32_t* valid,
                          int32_t W, int32_t T, int32_t H,
                          void* out, float* out_lse, void* hip_stream) {
-  return merge_common(outs, lses, valid, W, T, H, nullptr, false, out, out_lse, hip_stream);
+  return merge_common(outs, outs_dtype, lses, valid, W, T, H, nullptr, false, out, out_lse, hip_stream);
 }
 
-mla_status mla_merge_v_up_proj(const void* outs, const float* lses, const int32_t* valid,
+mla_status mla_merge_v_up_proj(const void* outs, int32_t outs_dtype, const float* lses, const int32_t* valid,
                                int32_t W, int32_t T, int32_t H, const void* W_UV,
                                void* out, float* out_lse, void* hip_stream) {
-  return merge_common(outs, lses, valid, W, T, H, W_UV, true, out, out_lse, hip_stream);
+  return merge_common(outs, outs_dtype, lses, valid, W, T, H, W_UV, true, out, out_lse, hip_stream);
 }
 
-mla_status mla_dcp_a2a_pack(const void* out_r, const float* lse_r, const int32_t* valid_r,
+mla_status mla_dcp_a2a_pack(const void* out_r, int32_t out_dtype, const float* lse_r, const int32_t* valid_r,
                             int32_t T, int32_t H, int32_t cp_world, const void* W_UV,
                             void* send_y, float* send_lse, void* hip_stream) {
-  if (T < 0 || H < 1 || H > MLA_MAX_HEADS || cp_world < 1 || H % cp_world != 0) return MLA_ERR_SHAPE;
+  if (T < 0 || H < 1 || H > MLA_MAX_HEADS || cp_world < 1 || H % cp_world != 0 || !dtype_ok(out_dtype))
+    return MLA_ERR_SHAPE;
   if (T == 0) return MLA_OK;
   if (!out_r || !lse_r || !W_UV || !send_y || !send_lse) return MLA_ERR_NULL;
   if (!aligned(out_r, 16) || !aligned(send_y, 16) || !aligned(W_UV, 16)) return MLA_ERR_SHAPE;
@@ -380,7 +386,9 @@ mla_status mla_dcp_a2a_pack(const void* out_r, const float* lse_r, const int32_t
   // The fused merge + projection over one partial (its merge is the identity),
   // writing head h into destination slice h / (H / cp_world).
   mla::MergeParams p;
-  p.outs = (const uint16_t*)out_r; p.lses = lse_r; p.valid = valid_r;
+  p.outs = out_dtype == MLA_DTYPE_BF16 ? (const uint16_t*)out_r : nullptr;
+  p.outs_f = out_dtype == MLA_DTYPE_F32 ? (const float*)out_r : nullptr;
+  p.lses = lse_r; p.valid = valid_r;
   p.W = 1; p.T = T; p.H = H;
   p.wuv = (const uint16_t*)W_UV; p.out = (uint16_t*)send_y; p.out_lse = send_lse; p.hs = H / cp_world;
   return mla::launch_merge_v_up(p, (hipStream_t)hip_stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;

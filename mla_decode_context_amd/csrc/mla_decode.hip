@@ -100,13 +100,8 @@ __device__ __forceinline__ void ticket_and_merge(const DecodeParams& a, int t, i
       const float inv = ssum > 0.f ? 1.f / ssum : 0.f;
       const float lse_tot = ssum > 0.f ? m + fast_log2(ssum) * kLn2 : -INFINITY;
       const size_t row = (size_t)t * a.H + h;
-      uint16_t* op = a.out + row * kLatent + d0;
 #pragma unroll
-      for (int k = 0; k < 8; k += 2)
-        *(u32x4*)(op + 4 * k) = u32x4{pack_bf16x2(acc[k][0] * inv, acc[k][1] * inv),
-                                      pack_bf16x2(acc[k][2] * inv, acc[k][3] * inv),
-                                      pack_bf16x2(acc[k + 1][0] * inv, acc[k + 1][1] * inv),
-                                      pack_bf16x2(acc[k + 1][2] * inv, acc[k + 1][3] * inv)};
+      for (int k = 0; k < 8; k += 2) store_out8(a, row, d0 + 4 * k, acc[k] * inv, acc[k + 1] * inv);
       if ((threadIdx.x & 15) == 0) a.lse[row] = lse_tot;
     }
   }
@@ -143,7 +138,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams a) {
       const int h = h0 + (idx >> 6);
       const int c = idx & 63;
       if (h < a.H) {
-        *(u32x4*)(a.out + ((size_t)t * a.H + h) * kLatent + c * 8) = u32x4{0u, 0u, 0u, 0u};
+        zero_out8(a, (size_t)t * a.H + h, c * 8);
         if (c == 0) a.lse[(size_t)t * a.H + h] = -INFINITY;
       }
     }
@@ -371,12 +366,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams a) {
     const float inv = 1.f / lt;
     const float lse_v = (m_run[mu] + fast_log2(lt)) * kLn2;
     if (nsplit == 1) {
-      uint16_t* op = a.out + ((size_t)t * a.H + h) * kLatent + kSlab * w + 4 * g;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const f32x4 x = o[dt][mu] * inv;
-        *(u32x2*)(op + 16 * dt) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-      }
+      for (int dt = 0; dt < 8; ++dt) store_out4(a, (size_t)t * a.H + h, kSlab * w + 4 * g + 16 * dt, o[dt][mu] * inv);
       if (w == 0 && g == 0) a.lse[(size_t)t * a.H + h] = lse_v;
     } else {
       float* wp = a.ws_o + (((size_t)split * a.T + t) * a.H + h) * kLatent + kSlab * w + 4 * g;
@@ -432,7 +423,7 @@ __device__ __forceinline__ void write_empty_row(const DecodeParams& a, int t) {
     const int h = idx >> 6;
     const int c = idx & 63;
     if (h < a.H) {
-      *(u32x4*)(a.out + ((size_t)t * a.H + h) * kLatent + c * 8) = u32x4{0u, 0u, 0u, 0u};
+      zero_out8(a, (size_t)t * a.H + h, c * 8);
       if (c == 0) a.lse[(size_t)t * a.H + h] = -INFINITY;
     }
   }
@@ -676,8 +667,7 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
         x *= inv;
         const int d = 16 * dt + 4 * g;     // lane holds dims d .. d+3 of head h
         if (nsplit == 1) {
-          *(u32x2*)(a.out + ((size_t)t * a.H + h) * kLatent + d) =
-              u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+          store_out4(a, (size_t)t * a.H + h, d, x);
         } else if (kDeferMerge) {
           // read by the combine kernel after this launch: plain stores
           *(f32x4*)(a.ws_o + (my_slot * a.H + h) * kLatent + d) = x;
@@ -906,9 +896,7 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const DecodeParams a
   }
   const float inv = ssum > 0.f ? 1.f / ssum : 0.f;
   const size_t row = (size_t)t * a.H + h;
-  *(u32x4*)(a.out + row * kLatent + d0) =
-      u32x4{pack_bf16x2(acc0[0] * inv, acc0[1] * inv), pack_bf16x2(acc0[2] * inv, acc0[3] * inv),
-            pack_bf16x2(acc1[0] * inv, acc1[1] * inv), pack_bf16x2(acc1[2] * inv, acc1[3] * inv)};
+  store_out8(a, row, d0, acc0 * inv, acc1 * inv);
   if (blockIdx.y == 0 && (threadIdx.x & 15) == 0)
     a.lse[row] = ssum > 0.f ? m + fast_log2(ssum) * kLn2 : -INFINITY;
 }

@@ -128,7 +128,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
     // The row sees no key on this rank: out = 0, lse = -inf (wave w: heads 8w..).
     for (int idx = lane; idx < 8 * 64; idx += 64) {
       const int h = h0 + 8 * w + (idx >> 6);
-      *(u32x4*)(a.out + ((size_t)t * a.H + h) * kLatent + 8 * (idx & 63)) = u32x4{0u, 0u, 0u, 0u};
+      zero_out8(a, (size_t)t * a.H + h, 8 * (idx & 63));
       if ((idx & 63) == 0) a.lse[(size_t)t * a.H + h] = -INFINITY;
     }
     return;
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
     const int hl = 32 * j + (lane & 31);
     const float inv = 1.f / (l_lds[hl] + l_lds[kXHeads + hl]);
     const int h = h0 + hl;
-    if (nsplit == 1) {
+    if (nsplit == 1 && !a.out_f) {
       // bf16 row of head hl, this wave's 128 dims, into the (now idle) ring.
       uint8_t* st = ring + pw * (kXHeads * kORow) + hl * kORow + 8 * hh;
 #pragma unroll
@@ -443,8 +443,10 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
               u32x2{pack_bf16x2(o[dt][j][4 * qd] * inv, o[dt][j][4 * qd + 1] * inv),
                     pack_bf16x2(o[dt][j][4 * qd + 2] * inv, o[dt][j][4 * qd + 3] * inv)};
     } else {
-      // Partial of split `split`, read by the combine kernel after this launch.
-      float* wp = a.ws_o + (((size_t)split * a.T + t) * a.H + h) * kLatent + 128 * pw + 4 * hh;
+      // fp32: the row itself (fp32 partials asked for), or the partial of
+      // split `split`, read by the combine kernel after this launch.
+      float* wp = (nsplit == 1 ? a.out_f + ((size_t)t * a.H + h) * kLatent
+                               : a.ws_o + (((size_t)split * a.T + t) * a.H + h) * kLatent) + 128 * pw + 4 * hh;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -453,7 +455,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
                                                    o[dt][j][4 * qd + 2] * inv, o[dt][j][4 * qd + 3] * inv};
     }
   }
-  if (nsplit == 1) {
+  if (nsplit == 1 && !a.out_f) {
     // Each wave reads back its own rows (its LDS writes are complete after the
     // wait) and stores them 256 contiguous bytes per head: lane l takes 16 bytes
     // l % 16 of head 4i + l / 16.
@@ -508,9 +510,7 @@ __global__ __launch_bounds__(256) void combine_fixed_kernel(const DecodeParams a
   }
   const float inv = ssum > 0.f ? 1.f / ssum : 0.f;
   const size_t row = (size_t)t * a.H + h;
-  *(u32x4*)(a.out + row * kLatent + d0) =
-      u32x4{pack_bf16x2(acc0[0] * inv, acc0[1] * inv), pack_bf16x2(acc0[2] * inv, acc0[3] * inv),
-            pack_bf16x2(acc1[0] * inv, acc1[1] * inv), pack_bf16x2(acc1[2] * inv, acc1[3] * inv)};
+  store_out8(a, row, d0, acc0 * inv, acc1 * inv);
   if (blockIdx.y == 0 && (threadIdx.x & 15) == 0)
     a.lse[row] = ssum > 0.f ? m + fast_log2(ssum) * kLn2 : -INFINITY;
 }

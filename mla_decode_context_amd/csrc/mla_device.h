@@ -128,6 +128,28 @@ __device__ __forceinline__ void dma_16B_to_lds_sbase(uint32_t lds_off, uint32_t 
                  : "memory");
 }
 
+// Output stores of the decode kernels: dims d .. d+3 (or d+7) of output row
+// `row` (= t*H + h), as bf16 (round to nearest even) or, when the caller asked
+// for fp32 partials, as fp32.  The branch is uniform (a kernel argument).
+__device__ __forceinline__ void store_out4(const DecodeParams& a, size_t row, int d, f32x4 x) {
+  if (a.out_f)
+    *(f32x4*)(a.out_f + row * kLatent + d) = x;
+  else
+    *(u32x2*)(a.out + row * kLatent + d) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+}
+__device__ __forceinline__ void store_out8(const DecodeParams& a, size_t row, int d, f32x4 x, f32x4 y) {
+  if (a.out_f) {
+    *(f32x4*)(a.out_f + row * kLatent + d) = x;
+    *(f32x4*)(a.out_f + row * kLatent + d + 4) = y;
+  } else {
+    *(u32x4*)(a.out + row * kLatent + d) = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                                 pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+  }
+}
+__device__ __forceinline__ void zero_out8(const DecodeParams& a, size_t row, int d) {
+  store_out8(a, row, d, f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f});
+}
+
 // max / sum over the four lanes l, l^16, l^32, l^48 (one MFMA column) with the
 // gfx950 lane-swap instructions (VALU, no LDS round trip).
 __device__ __forceinline__ float col_max(float x) {

@@ -21,7 +21,8 @@ struct DecodeParams {
   int32_t chunk;           // keys per split (multiple of the 32-key step)
   int32_t hblocks;         // head blocks per query token
   int32_t max_splits;      // grid extent along splits
-  uint16_t* out;           // bf16 [T,H,512]
+  uint16_t* out;           // bf16 [T,H,512] (when out_f is null)
+  float* out_f;            // fp32 [T,H,512] partials instead of bf16, or null
   float* lse;              // fp32 [T,H]
   float* ws_o;             // fp32 [slots,H,512] split partials (normalised)
   float* ws_lse;           // fp32 [slots,H]
@@ -31,7 +32,8 @@ struct DecodeParams {
 };
 
 struct MergeParams {
-  const uint16_t* outs;    // bf16 [W,T,H,512]
+  const uint16_t* outs;    // bf16 [W,T,H,512] (when outs_f is null)
+  const float* outs_f;     // fp32 [W,T,H,512] partials instead, or null
   const float* lses;       // fp32 [W,T,H]
   const int32_t* valid;    // int32 [W,T] or null
   int32_t W, T, H;

@@ -27,13 +27,42 @@ namespace mla {
 // an offset past the buffer's range, which reads zero (or writes nothing)
 // without touching memory, so the compiler's waits for the loads stay exact.
 // R = 4 when W <= 8 (fewer registers, more workgroups per CU; ranks 5..8 are a
-// second item of the same token), else 8.
+// second item of the same token), else 8; with fp32 partials (kF32: twice the
+// bytes per rank) half as many, so an item holds the same bytes.
 constexpr int kMergeHeads = 8;
 constexpr int kBufFlags = 0x00020000;              // buffer resource word 3 (raw 32-bit data)
 constexpr uint32_t kOffNone = 0x40000000u;         // past every buffer range used here
 
-template <int R, bool kValid>
+// 16 partial values of one rank as loaded (bf16: two 16-byte words; fp32:
+// four), as four fp32 vectors.
+template <bool kF32>
+__device__ __forceinline__ void unpack16(const u32x4* x, f32x4 (&v)[4]) {
+  if constexpr (kF32) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = __builtin_bit_cast(f32x4, x[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      v[2 * k] = f32x4{bf16_lo(x[k][0]), bf16_hi(x[k][0]), bf16_lo(x[k][1]), bf16_hi(x[k][1])};
+      v[2 * k + 1] = f32x4{bf16_lo(x[k][2]), bf16_hi(x[k][2]), bf16_lo(x[k][3]), bf16_hi(x[k][3])};
+    }
+  }
+}
+
+// acc = acc * c_old + x * c_new over the 16 values.
+template <bool kF32>
+__device__ __forceinline__ void axpy16(f32x4 (&acc)[4], float c_old, const u32x4* x, float c_new) {
+  f32x4 v[4];
+  unpack16<kF32>(x, v);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) acc[k] = acc[k] * c_old + v[k] * c_new;
+}
+
+template <int R, bool kValid, bool kF32>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams a) {
+  constexpr int kWords = kF32 ? 4 : 2;               // 16-byte loads per 16 values
+  constexpr int kElem = kF32 ? 4 : 2;                // bytes per partial value
+  const uint8_t* outs = kF32 ? (const uint8_t*)a.outs_f : (const uint8_t*)a.outs;
   const int hl = threadIdx.x >> 5;
   const int h0 = kMergeHeads * (int)blockIdx.x;
   const bool hok = h0 + hl < a.H;
@@ -46,7 +75,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams a) {
   const int ngroups = (a.W + R - 1) / R;
   const int nitems = (t_end - t_begin) * ngroups;
   struct Pend {
-    u32x4 x[R][2];
+    u32x4 x[R][kWords];
     float l[R];
     int part;          // bit u: rank w0 + u was read
   };
@@ -68,14 +97,14 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams a) {
     for (int u = 0; u < R; ++u) {
       const size_t row0 = min(w0 + u, a.W - 1) * plane + (size_t)t * a.H + h0;   // the item's first head
       const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(a.outs + row0 * kLatent), (short)0, kMergeHeads * kLatent * 2, kBufFlags);
+          (void*)(outs + row0 * kLatent * kElem), (short)0, kMergeHeads * kLatent * kElem, kBufFlags);
       const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(a.lses + row0), (short)0, kMergeHeads * 4, kBufFlags);
-      const uint32_t oo = vv[u] ? (uint32_t)(hl * kLatent * 2 + 2 * d0) : kOffNone;
+      const uint32_t oo = vv[u] ? (uint32_t)(hl * kLatent * kElem + kElem * d0) : kOffNone;
       const uint32_t ol = vv[u] ? (uint32_t)(hl * 4) : kOffNone;
       p.l[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, ol, 0, 0));
-      p.x[u][0] = __builtin_amdgcn_raw_buffer_load_b128(ro, oo, 0, 0);
-      p.x[u][1] = __builtin_amdgcn_raw_buffer_load_b128(ro, oo + 16, 0, 0);
+#pragma unroll
+      for (int k = 0; k < kWords; ++k) p.x[u][k] = __builtin_amdgcn_raw_buffer_load_b128(ro, oo + 16 * k, 0, 0);
       p.part |= vv[u] << u;
     }
   };
@@ -96,13 +125,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams a) {
       if (lu > -INFINITY && mn > -INFINITY) {
         const float c_old = m == -INFINITY ? 0.f : fast_exp2((m - mn) * kLog2e);
         const float c_new = fast_exp2((lu - mn) * kLog2e);
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          acc[2 * k] = acc[2 * k] * c_old + f32x4{bf16_lo(cur.x[u][k][0]), bf16_hi(cur.x[u][k][0]),
-                                                  bf16_lo(cur.x[u][k][1]), bf16_hi(cur.x[u][k][1])} * c_new;
-          acc[2 * k + 1] = acc[2 * k + 1] * c_old + f32x4{bf16_lo(cur.x[u][k][2]), bf16_hi(cur.x[u][k][2]),
-                                                          bf16_lo(cur.x[u][k][3]), bf16_hi(cur.x[u][k][3])} * c_new;
-        }
+        axpy16<kF32>(acc, c_old, cur.x[u], c_new);
         ssum = ssum * c_old + c_new;
         m = mn;
       }
@@ -171,11 +194,16 @@ constexpr int kProjBlk = 16;                       // tokens per block
 constexpr int kProjThreads = 512;
 constexpr int kWBytes = kLatent * kVHead * 2;      // 128 KiB
 
-// kOne (W = 1): the merge is the identity, and an item's four slots are four
-// consecutive token blocks of the one partial instead of four ranks of one
-// block, so that four times the bytes are in flight per item.
-template <bool kValid, bool kOne>
+// kOne (W = 1): the merge is the identity, and an item's slots are
+// consecutive token blocks of the one partial instead of ranks of one block,
+// so that several times the bytes are in flight per item.  An item has four
+// slots with bf16 partials and two with fp32 partials (kF32: the same bytes).
+template <bool kValid, bool kOne, bool kF32>
 __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const MergeParams a) {
+  constexpr int kSlots = kF32 ? 2 : 4;
+  constexpr int kWords = kF32 ? 4 : 2;               // 16-byte loads per 16 values
+  constexpr int kElem = kF32 ? 4 : 2;                // bytes per partial value
+  const uint8_t* outs = kF32 ? (const uint8_t*)a.outs_f : (const uint8_t*)a.outs;
   __shared__ __attribute__((aligned(16))) uint8_t w_lds[kWBytes];
   // Merged rows of a block, two buffers in turn (W_UV and both fill the 160 KiB).
   __shared__ __attribute__((aligned(16))) uint8_t o_buf[2][kProjBlk * kLatent * 2];
@@ -210,29 +238,29 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
   const int lr = lane & 15;
   const int g = lane >> 4;
 
-  // The thread's work is a sequence of items (block b, ranks w0 .. w0+3) with
-  // w0 = 4j, j < ngroups.
-  const int ngroups = kOne ? 1 : (a.W + 3) >> 2;
+  // The thread's work is a sequence of items (block b, ranks w0 .. w0+kSlots-1)
+  // with w0 = kSlots * j, j < ngroups.
+  const int ngroups = kOne ? 1 : (a.W + kSlots - 1) / kSlots;
   const int nblocks = (t_end - t_begin + kProjBlk - 1) / kProjBlk;
-  const int nitems = kOne ? (nblocks + 3) / 4 : nblocks * ngroups;
+  const int nitems = kOne ? (nblocks + kSlots - 1) / kSlots : nblocks * ngroups;
   auto item_tb = [&](int i) { return t_begin + (i / ngroups) * kProjBlk; };
-  auto item_w0 = [&](int i) { return 4 * (i % ngroups); };
+  auto item_w0 = [&](int i) { return kSlots * (i % ngroups); };
   // Slot u of item i: its first token, its rank and whether it exists.
-  auto slot_tb = [&](int i, int u) { return kOne ? t_begin + (4 * i + u) * kProjBlk : item_tb(i); };
+  auto slot_tb = [&](int i, int u) { return kOne ? t_begin + (kSlots * i + u) * kProjBlk : item_tb(i); };
   auto slot_w = [&](int i, int u) { return kOne ? 0 : min(item_w0(i) + u, a.W - 1); };
   auto slot_ok = [&](int i, int u) { return kOne ? slot_tb(i, u) < t_end : item_w0(i) + u < a.W; };
   struct Pend {
-    u32x4 x[4][2];
-    float l[4];
+    u32x4 x[kSlots][kWords];
+    float l[kSlots];
     int part;          // bit u: rank w0 + u was read for this lane
   };
-  // Participation of ranks w0 .. w0+3 for the thread's token.  With counts, the
+  // Participation of the item's ranks for the thread's token.  With counts, the
   // counts of the wave's two tokens come through scalar loads and ranks that do
   // not take part are not read; without counts every rank's row is read and
   // its LSE decides.
-  auto load_valid = [&](int i, int (&vv)[4]) {
+  auto load_valid = [&](int i, int (&vv)[kSlots]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kSlots; ++u) {
       const int tb = slot_tb(i, u);
       const int t = tb + tt;
       const int w = slot_w(i, u);
@@ -252,22 +280,22 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
   // takes part: buffer loads whose offset lies past the buffer's range return
   // zero without touching memory.  So the number of loads in flight never
   // depends on the data and the compiler's waits stay exact.
-  auto load_data = [&](int i, const int (&vv)[4], Pend& p) {
+  auto load_data = [&](int i, const int (&vv)[kSlots], Pend& p) {
     p.part = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kSlots; ++u) {
       const int tb = min(slot_tb(i, u), a.T - 1);
       const int w = slot_w(i, u);
       const size_t row0 = w * plane + (size_t)tb * a.H + h;     // the block's first token
-      const __amdgpu_buffer_rsrc_t ro =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(a.outs + row0 * kLatent), (short)0, kProjBlk * a.H * 1024, kBufFlags);
+      const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(outs + row0 * kLatent * kElem), (short)0, kProjBlk * a.H * kLatent * kElem, kBufFlags);
       const __amdgpu_buffer_rsrc_t rl =
           __builtin_amdgcn_make_buffer_rsrc((void*)(a.lses + row0), (short)0, kProjBlk * a.H * 4, kBufFlags);
-      const uint32_t oo = vv[u] ? (uint32_t)(tt * a.H * 1024 + 2 * d0) : kOffNone;
+      const uint32_t oo = vv[u] ? (uint32_t)(tt * a.H * kLatent * kElem + kElem * d0) : kOffNone;
       const uint32_t ol = vv[u] ? (uint32_t)(tt * a.H * 4) : kOffNone;
       p.l[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, ol, 0, 0));
-      p.x[u][0] = __builtin_amdgcn_raw_buffer_load_b128(ro, oo, 0, 0);
-      p.x[u][1] = __builtin_amdgcn_raw_buffer_load_b128(ro, oo + 16, 0, 0);
+#pragma unroll
+      for (int k = 0; k < kWords; ++k) p.x[u][k] = __builtin_amdgcn_raw_buffer_load_b128(ro, oo + 16 * k, 0, 0);
       p.part |= vv[u] << u;
     }
   };
@@ -347,19 +375,16 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
       // Each slot is a block of its own; the one partial is its merged row
       // (weight exp(lse - lse) = 1), or zero with LSE -inf if it takes no part.
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kSlots; ++u) {
         const int tb = slot_tb(i, u);
         if (tb >= t_end) break;                       // uniform: depends on i and u only
         const bool in = ((cur.part >> u) & 1) && cur.l[u] > -INFINITY;
         m = in ? cur.l[u] : -INFINITY;
         ssum = in ? 1.f : 0.f;
+        f32x4 v[4];
+        unpack16<kF32>(cur.x[u], v);
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          acc[2 * k] = in ? f32x4{bf16_lo(cur.x[u][k][0]), bf16_hi(cur.x[u][k][0]),
-                                  bf16_lo(cur.x[u][k][1]), bf16_hi(cur.x[u][k][1])} : f32x4{0.f, 0.f, 0.f, 0.f};
-          acc[2 * k + 1] = in ? f32x4{bf16_lo(cur.x[u][k][2]), bf16_hi(cur.x[u][k][2]),
-                                      bf16_lo(cur.x[u][k][3]), bf16_hi(cur.x[u][k][3])} : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int k = 0; k < 4; ++k) acc[k] = in ? v[k] : f32x4{0.f, 0.f, 0.f, 0.f};
         emit(tb);
       }
       return;
@@ -371,19 +396,13 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
         for (int k = 0; k < 4; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kSlots; ++u) {
         const float lu = (cur.part >> u) & 1 ? cur.l[u] : -INFINITY;
         const float mn = fmaxf(m, lu);
         if (lu > -INFINITY && mn > -INFINITY) {
           const float c_old = m == -INFINITY ? 0.f : fast_exp2((m - mn) * kLog2e);
           const float c_new = fast_exp2((lu - mn) * kLog2e);
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            acc[2 * k] = acc[2 * k] * c_old + f32x4{bf16_lo(cur.x[u][k][0]), bf16_hi(cur.x[u][k][0]),
-                                                    bf16_lo(cur.x[u][k][1]), bf16_hi(cur.x[u][k][1])} * c_new;
-            acc[2 * k + 1] = acc[2 * k + 1] * c_old + f32x4{bf16_lo(cur.x[u][k][2]), bf16_hi(cur.x[u][k][2]),
-                                                            bf16_lo(cur.x[u][k][3]), bf16_hi(cur.x[u][k][3])} * c_new;
-          }
+          axpy16<kF32>(acc, c_old, cur.x[u], c_new);
           ssum = ssum * c_old + c_new;
           m = mn;
         }
@@ -397,7 +416,7 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
   // items i + 1 and i + 2 are in flight (and the counts of item i + 3).  The
   // buffers are never copied (a copy would wait for its loads).
   Pend b0, b1, b2;
-  int vv[4];
+  int vv[kSlots];
   load_valid(0, vv);
   load_data(0, vv, b0);
   load_valid(1, vv);
@@ -427,12 +446,23 @@ hipError_t launch_lse_merge(const MergeParams& p, hipStream_t stream) {
   const int want = (256 + hblocks - 1) / hblocks;
   if (ranges < want) ranges = want < (p.T + 3) / 4 ? want : (p.T + 3) / 4;
   const dim3 grid((unsigned)hblocks, (unsigned)ranges);
+  const bool f32 = p.outs_f != nullptr;
   if (p.W <= 8) {
-    if (p.valid) hipLaunchKernelGGL((lse_merge_kernel<4, true>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((lse_merge_kernel<4, false>), grid, dim3(256), 0, stream, p);
+    if (f32) {
+      if (p.valid) hipLaunchKernelGGL((lse_merge_kernel<2, true, true>), grid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((lse_merge_kernel<2, false, true>), grid, dim3(256), 0, stream, p);
+    } else {
+      if (p.valid) hipLaunchKernelGGL((lse_merge_kernel<4, true, false>), grid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((lse_merge_kernel<4, false, false>), grid, dim3(256), 0, stream, p);
+    }
   } else {
-    if (p.valid) hipLaunchKernelGGL((lse_merge_kernel<8, true>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((lse_merge_kernel<8, false>), grid, dim3(256), 0, stream, p);
+    if (f32) {
+      if (p.valid) hipLaunchKernelGGL((lse_merge_kernel<4, true, true>), grid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((lse_merge_kernel<4, false, true>), grid, dim3(256), 0, stream, p);
+    } else {
+      if (p.valid) hipLaunchKernelGGL((lse_merge_kernel<8, true, false>), grid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((lse_merge_kernel<8, false, false>), grid, dim3(256), 0, stream, p);
+    }
   }
   return hipGetLastError();
 }
@@ -444,12 +474,24 @@ hipError_t launch_merge_v_up(const MergeParams& p, hipStream_t stream) {
   const int max_groups = (p.T + kProjBlk - 1) / kProjBlk;
   if (groups > max_groups) groups = max_groups;
   const dim3 grid((unsigned)p.H, (unsigned)groups);
+  const dim3 block(kProjThreads);
+  const bool f32 = p.outs_f != nullptr;
   if (p.W == 1) {
-    if (p.valid) hipLaunchKernelGGL((merge_v_up_kernel<true, true>), grid, dim3(kProjThreads), 0, stream, p);
-    else hipLaunchKernelGGL((merge_v_up_kernel<false, true>), grid, dim3(kProjThreads), 0, stream, p);
+    if (f32) {
+      if (p.valid) hipLaunchKernelGGL((merge_v_up_kernel<true, true, true>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((merge_v_up_kernel<false, true, true>), grid, block, 0, stream, p);
+    } else {
+      if (p.valid) hipLaunchKernelGGL((merge_v_up_kernel<true, true, false>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((merge_v_up_kernel<false, true, false>), grid, block, 0, stream, p);
+    }
   } else {
-    if (p.valid) hipLaunchKernelGGL((merge_v_up_kernel<true, false>), grid, dim3(kProjThreads), 0, stream, p);
-    else hipLaunchKernelGGL((merge_v_up_kernel<false, false>), grid, dim3(kProjThreads), 0, stream, p);
+    if (f32) {
+      if (p.valid) hipLaunchKernelGGL((merge_v_up_kernel<true, false, true>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((merge_v_up_kernel<false, false, true>), grid, block, 0, stream, p);
+    } else {
+      if (p.valid) hipLaunchKernelGGL((merge_v_up_kernel<true, false, false>), grid, block, 0, stream, p);
+      else hipLaunchKernelGGL((merge_v_up_kernel<false, false, false>), grid, block, 0, stream, p);
+    }
   }
   return hipGetLastError();
 }

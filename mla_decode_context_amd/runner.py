@@ -25,7 +25,7 @@ def _i32(a: np.ndarray, device) -> torch.Tensor:
 class DeviceWorkload:
     """Device copies of a ``workloads.Workload`` plus output buffers."""
 
-    def __init__(self, wl, device="cuda", num_splits: int = 0):
+    def __init__(self, wl, device="cuda", num_splits: int = 0, partial_dtype=None):
         self.wl = wl
         self.device = torch.device(device)
         dev = self.device
@@ -43,7 +43,8 @@ class DeviceWorkload:
         self.tables = [_i32(sh.block_table, dev) for sh in wl.shards]
         self.w_uv = _bf16(wl.w_uv, dev) if wl.w_uv is not None else None
         T, H, W = self.T, self.H, self.W
-        self.outs = torch.empty((W, T, H, 512), dtype=torch.bfloat16, device=dev)
+        # per-rank partials: bf16 by default, fp32 when asked for
+        self.outs = torch.empty((W, T, H, 512), dtype=partial_dtype or torch.bfloat16, device=dev)
         self.lses = torch.empty((W, T, H), dtype=torch.float32, device=dev)
         self.valid = torch.empty((W, T), dtype=torch.int32, device=dev)
         self.out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)

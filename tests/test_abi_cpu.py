@@ -33,12 +33,12 @@ def test_status_strings():
 def _decode(**kw):
     a = dict(q_nope=P, qn_t=16 * 512, qn_h=512, q_pe=P, qp_t=16 * 64, qp_h=64, kv=P, kv_bs=16 * 576, page=16,
              bt=P, bt_stride=4, seq=P, qsl=P, B=2, T=4, H=16, mq=2, ms=100, W=2, r=0, I=1, scale=0.07,
-             splits=0, out=P, lse=P, ws=None, ws_bytes=0)
+             splits=0, out=P, dtype=0, lse=P, ws=None, ws_bytes=0)
     a.update(kw)
     return lib.mla_decode_partial(a["q_nope"], a["qn_t"], a["qn_h"], a["q_pe"], a["qp_t"], a["qp_h"], a["kv"],
                                   a["kv_bs"], a["page"], a["bt"], a["bt_stride"], a["seq"], a["qsl"], a["B"],
                                   a["T"], a["H"], a["mq"], a["ms"], a["W"], a["r"], a["I"], a["scale"], a["splits"],
-                                  a["out"], a["lse"], a["ws"], a["ws_bytes"], None)
+                                  a["out"], a["dtype"], a["lse"], a["ws"], a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -53,6 +53,7 @@ def _decode(**kw):
     (dict(T=0), OK), (dict(B=0, T=0), OK), (dict(T=0, q_nope=None), OK),
     (dict(I=0), SHAPE), (dict(I=-3), SHAPE), (dict(W=4, I=1 << 29), SHAPE),
     (dict(W=2, I=1 << 28, T=0), OK),
+    (dict(dtype=2), SHAPE), (dict(dtype=-1), SHAPE), (dict(dtype=1, T=0), OK),
 ])
 def test_decode_argument_checks(kw, code):
     assert _decode(**kw) == code
@@ -91,13 +92,16 @@ def test_workspace_size_host_logic():
 
 def test_merge_argument_checks():
     m = lib.mla_lse_merge
-    assert m(P, P, None, 0, 4, 16, P, None, None) == SHAPE
-    assert m(P, P, None, 2, 4, 0, P, None, None) == SHAPE
-    assert m(None, P, None, 2, 4, 16, P, None, None) == NULL
-    assert m(P, P, None, 2, 0, 16, P, None, None) == OK
+    assert m(P, 0, P, None, 0, 4, 16, P, None, None) == SHAPE
+    assert m(P, 0, P, None, 2, 4, 0, P, None, None) == SHAPE
+    assert m(None, 0, P, None, 2, 4, 16, P, None, None) == NULL
+    assert m(P, 0, P, None, 2, 0, 16, P, None, None) == OK
+    assert m(P, 1, P, None, 2, 0, 16, P, None, None) == OK
+    assert m(P, 3, P, None, 2, 4, 16, P, None, None) == SHAPE     # unknown partial dtype
     v = lib.mla_merge_v_up_proj
-    assert v(P, P, None, 2, 4, 16, None, P, None, None) == NULL
-    assert v(P, P, None, 2, -1, 16, P, P, None, None) == SHAPE
+    assert v(P, 0, P, None, 2, 4, 16, None, P, None, None) == NULL
+    assert v(P, 0, P, None, 2, -1, 16, P, P, None, None) == SHAPE
+    assert v(P, 7, P, None, 2, 4, 16, P, P, None, None) == SHAPE
     s = lib.mla_dcp_local_seqlens
     assert s(P, P, 2, 4, 2, 2, 1, P, P, None) == SHAPE
     assert s(P, P, 2, 4, 2, 1, 0, P, P, None) == SHAPE
@@ -107,12 +111,13 @@ def test_merge_argument_checks():
 
 def test_exchange_argument_checks():
     pk = lib.mla_dcp_a2a_pack
-    assert pk(P, P, None, 4, 128, 3, P, P, P, None) == SHAPE       # H % W != 0
-    assert pk(P, P, None, 4, 0, 1, P, P, P, None) == SHAPE
-    assert pk(P, P, None, -1, 16, 2, P, P, P, None) == SHAPE
-    assert pk(P, P, None, 4, 16, 2, None, P, P, None) == NULL      # W_UV missing
-    assert pk(P, P, None, 4, 16, 2, P, P, None, None) == NULL      # send_lse missing
-    assert pk(P, P, None, 0, 16, 2, None, None, None, None) == OK  # T == 0
+    assert pk(P, 0, P, None, 4, 128, 3, P, P, P, None) == SHAPE       # H % W != 0
+    assert pk(P, 0, P, None, 4, 0, 1, P, P, P, None) == SHAPE
+    assert pk(P, 0, P, None, -1, 16, 2, P, P, P, None) == SHAPE
+    assert pk(P, 0, P, None, 4, 16, 2, None, P, P, None) == NULL      # W_UV missing
+    assert pk(P, 0, P, None, 4, 16, 2, P, P, None, None) == NULL      # send_lse missing
+    assert pk(P, 0, P, None, 0, 16, 2, None, None, None, None) == OK  # T == 0
+    assert pk(P, 2, P, None, 4, 16, 2, P, P, P, None) == SHAPE        # unknown partial dtype
     cb = lib.mla_dcp_a2a_combine
     rows = 4 * 8
     assert cb(P, rows * 128, P, rows, 0, 4, 8, P, None, None) == SHAPE
