@@ -496,9 +496,9 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
       // page_size % 16 == 0: the stage's 16 rows are consecutive slots of one page.
       const int pg = a.page_shift >= 0 ? j0 >> a.page_shift : j0 / a.P;
       const int blk = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pg];
-      const uint8_t* base = kv_bytes + ((int64_t)blk * a.kv_bs + (int64_t)(j0 - pg * a.P) * kRow) * 2;
+      const uint64_t sbase = make_sbase(kv_bytes + ((int64_t)blk * a.kv_bs + (int64_t)(j0 - pg * a.P) * kRow) * 2);
 #pragma unroll
-      for (int i2 = 0; i2 < kWBlocks; ++i2) dma_16B_to_lds_sbase<true>(ldst + 1024 * i2, doff[i2], base);
+      for (int i2 = 0; i2 < kWBlocks; ++i2) dma_16B_to_lds_sbase<true>(ldst + 1024 * i2, doff[i2], sbase);
     } else {
 #pragma unroll
       for (int i2 = 0; i2 < kWBlocks; ++i2) {

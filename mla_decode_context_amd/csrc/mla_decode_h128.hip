@@ -152,12 +152,12 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
     const int slot = i & (kXSlots - 1);
     const uint32_t ldst = ring_lds + slot * kXStageBytes;
     const bool fast = kPage32 && j0 + kXStep <= j_end;
-    const uint8_t* base = nullptr;
-    if (fast) {
+    uint64_t sbase = 0;
+    if (fast && w >= 4) {
       // page_size % 32 == 0: the stage's 32 rows are consecutive slots of one page.
       const int pg = a.page_shift >= 0 ? j0 >> a.page_shift : j0 / a.P;
       const int blk = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pg];
-      base = kv_bytes + ((int64_t)blk * a.kv_bs + (int64_t)(j0 - pg * a.P) * kRow) * 2;
+      sbase = make_sbase(kv_bytes + ((int64_t)blk * a.kv_bs + (int64_t)(j0 - pg * a.P) * kRow) * 2);
     }
 #pragma unroll
     for (int u = 0; u < 9; ++u) {
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
       const int cpos = (o - row * kRowBytes) >> 4;
       const uint32_t doff = (uint32_t)(row * kRowBytes + ((cpos ^ chunk_swizzle(row)) << 4));
       if (fast) {
-        dma_16B_to_lds_sbase<false>(ldst + 1024 * blkno, doff, base);
+        dma_16B_to_lds_sbase<false>(ldst + 1024 * blkno, doff, sbase);
       } else {
         const int ra = (1024 * blkno) / kRowBytes;   // the block spans rows ra and ra + 1
         const int j = min(j0 + row, j_end - 1);

@@ -101,28 +101,38 @@ struct SlotMap {
 // s_waitcnt operand: lgkmcnt(0), vmcnt and expcnt left at their maxima.
 #define MLA_LGKMCNT0 (15 | (3 << 14) | (7 << 4))
 
-// Direct-to-LDS load with a wave-uniform 64-bit base (SGPRs) and a per-lane
+// Direct-to-LDS loads with a wave-uniform 64-bit base in SGPRs and a per-lane
 // 32-bit byte offset; see dma_16B_to_lds.
-template <bool kNT>
-__device__ __forceinline__ void dma_16B_to_lds_sbase(uint32_t lds_off, uint32_t voff, const void* base) {
-  // The base must live in SGPRs: take each 32-bit half from the first lane (it
-  // is uniform).  readfirstlane returns int: widen through uint32_t so that the
-  // low half is zero-extended, never sign-extended into the high half.
+//
+// make_sbase() assembles the base in SGPRs: each 32-bit half comes from the
+// first lane (the value is uniform).  readfirstlane returns int: the low half
+// is widened through uint32_t so that it is zero-extended, never
+// sign-extended into the high half.  The readfirstlanes are VALU writes of the
+// SGPRs, and a VMEM instruction may read an SGPR only five wait states after a
+// VALU wrote it; the compiler inserts no wait states inside inline asm, so
+// make_sbase() ends with an s_nop 4 that names the new SGPRs as operands (it
+// is ordered after their writes and before the loads, which are volatile asm
+// too).  Every load of the stage then uses the settled base and needs only
+// the one wait state for M0.  A CPU test checks the compiled kernels for a
+// VALU write of a base SGPR closer than five wait states to a load.
+__device__ __forceinline__ uint64_t make_sbase(const void* base) {
   const uint64_t b = (uint64_t)(uintptr_t)base;
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
   const uint64_t sbase = ((uint64_t)hi << 32) | (uint64_t)lo;
-  // The readfirstlanes above are VALU writes of the base SGPRs, and a VMEM
-  // instruction may read an SGPR only five wait states after a VALU wrote it;
-  // the compiler inserts no wait states inside inline asm and may place the
-  // readfirstlanes right before it.  s_mov (one) + s_nop 4 (five) cover that.
+  asm volatile("s_nop 4" : : "s"(sbase));
+  return sbase;
+}
+
+template <bool kNT>
+__device__ __forceinline__ void dma_16B_to_lds_sbase(uint32_t lds_off, uint32_t voff, uint64_t sbase) {
   if (kNT)
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
                  :
                  : "s"(lds_off), "v"(voff), "s"(sbase)
                  : "memory");
   else
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %1, %2"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
                  : "s"(lds_off), "v"(voff), "s"(sbase)
                  : "memory");
