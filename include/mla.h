@@ -156,6 +156,39 @@ mla_status mla_decode_partial(
     void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * mla_decode_partial_noalloc -- mla_decode_partial for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, results and errors as
+ * mla_decode_partial (with the same split plan, bit for bit the same
+ * outputs), without the workspace: the split partials, split tickets and the
+ * 128-head dispatch order live in a device array of the library,
+ * MLA_NOALLOC_SCRATCH_BYTES (64 MiB) on every GPU it runs on, held until the
+ * process ends.  The call allocates nothing (no hipMalloc, no hipFree, no
+ * host allocation; MLA_DEBUG does not apply to it).  Its first call on a
+ * device looks up that device's copy of the array.
+ *   Returns MLA_ERR_WORKSPACE when the call's plan needs more than
+ *   MLA_NOALLOC_SCRATCH_BYTES (mla_decode_workspace_size of the same
+ *   arguments tells: it fits when that is at most the limit; long rows split
+ *   many ways, e.g. a few 128-head tokens with num_splits in the hundreds, do
+ *   not), otherwise as mla_decode_partial.
+ * All calls on one GPU share its array, which keeps the last call's contents
+ * (what must start at zero, the split tickets, is cleared by the calls that
+ * use them): calls that overlap in time on one GPU (two streams, two host
+ * threads) race and must not be issued.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+mla_status mla_decode_partial_noalloc(
+    const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
+    const void* q_pe, int64_t qp_stride_t, int64_t qp_stride_h,
+    const void* kv_cache, int64_t kv_block_stride, int32_t page_size,
+    const int32_t* block_table, int32_t bt_stride,
+    const int32_t* seq_lens, const int32_t* query_start_loc,
+    int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
+    int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, float scale, int32_t num_splits,
+    void* out, int32_t out_dtype, float* lse, void* hip_stream);
+
+/*
  * mla_check_decode_metadata -- the device-side contract of mla_decode_partial,
  * checked on HOST copies of its metadata (what MLA_DEBUG=1 runs).  All
  * pointers are host pointers: seq_lens [B], query_start_loc [B+1],

@@ -50,6 +50,12 @@ def load_library():
         _c_void_p, _i32, _c_void_p, _c_void_p,
         _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
         _c_void_p, _i32, _c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p]
+    lib.mla_decode_partial_noalloc.restype = _i32
+    lib.mla_decode_partial_noalloc.argtypes = [
+        _c_void_p, _i64, _i64, _c_void_p, _i64, _i64, _c_void_p, _i64, _i32,
+        _c_void_p, _i32, _c_void_p, _c_void_p,
+        _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
+        _c_void_p, _i32, _c_void_p, _c_void_p]
     lib.mla_decode_workspace_size.restype = ctypes.c_size_t
     lib.mla_decode_workspace_size.argtypes = [_i32] * 8
     lib.mla_lse_merge.restype = _i32
@@ -180,6 +186,34 @@ def mla_decode_partial(q_nope, q_pe, kv_cache, block_table, seq_lens, query_star
         float(scale),
         int(num_splits), _ptr(out), out_dtype, _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "mla_decode_partial")
+
+
+def mla_decode_partial_noalloc(q_nope, q_pe, kv_cache, block_table, seq_lens, query_start_loc,
+                               cp_world, cp_rank, scale, out, lse, *, max_query_len, max_seq_len,
+                               num_splits=0, stream=None, cp_interleave=1):
+    """mla_decode_partial without a workspace (the library's per-GPU scratch array
+    holds the split partials): for callers that cannot allocate."""
+    lib = load_library()
+    out_dtype = _partial_dtype(out, "out")
+    for t, dt, n, d in ((q_nope, torch.bfloat16, "q_nope", 3), (q_pe, torch.bfloat16, "q_pe", 3),
+                        (kv_cache, torch.bfloat16, "kv_cache", 3), (block_table, torch.int32, "block_table", 2),
+                        (seq_lens, torch.int32, "seq_lens", 1), (query_start_loc, torch.int32, "query_start_loc", 1),
+                        (out, out.dtype, "out", 3), (lse, torch.float32, "lse", 2)):
+        _need(t, dt, n, d)
+    T, H, _ = q_nope.shape
+    nblk, page, row = kv_cache.shape
+    if row != D_ROW or kv_cache.stride(1) != D_ROW or tuple(out.shape) != (T, H, D_LATENT) or tuple(lse.shape) != (T, H):
+        raise MlaError("mla_decode_partial_noalloc: shapes disagree")
+    if T and not (out.is_contiguous() and lse.is_contiguous() and q_nope.stride(2) == 1 and q_pe.stride(2) == 1):
+        raise MlaError("mla_decode_partial_noalloc: out/lse contiguous, q rows contiguous")
+    B = seq_lens.shape[0]
+    st = lib.mla_decode_partial_noalloc(
+        _ptr(q_nope), q_nope.stride(0), q_nope.stride(1), _ptr(q_pe), q_pe.stride(0), q_pe.stride(1),
+        _ptr(kv_cache), kv_cache.stride(0), page, _ptr(block_table), block_table.stride(0),
+        _ptr(seq_lens), _ptr(query_start_loc), B, T, H, int(max_query_len), int(max_seq_len),
+        int(cp_world), int(cp_rank), int(cp_interleave), float(scale), int(num_splits),
+        _ptr(out), out_dtype, _ptr(lse), _stream(stream))
+    _check(st, "mla_decode_partial_noalloc")
 
 
 def mla_lse_merge(outs, lses, valid, out, out_lse=None, stream=None):

@@ -6,10 +6,17 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "mla.h"
 #include "mla_kernels.h"
+
+// Scratch of mla_decode_partial_noalloc: one copy in every GPU's memory,
+// held until the process ends.  In host code `scratch` is only a handle for
+// hipGetSymbolAddress; the address on each device is looked up once and kept
+// in g_scratch (the kernels take it as an argument).
+static __device__ __align__(256) uint8_t scratch[MLA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -28,6 +35,29 @@ mla_status check_device() {
     __atomic_store_n(&g_device_state[dev], st, __ATOMIC_RELEASE);
   }
   return st == 1 ? MLA_OK : MLA_ERR_UNSUPPORTED;
+}
+
+// Device address of `scratch` on each device (looked up on the first
+// mla_decode_partial_noalloc call made with that device current).
+struct ScratchSlot {
+  std::once_flag once;
+  hipError_t err = hipSuccess;
+  void* ptr = nullptr;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+mla_status scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MLA_ERR_UNSUPPORTED;
+  ScratchSlot& s = g_scratch[dev];
+  std::call_once(s.once, [&s] {
+    s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch));
+    if (s.err != hipSuccess) s.ptr = nullptr;
+  });
+  if (s.err != hipSuccess || s.ptr == nullptr) return MLA_ERR_HIP;
+  *out = s.ptr;
+  return MLA_OK;
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -133,6 +163,9 @@ Plan make_plan(int B, int T, int H, int max_seq_len, int W, int I, int num_split
 // (balanced schedule; two per workgroup).  The split regions exist only when
 // the plan splits.
 bool splits_ws(const Plan& p) { return p.workers > 0 || p.max_splits > 1; }
+// Plans whose split rows merge through ticketed last-arriver workgroups
+// (fixed splits of the 16-head and generic kernels).
+bool uses_tickets(const Plan& p) { return !p.h128 && p.workers == 0 && p.max_splits > 1; }
 bool uses_workspace(const Plan& p) { return splits_ws(p) || p.ordered; }
 int64_t slots_of(const Plan& p, int T) { return p.workers > 0 ? 2 * (int64_t)p.workers : (int64_t)p.max_splits * T; }
 size_t map_bytes(const Plan& p, int T) {
@@ -254,7 +287,12 @@ size_t mla_decode_workspace_size(int32_t B, int32_t T, int32_t H, int32_t max_qu
   return workspace_bytes_for(p, T, H);
 }
 
-mla_status mla_decode_partial(
+}  // extern "C"
+
+// mla_decode_partial and mla_decode_partial_noalloc: the same checks, plan
+// and kernels; `noalloc` takes the workspace from this device's scratch array
+// (never MLA_DEBUG, whose host copies would allocate).
+static mla_status decode_impl(
     const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
     const void* q_pe, int64_t qp_stride_t, int64_t qp_stride_h,
     const void* kv_cache, int64_t kv_block_stride, int32_t page_size,
@@ -263,7 +301,7 @@ mla_status mla_decode_partial(
     int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
     int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, float scale, int32_t num_splits,
     void* out, int32_t out_dtype, float* lse,
-    void* workspace, size_t workspace_bytes, void* hip_stream) {
+    void* workspace, size_t workspace_bytes, void* hip_stream, bool noalloc) {
   if (B < 0 || T < 0 || H < 1 || H > MLA_MAX_HEADS || page_size < 1 || !layout_ok(cp_world, cp_interleave) ||
       cp_rank < 0 || cp_rank >= cp_world || max_query_len < 0 || max_seq_len < 0 ||
       num_splits < 0 || !isfinite(scale) || !(scale > 0.f) || !dtype_ok(out_dtype))
@@ -284,7 +322,7 @@ mla_status mla_decode_partial(
   if (bt_stride < 1 || !aligned(out, 16)) return MLA_ERR_SHAPE;
   mla_status st = check_device();
   if (st != MLA_OK) return st;
-  if (debug_mode()) {
+  if (!noalloc && debug_mode()) {
     // Host copies of the metadata, one wait, the contract checked before
     // anything is enqueued.  Not valid inside capture.
     hipStream_t s = (hipStream_t)hip_stream;
@@ -307,8 +345,17 @@ mla_status mla_decode_partial(
     }
   }
 
-  const Plan plan = make_plan(B, T, H, max_seq_len, cp_world, cp_interleave, num_splits, workspace != nullptr);
+  const Plan plan = make_plan(B, T, H, max_seq_len, cp_world, cp_interleave, num_splits,
+                              noalloc || workspace != nullptr);
   const size_t need = workspace_bytes_for(plan, T, H);
+  if (noalloc) {
+    if (need > (size_t)MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_WORKSPACE;
+    if (need > 0) {
+      st = scratch_address(&workspace);
+      if (st != MLA_OK) return st;
+      workspace_bytes = MLA_NOALLOC_SCRATCH_BYTES;
+    }
+  }
   if (need > 0 && workspace_bytes < need) return MLA_ERR_WORKSPACE;
 
   mla::DecodeParams p;
@@ -336,9 +383,49 @@ mla_status mla_decode_partial(
     p.ws_lse = (float*)(base + d_end);
     p.ws_o = (float*)(base + d_end + lse_bytes(plan, T, H));
   }
+  if (noalloc && uses_tickets(plan)) {
+    // The split tickets must start at zero; a caller-owned workspace is
+    // zero-filled once by its owner, the scratch array is cleared here (a
+    // kernel, so the call stays capturable).
+    const hipError_t ez = mla::launch_zero_i32(p.counters, (int)(counters_bytes(plan, T) / 4), (hipStream_t)hip_stream);
+    if (ez != hipSuccess) return MLA_ERR_HIP;
+  }
   hipError_t e = plan.h128 ? mla::launch_decode_h128(p, (hipStream_t)hip_stream)
                            : mla::launch_decode(p, plan.mtiles, plan.max_splits, plan.workers, (hipStream_t)hip_stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+extern "C" {
+
+mla_status mla_decode_partial(
+    const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
+    const void* q_pe, int64_t qp_stride_t, int64_t qp_stride_h,
+    const void* kv_cache, int64_t kv_block_stride, int32_t page_size,
+    const int32_t* block_table, int32_t bt_stride,
+    const int32_t* seq_lens, const int32_t* query_start_loc,
+    int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
+    int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, float scale, int32_t num_splits,
+    void* out, int32_t out_dtype, float* lse,
+    void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return decode_impl(q_nope, qn_stride_t, qn_stride_h, q_pe, qp_stride_t, qp_stride_h, kv_cache, kv_block_stride,
+                     page_size, block_table, bt_stride, seq_lens, query_start_loc, B, T, H, max_query_len,
+                     max_seq_len, cp_world, cp_rank, cp_interleave, scale, num_splits, out, out_dtype, lse,
+                     workspace, workspace_bytes, hip_stream, false);
+}
+
+mla_status mla_decode_partial_noalloc(
+    const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
+    const void* q_pe, int64_t qp_stride_t, int64_t qp_stride_h,
+    const void* kv_cache, int64_t kv_block_stride, int32_t page_size,
+    const int32_t* block_table, int32_t bt_stride,
+    const int32_t* seq_lens, const int32_t* query_start_loc,
+    int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
+    int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, float scale, int32_t num_splits,
+    void* out, int32_t out_dtype, float* lse, void* hip_stream) {
+  return decode_impl(q_nope, qn_stride_t, qn_stride_h, q_pe, qp_stride_t, qp_stride_h, kv_cache, kv_block_stride,
+                     page_size, block_table, bt_stride, seq_lens, query_start_loc, B, T, H, max_query_len,
+                     max_seq_len, cp_world, cp_rank, cp_interleave, scale, num_splits, out, out_dtype, lse,
+                     nullptr, 0, hip_stream, true);
 }
 
 static mla_status merge_common(const void* outs, int32_t outs_dtype, const float* lses, const int32_t* valid,

@@ -926,6 +926,17 @@ hipError_t launch_decode(const DecodeParams& p, int mtiles, int max_splits, int 
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_local_seqlens(const int32_t* seq_lens, const int32_t* qsl, int B, int T, int W,
                                 int r, int I, int32_t* row_seqlen, int32_t* shard_len, hipStream_t stream) {
   const int n = T > B ? T : B;

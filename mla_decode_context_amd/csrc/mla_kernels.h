@@ -67,6 +67,7 @@ hipError_t launch_decode(const DecodeParams& p, int mtiles, int max_splits, int 
 hipError_t launch_decode_h128(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_local_seqlens(const int32_t* seq_lens, const int32_t* qsl, int B, int T, int W,
                                 int r, int I, int32_t* row_seqlen, int32_t* shard_len, hipStream_t stream);
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_merge_v_up(const MergeParams& p, hipStream_t stream);
 hipError_t launch_slice_combine(const SliceParams& p, hipStream_t stream);

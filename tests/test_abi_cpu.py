@@ -18,6 +18,7 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"mla_status_string", "mla_decode_partial", "mla_decode_workspace_size",
                           "mla_lse_merge", "mla_merge_v_up_proj", "mla_dcp_local_seqlens",
                           "mla_dcp_a2a_pack", "mla_dcp_a2a_combine", "mla_check_decode_metadata",
+                          "mla_decode_partial_noalloc",
                           "mla_calib_hbm_read", "mla_calib_mfma_bf16", "mla_calib_mfma_flops"}
     for n in names:
         assert hasattr(lib, n), n
