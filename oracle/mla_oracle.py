@@ -17,6 +17,9 @@ with NumPy, slow on purpose and meant to be checked by eye against the pages:
 * "[Attention] DCP sparse MLA output-merge optimizations" (vLLM PR #48196):
   the exact LSE-weighted merge of the per-rank partials, per-row valid counts,
   and the W_UV projection that commutes with the merge.
+* The same PR #24453 thread's alternative for query_len > 1: a two-stage
+  decode, the context KV without a causal mask and the query KV with one,
+  merged by LSE.
 
 Readings where the pages are silent (all listed in the design notes):
 ``seq_lens`` holds the global total S_b including the request's query tokens;
@@ -190,6 +193,86 @@ def decode_partial(seq_lens, query_start_loc, q_nope_bits, q_pe_bits, global_kv,
         keys = cache[b][visible_keys(p, W, r, I)]
         outs[n_out], lses[n_out] = attend(bf16_bits_to_f64(q_nope_bits[t]),
                                           bf16_bits_to_f64(q_pe_bits[t]), keys, scale)
+    return outs, lses
+
+
+# ---------------------------------------------------------------------------
+# The two-stage split of a decode with more than one query row
+# ---------------------------------------------------------------------------
+#
+# PR #24453 review thread (youzhedian): with query_len > 1 the DCP decode can
+# be run in two stages instead of with the interleaved mask -- the context KV
+# with causal=False and the query KV with causal=True -- so that no backend
+# needs a custom mask.  Reading: the context of a request is its tokens before
+# its Q query tokens (global positions 0 .. S-Q-1); every query row sees all of
+# them, and each DCP rank attends to the ones it stores.  The query KV is the
+# request's own Q tokens (positions S-Q .. S-1), which a causal mask restricted
+# to them makes row i see the first i+1 of; it is one dense block, attended
+# once (not per rank).  The W context partials and the query partial merge by
+# LSE into the unsharded result.
+
+def context_keys(S: int, Q: int, W: int, r: int, I: int = 1) -> list[int]:
+    """Global positions of the context part that shard r stores: the request's
+    tokens before its Q query tokens.  Every query row of the request sees all
+    of them (no causal mask inside the context)."""
+    return [k for k in range(S - Q) if holder(k, W, I) == r]
+
+
+def query_part_keys(S: int, Q: int, i: int) -> list[int]:
+    """Global positions of the query part that query row i sees: the request's
+    own query tokens S-Q .. S-Q+i (the causal mask among its Q tokens)."""
+    return list(range(S - Q, S - Q + i + 1))
+
+
+def context_count(S: int, Q: int, W: int, r: int, I: int = 1) -> int:
+    """Closed form of len(context_keys(...)): what shard r stores of the first
+    S - Q positions (the same for every query row of the request)."""
+    return shard_length(S - Q, W, r, I)
+
+
+def decode_context_part(seq_lens, query_start_loc, q_nope_bits, q_pe_bits, global_kv, scale: float,
+                        W: int = 1, r: int = 0, tokens=None, I: int = 1):
+    """Stage 1 on shard r: every query row attends, without a causal mask, to
+    the context keys shard r stores.  Returns out [n,H,512], lse [n,H] (empty
+    context: out 0, lse -inf)."""
+    rows = query_rows(seq_lens, query_start_loc)
+    qsl = [int(x) for x in query_start_loc]
+    sel = range(len(rows)) if tokens is None else [int(t) for t in tokens]
+    H = q_nope_bits.shape[1]
+    outs = np.zeros((len(sel), H, D_LATENT))
+    lses = np.zeros((len(sel), H))
+    cache = {}
+    for n_out, t in enumerate(sel):
+        b, _, _ = rows[t]
+        if b not in cache:
+            cache.clear()
+            cache[b] = bf16_bits_to_f64(global_kv(b))
+        S, Q = int(seq_lens[b]), qsl[b + 1] - qsl[b]
+        keys = cache[b][context_keys(S, Q, W, r, I)]
+        outs[n_out], lses[n_out] = attend(bf16_bits_to_f64(q_nope_bits[t]), bf16_bits_to_f64(q_pe_bits[t]),
+                                          keys, scale)
+    return outs, lses
+
+
+def decode_query_part(seq_lens, query_start_loc, q_nope_bits, q_pe_bits, global_kv, scale: float, tokens=None):
+    """Stage 2, once for all ranks: query row i of a request attends causally to
+    the request's own query tokens 0..i (global positions S-Q .. S-Q+i)."""
+    rows = query_rows(seq_lens, query_start_loc)
+    sel = range(len(rows)) if tokens is None else [int(t) for t in tokens]
+    H = q_nope_bits.shape[1]
+    outs = np.zeros((len(sel), H, D_LATENT))
+    lses = np.zeros((len(sel), H))
+    qsl = [int(x) for x in query_start_loc]
+    cache = {}
+    for n_out, t in enumerate(sel):
+        b, i, _ = rows[t]
+        if b not in cache:
+            cache.clear()
+            cache[b] = bf16_bits_to_f64(global_kv(b))
+        S, Q = int(seq_lens[b]), qsl[b + 1] - qsl[b]
+        keys = cache[b][query_part_keys(S, Q, i)]
+        outs[n_out], lses[n_out] = attend(bf16_bits_to_f64(q_nope_bits[t]), bf16_bits_to_f64(q_pe_bits[t]),
+                                          keys, scale)
     return outs, lses
 
 

@@ -450,7 +450,98 @@ def check_a2a_pack_combine(seed=6) -> bool:
     return True
 
 
+def check_two_stage_keys(max_w=5, max_i=4, max_s=40, max_q=7) -> bool:
+    """Two-stage split: the context count is the size of the explicit context set;
+    for every row the shards' context keys and the row's query-part keys
+    partition 0..p exactly once; the context part is the same for every row of a
+    request."""
+    for W in range(1, max_w + 1):
+        for I in range(1, max_i + 1):
+            for S in range(1, max_s):
+                for Q in range(1, min(max_q, S) + 1):
+                    ctx = []
+                    for r in range(W):
+                        keys = O.context_keys(S, Q, W, r, I)
+                        if keys != [k for k in range(S - Q) if (k // I) % W == r]:
+                            return False
+                        if O.context_count(S, Q, W, r, I) != len(keys):
+                            return False
+                        ctx += keys
+                    if sorted(ctx) != list(range(S - Q)):
+                        return False
+                    for i in range(Q):
+                        p = S - Q + i
+                        qk = O.query_part_keys(S, Q, i)
+                        if sorted(ctx + qk) != list(range(p + 1)) or len(qk) != i + 1:
+                            return False
+    return True
+
+
+def check_two_stage_against_sdpa(seed=8) -> bool:
+    """Stage 1 on each shard == torch SDPA without a mask over that shard's
+    context keys; stage 2 == torch SDPA with is_causal=True over the request's
+    Q query tokens' own KV (square Q x Q causal: row i sees keys 0..i)."""
+    rng = np.random.default_rng(seed)
+    scale = 1 / math.sqrt(192)
+    for (S, Q, H, W, I) in [(9, 3, 2, 2, 1), (13, 5, 3, 3, 1), (20, 4, 2, 2, 3), (6, 6, 2, 2, 1), (7, 1, 2, 4, 1)]:
+        kvb, qnb, qpb = _rand_case(rng, S, Q, H)
+        kv = _torch_widen(kvb)
+        q = torch.from_numpy(np.concatenate([_torch_widen(qnb), _torch_widen(qpb)], axis=-1)).permute(1, 0, 2)
+        qsl = [0, Q]
+        for r in range(W):
+            out, lse = O.decode_context_part([S], qsl, qnb, qpb, lambda b: kvb, scale, W, r, I=I)
+            keys = [k for k in range(S - Q) if (k // I) % W == r]
+            if not keys:
+                if np.any(out != 0) or np.any(lse != -np.inf):
+                    return False
+                continue
+            kt = torch.from_numpy(kv[keys]).expand(H, len(keys), 576).unsqueeze(0)
+            vt = torch.from_numpy(kv[keys, :512]).expand(H, len(keys), 512).unsqueeze(0)
+            ref = torch.nn.functional.scaled_dot_product_attention(q.unsqueeze(0), kt, vt, scale=scale)[0]
+            if not np.allclose(out, ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12):
+                return False
+        out, lse = O.decode_query_part([S], qsl, qnb, qpb, lambda b: kvb, scale)
+        new = kv[S - Q:]
+        kt = torch.from_numpy(new).expand(H, Q, 576).unsqueeze(0)
+        vt = torch.from_numpy(new[:, :512]).expand(H, Q, 512).unsqueeze(0)
+        ref = torch.nn.functional.scaled_dot_product_attention(q.unsqueeze(0), kt, vt, scale=scale, is_causal=True)[0]
+        if not np.allclose(out, ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12):
+            return False
+        # one query row: the query part is that token's own row exactly, LSE its score
+        if Q == 1:
+            s0 = scale * (_torch_widen(qnb[0]) @ kv[S - 1, :512] + _torch_widen(qpb[0]) @ kv[S - 1, 512:])
+            if not (np.array_equal(out[0], np.repeat(kv[S - 1:, :512], H, axis=0)) and np.allclose(lse[0], s0)):
+                return False
+    return True
+
+
+def check_two_stage_merge(seed=9) -> bool:
+    """merge(W context partials + the query partial) == unsharded attention ==
+    merge of the one-stage shard partials (fp64), for several requests,
+    layouts and query lengths, including requests with no context (Q = S)."""
+    rng = np.random.default_rng(seed)
+    scale = 1 / math.sqrt(192)
+    for seq_lens, q_lens, H, W, I in [([6, 9], [4, 3], 2, 2, 1), ([2, 3, 17], [2, 3, 5], 2, 4, 1),
+                                      ([30, 12], [6, 1], 2, 8, 2), ([5, 40], [5, 2], 1, 3, 4)]:
+        qsl, kvs, qnb, qpb = _sharded_case(rng, seq_lens, q_lens, H, W)
+        gkv = lambda b: kvs[b]
+        full, full_lse = O.decode_partial(seq_lens, qsl, qnb, qpb, gkv, scale, 1, 0)
+        ctx = [O.decode_context_part(seq_lens, qsl, qnb, qpb, gkv, scale, W, r, I=I) for r in range(W)]
+        qp = O.decode_query_part(seq_lens, qsl, qnb, qpb, gkv, scale)
+        outs = np.stack([c[0] for c in ctx] + [qp[0]])
+        lses = np.stack([c[1] for c in ctx] + [qp[1]])
+        m, ml = O.lse_merge(outs, lses, None)
+        if not (np.allclose(m, full, atol=1e-12) and np.allclose(ml, full_lse, atol=1e-12)):
+            return False
+        one = [O.decode_partial(seq_lens, qsl, qnb, qpb, gkv, scale, W, r, I=I) for r in range(W)]
+        m1, ml1 = O.lse_merge(np.stack([o[0] for o in one]), np.stack([o[1] for o in one]), None)
+        if not (np.allclose(m, m1, atol=1e-12) and np.allclose(ml, ml1, atol=1e-12)):
+            return False
+    return True
+
+
 ALL_CHECKS = [check_bf16_widening, check_worked_masks, check_ab_example, check_counts_bruteforce,
               check_against_sdpa, check_closed_forms, check_merge_equals_unsharded, check_merge_identities,
               check_wuv_commutes, check_v_up_proj_closed_forms, check_runs_bruteforce,
-              check_runs_merge_equals_unsharded, check_a2a_pack_combine]
+              check_runs_merge_equals_unsharded, check_a2a_pack_combine, check_two_stage_keys,
+              check_two_stage_against_sdpa, check_two_stage_merge]

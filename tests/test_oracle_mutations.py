@@ -127,6 +127,23 @@ def _widen_flush_subnormals(bits):          # flushes subnormals to zero
 _real_widen = O.bf16_bits_to_f64
 
 
+def _query_part_shifted(S, Q, i):            # the query part one position late
+    return list(range(S - Q + 1, S - Q + i + 2))
+
+
+def _query_part_exclusive(S, Q, i):          # a row does not see its own token
+    return list(range(S - Q, S - Q + i))
+
+
+def _context_includes_first_query(S, Q, W, r, I=1):   # context runs through the first query token
+    return [k for k in range(S - Q + 1) if (k // I) % W == r]
+
+
+def _context_count_interleaved_only(S, Q, W, r, I=1):  # ignores the run length
+    n = S - Q
+    return 0 if n <= r else (n - r + W - 1) // W
+
+
 MUTANTS = [
     ("visible_count", _count_drop_plus_one),
     ("visible_count", _count_floor),
@@ -147,6 +164,10 @@ MUTANTS = [
     ("bf16_bits_to_f64", _widen_as_fp16),
     ("bf16_bits_to_f64", _widen_shift15),
     ("bf16_bits_to_f64", _widen_flush_subnormals),
+    ("query_part_keys", _query_part_shifted),
+    ("query_part_keys", _query_part_exclusive),
+    ("context_keys", _context_includes_first_query),
+    ("context_count", _context_count_interleaved_only),
 ]
 
 
@@ -154,9 +175,10 @@ MUTANTS = [
 def test_pins_catch_mutant(monkeypatch, name, fn):
     monkeypatch.setattr(O, name, fn)
     results = {c.__name__: _safe(c) for c in _pins.ALL_CHECKS
-               if c not in (_pins.check_counts_bruteforce, _pins.check_runs_bruteforce)}
+               if c not in (_pins.check_counts_bruteforce, _pins.check_runs_bruteforce, _pins.check_two_stage_keys)}
     results["check_counts_bruteforce"] = _safe(lambda: _pins.check_counts_bruteforce(5, 30, 5))
     results["check_runs_bruteforce"] = _safe(lambda: _pins.check_runs_bruteforce(4, 5, 40))
+    results["check_two_stage_keys"] = _safe(lambda: _pins.check_two_stage_keys(4, 3, 25, 5))
     assert not all(results.values()), f"no pin failed for mutant {name}:{fn.__name__}"
 
 
