@@ -213,9 +213,22 @@ def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True
         torch.cuda.synchronize()
         mg_step_ms = float(np.median([a.elapsed_time(b) for a, b in mevs]))
     xchg = exchange_times(dw, wl, steps, torch) if merging and proj and wl.H % wl.W == 0 else None
+    # The two-stage path (query rows > 1): every rank's context stage, the query
+    # stage over the query tokens' own KV, the merge of the W + 1 partials;
+    # timed as a whole step and per stage, beside the one-stage step above.
+    two = None
+    if wl.max_query_len > 1:
+        dw.setup_two_stage()
+        dw.two_stage_step()
+        two = {"two_stage_ms_per_step": loop_ms(dw.two_stage_step),
+               "two_stage_context_ms_per_shard": loop_ms(lambda: [dw.context_partial(r) for r in range(wl.W)]) / wl.W,
+               "two_stage_query_ms": loop_ms(dw.query_partial)}
+        two["two_stage_vs_one_stage"] = two["two_stage_ms_per_step"] / float(ev_ms_step)
     res = dict(workload=name, T=wl.T, B=wl.B, H=wl.H, W=wl.W, ms_per_step=ms_step)
     if xchg is not None:
         res.update(xchg)
+    if two is not None:
+        res.update(two)
     kv_total = sum(p["kv"] for p in per_shard)
     res["kv_GBps"] = kv_total / (ms_step * 1e-3) / 1e9
     res["query_tokens_per_s"] = wl.T / (ms_step * 1e-3)
@@ -550,6 +563,9 @@ def main():
     }
     if "kv_GBps_same_cache" in head:
         line["kv_GBps_same_cache"] = round(head["kv_GBps_same_cache"], 2)
+    for k in ("two_stage_ms_per_step", "two_stage_context_ms_per_shard", "two_stage_query_ms", "two_stage_vs_one_stage"):
+        if k in head:
+            line[k] = round(head[k], 5)
     print(json.dumps(line))
 
 

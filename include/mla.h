@@ -60,6 +60,22 @@ typedef int32_t mla_status;
 #define MLA_DTYPE_BF16 0
 #define MLA_DTYPE_F32  1
 
+/* Which keys a query row sees (mask_mode of the decode calls).
+ * MLA_MASK_CAUSAL: row i of a request, at global position p = S_b - Q_b + i,
+ *   sees the keys at positions 0..p (on a DCP rank: the ones it stores; the
+ *   interleaved causal mask of the PR #24453 thread).
+ * MLA_MASK_CONTEXT: every row of the request sees the keys at positions
+ *   0..S_b-Q_b-1, its tokens before the query tokens, without a causal mask:
+ *   the context stage of the two-stage decode the same thread proposes for
+ *   query_len > 1 (context KV with causal=False, query KV with causal=True).
+ *   The query stage is an ordinary MLA_MASK_CAUSAL call with cp_world = 1 over
+ *   the query tokens' own KV rows: for example kv_cache = those rows as
+ *   [T, 1, 576] (page_size 1), block_table[b][j] = query_start_loc[b] + j and
+ *   seq_lens[b] = Q_b.  Merging the cp_world context partials and the query
+ *   partial with mla_lse_merge gives the unsharded result. */
+#define MLA_MASK_CAUSAL  0
+#define MLA_MASK_CONTEXT 1
+
 /* Fixed head dimensions of the absorbed form. */
 #define MLA_D_LATENT 512   /* kv_lora_rank: c_kv, q_nope and output width */
 #define MLA_D_ROPE    64   /* qk_rope_head_dim: k_pe and q_pe width       */
@@ -93,7 +109,10 @@ const char* mla_status_string(mla_status status);
  *   s_j  = scale * (q_nope[t,h,:] . c_kv_j + q_pe[t,h,:] . k_pe_j)
  *   lse  = ln sum_j exp(s_j)                       (natural log, fp32)
  *   out  = sum_j exp(s_j - lse) * c_kv_j           (bf16, round to nearest even)
- * A row that sees no key on this rank gets out = 0 and lse = -inf.
+ * A row that sees no key on this rank gets out = 0 and lse = -inf.  With
+ * mask_mode = MLA_MASK_CONTEXT every row of request b sees instead the rank's
+ * first Lx_b local keys, Lx_b = the count above for n = S_b - Q_b (the context
+ * stage of the two-stage decode; only those keys need to be in the cache).
  *
  * Layouts (all last dimensions contiguous):
  *   q_nope   bf16 [T,H,512], element (t,h,d) at q_nope + t*qn_stride_t + h*qn_stride_h + d
@@ -128,8 +147,8 @@ const char* mla_status_string(mla_status status);
  * Returns MLA_OK, or MLA_ERR_NULL / MLA_ERR_SHAPE (B<0, T<0, H outside
  * [1,128], page_size<1, cp_world<1, cp_rank outside [0,cp_world),
  * cp_interleave<1 or cp_world*cp_interleave > 2^30, strides
- * smaller than the data, scale not finite or not positive, out_dtype not one
- * of the two) / MLA_ERR_WORKSPACE /
+ * smaller than the data, scale not finite or not positive, out_dtype or
+ * mask_mode not one of the two) / MLA_ERR_WORKSPACE /
  * MLA_ERR_UNSUPPORTED / MLA_ERR_HIP.  B == 0 or T == 0 enqueues nothing and
  * returns MLA_OK (the grid is sized from host ints and may be empty).
  * Device-side contract: Q_b <= S_b <= max_seq_len, Q_b <= max_query_len,
@@ -151,7 +170,8 @@ mla_status mla_decode_partial(
     const int32_t* block_table, int32_t bt_stride,
     const int32_t* seq_lens, const int32_t* query_start_loc,
     int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
-    int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, float scale, int32_t num_splits,
+    int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, int32_t mask_mode, float scale,
+    int32_t num_splits,
     void* out, int32_t out_dtype, float* lse,
     void* workspace, size_t workspace_bytes, void* hip_stream);
 
@@ -185,7 +205,8 @@ mla_status mla_decode_partial_noalloc(
     const int32_t* block_table, int32_t bt_stride,
     const int32_t* seq_lens, const int32_t* query_start_loc,
     int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
-    int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, float scale, int32_t num_splits,
+    int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, int32_t mask_mode, float scale,
+    int32_t num_splits,
     void* out, int32_t out_dtype, float* lse, void* hip_stream);
 
 /*
@@ -195,9 +216,10 @@ mla_status mla_decode_partial_noalloc(
  * block_table [B * bt_stride].  Checks, in order:
  *   query_start_loc[0] == 0, nondecreasing, query_start_loc[B] == T;
  *   per request: 0 <= Q_b <= max_query_len, Q_b <= S_b <= max_seq_len;
- *   the ceil(Lc_b / page_size) blocks that hold rank cp_rank's Lc_b stored
- *   tokens fit in the row (<= bt_stride) and have ids in [0, num_blocks)
- *   (num_blocks < 0: only ids >= 0 are required).
+ *   the ceil(Lc_b / page_size) blocks that hold the Lc_b local tokens the call
+ *   reads (rank cp_rank's share of all S_b tokens, or with MLA_MASK_CONTEXT of
+ *   the first S_b - Q_b) fit in the row (<= bt_stride) and have ids in
+ *   [0, num_blocks) (num_blocks < 0: only ids >= 0 are required).
  * Returns MLA_OK, MLA_ERR_NULL, or MLA_ERR_SHAPE for the first violation,
  * whose description goes to `reason` (NUL-terminated, truncated to
  * reason_len; may be NULL).  Pure host code: no device access.
@@ -206,7 +228,7 @@ mla_status mla_check_decode_metadata(const int32_t* seq_lens, const int32_t* que
                                      const int32_t* block_table, int32_t bt_stride, int32_t B, int32_t T,
                                      int32_t max_query_len, int32_t max_seq_len, int32_t page_size,
                                      int32_t cp_world, int32_t cp_rank, int32_t cp_interleave,
-                                     int64_t num_blocks, char* reason, size_t reason_len);
+                                     int32_t mask_mode, int64_t num_blocks, char* reason, size_t reason_len);
 
 /*
  * Bytes of workspace mla_decode_partial needs for the same host arguments
@@ -305,15 +327,16 @@ mla_status mla_dcp_a2a_combine(const void* recv_y, int64_t recv_y_stride, const 
  * (PR #24453 review thread; shard layout with runs of cp_interleave tokens as
  * for mla_decode_partial), computed on the device by the same device function
  * the decode kernel uses.  row_seqlen int32 [T] (row t's visible key
- * count on rank cp_rank; usable directly as `valid[cp_rank]` of the merge) and
+ * count on rank cp_rank under mask_mode; usable directly as `valid[cp_rank]`
+ * of the merge) and
  * shard_len int32 [B] (request b's tokens stored on the rank), either may be
  * NULL.  Returns MLA_OK, MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_UNSUPPORTED or
  * MLA_ERR_HIP.
  */
 mla_status mla_dcp_local_seqlens(const int32_t* seq_lens, const int32_t* query_start_loc,
                                  int32_t B, int32_t T, int32_t cp_world, int32_t cp_rank,
-                                 int32_t cp_interleave, int32_t* row_seqlen, int32_t* shard_len,
-                                 void* hip_stream);
+                                 int32_t cp_interleave, int32_t mask_mode, int32_t* row_seqlen,
+                                 int32_t* shard_len, void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,7 @@ HEADER = os.path.join(INCLUDE, "mla.h")
 MLA_OK = 0
 D_LATENT, D_ROPE, D_ROW, D_V = 512, 64, 576, 128
 DTYPE_BF16, DTYPE_F32 = 0, 1          # MLA_DTYPE_BF16 / MLA_DTYPE_F32
+MASK_CAUSAL, MASK_CONTEXT = 0, 1       # MLA_MASK_CAUSAL / MLA_MASK_CONTEXT
 
 _lib = None
 
@@ -48,13 +49,13 @@ def load_library():
     lib.mla_decode_partial.argtypes = [
         _c_void_p, _i64, _i64, _c_void_p, _i64, _i64, _c_void_p, _i64, _i32,
         _c_void_p, _i32, _c_void_p, _c_void_p,
-        _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
+        _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
         _c_void_p, _i32, _c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p]
     lib.mla_decode_partial_noalloc.restype = _i32
     lib.mla_decode_partial_noalloc.argtypes = [
         _c_void_p, _i64, _i64, _c_void_p, _i64, _i64, _c_void_p, _i64, _i32,
         _c_void_p, _i32, _c_void_p, _c_void_p,
-        _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
+        _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
         _c_void_p, _i32, _c_void_p, _c_void_p]
     lib.mla_decode_workspace_size.restype = ctypes.c_size_t
     lib.mla_decode_workspace_size.argtypes = [_i32] * 8
@@ -71,11 +72,11 @@ def load_library():
     lib.mla_dcp_a2a_combine.argtypes = [_c_void_p, _i64, _c_void_p, _i64, _i32, _i32, _i32,
                                         _c_void_p, _c_void_p, _c_void_p]
     lib.mla_dcp_local_seqlens.restype = _i32
-    lib.mla_dcp_local_seqlens.argtypes = [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32,
+    lib.mla_dcp_local_seqlens.argtypes = [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32,
                                           _c_void_p, _c_void_p, _c_void_p]
     lib.mla_check_decode_metadata.restype = _i32
     lib.mla_check_decode_metadata.argtypes = [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32,
-                                              _i32, _i32, _i32, _i32, _i64, ctypes.c_char_p, ctypes.c_size_t]
+                                              _i32, _i32, _i32, _i32, _i32, _i64, ctypes.c_char_p, ctypes.c_size_t]
     lib.mla_calib_hbm_read.restype = _i32
     lib.mla_calib_hbm_read.argtypes = [_c_void_p, ctypes.c_size_t, _i32, _c_void_p, _c_void_p]
     lib.mla_calib_mfma_bf16.restype = _i32
@@ -139,7 +140,7 @@ def workspace_size(B, T, H, max_query_len, max_seq_len, cp_world, num_splits=0, 
 
 def mla_decode_partial(q_nope, q_pe, kv_cache, block_table, seq_lens, query_start_loc,
                        cp_world, cp_rank, scale, out, lse, *, max_query_len, max_seq_len,
-                       workspace=None, num_splits=0, stream=None, cp_interleave=1):
+                       workspace=None, num_splits=0, stream=None, cp_interleave=1, mask_mode=MASK_CAUSAL):
     """One DCP rank's partial attention; writes ``out`` [T,H,512] (bf16, or fp32
     partials when ``out`` is a float32 tensor) and ``lse`` [T,H] fp32.
     ``cp_interleave``: tokens per run of the shard layout (1 = token p on rank p mod W)."""
@@ -183,14 +184,14 @@ def mla_decode_partial(q_nope, q_pe, kv_cache, block_table, seq_lens, query_star
         _ptr(block_table), block_table.stride(0),
         _ptr(seq_lens), _ptr(query_start_loc),
         B, T, H, int(max_query_len), int(max_seq_len), int(cp_world), int(cp_rank), int(cp_interleave),
-        float(scale),
+        int(mask_mode), float(scale),
         int(num_splits), _ptr(out), out_dtype, _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "mla_decode_partial")
 
 
 def mla_decode_partial_noalloc(q_nope, q_pe, kv_cache, block_table, seq_lens, query_start_loc,
                                cp_world, cp_rank, scale, out, lse, *, max_query_len, max_seq_len,
-                               num_splits=0, stream=None, cp_interleave=1):
+                               num_splits=0, stream=None, cp_interleave=1, mask_mode=MASK_CAUSAL):
     """mla_decode_partial without a workspace (the library's per-GPU scratch array
     holds the split partials): for callers that cannot allocate."""
     lib = load_library()
@@ -211,7 +212,7 @@ def mla_decode_partial_noalloc(q_nope, q_pe, kv_cache, block_table, seq_lens, qu
         _ptr(q_nope), q_nope.stride(0), q_nope.stride(1), _ptr(q_pe), q_pe.stride(0), q_pe.stride(1),
         _ptr(kv_cache), kv_cache.stride(0), page, _ptr(block_table), block_table.stride(0),
         _ptr(seq_lens), _ptr(query_start_loc), B, T, H, int(max_query_len), int(max_seq_len),
-        int(cp_world), int(cp_rank), int(cp_interleave), float(scale), int(num_splits),
+        int(cp_world), int(cp_rank), int(cp_interleave), int(mask_mode), float(scale), int(num_splits),
         _ptr(out), out_dtype, _ptr(lse), _stream(stream))
     _check(st, "mla_decode_partial_noalloc")
 
@@ -340,7 +341,7 @@ def calib_mfma_bf16(iters, sink, stream=None) -> float:
 
 
 def mla_dcp_local_seqlens(seq_lens, query_start_loc, T, cp_world, cp_rank, row_seqlen=None,
-                          shard_len=None, stream=None, cp_interleave=1):
+                          shard_len=None, stream=None, cp_interleave=1, mask_mode=MASK_CAUSAL):
     """Per-row visible key counts [T] and per-request stored token counts [B] on rank cp_rank."""
     lib = load_library()
     _need(seq_lens, torch.int32, "seq_lens", 1)
@@ -355,6 +356,6 @@ def mla_dcp_local_seqlens(seq_lens, query_start_loc, T, cp_world, cp_rank, row_s
         if shard_len.shape[0] != B:
             raise MlaError("shard_len: expected [B]")
     st = lib.mla_dcp_local_seqlens(_ptr(seq_lens), _ptr(query_start_loc), B, int(T), int(cp_world),
-                                   int(cp_rank), int(cp_interleave), _ptr(row_seqlen), _ptr(shard_len),
-                                   _stream(stream))
+                                   int(cp_rank), int(cp_interleave), int(mask_mode), _ptr(row_seqlen),
+                                   _ptr(shard_len), _stream(stream))
     _check(st, "mla_dcp_local_seqlens")

@@ -187,6 +187,7 @@ size_t workspace_bytes_for(const Plan& p, int T, int H) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 bool dtype_ok(int32_t d) { return d == MLA_DTYPE_BF16 || d == MLA_DTYPE_F32; }
+bool mask_ok(int32_t m) { return m == MLA_MASK_CAUSAL || m == MLA_MASK_CONTEXT; }
 
 mla_status fail(char* reason, size_t len, const char* fmt, ...) {
   if (reason && len > 0) {
@@ -239,10 +240,10 @@ mla_status mla_check_decode_metadata(const int32_t* seq_lens, const int32_t* que
                                      const int32_t* block_table, int32_t bt_stride, int32_t B, int32_t T,
                                      int32_t max_query_len, int32_t max_seq_len, int32_t page_size,
                                      int32_t cp_world, int32_t cp_rank, int32_t cp_interleave,
-                                     int64_t num_blocks, char* reason, size_t reason_len) {
+                                     int32_t mask_mode, int64_t num_blocks, char* reason, size_t reason_len) {
   if (reason && reason_len) reason[0] = 0;
   if (B < 0 || T < 0 || page_size < 1 || !layout_ok(cp_world, cp_interleave) || cp_rank < 0 ||
-      cp_rank >= cp_world || bt_stride < 1)
+      cp_rank >= cp_world || bt_stride < 1 || !mask_ok(mask_mode))
     return fail(reason, reason_len, "invalid sizes");
   if (B == 0) return T == 0 ? MLA_OK : fail(reason, reason_len, "T = %d tokens without requests", T);
   if (!seq_lens || !query_start_loc || !block_table) return MLA_ERR_NULL;
@@ -259,7 +260,7 @@ mla_status mla_check_decode_metadata(const int32_t* seq_lens, const int32_t* que
     if (S < q) return fail(reason, reason_len, "request %d: seq_len %d < its %d query rows", b, S, q);
     if (S > max_seq_len)
       return fail(reason, reason_len, "request %d: seq_len %d > max_seq_len %d", b, S, max_seq_len);
-    const int64_t lc = host_shard_count(S, cp_world, cp_rank, cp_interleave);
+    const int64_t lc = host_shard_count(mask_mode == MLA_MASK_CONTEXT ? S - q : S, cp_world, cp_rank, cp_interleave);
     const int64_t nb = ceil_div(lc, page_size);
     if (nb > bt_stride)
       return fail(reason, reason_len, "request %d needs %lld blocks on rank %d, the block table row has %d", b,
@@ -299,12 +300,13 @@ static mla_status decode_impl(
     const int32_t* block_table, int32_t bt_stride,
     const int32_t* seq_lens, const int32_t* query_start_loc,
     int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
-    int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, float scale, int32_t num_splits,
+    int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, int32_t mask_mode, float scale,
+    int32_t num_splits,
     void* out, int32_t out_dtype, float* lse,
     void* workspace, size_t workspace_bytes, void* hip_stream, bool noalloc) {
   if (B < 0 || T < 0 || H < 1 || H > MLA_MAX_HEADS || page_size < 1 || !layout_ok(cp_world, cp_interleave) ||
       cp_rank < 0 || cp_rank >= cp_world || max_query_len < 0 || max_seq_len < 0 ||
-      num_splits < 0 || !isfinite(scale) || !(scale > 0.f) || !dtype_ok(out_dtype))
+      num_splits < 0 || !isfinite(scale) || !(scale > 0.f) || !dtype_ok(out_dtype) || !mask_ok(mask_mode))
     return MLA_ERR_SHAPE;
   if (B == 0 && T > 0) return MLA_ERR_SHAPE;   // tokens without requests
   if (B == 0 || T == 0) return MLA_OK;
@@ -338,7 +340,7 @@ static mla_status decode_impl(
     char why[256];
     const mla_status cst = mla_check_decode_metadata(
         hs.data(), hq.data(), hb.data(), bt_stride, B, T, max_query_len, max_seq_len, page_size, cp_world, cp_rank,
-        cp_interleave, blocks_in_allocation(kv_cache, kv_block_stride, page_size), why, sizeof(why));
+        cp_interleave, mask_mode, blocks_in_allocation(kv_cache, kv_block_stride, page_size), why, sizeof(why));
     if (cst != MLA_OK) {
       fprintf(stderr, "mla_decode_partial (MLA_DEBUG): %s\n", why);
       return cst;
@@ -365,7 +367,7 @@ static mla_status decode_impl(
   p.page_shift = (page_size & (page_size - 1)) == 0 ? __builtin_ctz((unsigned)page_size) : -1;
   p.bt = block_table; p.bt_stride = bt_stride;
   p.seq_lens = seq_lens; p.qsl = query_start_loc;
-  p.B = B; p.T = T; p.H = H; p.W = cp_world; p.r = cp_rank; p.I = cp_interleave;
+  p.B = B; p.T = T; p.H = H; p.W = cp_world; p.r = cp_rank; p.I = cp_interleave; p.mode = mask_mode;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
   p.chunk = plan.chunk; p.hblocks = plan.hblocks; p.max_splits = plan.max_splits;
   p.out = out_dtype == MLA_DTYPE_BF16 ? (uint16_t*)out : nullptr;
@@ -404,12 +406,13 @@ mla_status mla_decode_partial(
     const int32_t* block_table, int32_t bt_stride,
     const int32_t* seq_lens, const int32_t* query_start_loc,
     int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
-    int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, float scale, int32_t num_splits,
+    int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, int32_t mask_mode, float scale,
+    int32_t num_splits,
     void* out, int32_t out_dtype, float* lse,
     void* workspace, size_t workspace_bytes, void* hip_stream) {
   return decode_impl(q_nope, qn_stride_t, qn_stride_h, q_pe, qp_stride_t, qp_stride_h, kv_cache, kv_block_stride,
                      page_size, block_table, bt_stride, seq_lens, query_start_loc, B, T, H, max_query_len,
-                     max_seq_len, cp_world, cp_rank, cp_interleave, scale, num_splits, out, out_dtype, lse,
+                     max_seq_len, cp_world, cp_rank, cp_interleave, mask_mode, scale, num_splits, out, out_dtype, lse,
                      workspace, workspace_bytes, hip_stream, false);
 }
 
@@ -420,11 +423,12 @@ mla_status mla_decode_partial_noalloc(
     const int32_t* block_table, int32_t bt_stride,
     const int32_t* seq_lens, const int32_t* query_start_loc,
     int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
-    int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, float scale, int32_t num_splits,
+    int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, int32_t mask_mode, float scale,
+    int32_t num_splits,
     void* out, int32_t out_dtype, float* lse, void* hip_stream) {
   return decode_impl(q_nope, qn_stride_t, qn_stride_h, q_pe, qp_stride_t, qp_stride_h, kv_cache, kv_block_stride,
                      page_size, block_table, bt_stride, seq_lens, query_start_loc, B, T, H, max_query_len,
-                     max_seq_len, cp_world, cp_rank, cp_interleave, scale, num_splits, out, out_dtype, lse,
+                     max_seq_len, cp_world, cp_rank, cp_interleave, mask_mode, scale, num_splits, out, out_dtype, lse,
                      nullptr, 0, hip_stream, true);
 }
 
@@ -502,9 +506,10 @@ mla_status mla_dcp_a2a_combine(const void* recv_y, int64_t recv_y_stride, const 
 
 mla_status mla_dcp_local_seqlens(const int32_t* seq_lens, const int32_t* query_start_loc,
                                  int32_t B, int32_t T, int32_t cp_world, int32_t cp_rank,
-                                 int32_t cp_interleave, int32_t* row_seqlen, int32_t* shard_len,
-                                 void* hip_stream) {
-  if (B < 0 || T < 0 || !layout_ok(cp_world, cp_interleave) || cp_rank < 0 || cp_rank >= cp_world)
+                                 int32_t cp_interleave, int32_t mask_mode, int32_t* row_seqlen,
+                                 int32_t* shard_len, void* hip_stream) {
+  if (B < 0 || T < 0 || !layout_ok(cp_world, cp_interleave) || cp_rank < 0 || cp_rank >= cp_world ||
+      !mask_ok(mask_mode))
     return MLA_ERR_SHAPE;
   if (B == 0 && T > 0) return MLA_ERR_SHAPE;
   if (B == 0 && T == 0) return MLA_OK;
@@ -512,7 +517,7 @@ mla_status mla_dcp_local_seqlens(const int32_t* seq_lens, const int32_t* query_s
   mla_status st = check_device();
   if (st != MLA_OK) return st;
   hipError_t e = mla::launch_local_seqlens(seq_lens, query_start_loc, B, T, cp_world, cp_rank,
-                                           cp_interleave, row_seqlen, shard_len, (hipStream_t)hip_stream);
+                                           cp_interleave, mask_mode, row_seqlen, shard_len, (hipStream_t)hip_stream);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

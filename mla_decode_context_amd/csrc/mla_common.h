@@ -47,8 +47,15 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 struct RowInfo {
   int b;        // request
   int L;        // visible local keys of this row on rank r
-  int Lc;       // local keys of the request stored on rank r
 };
+
+// Mask modes of a decode call.  kMaskCausal: row i of a request (global
+// position p = S - Q + i) sees the keys 0..p (per rank, the interleaved DCP
+// mask).  kMaskContext: every row of the request sees the keys 0..S-Q-1, its
+// tokens before the query tokens, without a causal mask (the context stage of
+// the two-stage split of a decode with more than one query row).
+constexpr int kMaskCausal = 0;
+constexpr int kMaskContext = 1;
 
 __device__ __forceinline__ int ceil_div_pos(int n, int W) { return n > 0 ? (n + W - 1) / W : 0; }
 
@@ -73,9 +80,15 @@ __device__ __forceinline__ int shard_position(int j, int W, int r, int I) {
   return (run * W + r) * I + (j - run * I);
 }
 
+// Local keys that row i of a request (S tokens, Q query rows) sees on rank r:
+// a prefix of the rank's local order under either mask mode.
+__device__ __forceinline__ int row_key_count(int S, int Q, int i, int W, int r, int I, int mode) {
+  return shard_count(mode == kMaskContext ? S - Q : S - Q + i + 1, W, r, I);
+}
+
 __device__ __forceinline__ RowInfo locate_row(const int32_t* __restrict__ qsl,
                                               const int32_t* __restrict__ seq_lens,
-                                              int B, int t, int W, int r, int I) {
+                                              int B, int t, int W, int r, int I, int mode) {
   // last b with qsl[b] <= t; it has qsl[b+1] > t because t < qsl[B]
   int lo = 0, hi = B - 1;
   while (lo < hi) {
@@ -84,12 +97,9 @@ __device__ __forceinline__ RowInfo locate_row(const int32_t* __restrict__ qsl,
   }
   const int q0 = qsl[lo];
   const int q = qsl[lo + 1] - q0;
-  const int S = seq_lens[lo];
-  const int p = S - q + (t - q0);
   RowInfo ri;
   ri.b = lo;
-  ri.L = shard_count(p + 1, W, r, I);
-  ri.Lc = shard_count(S, W, r, I);
+  ri.L = row_key_count(seq_lens[lo], q, t - q0, W, r, I, mode);
   return ri;
 }
 

@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams a) {
   const int t = blockIdx.x / a.hblocks;
   const int hb = blockIdx.x - t * a.hblocks;
   const int split = blockIdx.y;
-  const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r, a.I);
+  const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r, a.I, a.mode);
   const int L = ri.L;
   const int nsplit = num_splits_of(L, a.chunk, (int)gridDim.y);
   if (split >= nsplit) return;
@@ -388,10 +388,10 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams a) {
 }
 
 __global__ __launch_bounds__(256) void local_seqlens_kernel(const int32_t* seq_lens, const int32_t* qsl,
-                                                            int B, int T, int W, int r, int I,
+                                                            int B, int T, int W, int r, int I, int mode,
                                                             int32_t* row_seqlen, int32_t* shard_len) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (row_seqlen && i < T) row_seqlen[i] = locate_row(qsl, seq_lens, B, i, W, r, I).L;
+  if (row_seqlen && i < T) row_seqlen[i] = locate_row(qsl, seq_lens, B, i, W, r, I, mode).L;
   if (shard_len && i < B) shard_len[i] = shard_count(seq_lens[i], W, r, I);
 }
 
@@ -730,7 +730,7 @@ __device__ __forceinline__ int request_units(const DecodeParams& a, int I, int b
   Q = a.qsl[b + 1] - q0;
   S = a.seq_lens[b];
   int u = 0;
-  for (int i = 0; i < Q; ++i) u += kRowUnits + h16_stages(shard_count(S - Q + i + 1, a.W, a.r, I));
+  for (int i = 0; i < Q; ++i) u += kRowUnits + h16_stages(row_key_count(S, Q, i, a.W, a.r, I, a.mode));
   return u;
 }
 
@@ -746,7 +746,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a
     // Grid (token, split): split s takes keys [s*chunk, (s+1)*chunk) of the row.
     const int t = blockIdx.x;
     const int split = blockIdx.y;
-    const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r, I);
+    const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r, I, a.mode);
     const int nsplit = num_splits_of(ri.L, a.chunk, (int)gridDim.y);
     if (split >= nsplit) return;
     if (ri.L == 0) {
@@ -822,7 +822,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a
         i = 0;
         continue;
       }
-      const int L = shard_count(S - Q + i + 1, a.W, a.r, I);
+      const int L = row_key_count(S, Q, i, a.W, a.r, I, a.mode);
       const int n = h16_stages(L);
       const int t = q0 + i;
       if (pos + kRowUnits + n > x0) {
@@ -938,11 +938,11 @@ hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t stream) {
 }
 
 hipError_t launch_local_seqlens(const int32_t* seq_lens, const int32_t* qsl, int B, int T, int W,
-                                int r, int I, int32_t* row_seqlen, int32_t* shard_len, hipStream_t stream) {
+                                int r, int I, int mode, int32_t* row_seqlen, int32_t* shard_len, hipStream_t stream) {
   const int n = T > B ? T : B;
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(local_seqlens_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, seq_lens, qsl,
-                     B, T, W, r, I, row_seqlen, shard_len);
+                     B, T, W, r, I, mode, row_seqlen, shard_len);
   return hipGetLastError();
 }
 

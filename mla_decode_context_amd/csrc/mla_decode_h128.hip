@@ -115,7 +115,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
   const int hb = item % hblocks;
   const int t = (item / hblocks) % a.T;
   const int split = item / (hblocks * a.T);
-  const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r, kRuns ? a.I : 1);
+  const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r, kRuns ? a.I : 1, a.mode);
   const int L = ri.L;
   const int nsplit = num_splits_of(L, a.chunk, a.max_splits);
   if (split >= nsplit) return;
@@ -475,7 +475,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
 // group hg): thread (head 16hg + tid / 16, dims 128qd + 8(tid % 16) .. +8).
 __global__ __launch_bounds__(256) void combine_fixed_kernel(const DecodeParams a) {
   const int t = blockIdx.x;
-  const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r, a.I);
+  const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r, a.I, a.mode);
   const int np = num_splits_of(ri.L, a.chunk, a.max_splits);
   if (np <= 1) return;
   const int h = 16 * blockIdx.z + (threadIdx.x >> 4);
@@ -550,12 +550,22 @@ __device__ __forceinline__ UnitInfo unit_info(const DecodeParams& a, int u, cons
   const int Q = rq[b];
   const int S = rs[b];
   const int c = s * a.chunk;
-  // Row i (global position S - Q + i) sees more than c local keys exactly when
-  // it sits past the position of local key c, i.e. i >= pos(c) - S + Q.  Split 0
-  // also keeps the rows without keys (they write their empty result).
-  ui.first = s == 0 ? 0 : max(0, shard_position(c, a.W, a.r, a.I) - S + Q);
+  int cnt;
+  if (a.mode == kMaskContext) {
+    // Every row sees the same Lx keys: all rows have keys in split s when
+    // Lx > c (split 0 keeps them regardless: rows without keys write their
+    // empty result).
+    const int Lx = shard_count(S - Q, a.W, a.r, a.I);
+    ui.first = (s == 0 || Lx > c) ? 0 : Q;
+    cnt = min(Lx - c, a.chunk);
+  } else {
+    // Row i (global position S - Q + i) sees more than c local keys exactly
+    // when it sits past the position of local key c, i.e. i >= pos(c) - S + Q.
+    // Split 0 also keeps the rows without keys (they write their empty result).
+    ui.first = s == 0 ? 0 : max(0, shard_position(c, a.W, a.r, a.I) - S + Q);
+    cnt = min(shard_count(S, a.W, a.r, a.I) - c, a.chunk);
+  }
   ui.rows = max(0, Q - ui.first);
-  const int cnt = min(shard_count(S, a.W, a.r, a.I) - c, a.chunk);
   ui.stages = ui.rows > 0 && cnt > 0 ? (cnt + kXStep - 1) / kXStep : 0;
   return ui;
 }

@@ -17,6 +17,7 @@ struct DecodeParams {
   const int32_t* qsl;
   int32_t B, T, H, W, r;
   int32_t I;               // shard run length: token p lives on rank (p div I) mod W
+  int32_t mode;            // kMaskCausal or kMaskContext (which keys a row sees)
   float scale_log2;        // softmax scale * log2(e): scores are kept in base 2
   int32_t chunk;           // keys per split (multiple of the 32-key step)
   int32_t hblocks;         // head blocks per query token
@@ -66,7 +67,7 @@ hipError_t launch_decode(const DecodeParams& p, int mtiles, int max_splits, int 
 // items longest first (the decode grid then runs them in that order).
 hipError_t launch_decode_h128(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_local_seqlens(const int32_t* seq_lens, const int32_t* qsl, int B, int T, int W,
-                                int r, int I, int32_t* row_seqlen, int32_t* shard_len, hipStream_t stream);
+                                int r, int I, int mode, int32_t* row_seqlen, int32_t* shard_len, hipStream_t stream);
 hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t stream);
 hipError_t launch_lse_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_merge_v_up(const MergeParams& p, hipStream_t stream);

@@ -93,6 +93,58 @@ class DeviceWorkload:
             mla.mla_dcp_local_seqlens(self.seq_lens, self.qsl, self.T, self.W, r,
                                       row_seqlen=self.valid[r], stream=stream, cp_interleave=self.I)
 
+    # ---- the two-stage decode (query rows > 1): context stage per rank, one
+    # query stage over the query tokens' own KV, merge of the W + 1 partials ----
+
+    def setup_two_stage(self):
+        from . import workloads as WL
+        rows, table, qlens = WL.query_part_layout(self.wl)
+        dev = self.device
+        T, H, W = self.T, self.H, self.W
+        self.qkv = _bf16(rows, dev).view(T, 1, 576)          # one-token pages
+        self.q_table = _i32(table, dev)
+        self.q_lens = _i32(qlens, dev)
+        dt = self.outs.dtype
+        self.outs2 = torch.empty((W + 1, T, H, 512), dtype=dt, device=dev)
+        self.lses2 = torch.empty((W + 1, T, H), dtype=torch.float32, device=dev)
+        self.valid2 = torch.empty((W + 1, T), dtype=torch.int32, device=dev)
+        n = mla.workspace_size(self.B, T, H, self.max_query_len, self.max_query_len, 1, self.num_splits)
+        self.q_workspace = torch.zeros(n, dtype=torch.uint8, device=dev) if n else None
+
+    def context_partial(self, r: int, stream=None):
+        mla.mla_decode_partial(
+            self.q_nope, self.q_pe, self.caches[r], self.tables[r], self.seq_lens, self.qsl,
+            self.W, r, self.scale, self.outs2[r], self.lses2[r],
+            max_query_len=self.max_query_len, max_seq_len=self.max_seq_len, workspace=self.workspace,
+            num_splits=self.num_splits, stream=stream, cp_interleave=self.I, mask_mode=mla.MASK_CONTEXT)
+
+    def query_partial(self, stream=None):
+        mla.mla_decode_partial(
+            self.q_nope, self.q_pe, self.qkv, self.q_table, self.q_lens, self.qsl, 1, 0, self.scale,
+            self.outs2[self.W], self.lses2[self.W], max_query_len=self.max_query_len,
+            max_seq_len=self.max_query_len, workspace=self.q_workspace, num_splits=self.num_splits, stream=stream)
+
+    def two_stage_counts(self, stream=None):
+        for r in range(self.W):
+            mla.mla_dcp_local_seqlens(self.seq_lens, self.qsl, self.T, self.W, r, row_seqlen=self.valid2[r],
+                                      stream=stream, cp_interleave=self.I, mask_mode=mla.MASK_CONTEXT)
+        mla.mla_dcp_local_seqlens(self.q_lens, self.qsl, self.T, 1, 0, row_seqlen=self.valid2[self.W],
+                                  stream=stream)
+
+    def two_stage_step(self, stream=None):
+        """The two-stage path: every rank's context partial, the query partial,
+        their counts and the merge of the W + 1 partials into out / out_lse
+        (or out_proj with W_UV)."""
+        for r in range(self.W):
+            self.context_partial(r, stream)
+        self.query_partial(stream)
+        self.two_stage_counts(stream)
+        if self.w_uv is not None:
+            mla.mla_merge_v_up_proj(self.outs2, self.lses2, self.valid2, self.w_uv, self.out_proj, self.out_lse,
+                                    stream=stream)
+        else:
+            mla.mla_lse_merge(self.outs2, self.lses2, self.valid2, self.out, self.out_lse, stream=stream)
+
     def merge(self, stream=None):
         mla.mla_lse_merge(self.outs, self.lses, self.valid, self.out, self.out_lse, stream=stream)
 

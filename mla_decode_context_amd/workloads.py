@@ -156,6 +156,29 @@ class Workload:
         return _request_kv(self.seed, b, int(self.seq_lens[b]))
 
 
+def query_part_layout(wl: Workload):
+    """The query tokens' own KV rows laid out for the query stage of the
+    two-stage decode: rows [T, 576] (row t = the KV row of query token t, i.e.
+    global position S_b - Q_b + i of its request), a block table [B, max Q]
+    naming row qsl[b] + j as block j of request b when the rows are read as a
+    cache of one-token pages (-1 past Q_b), and the per-request lengths Q_b.
+    Pure layout: copies rows, computes no attention."""
+    T, B = wl.T, wl.B
+    rows = np.empty((T, D_ROW), dtype=np.uint16)
+    qsl = wl.query_start_loc
+    for b in range(B):
+        q0, q1 = int(qsl[b]), int(qsl[b + 1])
+        if q1 > q0:
+            S = int(wl.seq_lens[b])
+            rows[q0:q1] = wl.global_kv(b)[S - (q1 - q0):S]
+    mq = max(1, wl.max_query_len)
+    table = np.full((B, mq), -1, dtype=np.int32)
+    for b in range(B):
+        q0, q1 = int(qsl[b]), int(qsl[b + 1])
+        table[b, :q1 - q0] = np.arange(q0, q1, dtype=np.int32)
+    return rows, table, wl.query_lens.astype(np.int32).copy()
+
+
 def _request_kv(seed: int, b: int, S: int) -> np.ndarray:
     rng = np.random.default_rng([seed, 2, b])
     return _normal_bf16(rng, (S, D_ROW))

@@ -33,12 +33,13 @@ def test_status_strings():
 
 def _decode(**kw):
     a = dict(q_nope=P, qn_t=16 * 512, qn_h=512, q_pe=P, qp_t=16 * 64, qp_h=64, kv=P, kv_bs=16 * 576, page=16,
-             bt=P, bt_stride=4, seq=P, qsl=P, B=2, T=4, H=16, mq=2, ms=100, W=2, r=0, I=1, scale=0.07,
+             bt=P, bt_stride=4, seq=P, qsl=P, B=2, T=4, H=16, mq=2, ms=100, W=2, r=0, I=1, mask=0, scale=0.07,
              splits=0, out=P, dtype=0, lse=P, ws=None, ws_bytes=0)
     a.update(kw)
     return lib.mla_decode_partial(a["q_nope"], a["qn_t"], a["qn_h"], a["q_pe"], a["qp_t"], a["qp_h"], a["kv"],
                                   a["kv_bs"], a["page"], a["bt"], a["bt_stride"], a["seq"], a["qsl"], a["B"],
-                                  a["T"], a["H"], a["mq"], a["ms"], a["W"], a["r"], a["I"], a["scale"], a["splits"],
+                                  a["T"], a["H"], a["mq"], a["ms"], a["W"], a["r"], a["I"], a["mask"], a["scale"],
+                                  a["splits"],
                                   a["out"], a["dtype"], a["lse"], a["ws"], a["ws_bytes"], None)
 
 
@@ -55,6 +56,7 @@ def _decode(**kw):
     (dict(I=0), SHAPE), (dict(I=-3), SHAPE), (dict(W=4, I=1 << 29), SHAPE),
     (dict(W=2, I=1 << 28, T=0), OK),
     (dict(dtype=2), SHAPE), (dict(dtype=-1), SHAPE), (dict(dtype=1, T=0), OK),
+    (dict(mask=2), SHAPE), (dict(mask=-1), SHAPE), (dict(mask=1, T=0), OK),
 ])
 def test_decode_argument_checks(kw, code):
     assert _decode(**kw) == code
@@ -104,10 +106,11 @@ def test_merge_argument_checks():
     assert v(P, 0, P, None, 2, -1, 16, P, P, None, None) == SHAPE
     assert v(P, 7, P, None, 2, 4, 16, P, P, None, None) == SHAPE
     s = lib.mla_dcp_local_seqlens
-    assert s(P, P, 2, 4, 2, 2, 1, P, P, None) == SHAPE
-    assert s(P, P, 2, 4, 2, 1, 0, P, P, None) == SHAPE
-    assert s(None, P, 2, 4, 2, 1, 1, P, P, None) == NULL
-    assert s(P, P, 0, 0, 2, 1, 16, P, P, None) == OK
+    assert s(P, P, 2, 4, 2, 2, 1, 0, P, P, None) == SHAPE
+    assert s(P, P, 2, 4, 2, 1, 0, 0, P, P, None) == SHAPE
+    assert s(P, P, 2, 4, 2, 1, 1, 5, P, P, None) == SHAPE          # unknown mask mode
+    assert s(None, P, 2, 4, 2, 1, 1, 0, P, P, None) == NULL
+    assert s(P, P, 0, 0, 2, 1, 16, 1, P, P, None) == OK
 
 
 def test_exchange_argument_checks():
@@ -148,7 +151,8 @@ def test_calibration_argument_checks():
 
 def _meta(**kw):
     """A valid metadata set: 3 requests, W = 2, rank 1, page 4, 40 blocks."""
-    m = dict(S=[9, 2, 17], qsl=[0, 2, 3, 7], bt=None, bt_stride=3, T=7, mq=4, ms=17, P=4, W=2, r=1, I=1, nblk=40)
+    m = dict(S=[9, 2, 17], qsl=[0, 2, 3, 7], bt=None, bt_stride=3, T=7, mq=4, ms=17, P=4, W=2, r=1, I=1, mode=0,
+             nblk=40)
     m.update(kw)
     if m["bt"] is None:
         m["bt"] = [0, 1, -1, 2, -1, -1, 3, 4, 5]     # rank 1 holds 4, 1, 8 tokens -> 1, 1, 2 blocks
@@ -161,7 +165,7 @@ def _check_meta(m):
     bt = (ctypes.c_int32 * len(m["bt"]))(*m["bt"])
     why = ctypes.create_string_buffer(256)
     st = lib.mla_check_decode_metadata(S, q, bt, m["bt_stride"], len(m["S"]), m["T"], m["mq"], m["ms"], m["P"],
-                                       m["W"], m["r"], m["I"], m["nblk"], why, 256)
+                                       m["W"], m["r"], m["I"], m["mode"], m["nblk"], why, 256)
     return st, why.value.decode()
 
 
@@ -193,4 +197,10 @@ def test_check_metadata_accepts_valid_sets():
     bt = [0, 1, 2, -1, -1, 3, -1, -1, -1, -1, 4, 5, 6, 7, 8]
     assert _check_meta(_meta(W=1, r=0, bt=bt, bt_stride=5))[0] == OK
     assert _check_meta(_meta(S=[], qsl=[0], bt=[0], T=0))[0] == OK
+    # context mode reads only the first S - Q tokens' share: request 2 (S 17,
+    # Q 4) holds 6 of its 13 context tokens on rank 1 -> 2 blocks, request 0
+    # (S 9, Q 2) 3 of 7 -> 1 block, request 1 none; entries past them unread
+    assert _check_meta(_meta(mode=1, bt=[0, -1, -1, -1, -1, -1, 3, 4, -1]))[0] == OK
+    assert _check_meta(_meta(mode=0, bt=[0, -1, -1, -1, -1, -1, 3, 4, -1]))[0] == SHAPE
+    assert _check_meta(_meta(mode=2))[0] == SHAPE
     assert _check_meta(_meta(S=[], qsl=[0], bt=[0], T=2))[0] == SHAPE
