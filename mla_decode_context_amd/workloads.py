@@ -51,6 +51,8 @@ D_ROPE = 64             # qk_rope_head_dim: width of k_pe / q_pe
 D_ROW = D_LATENT + D_ROPE
 D_V = 128               # v_head_dim: width after the W_UV up-projection
 BF16_NAN = 0x7FC0
+FP8_NAN = 0x7F          # E4M3 (OCP "fn") NaN code
+FP8_SCALE = 0.0137      # scale of the FP8 caches: values are code * FP8_SCALE
 
 # The five workloads.  Lengths are global totals S_b including the request's own
 # query tokens; "lo..hi" draws are inclusive integer uniforms.
@@ -75,12 +77,16 @@ CONFIGS = {
              "W=4, context 512..16384, page 64, W_UV [128,512,128] ~ 0.02*N(0,1)",
         B=98, n_decode=96, decode_q=(1, 2, 4), chunk_q=512, seq_range=(512, 16384),
         H=128, W=4, P=64, seed=4, w_uv=True),
+    "plain_fp8": dict(
+        desc="plain with an FP8 E4M3 latent cache (one scale per cache): batch 64, Q=1, H=16, W=1, "
+             "context 1024..8192, page 64",
+        B=64, seq_range=(1024, 8192), q_len=1, H=16, W=1, P=64, seed=1, kv_fp8=True),
     "mtp_dcp4_pages": dict(
         desc="mtp_dcp4 with whole pages per shard: runs of 64 tokens (one page) "
              "dealt to the 4 shards in turn",
         B=128, seq_range=(1024, 4096), q_len=2, H=128, W=4, P=64, seed=2, I=64),
 }
-CONFIG_ORDER = ["tiny_dcp", "plain", "mtp_dcp4", "long_dcp8", "mixed_wuv", "mtp_dcp4_pages"]
+CONFIG_ORDER = ["tiny_dcp", "plain", "mtp_dcp4", "long_dcp8", "mixed_wuv", "mtp_dcp4_pages", "plain_fp8"]
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -88,6 +94,28 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     bias = ((u >> 16) & np.uint32(1)) + np.uint32(0x7FFF)
     return ((u + bias) >> 16).astype(np.uint16)
+
+
+def _e4m3_magnitudes() -> np.ndarray:
+    """Values of the non-negative finite E4M3 codes 0x00 .. 0x7E, ascending."""
+    c = np.arange(0x7F)
+    e, f = c >> 3, (c & 7).astype(np.float64)
+    return np.where(e == 0, np.ldexp(f / 8.0, -6), np.ldexp(1.0 + f / 8.0, e - 7))
+
+
+def f64_to_fp8_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest E4M3 (OCP "fn") value, ties to the even code,
+    saturating at +-448; returns uint8 codes.  Input drawing only (the
+    synthetic FP8 caches), not part of the decode."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    vals = _e4m3_magnitudes()
+    hi = np.clip(np.searchsorted(vals, a), 1, 126)
+    lo = hi - 1
+    d_lo, d_hi = a - vals[lo], vals[hi] - a
+    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0)), hi, lo)
+    code = np.where(a >= vals[126], 126, code)
+    return (code | (np.signbit(x).astype(np.int64) << 7)).astype(np.uint8)
 
 
 def _normal_bf16(rng: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
@@ -138,6 +166,7 @@ class Workload:
     shards: list = field(default_factory=list)
     w_uv: np.ndarray | None = None   # uint16 [H,512,128]
     I: int = 1                       # shard run length: token p on shard (p div I) mod W
+    kv_scale: float | None = None    # FP8 caches: uint8 E4M3 codes, value = code * kv_scale
 
     @property
     def T(self) -> int:
@@ -152,8 +181,9 @@ class Workload:
         return int(self.seq_lens.max()) if self.B else 0
 
     def global_kv(self, b: int) -> np.ndarray:
-        """Regenerate the global KV rows [S_b, 576] (bf16 bits) of request b."""
-        return _request_kv(self.seed, b, int(self.seq_lens[b]))
+        """Regenerate the global KV rows [S_b, 576] of request b as stored: bf16
+        bits, or E4M3 codes for an FP8 cache."""
+        return _request_kv(self.seed, b, int(self.seq_lens[b]), self.kv_scale)
 
 
 def query_part_layout(wl: Workload):
@@ -164,7 +194,7 @@ def query_part_layout(wl: Workload):
     cache of one-token pages (-1 past Q_b), and the per-request lengths Q_b.
     Pure layout: copies rows, computes no attention."""
     T, B = wl.T, wl.B
-    rows = np.empty((T, D_ROW), dtype=np.uint16)
+    rows = np.empty((T, D_ROW), dtype=np.uint8 if wl.kv_scale is not None else np.uint16)
     qsl = wl.query_start_loc
     for b in range(B):
         q0, q1 = int(qsl[b]), int(qsl[b + 1])
@@ -179,9 +209,12 @@ def query_part_layout(wl: Workload):
     return rows, table, wl.query_lens.astype(np.int32).copy()
 
 
-def _request_kv(seed: int, b: int, S: int) -> np.ndarray:
+def _request_kv(seed: int, b: int, S: int, kv_scale=None) -> np.ndarray:
     rng = np.random.default_rng([seed, 2, b])
-    return _normal_bf16(rng, (S, D_ROW))
+    if kv_scale is None:
+        return _normal_bf16(rng, (S, D_ROW))
+    x = rng.standard_normal((S, D_ROW), dtype=np.float32)
+    return f64_to_fp8_e4m3_bits(x.astype(np.float64) / kv_scale)
 
 
 def _draw_lengths(cfg: dict, seed: int):
@@ -206,7 +239,7 @@ def _draw_lengths(cfg: dict, seed: int):
 
 
 def build_shard(seed: int, r: int, W: int, P: int, seq_lens: np.ndarray,
-                kv_rows_of, spare_frac: float = 0.05, I: int = 1) -> Shard:
+                kv_rows_of, spare_frac: float = 0.05, I: int = 1, fp8: bool = False) -> Shard:
     """Lay shard r's tokens of every request (p = r, r+W, ... when I = 1) into its pages.
 
     ``kv_rows_of(b)`` returns the shard-local rows of request b ([n, 576] bf16 bits)
@@ -221,7 +254,8 @@ def build_shard(seed: int, r: int, W: int, P: int, seq_lens: np.ndarray,
     perm = np.random.default_rng([seed, 3, r]).permutation(pool).astype(np.int32)
     max_blocks = max(1, int(nblk.max()) if B else 1)
     table = np.full((B, max_blocks), -1, dtype=np.int32)
-    cache = np.full((pool, P, D_ROW), BF16_NAN, dtype=np.uint16)
+    cache = np.full((pool, P, D_ROW), FP8_NAN, dtype=np.uint8) if fp8 else \
+        np.full((pool, P, D_ROW), BF16_NAN, dtype=np.uint16)
     off = 0
     for b in range(B):
         nb = int(nblk[b])
@@ -257,12 +291,15 @@ def make_workload(name: str, *, threads: int = 8, seed: int | None = None,
     P = cfg["P"] if P is None else P
     I = cfg.get("I", 1) if I is None else I
     return make_custom(name, S, Q, H=H, W=W, P=P, seed=seed,
-                       w_uv=cfg.get("w_uv", False), threads=threads, I=I)
+                       w_uv=cfg.get("w_uv", False), threads=threads, I=I,
+                       kv_scale=FP8_SCALE if cfg.get("kv_fp8") else None)
 
 
 def make_custom(name: str, seq_lens, query_lens, *, H: int, W: int, P: int, seed: int,
-                w_uv: bool = False, threads: int = 8, scale: float | None = None, I: int = 1) -> Workload:
-    """Build a workload from explicit per-request lengths."""
+                w_uv: bool = False, threads: int = 8, scale: float | None = None, I: int = 1,
+                kv_scale: float | None = None) -> Workload:
+    """Build a workload from explicit per-request lengths (an FP8 E4M3 cache
+    with that scale when kv_scale is given)."""
     S = np.asarray(seq_lens, dtype=np.int32)
     Q = np.asarray(query_lens, dtype=np.int32)
     assert S.shape == Q.shape and np.all(Q >= 0) and np.all(Q <= S)
@@ -273,15 +310,16 @@ def make_custom(name: str, seq_lens, query_lens, *, H: int, W: int, P: int, seed
     rq = np.random.default_rng([seed, 1])
     q_nope = _normal_bf16(rq, (T, H, D_LATENT))
     q_pe = _normal_bf16(rq, (T, H, D_ROPE))
-    wl = Workload(name=name, B=B, H=H, W=W, P=P, seed=seed, I=I,
+    wl = Workload(name=name, B=B, H=H, W=W, P=P, seed=seed, I=I, kv_scale=kv_scale,
                   scale=(1.0 / math.sqrt(D_V + D_ROPE)) if scale is None else scale,
                   seq_lens=S, query_lens=Q, query_start_loc=qsl, q_nope=q_nope, q_pe=q_pe)
     # Global KV is generated per request (in parallel: each request has its own
     # stream, so the result does not depend on scheduling) and scattered to shards.
     with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
-        kv = list(ex.map(lambda b: _request_kv(seed, b, int(S[b])), range(B)))
+        kv = list(ex.map(lambda b: _request_kv(seed, b, int(S[b]), kv_scale), range(B)))
         wl.shards = list(ex.map(
-            lambda r: build_shard(seed, r, W, P, S, lambda b: kv[b][shard_token_rows(int(S[b]), W, r, I)], I=I),
+            lambda r: build_shard(seed, r, W, P, S, lambda b: kv[b][shard_token_rows(int(S[b]), W, r, I)], I=I,
+                                  fp8=kv_scale is not None),
             range(W)))
     del kv
     if w_uv:

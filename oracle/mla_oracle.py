@@ -48,6 +48,33 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
+def fp8_e4m3_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of FP8 E4M3 codes (uint8), the OCP "fn" variant: sign bit,
+    4 exponent bits with bias 7, 3 fraction bits; exponent field 0 holds the
+    subnormals f/8 * 2^-6; the code S.1111.111 is NaN and there are no
+    infinities (largest finite 448).
+
+    The pages give no convention for an FP8 latent cache ("flashattn_mla" API
+    page: FP8 KV cache not yet supported).  Reading: each cached element is an
+    E4M3 code, and the cache carries one fp32 scale; the element's value is
+    code value * scale.
+    """
+    c = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    f = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(f / 8.0, -6), np.ldexp(1.0 + f / 8.0, e - 7))
+    return np.where((e == 15) & (f == 7), np.nan, sign * mag)
+
+
+def kv_rows_to_f64(rows: np.ndarray, kv_scale=None) -> np.ndarray:
+    """Cache rows as stored -> float64 values: bf16 bits widened exactly, or
+    (kv_scale given) FP8 E4M3 codes times the cache's scale."""
+    if kv_scale is None:
+        return bf16_bits_to_f64(rows)
+    return fp8_e4m3_bits_to_f64(rows) * float(kv_scale)
+
+
 # ---------------------------------------------------------------------------
 # Where the query rows sit, and which keys each row sees on each shard
 # ---------------------------------------------------------------------------
@@ -172,10 +199,11 @@ def attend(q_nope: np.ndarray, q_pe: np.ndarray, keys: np.ndarray, scale: float)
 
 
 def decode_partial(seq_lens, query_start_loc, q_nope_bits, q_pe_bits, global_kv, scale: float,
-                   W: int = 1, r: int = 0, tokens=None, I: int = 1):
+                   W: int = 1, r: int = 0, tokens=None, I: int = 1, kv_scale=None):
     """Shard r's partial attention for every query token (or the listed ones).
 
-    ``global_kv(b)`` returns request b's global token rows [S_b, 576] as bf16 bits.
+    ``global_kv(b)`` returns request b's global token rows [S_b, 576] as stored:
+    bf16 bits, or FP8 E4M3 codes when ``kv_scale`` (the cache's scale) is given.
     Each row attends to visible_keys(p, W, r, I).  Returns out [n,H,512], lse [n,H]
     (float64) for the selected tokens in the order given.
     """
@@ -189,7 +217,7 @@ def decode_partial(seq_lens, query_start_loc, q_nope_bits, q_pe_bits, global_kv,
         b, _, p = rows[t]
         if b not in cache:
             cache.clear()
-            cache[b] = bf16_bits_to_f64(global_kv(b))
+            cache[b] = kv_rows_to_f64(global_kv(b), kv_scale)
         keys = cache[b][visible_keys(p, W, r, I)]
         outs[n_out], lses[n_out] = attend(bf16_bits_to_f64(q_nope_bits[t]),
                                           bf16_bits_to_f64(q_pe_bits[t]), keys, scale)
@@ -231,7 +259,7 @@ def context_count(S: int, Q: int, W: int, r: int, I: int = 1) -> int:
 
 
 def decode_context_part(seq_lens, query_start_loc, q_nope_bits, q_pe_bits, global_kv, scale: float,
-                        W: int = 1, r: int = 0, tokens=None, I: int = 1):
+                        W: int = 1, r: int = 0, tokens=None, I: int = 1, kv_scale=None):
     """Stage 1 on shard r: every query row attends, without a causal mask, to
     the context keys shard r stores.  Returns out [n,H,512], lse [n,H] (empty
     context: out 0, lse -inf)."""
@@ -246,7 +274,7 @@ def decode_context_part(seq_lens, query_start_loc, q_nope_bits, q_pe_bits, globa
         b, _, _ = rows[t]
         if b not in cache:
             cache.clear()
-            cache[b] = bf16_bits_to_f64(global_kv(b))
+            cache[b] = kv_rows_to_f64(global_kv(b), kv_scale)
         S, Q = int(seq_lens[b]), qsl[b + 1] - qsl[b]
         keys = cache[b][context_keys(S, Q, W, r, I)]
         outs[n_out], lses[n_out] = attend(bf16_bits_to_f64(q_nope_bits[t]), bf16_bits_to_f64(q_pe_bits[t]),
@@ -254,7 +282,8 @@ def decode_context_part(seq_lens, query_start_loc, q_nope_bits, q_pe_bits, globa
     return outs, lses
 
 
-def decode_query_part(seq_lens, query_start_loc, q_nope_bits, q_pe_bits, global_kv, scale: float, tokens=None):
+def decode_query_part(seq_lens, query_start_loc, q_nope_bits, q_pe_bits, global_kv, scale: float, tokens=None,
+                      kv_scale=None):
     """Stage 2, once for all ranks: query row i of a request attends causally to
     the request's own query tokens 0..i (global positions S-Q .. S-Q+i)."""
     rows = query_rows(seq_lens, query_start_loc)
@@ -268,7 +297,7 @@ def decode_query_part(seq_lens, query_start_loc, q_nope_bits, q_pe_bits, global_
         b, i, _ = rows[t]
         if b not in cache:
             cache.clear()
-            cache[b] = bf16_bits_to_f64(global_kv(b))
+            cache[b] = kv_rows_to_f64(global_kv(b), kv_scale)
         S, Q = int(seq_lens[b]), qsl[b + 1] - qsl[b]
         keys = cache[b][query_part_keys(S, Q, i)]
         outs[n_out], lses[n_out] = attend(bf16_bits_to_f64(q_nope_bits[t]), bf16_bits_to_f64(q_pe_bits[t]),

@@ -105,6 +105,80 @@ def check_v_up_proj_closed_forms(seed=7) -> bool:
     return True
 
 
+# FP8 E4M3 (OCP "fn") codes and the values the format gives them: sign bit,
+# exponent bias 7, 3 fraction bits, subnormals f/8 * 2^-6, S.1111.111 NaN.
+FP8_FIXED = [
+    (0x38, 1.0), (0xB8, -1.0), (0x40, 2.0), (0x3C, 1.5), (0x30, 0.5), (0x7E, 448.0), (0xFE, -448.0),
+    (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9), (0x08, 2.0 ** -6), (0x00, 0.0), (0x80, -0.0), (0x77, 240.0),
+    (0x4D, 6.5), (0x29, 0.28125),
+]
+
+
+def _torch_widen_fp8(codes) -> np.ndarray:
+    """E4M3 codes -> float64 through torch's float8_e4m3fn dtype."""
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def check_fp8_widening() -> bool:
+    """The oracle's E4M3 decoding against fixed codes, both NaN codes, and
+    torch's float8_e4m3fn on all 256 codes; positive codes are increasing."""
+    got = O.fp8_e4m3_bits_to_f64(np.array([c for c, _ in FP8_FIXED], dtype=np.uint8))
+    for g, (c, want) in zip(got, FP8_FIXED):
+        if not (g == want and np.signbit(g) == np.signbit(want)):
+            return False
+    if not np.all(np.isnan(O.fp8_e4m3_bits_to_f64(np.array([0x7F, 0xFF], dtype=np.uint8)))):
+        return False
+    every = np.arange(256).astype(np.uint8)
+    a, b = O.fp8_e4m3_bits_to_f64(every), _torch_widen_fp8(every)
+    num = ~np.isnan(b)                       # a NaN's sign carries nothing
+    if not (np.array_equal(np.isnan(a), np.isnan(b)) and np.array_equal(a[num], b[num])
+            and np.array_equal(np.signbit(a[num]), np.signbit(b[num]))):
+        return False
+    return bool(np.all(np.diff(a[:0x7F]) > 0))
+
+
+def check_fp8_decode(seed=10) -> bool:
+    """Decode over an FP8 cache: (i) against torch SDPA on the values torch's
+    float8_e4m3fn dtype gives the codes times the scale; (ii) with a power-of-two
+    scale the values are bf16-exact, and the result equals the decode of the
+    same values stored as bf16; (iii) q = 0 gives the mean of code * scale."""
+    rng = np.random.default_rng(seed)
+    scale = 1 / math.sqrt(192)
+    for (S, Q, H, W, ks) in [(9, 3, 2, 2, 0.0137), (13, 4, 3, 1, 0.05), (20, 2, 2, 3, 1.7)]:
+        codes = rng.integers(0, 256, size=(S, 576)).astype(np.uint8)
+        codes[(codes & 0x7F) == 0x7F] = 0x3A           # no NaN codes in the rows
+        qn = _bits(rng.standard_normal((Q, H, 512)).astype(np.float32))
+        qp = _bits(rng.standard_normal((Q, H, 64)).astype(np.float32))
+        kv = _torch_widen_fp8(codes) * ks
+        q = torch.from_numpy(np.concatenate([_torch_widen(qn), _torch_widen(qp)], axis=-1)).permute(1, 0, 2)
+        for r in range(W):
+            out, lse = O.decode_partial([S], [0, Q], qn, qp, lambda b: codes, scale, W, r, kv_scale=ks)
+            mask = torch.from_numpy(O.dense_mask(S, Q, W, r))
+            ne = mask.any(dim=1).numpy()
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                q.unsqueeze(0), torch.from_numpy(kv).expand(1, H, S, 576), torch.from_numpy(kv[:, :512]).expand(1, H, S, 512),
+                attn_mask=mask.expand(1, H, Q, S), scale=scale)[0].permute(1, 0, 2).numpy()
+            if not np.allclose(out[ne], ref[ne], rtol=1e-12, atol=1e-12):
+                return False
+        # power-of-two scale: bf16-exact values, same result as a bf16 cache
+        bf = _bits((_torch_widen_fp8(codes) * 0.125).astype(np.float32))
+        o8, l8 = O.decode_partial([S], [0, Q], qn, qp, lambda b: codes, scale, 1, 0, kv_scale=0.125)
+        o16, l16 = O.decode_partial([S], [0, Q], qn, qp, lambda b: bf, scale, 1, 0)
+        if not (np.array_equal(o8, o16) and np.array_equal(l8, l16)):
+            return False
+        # q = 0: every visible key weighs the same
+        z = np.zeros_like(qn)
+        zp = np.zeros_like(qp)
+        oz, lz = O.decode_partial([S], [0, Q], z, zp, lambda b: codes, scale, 1, 0, kv_scale=ks)
+        for i in range(Q):
+            n = S - Q + i + 1
+            if not (np.allclose(oz[i], kv[:n, :512].mean(axis=0)[None], atol=1e-12)
+                    and np.allclose(lz[i], math.log(n), atol=1e-14)):
+                return False
+    return True
+
+
 def load_worked_masks():
     out = []
     with open(os.path.join(GOLDEN, "pr24453_worked_masks.txt")) as f:
@@ -540,7 +614,7 @@ def check_two_stage_merge(seed=9) -> bool:
     return True
 
 
-ALL_CHECKS = [check_bf16_widening, check_worked_masks, check_ab_example, check_counts_bruteforce,
+ALL_CHECKS = [check_bf16_widening, check_fp8_widening, check_fp8_decode, check_worked_masks, check_ab_example, check_counts_bruteforce,
               check_against_sdpa, check_closed_forms, check_merge_equals_unsharded, check_merge_identities,
               check_wuv_commutes, check_v_up_proj_closed_forms, check_runs_bruteforce,
               check_runs_merge_equals_unsharded, check_a2a_pack_combine, check_two_stage_keys,

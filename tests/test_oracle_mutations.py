@@ -127,6 +127,27 @@ def _widen_flush_subnormals(bits):          # flushes subnormals to zero
 _real_widen = O.bf16_bits_to_f64
 
 
+def _fp8_bias8(bits):                        # the FNUZ exponent bias
+    c = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    e, f = (c >> 3) & 15, (c & 7).astype(np.float64)
+    v = np.where(e == 0, np.ldexp(f / 8.0, -7), np.ldexp(1.0 + f / 8.0, e - 8))
+    return np.where(c >> 7, -v, v)
+
+
+_real_fp8 = O.fp8_e4m3_bits_to_f64
+
+
+def _fp8_subnormal_as_normal(bits):          # subnormals given an implicit leading one
+    c = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    v = _real_fp8(bits)
+    e, f = (c >> 3) & 15, (c & 7).astype(np.float64)
+    return np.where(e == 0, np.where(c >> 7, -1.0, 1.0) * np.ldexp(1.0 + f / 8.0, -6), v)
+
+
+def _kv_scale_ignored(rows, kv_scale=None):  # FP8 codes used without the cache's scale
+    return O.bf16_bits_to_f64(rows) if kv_scale is None else _real_fp8(rows)
+
+
 def _query_part_shifted(S, Q, i):            # the query part one position late
     return list(range(S - Q + 1, S - Q + i + 2))
 
@@ -164,6 +185,9 @@ MUTANTS = [
     ("bf16_bits_to_f64", _widen_as_fp16),
     ("bf16_bits_to_f64", _widen_shift15),
     ("bf16_bits_to_f64", _widen_flush_subnormals),
+    ("fp8_e4m3_bits_to_f64", _fp8_bias8),
+    ("fp8_e4m3_bits_to_f64", _fp8_subnormal_as_normal),
+    ("kv_rows_to_f64", _kv_scale_ignored),
     ("query_part_keys", _query_part_shifted),
     ("query_part_keys", _query_part_exclusive),
     ("context_keys", _context_includes_first_query),
