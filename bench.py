@@ -54,10 +54,11 @@ def workload_bytes(wl, valid):
     Flops: 2176 per visible (key, head, row) -- 1152 for the scores, 1024 for PV.
     """
     per_shard = []
+    row_bytes = 576 if wl.kv_scale is not None else 1152      # FP8 E4M3 or bf16 cache rows
     for r in range(wl.W):
         kv_tokens = int(sum(sh for sh in wl.shards[r].token_counts))
         flops = float(valid[r].astype(np.float64).sum()) * wl.H * 2176.0
-        kv = kv_tokens * 1152
+        kv = kv_tokens * row_bytes
         q = wl.T * wl.H * 1152
         out = wl.T * wl.H * 1028
         per_shard.append(dict(kv=kv, q=q, out=out, flops=flops, total=kv + q + out))
@@ -486,7 +487,7 @@ def main():
                     help="untimed steps first (the GPU's clocks settle over the first few thousand calls; "
                          "300 long_dcp8 steps are about 1 s)")
     ap.add_argument("--workload", default="long_dcp8")
-    ap.add_argument("--configs", default="plain,mtp_dcp4,mixed_wuv,mtp_dcp4_pages",
+    ap.add_argument("--configs", default="plain,plain_fp8,mtp_dcp4,mixed_wuv,mtp_dcp4_pages",
                     help="comma-separated secondary workloads ('' for none)")
     ap.add_argument("--config-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -520,8 +521,9 @@ def main():
     configs = {}
     for name in [c for c in args.configs.split(",") if c and c != args.workload]:
         print(f"[bench] {name}: generating inputs", file=sys.stderr, flush=True)
-        res, _ = time_workload(name, args.config_steps, 3 if name != "plain" else 300, torch,
-                               alternate=name == "plain")
+        plain_like = name.startswith("plain")      # 70 us steps: more of them
+        res, _ = time_workload(name, 20 * args.config_steps if plain_like else args.config_steps,
+                               300 if plain_like else 3, torch, alternate=plain_like)
         res["roofline"] = make_roofline(res, name, calib)
         configs[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()
                          if not k.startswith("_")}

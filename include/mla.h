@@ -59,6 +59,12 @@ typedef int32_t mla_status;
  * (at twice the partials' bytes). */
 #define MLA_DTYPE_BF16 0
 #define MLA_DTYPE_F32  1
+/* Element type of an FP8 latent cache (mla_decode_partial's kv_dtype): OCP
+ * FP8 E4M3 ("fn": exponent bias 7, no infinities, largest finite 448) codes,
+ * one fp32 scale per cache, element value = code value * kv_scale.  The pages
+ * leave the convention open (FP8 is "not yet supported" there); this is the
+ * reading this library implements. */
+#define MLA_DTYPE_FP8_E4M3 2
 
 /* Which keys a query row sees (mask_mode of the decode calls).
  * MLA_MASK_CAUSAL: row i of a request, at global position p = S_b - Q_b + i,
@@ -119,8 +125,13 @@ const char* mla_status_string(mla_status status);
  *            (strides in elements)
  *   q_pe     bf16 [T,H,64], strides qp_stride_t / qp_stride_h in elements; may
  *            alias q_nope + 512 when q is one [T,H,576] tensor
- *   kv_cache bf16 [num_blocks, page_size, 576]; block stride kv_block_stride
- *            elements (>= page_size*576); row stride 576 elements
+ *   kv_cache [num_blocks, page_size, 576] of element type kv_dtype: bf16
+ *            (MLA_DTYPE_BF16; kv_scale is ignored) or FP8 E4M3 codes
+ *            (MLA_DTYPE_FP8_E4M3: every value is code * kv_scale, kv_scale
+ *            finite and > 0; only for H <= 16, the bandwidth-bound decode:
+ *            more heads return MLA_ERR_UNSUPPORTED); block stride
+ *            kv_block_stride elements (>= page_size*576, a multiple of 16
+ *            bytes); row stride 576 elements
  *   block_table int32 [B, bt_stride]; entries past a request's last block are
  *            never read (may be -1)
  *   seq_lens int32 [B]; query_start_loc int32 [B+1], query_start_loc[0] = 0,
@@ -147,8 +158,9 @@ const char* mla_status_string(mla_status status);
  * Returns MLA_OK, or MLA_ERR_NULL / MLA_ERR_SHAPE (B<0, T<0, H outside
  * [1,128], page_size<1, cp_world<1, cp_rank outside [0,cp_world),
  * cp_interleave<1 or cp_world*cp_interleave > 2^30, strides
- * smaller than the data, scale not finite or not positive, out_dtype or
- * mask_mode not one of the two) / MLA_ERR_WORKSPACE /
+ * smaller than the data, scale not finite or not positive, out_dtype,
+ * mask_mode or kv_dtype not one of theirs, an FP8 kv_scale not finite or
+ * not positive) / MLA_ERR_WORKSPACE /
  * MLA_ERR_UNSUPPORTED / MLA_ERR_HIP.  B == 0 or T == 0 enqueues nothing and
  * returns MLA_OK (the grid is sized from host ints and may be empty).
  * Device-side contract: Q_b <= S_b <= max_seq_len, Q_b <= max_query_len,
@@ -166,7 +178,7 @@ const char* mla_status_string(mla_status status);
 mla_status mla_decode_partial(
     const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
     const void* q_pe, int64_t qp_stride_t, int64_t qp_stride_h,
-    const void* kv_cache, int64_t kv_block_stride, int32_t page_size,
+    const void* kv_cache, int32_t kv_dtype, float kv_scale, int64_t kv_block_stride, int32_t page_size,
     const int32_t* block_table, int32_t bt_stride,
     const int32_t* seq_lens, const int32_t* query_start_loc,
     int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
@@ -201,7 +213,7 @@ mla_status mla_decode_partial(
 mla_status mla_decode_partial_noalloc(
     const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
     const void* q_pe, int64_t qp_stride_t, int64_t qp_stride_h,
-    const void* kv_cache, int64_t kv_block_stride, int32_t page_size,
+    const void* kv_cache, int32_t kv_dtype, float kv_scale, int64_t kv_block_stride, int32_t page_size,
     const int32_t* block_table, int32_t bt_stride,
     const int32_t* seq_lens, const int32_t* query_start_loc,
     int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,

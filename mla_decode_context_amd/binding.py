@@ -23,6 +23,7 @@ MLA_OK = 0
 D_LATENT, D_ROPE, D_ROW, D_V = 512, 64, 576, 128
 DTYPE_BF16, DTYPE_F32 = 0, 1          # MLA_DTYPE_BF16 / MLA_DTYPE_F32
 MASK_CAUSAL, MASK_CONTEXT = 0, 1       # MLA_MASK_CAUSAL / MLA_MASK_CONTEXT
+DTYPE_FP8_E4M3 = 2                     # MLA_DTYPE_FP8_E4M3 (cache elements)
 
 _lib = None
 
@@ -47,13 +48,13 @@ def load_library():
     lib.mla_status_string.argtypes = [_i32]
     lib.mla_decode_partial.restype = _i32
     lib.mla_decode_partial.argtypes = [
-        _c_void_p, _i64, _i64, _c_void_p, _i64, _i64, _c_void_p, _i64, _i32,
+        _c_void_p, _i64, _i64, _c_void_p, _i64, _i64, _c_void_p, _i32, ctypes.c_float, _i64, _i32,
         _c_void_p, _i32, _c_void_p, _c_void_p,
         _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
         _c_void_p, _i32, _c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p]
     lib.mla_decode_partial_noalloc.restype = _i32
     lib.mla_decode_partial_noalloc.argtypes = [
-        _c_void_p, _i64, _i64, _c_void_p, _i64, _i64, _c_void_p, _i64, _i32,
+        _c_void_p, _i64, _i64, _c_void_p, _i64, _i64, _c_void_p, _i32, ctypes.c_float, _i64, _i32,
         _c_void_p, _i32, _c_void_p, _c_void_p,
         _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
         _c_void_p, _i32, _c_void_p, _c_void_p]
@@ -130,6 +131,18 @@ def _partial_dtype(t, name):
     raise MlaError(f"{name}: expected bfloat16 or float32 partials, got {t.dtype}")
 
 
+def _kv_dtype(kv_cache, kv_scale):
+    """ABI code and scale of a cache tensor: bf16, or FP8 E4M3 codes (uint8 or
+    float8_e4m3fn) with their scale."""
+    if kv_cache.dtype == torch.bfloat16:
+        return DTYPE_BF16, 1.0
+    if kv_cache.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)):
+        if kv_scale is None:
+            raise MlaError("kv_cache: an FP8 E4M3 cache needs kv_scale")
+        return DTYPE_FP8_E4M3, float(kv_scale)
+    raise MlaError(f"kv_cache: expected bfloat16 or FP8 E4M3 codes, got {kv_cache.dtype}")
+
+
 def workspace_size(B, T, H, max_query_len, max_seq_len, cp_world, num_splits=0, cp_interleave=1) -> int:
     n = load_library().mla_decode_workspace_size(B, T, H, max_query_len, max_seq_len, cp_world,
                                                  cp_interleave, num_splits)
@@ -140,14 +153,16 @@ def workspace_size(B, T, H, max_query_len, max_seq_len, cp_world, num_splits=0, 
 
 def mla_decode_partial(q_nope, q_pe, kv_cache, block_table, seq_lens, query_start_loc,
                        cp_world, cp_rank, scale, out, lse, *, max_query_len, max_seq_len,
-                       workspace=None, num_splits=0, stream=None, cp_interleave=1, mask_mode=MASK_CAUSAL):
+                       workspace=None, num_splits=0, stream=None, cp_interleave=1, mask_mode=MASK_CAUSAL,
+                       kv_scale=None):
     """One DCP rank's partial attention; writes ``out`` [T,H,512] (bf16, or fp32
     partials when ``out`` is a float32 tensor) and ``lse`` [T,H] fp32.
     ``cp_interleave``: tokens per run of the shard layout (1 = token p on rank p mod W)."""
     lib = load_library()
     _need(q_nope, torch.bfloat16, "q_nope", 3)
     _need(q_pe, torch.bfloat16, "q_pe", 3)
-    _need(kv_cache, torch.bfloat16, "kv_cache", 3)
+    kv_dtype, kv_sc = _kv_dtype(kv_cache, kv_scale)
+    _need(kv_cache, kv_cache.dtype, "kv_cache", 3)
     _need(block_table, torch.int32, "block_table", 2)
     _need(seq_lens, torch.int32, "seq_lens", 1)
     _need(query_start_loc, torch.int32, "query_start_loc", 1)
@@ -180,7 +195,7 @@ def mla_decode_partial(q_nope, q_pe, kv_cache, block_table, seq_lens, query_star
     st = lib.mla_decode_partial(
         _ptr(q_nope), qn_st, qn_sh,
         _ptr(q_pe), qp_st, qp_sh,
-        _ptr(kv_cache), kv_cache.stride(0), page,
+        _ptr(kv_cache), kv_dtype, kv_sc, kv_cache.stride(0), page,
         _ptr(block_table), block_table.stride(0),
         _ptr(seq_lens), _ptr(query_start_loc),
         B, T, H, int(max_query_len), int(max_seq_len), int(cp_world), int(cp_rank), int(cp_interleave),
@@ -191,13 +206,14 @@ def mla_decode_partial(q_nope, q_pe, kv_cache, block_table, seq_lens, query_star
 
 def mla_decode_partial_noalloc(q_nope, q_pe, kv_cache, block_table, seq_lens, query_start_loc,
                                cp_world, cp_rank, scale, out, lse, *, max_query_len, max_seq_len,
-                               num_splits=0, stream=None, cp_interleave=1, mask_mode=MASK_CAUSAL):
+                               num_splits=0, stream=None, cp_interleave=1, mask_mode=MASK_CAUSAL, kv_scale=None):
     """mla_decode_partial without a workspace (the library's per-GPU scratch array
     holds the split partials): for callers that cannot allocate."""
     lib = load_library()
     out_dtype = _partial_dtype(out, "out")
+    kv_dtype, kv_sc = _kv_dtype(kv_cache, kv_scale)
     for t, dt, n, d in ((q_nope, torch.bfloat16, "q_nope", 3), (q_pe, torch.bfloat16, "q_pe", 3),
-                        (kv_cache, torch.bfloat16, "kv_cache", 3), (block_table, torch.int32, "block_table", 2),
+                        (kv_cache, kv_cache.dtype, "kv_cache", 3), (block_table, torch.int32, "block_table", 2),
                         (seq_lens, torch.int32, "seq_lens", 1), (query_start_loc, torch.int32, "query_start_loc", 1),
                         (out, out.dtype, "out", 3), (lse, torch.float32, "lse", 2)):
         _need(t, dt, n, d)
@@ -210,7 +226,7 @@ def mla_decode_partial_noalloc(q_nope, q_pe, kv_cache, block_table, seq_lens, qu
     B = seq_lens.shape[0]
     st = lib.mla_decode_partial_noalloc(
         _ptr(q_nope), q_nope.stride(0), q_nope.stride(1), _ptr(q_pe), q_pe.stride(0), q_pe.stride(1),
-        _ptr(kv_cache), kv_cache.stride(0), page, _ptr(block_table), block_table.stride(0),
+        _ptr(kv_cache), kv_dtype, kv_sc, kv_cache.stride(0), page, _ptr(block_table), block_table.stride(0),
         _ptr(seq_lens), _ptr(query_start_loc), B, T, H, int(max_query_len), int(max_seq_len),
         int(cp_world), int(cp_rank), int(cp_interleave), int(mask_mode), float(scale), int(num_splits),
         _ptr(out), out_dtype, _ptr(lse), _stream(stream))

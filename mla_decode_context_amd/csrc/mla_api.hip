@@ -206,7 +206,7 @@ bool debug_mode() {
 
 // Blocks of the allocation that holds kv_cache, from kv_cache on (a block k is
 // usable when its page_size rows end inside the allocation); -1 if unknown.
-int64_t blocks_in_allocation(const void* kv_cache, int64_t kv_block_stride, int32_t page_size) {
+int64_t blocks_in_allocation(const void* kv_cache, int64_t kv_block_stride, int32_t page_size, int elem_bytes) {
   hipDeviceptr_t base = nullptr;
   size_t size = 0;
   if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)kv_cache) != hipSuccess || !base) {
@@ -214,9 +214,9 @@ int64_t blocks_in_allocation(const void* kv_cache, int64_t kv_block_stride, int3
     return -1;
   }
   const int64_t avail = (int64_t)((uintptr_t)base + size - (uintptr_t)kv_cache);
-  const int64_t block = (int64_t)page_size * MLA_D_ROW * 2;
+  const int64_t block = (int64_t)page_size * MLA_D_ROW * elem_bytes;
   if (avail < block) return 0;
-  return (avail - block) / (kv_block_stride * 2) + 1;
+  return (avail - block) / (kv_block_stride * elem_bytes) + 1;
 }
 
 }  // namespace
@@ -296,7 +296,7 @@ size_t mla_decode_workspace_size(int32_t B, int32_t T, int32_t H, int32_t max_qu
 static mla_status decode_impl(
     const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
     const void* q_pe, int64_t qp_stride_t, int64_t qp_stride_h,
-    const void* kv_cache, int64_t kv_block_stride, int32_t page_size,
+    const void* kv_cache, int32_t kv_dtype, float kv_scale, int64_t kv_block_stride, int32_t page_size,
     const int32_t* block_table, int32_t bt_stride,
     const int32_t* seq_lens, const int32_t* query_start_loc,
     int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
@@ -319,8 +319,12 @@ static mla_status decode_impl(
   if (qp_stride_h < MLA_D_ROPE || qp_stride_t < (int64_t)(H - 1) * qp_stride_h + MLA_D_ROPE ||
       qp_stride_h % 4 || qp_stride_t % 4 || !aligned(q_pe, 8))
     return MLA_ERR_SHAPE;
-  if (kv_block_stride < (int64_t)page_size * MLA_D_ROW || kv_block_stride % 8 || !aligned(kv_cache, 16))
+  const bool fp8 = kv_dtype == MLA_DTYPE_FP8_E4M3;
+  if (kv_dtype != MLA_DTYPE_BF16 && !fp8) return MLA_ERR_SHAPE;
+  if (fp8 && (!isfinite(kv_scale) || !(kv_scale > 0.f))) return MLA_ERR_SHAPE;
+  if (kv_block_stride < (int64_t)page_size * MLA_D_ROW || kv_block_stride % (fp8 ? 16 : 8) || !aligned(kv_cache, 16))
     return MLA_ERR_SHAPE;
+  if (fp8 && H > 16) return MLA_ERR_UNSUPPORTED;
   if (bt_stride < 1 || !aligned(out, 16)) return MLA_ERR_SHAPE;
   mla_status st = check_device();
   if (st != MLA_OK) return st;
@@ -340,7 +344,8 @@ static mla_status decode_impl(
     char why[256];
     const mla_status cst = mla_check_decode_metadata(
         hs.data(), hq.data(), hb.data(), bt_stride, B, T, max_query_len, max_seq_len, page_size, cp_world, cp_rank,
-        cp_interleave, mask_mode, blocks_in_allocation(kv_cache, kv_block_stride, page_size), why, sizeof(why));
+        cp_interleave, mask_mode, blocks_in_allocation(kv_cache, kv_block_stride, page_size, fp8 ? 1 : 2), why,
+        sizeof(why));
     if (cst != MLA_OK) {
       fprintf(stderr, "mla_decode_partial (MLA_DEBUG): %s\n", why);
       return cst;
@@ -368,7 +373,9 @@ static mla_status decode_impl(
   p.bt = block_table; p.bt_stride = bt_stride;
   p.seq_lens = seq_lens; p.qsl = query_start_loc;
   p.B = B; p.T = T; p.H = H; p.W = cp_world; p.r = cp_rank; p.I = cp_interleave; p.mode = mask_mode;
-  p.scale_log2 = (float)((double)scale * 1.4426950408889634074);
+  p.kv_fp8 = fp8 ? 1 : 0;
+  p.scale_log2 = (float)((double)scale * (fp8 ? (double)kv_scale : 1.0) * 1.4426950408889634074);
+  p.out_scale = fp8 ? kv_scale : 1.f;
   p.chunk = plan.chunk; p.hblocks = plan.hblocks; p.max_splits = plan.max_splits;
   p.out = out_dtype == MLA_DTYPE_BF16 ? (uint16_t*)out : nullptr;
   p.out_f = out_dtype == MLA_DTYPE_F32 ? (float*)out : nullptr;
@@ -402,7 +409,7 @@ extern "C" {
 mla_status mla_decode_partial(
     const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
     const void* q_pe, int64_t qp_stride_t, int64_t qp_stride_h,
-    const void* kv_cache, int64_t kv_block_stride, int32_t page_size,
+    const void* kv_cache, int32_t kv_dtype, float kv_scale, int64_t kv_block_stride, int32_t page_size,
     const int32_t* block_table, int32_t bt_stride,
     const int32_t* seq_lens, const int32_t* query_start_loc,
     int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
@@ -410,7 +417,8 @@ mla_status mla_decode_partial(
     int32_t num_splits,
     void* out, int32_t out_dtype, float* lse,
     void* workspace, size_t workspace_bytes, void* hip_stream) {
-  return decode_impl(q_nope, qn_stride_t, qn_stride_h, q_pe, qp_stride_t, qp_stride_h, kv_cache, kv_block_stride,
+  return decode_impl(q_nope, qn_stride_t, qn_stride_h, q_pe, qp_stride_t, qp_stride_h, kv_cache, kv_dtype, kv_scale,
+                     kv_block_stride,
                      page_size, block_table, bt_stride, seq_lens, query_start_loc, B, T, H, max_query_len,
                      max_seq_len, cp_world, cp_rank, cp_interleave, mask_mode, scale, num_splits, out, out_dtype, lse,
                      workspace, workspace_bytes, hip_stream, false);
@@ -419,14 +427,15 @@ mla_status mla_decode_partial(
 mla_status mla_decode_partial_noalloc(
     const void* q_nope, int64_t qn_stride_t, int64_t qn_stride_h,
     const void* q_pe, int64_t qp_stride_t, int64_t qp_stride_h,
-    const void* kv_cache, int64_t kv_block_stride, int32_t page_size,
+    const void* kv_cache, int32_t kv_dtype, float kv_scale, int64_t kv_block_stride, int32_t page_size,
     const int32_t* block_table, int32_t bt_stride,
     const int32_t* seq_lens, const int32_t* query_start_loc,
     int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
     int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, int32_t mask_mode, float scale,
     int32_t num_splits,
     void* out, int32_t out_dtype, float* lse, void* hip_stream) {
-  return decode_impl(q_nope, qn_stride_t, qn_stride_h, q_pe, qp_stride_t, qp_stride_h, kv_cache, kv_block_stride,
+  return decode_impl(q_nope, qn_stride_t, qn_stride_h, q_pe, qp_stride_t, qp_stride_h, kv_cache, kv_dtype, kv_scale,
+                     kv_block_stride,
                      page_size, block_table, bt_stride, seq_lens, query_start_loc, B, T, H, max_query_len,
                      max_seq_len, cp_world, cp_rank, cp_interleave, mask_mode, scale, num_splits, out, out_dtype, lse,
                      nullptr, 0, hip_stream, true);

@@ -434,7 +434,16 @@ __device__ __forceinline__ void write_empty_row(const DecodeParams& a, int t) {
 // the piece is the whole row and writes out / lse; otherwise it writes its
 // partial to workspace row my_slot and takes part in the row's ticketed merge
 // (counter `counter`, slots `sm`).
-template <bool kPage16, bool kDeferMerge>
+//
+// kFP8: the cache holds FP8 E4M3 codes (576-byte rows, one scale per cache).
+// A wave's 36 KiB of LDS then holds two 9 KiB slots of E4M3 rows, filled by
+// direct-to-LDS loads as for bf16 (half the bytes per stage), and an 18 KiB
+// bf16 copy of the current stage: once a stage has landed the wave expands
+// it with the exact E4M3 -> bf16 conversion into the swizzled bf16 layout,
+// and the MFMA reads below run on that copy unchanged.  The cache scale is in
+// the scores' exponent factor (scale_log2) and in the final normalisation
+// (out_scale), so the conversion adds no rounding.
+template <bool kPage16, bool kDeferMerge, bool kFP8>
 __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_block, int t, int b,
                                           int j_begin, int j_end, int nsplit, int64_t my_slot, SlotMap sm,
                                           int counter) {
@@ -468,7 +477,12 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
 
   const int32_t* bt_row = a.bt + (int64_t)b * a.bt_stride;
   const uint8_t* kv_bytes = (const uint8_t*)a.kv;
-  uint8_t* ring = lds_block + w * kWRing * kWStageBytes;
+  constexpr int kRowB = kFP8 ? kRow : kRowBytes;           // bytes per cache row
+  constexpr int kSlotB = kWStage * kRowB;                  // bytes per ring slot (9 or 18 KiB)
+  constexpr int kBlk = kSlotB / 1024;                      // load instructions per stage
+  constexpr int kElemB = kFP8 ? 1 : 2;                     // bytes per cache element
+  uint8_t* ring = lds_block + w * kWRing * kWStageBytes;   // 36 KiB per wave either way
+  uint8_t* stage16 = ring + kWRing * kSlotB;               // FP8: bf16 copy of the stage
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring);
 
@@ -478,27 +492,50 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
   // different chunks).  Block i (1 KiB) is written by one load: lane l -> bytes
   // 1024i + 16l .. +16, fetched from the byte offset below within the stage's
   // 16 consecutive cache rows.
-  uint32_t doff[kWBlocks];
+  // FP8 stages land unswizzled (byte o of the slot = byte o of the 16 rows);
+  // the expansion into the bf16 copy applies the swizzle.
+  uint32_t doff[kBlk];
 #pragma unroll
-  for (int i2 = 0; i2 < kWBlocks; ++i2) {
+  for (int i2 = 0; i2 < kBlk; ++i2) {
     const int o = 1024 * i2 + 16 * lane;
-    const int row = o / kRowBytes;
-    const int cpos = (o - row * kRowBytes) >> 4;
-    doff[i2] = (uint32_t)(row * kRowBytes + ((cpos ^ (row & 7)) << 4));
+    const int row = o / kRowB;
+    const int cpos = (o - row * kRowB) >> 4;
+    doff[i2] = kFP8 ? (uint32_t)o : (uint32_t)(row * kRowBytes + ((cpos ^ (row & 7)) << 4));
   }
   // Issue piece stage st into ring slot `slot`.  Keys at or past j_end (the
   // ragged last stage) are clamped to key j_end - 1 -- a real cached row, masked
   // to probability 0 -- so every path issues exactly kWBlocks loads.
   auto issue = [&](int st, int slot) {
     const int j0 = j_begin + kWStage * st;
-    const uint32_t ldst = ring_lds + slot * kWStageBytes;
+    const uint32_t ldst = ring_lds + slot * kSlotB;
     if (kPage16 && j0 + kWStage <= j_end) {
       // page_size % 16 == 0: the stage's 16 rows are consecutive slots of one page.
       const int pg = a.page_shift >= 0 ? j0 >> a.page_shift : j0 / a.P;
       const int blk = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pg];
-      const uint64_t sbase = make_sbase(kv_bytes + ((int64_t)blk * a.kv_bs + (int64_t)(j0 - pg * a.P) * kRow) * 2);
+      const uint64_t sbase =
+          make_sbase(kv_bytes + ((int64_t)blk * a.kv_bs + (int64_t)(j0 - pg * a.P) * kRow) * kElemB);
 #pragma unroll
-      for (int i2 = 0; i2 < kWBlocks; ++i2) dma_16B_to_lds_sbase<true>(ldst + 1024 * i2, doff[i2], sbase);
+      for (int i2 = 0; i2 < kBlk; ++i2) dma_16B_to_lds_sbase<true>(ldst + 1024 * i2, doff[i2], sbase);
+    } else if constexpr (kFP8) {
+      // A 1 KiB block spans at most three 576-byte rows, ra .. ra + 2; a lane's
+      // 16 bytes lie in one of them.  Keys at or past j_end are clamped as below.
+#pragma unroll
+      for (int i2 = 0; i2 < kBlk; ++i2) {
+        const int o = 1024 * i2 + 16 * lane;
+        const int row = o / kRow;
+        const int ra = (1024 * i2) / kRow;
+        const int j = min(j0 + row, j_end - 1);
+        int pgx[3], bx[3];
+#pragma unroll
+        for (int x = 0; x < 3; ++x) {
+          pgx[x] = __builtin_amdgcn_readfirstlane(min(j0 + ra + x, j_end - 1) / a.P);
+          bx[x] = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pgx[x]];
+        }
+        const int pg = j / a.P;                    // one of pgx[0..2]
+        const int blk = pg == pgx[0] ? bx[0] : (pg == pgx[1] ? bx[1] : bx[2]);
+        const int64_t rbase = (int64_t)blk * a.kv_bs + (int64_t)(j - pg * a.P) * kRow;
+        dma_16B_to_lds_stream(kv_bytes + rbase + (o - row * kRow), ring + slot * kSlotB + 1024 * i2);
+      }
     } else {
 #pragma unroll
       for (int i2 = 0; i2 < kWBlocks; ++i2) {
@@ -553,7 +590,33 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
     } else {
       __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
     }
-    const uint8_t* sb = ring + slot * kWStageBytes;
+    const uint8_t* sb = ring + slot * kSlotB;
+    if constexpr (kFP8) {
+      // Expand the E4M3 stage into the bf16 layout of the reads below: lane
+      // takes the 16-byte chunks lane + 64u (16 codes of one row each; 36 per
+      // row), converts them exactly and writes bf16 chunks 2ch and 2ch + 1 of
+      // the row at their swizzled places.  Same wave, LDS in order: the writes
+      // land after the previous stage's reads of the copy and before the reads
+      // below.
+#pragma unroll
+      for (int u = 0; u < kBlk; ++u) {
+        const int c = lane + 64 * u;
+        const int row = c / 36, ch = c - row * 36;
+        const u32x4 v = *(const u32x4*)(sb + 16 * c);
+        u32x4 lo, hi;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          lo[2 * e] = fp8x2_to_bf16x2<false>(v[e]);
+          lo[2 * e + 1] = fp8x2_to_bf16x2<true>(v[e]);
+          hi[2 * e] = fp8x2_to_bf16x2<false>(v[2 + e]);
+          hi[2 * e + 1] = fp8x2_to_bf16x2<true>(v[2 + e]);
+        }
+        const int d0 = row * kRowBytes + 16 * ((2 * ch) ^ (row & 7));
+        *(u32x4*)(stage16 + d0) = lo;
+        *(u32x4*)(stage16 + (d0 ^ 16)) = hi;
+      }
+      sb = stage16;
+    }
     const int j0 = j_begin + kWStage * (w + 4 * k);
 
     // S^T[key][head] over 576 dims (A = keys: lane key lr, dims 32s + 8g), two
@@ -655,7 +718,7 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
       c[u] = mv[u] == -INFINITY ? 0.f : fast_exp2(mv[u] - M);
       Lsum += c[u] * lv[u];
     }
-    const float inv = 1.f / Lsum;
+    const float inv = (kFP8 ? a.out_scale : 1.f) / Lsum;
     const float lse_v = (M + fast_log2(Lsum)) * kLn2;
     if (h < a.H) {
 #pragma unroll
@@ -736,7 +799,7 @@ __device__ __forceinline__ int request_units(const DecodeParams& a, int I, int b
 
 // kRuns: the shard layout has runs longer than one token (cp_interleave > 1);
 // without it the run length is the constant 1 and the layout arithmetic folds.
-template <bool kPage16, bool kBalanced, bool kRuns>
+template <bool kPage16, bool kBalanced, bool kRuns, bool kFP8>
 __global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a) {
   const int I = kRuns ? a.I : 1;
   // Four wave rings of two 18 KiB slots; reused for the four-wave merge.
@@ -755,7 +818,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a
     }
     const int j_begin = split * a.chunk;
     const int j_end = split == nsplit - 1 ? ri.L : j_begin + a.chunk;
-    h16_piece<kPage16, false>(a, lds_block, t, ri.b, j_begin, j_end, nsplit, (int64_t)split * a.T + t,
+    h16_piece<kPage16, false, kFP8>(a, lds_block, t, ri.b, j_begin, j_end, nsplit, (int64_t)split * a.T + t,
                               SlotMap{t, a.T, 0}, t);
   } else {
     const int G = (int)gridDim.x;
@@ -842,7 +905,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a
             // The worker of the row's first piece tells the combine kernel how
             // to find the row's pieces.
             if (g == gf && threadIdx.x == 0) a.row_desc[t] = int4{gl - gf + 1, sm.base, sm.adj0, 0};
-            h16_piece<kPage16, true>(a, lds_block, t, b, lo * kWStage, min(hi * kWStage, L), gl - gf + 1,
+            h16_piece<kPage16, true, kFP8>(a, lds_block, t, b, lo * kWStage, min(hi * kWStage, L), gl - gf + 1,
                                      sm.row(g - gf), sm, t);
             __syncthreads();                         // LDS is reused by the next piece
           }
@@ -906,10 +969,16 @@ hipError_t launch_decode(const DecodeParams& p, int mtiles, int max_splits, int 
   if (mtiles == 1 && workers > 0) {
     const dim3 grid((unsigned)workers);
     const bool runs = p.I != 1;
-    if (page16 && !runs) hipLaunchKernelGGL((decode_kernel_h16<true, true, false>), grid, dim3(256), 0, stream, p);
-    else if (page16) hipLaunchKernelGGL((decode_kernel_h16<true, true, true>), grid, dim3(256), 0, stream, p);
-    else if (!runs) hipLaunchKernelGGL((decode_kernel_h16<false, true, false>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((decode_kernel_h16<false, true, true>), grid, dim3(256), 0, stream, p);
+    if (p.kv_fp8) {
+      if (page16 && !runs) hipLaunchKernelGGL((decode_kernel_h16<true, true, false, true>), grid, dim3(256), 0, stream, p);
+      else if (page16) hipLaunchKernelGGL((decode_kernel_h16<true, true, true, true>), grid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((decode_kernel_h16<false, true, true, true>), grid, dim3(256), 0, stream, p);
+    } else {
+      if (page16 && !runs) hipLaunchKernelGGL((decode_kernel_h16<true, true, false, false>), grid, dim3(256), 0, stream, p);
+      else if (page16) hipLaunchKernelGGL((decode_kernel_h16<true, true, true, false>), grid, dim3(256), 0, stream, p);
+      else if (!runs) hipLaunchKernelGGL((decode_kernel_h16<false, true, false, false>), grid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((decode_kernel_h16<false, true, true, false>), grid, dim3(256), 0, stream, p);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(split_combine_kernel, dim3((unsigned)p.T, 4), dim3(256), 0, stream, p);
@@ -917,8 +986,13 @@ hipError_t launch_decode(const DecodeParams& p, int mtiles, int max_splits, int 
   }
   const dim3 grid((unsigned)(p.T * p.hblocks), (unsigned)max_splits);
   if (mtiles == 1) {
-    if (page16) hipLaunchKernelGGL((decode_kernel_h16<true, false, true>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((decode_kernel_h16<false, false, true>), grid, dim3(256), 0, stream, p);
+    if (p.kv_fp8) {
+      if (page16) hipLaunchKernelGGL((decode_kernel_h16<true, false, true, true>), grid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((decode_kernel_h16<false, false, true, true>), grid, dim3(256), 0, stream, p);
+    } else {
+      if (page16) hipLaunchKernelGGL((decode_kernel_h16<true, false, true, false>), grid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((decode_kernel_h16<false, false, true, false>), grid, dim3(256), 0, stream, p);
+    }
   } else {
     if (page16) hipLaunchKernelGGL((decode_kernel<2, kStages, true>), grid, dim3(256), 0, stream, p);
     else hipLaunchKernelGGL((decode_kernel<2, kStages, false>), grid, dim3(256), 0, stream, p);

@@ -58,6 +58,14 @@ __device__ __forceinline__ void dma_16B_to_lds_stream(const void* src, const uin
                : "memory");
 }
 
+// Two FP8 E4M3 codes (bytes 0-1 of `w`, or bytes 2-3 with kHi) -> two bf16
+// (low half = the lower byte's value).  Exact: every E4M3 value is a bf16
+// value; the scale operand is 1.
+template <bool kHi>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
+}
+
 // Empty asm that "uses" a pointer, extending its registers' live range.
 __device__ __forceinline__ void keep_live(const void* p) { asm volatile("" : : "v"(p)); }
 

@@ -18,7 +18,9 @@ struct DecodeParams {
   int32_t B, T, H, W, r;
   int32_t I;               // shard run length: token p lives on rank (p div I) mod W
   int32_t mode;            // kMaskCausal or kMaskContext (which keys a row sees)
-  float scale_log2;        // softmax scale * log2(e): scores are kept in base 2
+  int32_t kv_fp8;          // cache rows hold FP8 E4M3 codes (576 bytes) instead of bf16
+  float scale_log2;        // softmax scale * log2(e) (* the FP8 cache's scale): scores in base 2
+  float out_scale;         // factor of the normalised output: the FP8 cache's scale, else 1
   int32_t chunk;           // keys per split (multiple of the 32-key step)
   int32_t hblocks;         // head blocks per query token
   int32_t max_splits;      // grid extent along splits

@@ -39,7 +39,10 @@ class DeviceWorkload:
         self.q_pe = _bf16(wl.q_pe, dev)
         self.seq_lens = _i32(wl.seq_lens, dev)
         self.qsl = _i32(wl.query_start_loc, dev)
-        self.caches = [_bf16(sh.cache, dev) for sh in wl.shards]
+        # bf16 caches, or FP8 E4M3 codes (uint8) with the cache's scale
+        self.kv_scale = wl.kv_scale
+        self.caches = [_bf16(sh.cache, dev) if wl.kv_scale is None else torch.from_numpy(sh.cache).to(dev)
+                       for sh in wl.shards]
         self.tables = [_i32(sh.block_table, dev) for sh in wl.shards]
         self.w_uv = _bf16(wl.w_uv, dev) if wl.w_uv is not None else None
         T, H, W = self.T, self.H, self.W
@@ -74,11 +77,12 @@ class DeviceWorkload:
             name = "h128_order_kernel+" + name
             return name + "+combine_fixed_kernel" if self.workspace.numel() > order_only else name
         page16 = "true" if self.wl.P % 16 == 0 else "false"
+        fp8 = "true" if self.kv_scale is not None else "false"
         if self.H <= 16:
             if self.num_splits == 0 and self.workspace is not None:
-                runs = "true" if self.I != 1 else "false"
-                return f"decode_kernel_h16<{page16}, true, {runs}>+split_combine_kernel"
-            return f"decode_kernel_h16<{page16}, false, true>"
+                runs = "true" if self.I != 1 or (fp8 == "true" and page16 == "false") else "false"
+                return f"decode_kernel_h16<{page16}, true, {runs}, {fp8}>+split_combine_kernel"
+            return f"decode_kernel_h16<{page16}, false, true, {fp8}>"
         return f"decode_kernel<2, 3, {page16}>"
 
     def partial(self, r: int, stream=None):
@@ -86,7 +90,8 @@ class DeviceWorkload:
             self.q_nope, self.q_pe, self.caches[r], self.tables[r], self.seq_lens, self.qsl,
             self.W, r, self.scale, self.outs[r], self.lses[r],
             max_query_len=self.max_query_len, max_seq_len=self.max_seq_len,
-            workspace=self.workspace, num_splits=self.num_splits, stream=stream, cp_interleave=self.I)
+            workspace=self.workspace, num_splits=self.num_splits, stream=stream, cp_interleave=self.I,
+            kv_scale=self.kv_scale)
 
     def valid_counts(self, stream=None):
         for r in range(self.W):
@@ -101,7 +106,7 @@ class DeviceWorkload:
         rows, table, qlens = WL.query_part_layout(self.wl)
         dev = self.device
         T, H, W = self.T, self.H, self.W
-        self.qkv = _bf16(rows, dev).view(T, 1, 576)          # one-token pages
+        self.qkv = (_bf16(rows, dev) if self.kv_scale is None else torch.from_numpy(rows).to(dev)).view(T, 1, 576)
         self.q_table = _i32(table, dev)
         self.q_lens = _i32(qlens, dev)
         dt = self.outs.dtype
@@ -116,13 +121,15 @@ class DeviceWorkload:
             self.q_nope, self.q_pe, self.caches[r], self.tables[r], self.seq_lens, self.qsl,
             self.W, r, self.scale, self.outs2[r], self.lses2[r],
             max_query_len=self.max_query_len, max_seq_len=self.max_seq_len, workspace=self.workspace,
-            num_splits=self.num_splits, stream=stream, cp_interleave=self.I, mask_mode=mla.MASK_CONTEXT)
+            num_splits=self.num_splits, stream=stream, cp_interleave=self.I, mask_mode=mla.MASK_CONTEXT,
+            kv_scale=self.kv_scale)
 
     def query_partial(self, stream=None):
         mla.mla_decode_partial(
             self.q_nope, self.q_pe, self.qkv, self.q_table, self.q_lens, self.qsl, 1, 0, self.scale,
             self.outs2[self.W], self.lses2[self.W], max_query_len=self.max_query_len,
-            max_seq_len=self.max_query_len, workspace=self.q_workspace, num_splits=self.num_splits, stream=stream)
+            max_seq_len=self.max_query_len, workspace=self.q_workspace, num_splits=self.num_splits, stream=stream,
+            kv_scale=self.kv_scale)
 
     def two_stage_counts(self, stream=None):
         for r in range(self.W):

@@ -34,10 +34,10 @@ def test_status_strings():
 def _decode(**kw):
     a = dict(q_nope=P, qn_t=16 * 512, qn_h=512, q_pe=P, qp_t=16 * 64, qp_h=64, kv=P, kv_bs=16 * 576, page=16,
              bt=P, bt_stride=4, seq=P, qsl=P, B=2, T=4, H=16, mq=2, ms=100, W=2, r=0, I=1, mask=0, scale=0.07,
-             splits=0, out=P, dtype=0, lse=P, ws=None, ws_bytes=0)
+             splits=0, out=P, dtype=0, lse=P, ws=None, ws_bytes=0, kvt=0, kvs=1.0)
     a.update(kw)
     return lib.mla_decode_partial(a["q_nope"], a["qn_t"], a["qn_h"], a["q_pe"], a["qp_t"], a["qp_h"], a["kv"],
-                                  a["kv_bs"], a["page"], a["bt"], a["bt_stride"], a["seq"], a["qsl"], a["B"],
+                                  a["kvt"], a["kvs"], a["kv_bs"], a["page"], a["bt"], a["bt_stride"], a["seq"], a["qsl"], a["B"],
                                   a["T"], a["H"], a["mq"], a["ms"], a["W"], a["r"], a["I"], a["mask"], a["scale"],
                                   a["splits"],
                                   a["out"], a["dtype"], a["lse"], a["ws"], a["ws_bytes"], None)
@@ -57,6 +57,9 @@ def _decode(**kw):
     (dict(W=2, I=1 << 28, T=0), OK),
     (dict(dtype=2), SHAPE), (dict(dtype=-1), SHAPE), (dict(dtype=1, T=0), OK),
     (dict(mask=2), SHAPE), (dict(mask=-1), SHAPE), (dict(mask=1, T=0), OK),
+    (dict(kvt=1), SHAPE), (dict(kvt=3), SHAPE), (dict(kvt=2, kvs=0.0), SHAPE), (dict(kvt=2, kvs=-1.0), SHAPE),
+    (dict(kvt=2, kvs=float("nan")), SHAPE), (dict(kvt=2, kv_bs=16 * 576 + 8), SHAPE),
+    (dict(kvt=0, kvs=float("nan"), T=0), OK), (dict(kvt=2, kvs=0.01, T=0), OK),
 ])
 def test_decode_argument_checks(kw, code):
     assert _decode(**kw) == code
