@@ -6,27 +6,33 @@
 // scale, causal, LSE per token and head) and the PR #24453 review thread (per
 // row, per rank seqlen_k under interleaved token placement).
 //
-// Work decomposition.  One workgroup of 4 wavefronts owns one query token, a
-// block of 16*MT heads (the MFMA M dimension) and one split of that row's
-// visible local keys.  The four waves split the 576-wide contraction and the
-// 512-wide output between them: wave w owns latent dims [128w, 128w+128) and
-// rope dims [16w, 16w+16).  Per step of 32 keys:
-//   1. each wave loads only its 288 bytes of each of the 32 cache rows straight
-//      into registers (block-table indirection per key; the four waves together
-//      read every 1152-byte row exactly once);
-//   2. partial scores S^T = K Q^T over the wave's dims with MFMA (keys as M=16
-//      rows of the A operand, heads as N columns of the B operand);
-//   3. the four partial score tiles are summed through LDS;
-//   4. every wave runs the same online softmax (base 2, fp32) on the full
-//      scores -- masked keys get probability 0 and zeroed values;
-//   5. O^T += V^T P^T with MFMA on the wave's own 128 latent dims, where V^T
-//      comes from the wave's LDS copy of the rows via the transposed LDS read
-//      (ds_read_b64_tr_b16) and P^T is the softmax output already in the
-//      B-operand layout.
-// The next step's rows are loaded while the current step computes.  When a
-// row's keys are split over several workgroups, each writes its normalised
-// partial (fp32) and LSE to the workspace and the last one to finish merges
-// them (exact LSE-weighted combine) in the same launch.
+// The file holds the decode kernels for every head count except 128 (which
+// has its own file), the split combine, the per-row seqlen kernel and a fill.
+//
+// decode_kernel_h16 (H <= 16, the bandwidth-bound case, about 30 flop per
+// cache byte).  One workgroup of four waves per CU; each wave streams its own
+// 16-key stages (stage s of a piece belongs to wave s mod 4) from HBM into a
+// private two-slot LDS ring with direct-to-LDS loads, the next stage in flight
+// while the current one computes, and computes everything for its stages
+// alone: the 576-wide scores (MFMA 16x16x32, keys on M, heads on N), the online
+// softmax and PV over all 512 latent dims (V^T from transposed LDS reads).
+// No barrier in the loop; at the end of a piece the four waves' states merge
+// through LDS.  With the balanced schedule (num_splits = 0) the launch's
+// rows are cut into equal shares of cache rows per workgroup, computed by every
+// wave from seq_lens alone; rows cut at share boundaries become pieces with
+// fp32 partials, merged by split_combine_kernel in a second launch.  With a
+// fixed split count, each split of a row is one workgroup and the last one to
+// finish merges the row (ticket).  An FP8 E4M3 cache is expanded to bf16 per
+// stage in LDS (see h16_piece).
+//
+// decode_kernel (other head counts; 32 heads per workgroup).  Four waves split
+// the 576-wide contraction and the 512-wide output: wave w owns latent dims
+// 128w .. 128w+127 and rope dims 16w .. 16w+15.  Per 32-key step, the
+// workgroup fills a 36 KiB stage of a three-slot ring with direct-to-LDS loads
+// (wave w issues nine of its 36 1 KiB loads), every wave forms its partial
+// scores over its dims, the four partial score tiles are summed through LDS,
+// every wave runs the same online softmax and accumulates PV over its 128
+// latent dims.  Split rows merge by ticket as above.
 #include "mla_common.h"
 #include "mla_device.h"
 #include "mla_kernels.h"

@@ -1,10 +1,17 @@
-"""GPU parity at the full sizes of the four large workloads, in the launch
-configuration the benchmark times, on sampled rows the oracle computes one by one.
+"""GPU parity at the full sizes of the large workloads, in the launch
+configuration the benchmark times.
 
-For each workload: every rank's partial for the sampled tokens against the
-oracle's partial, the merged rows against the oracle's unsharded attention
-(merge(shards) == unsharded), valid counts bit-exact, and for the mixed batch
-the fused merge + W_UV against the oracle's project-then-merge.
+Plain and the two MTP DCP4 workloads are checked on every row (the plain
+decode's balanced schedule cuts every row into pieces at worker boundaries, so
+all its piece boundaries are covered); the long DCP8 and mixed workloads on
+sampled rows the oracle computes one by one: the first and last rows, the
+shortened and prefill-chunk requests, every row of the four longest requests
+(the first items of the longest-first dispatch order) and seeded random rows.
+
+For each workload: every rank's partial against the oracle's partial, the
+merged rows against the oracle's unsharded attention (merge(shards) ==
+unsharded), valid counts bit-exact, and for the mixed batch the fused merge +
+W_UV against the oracle's project-then-merge.
 """
 from __future__ import annotations
 
@@ -32,7 +39,11 @@ def test_full_config_sampled_rows(name):
     dw.outs.fill_(float("nan"))
     dw.step()
     torch.cuda.synchronize()
-    toks = sample_tokens(wl, n_random=10, extra_requests=SHORT.get(name, ()))
+    if name in ("plain", "mtp_dcp4", "mtp_dcp4_pages"):
+        toks = list(range(wl.T))
+    else:
+        longest = [int(b) for b in np.argsort(-np.asarray(wl.seq_lens))[:4]]
+        toks = sample_tokens(wl, n_random=10, extra_requests=tuple(SHORT.get(name, ())) + tuple(longest))
     log(f"[{name}] oracle on {len(toks)} sampled tokens")
     kv = {}
     ref_o, ref_l = oracle_partials(wl, toks, kv)

@@ -127,3 +127,37 @@ def test_merge_v_up_proj_random(W, T, H):
     mla.mla_merge_v_up_proj(outs_p.cuda(), torch.from_numpy(lses_m).cuda(), None, wuv_t.cuda(), y2, yl2)
     torch.cuda.synchronize()
     assert torch.equal(y2, y) and torch.equal(yl2, yl), f"merge_v_up W={W} valid=None"
+
+
+def test_merge_v_up_proj_hip_graph_replay():
+    """mla_merge_v_up_proj captured alone in a HIP graph: every replay, with
+    eager work and synchronisations between the replays, reproduces the eager
+    result bit for bit."""
+    W, T, H = 4, 70, 128
+    outs_t, lses, valid = _random_partials(W, T, H, seed=91)
+    rng = np.random.default_rng(5)
+    wuv = _bf16_round(0.02 * rng.standard_normal((H, 512, 128))).cuda()
+    d_outs, d_lses, d_valid = outs_t.cuda(), torch.from_numpy(lses).cuda(), torch.from_numpy(valid).cuda()
+    y = torch.empty((T, H, 128), dtype=torch.bfloat16, device="cuda")
+    yl = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    mla.mla_merge_v_up_proj(d_outs, d_lses, d_valid, wuv, y, yl)
+    torch.cuda.synchronize()
+    ref_y, ref_l = y.clone(), yl.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        mla.mla_merge_v_up_proj(d_outs, d_lses, d_valid, wuv, y, yl, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        mla.mla_merge_v_up_proj(d_outs, d_lses, d_valid, wuv, y, yl)
+    for k in range(4):
+        y.fill_(float("nan"))
+        yl.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda").sum()       # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref_y) and torch.equal(yl, ref_l), f"replay {k}"
+        del junk
