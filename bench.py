@@ -21,8 +21,11 @@ Printed: one JSON line.  ``value`` is KV-cache GB/s of the whole step (bytes of
 cache rows the method must read once, divided by the step time) with inputs
 already resident in HBM.  ``roofline`` is the dominant kernel's algorithmic
 flops (or bytes, for an HBM-bound workload) per call over its average call
-duration, measured with HIP events on the launch stream around every step's
-decode calls inside the timed region; ``calibration`` holds what a streaming
+duration, measured with HIP events on the launch stream: for a one-call step
+(the plain workloads) the timed region's own pair of events, otherwise one
+pair around `steps` passes over every shard's decode, issued back to back as a
+step issues them (events between the calls of the timed region would idle the
+GPU a few microseconds each); ``calibration`` holds what a streaming
 read and a register-resident MFMA loop reach on the same GPU (the roofline is
 also given as a fraction of those); ``cpu_baseline`` times the fp64 oracle on
 the host for a bounded sample of the same workload.
@@ -402,7 +405,7 @@ def cpu_model() -> str:
 
 
 def calibrate(torch, reps=5):
-    """KO5: what this GPU reaches for a streaming read of 4 GiB (plain and
+    """What this GPU reaches for a streaming read of 4 GiB (plain and
     non-temporal loads; 16x the last-level cache) and for a register-resident
     bf16 MFMA loop.  Best of `reps` timed calls after one untimed call."""
     from mla_decode_context_amd import binding as mla
@@ -508,16 +511,19 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe_mib > 0:
         copy_probe(torch, args.copy_probe_mib)
+    calib = None
+    if not args.no_calib:
+        # First, so that the GPU has left its idle clocks before any workload
+        # is timed (the calibration is a second or so of streaming reads and
+        # MFMA loops).
+        print("[bench] calibration: streaming read and MFMA loop", file=sys.stderr, flush=True)
+        calib = calibrate(torch)
+        print(f"[bench] calibration: {json.dumps(calib)}", file=sys.stderr, flush=True)
     print(f"[bench] {args.workload}: generating inputs", file=sys.stderr, flush=True)
     head, wl = time_workload(args.workload, args.steps, args.warmup, torch, headline=True,
                              cold=not args.no_cold, alternate=args.workload == "plain")
     print(f"[bench] {args.workload}: {head['ms_per_step']:.4f} ms/step, {head['kv_GBps']:.1f} GB/s",
           file=sys.stderr, flush=True)
-    calib = None
-    if not args.no_calib:
-        print("[bench] calibration: streaming read and MFMA loop", file=sys.stderr, flush=True)
-        calib = calibrate(torch)
-        print(f"[bench] calibration: {json.dumps(calib)}", file=sys.stderr, flush=True)
     configs = {}
     for name in [c for c in args.configs.split(",") if c and c != args.workload]:
         print(f"[bench] {name}: generating inputs", file=sys.stderr, flush=True)

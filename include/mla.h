@@ -62,7 +62,7 @@ typedef int32_t mla_status;
 /* Element type of an FP8 latent cache (mla_decode_partial's kv_dtype): OCP
  * FP8 E4M3 ("fn": exponent bias 7, no infinities, largest finite 448) codes,
  * one fp32 scale per cache, element value = code value * kv_scale.  The pages
- * leave the convention open (FP8 is "not yet supported" there); this is the
+ * leave the convention open (they reject FP8 caches as unsupported); this is the
  * reading this library implements. */
 #define MLA_DTYPE_FP8_E4M3 2
 

@@ -54,8 +54,8 @@ def fp8_e4m3_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     subnormals f/8 * 2^-6; the code S.1111.111 is NaN and there are no
     infinities (largest finite 448).
 
-    The pages give no convention for an FP8 latent cache ("flashattn_mla" API
-    page: FP8 KV cache not yet supported).  Reading: each cached element is an
+    The pages give no convention for an FP8 latent cache (the "flashattn_mla"
+    API page rejects an FP8 KV cache as unsupported).  Reading: each cached element is an
     E4M3 code, and the cache carries one fp32 scale; the element's value is
     code value * scale.
     """
