@@ -155,6 +155,7 @@ Plan make_plan(int B, int T, int H, int max_seq_len, int W, int I, int num_split
 
 // Workspace layout (offsets from the 256-byte aligned base):
 //   int32 item_map[T * hblocks * max_splits]  128 heads only: dispatch order
+//   int2  item_info[T * hblocks * max_splits] 128 heads only: {request, keys} per position
 //   int32 counters[T * hblocks]          split tickets, zero between calls
 //   int4  row_desc[T]                    balanced schedule only: pieces per row
 //   fp32  lse[slots][H]                  split LSEs
@@ -171,13 +172,16 @@ int64_t slots_of(const Plan& p, int T) { return p.workers > 0 ? 2 * (int64_t)p.w
 size_t map_bytes(const Plan& p, int T) {
   return p.ordered ? (size_t)round_up((int64_t)T * p.hblocks * p.max_splits * 4, 256) : 0;
 }
+size_t info_bytes(const Plan& p, int T) {
+  return p.ordered ? (size_t)round_up((int64_t)T * p.hblocks * p.max_splits * 8, 256) : 0;
+}
 size_t counters_bytes(const Plan& p, int T) { return (size_t)round_up((int64_t)T * p.hblocks * 4, 256); }
 size_t desc_bytes(const Plan& p, int T) { return p.workers > 0 ? (size_t)round_up((int64_t)T * 16, 256) : 0; }
 size_t lse_bytes(const Plan& p, int T, int H) { return (size_t)round_up(slots_of(p, T) * H * 4, 256); }
 
 size_t workspace_bytes_for(const Plan& p, int T, int H) {
   if (!uses_workspace(p)) return 0;
-  size_t n = map_bytes(p, T) + 256;
+  size_t n = map_bytes(p, T) + info_bytes(p, T) + 256;
   if (splits_ws(p)) {
     const size_t rows = (size_t)slots_of(p, T) * H;
     n += counters_bytes(p, T) + desc_bytes(p, T) + lse_bytes(p, T, H) + rows * MLA_D_LATENT * sizeof(float);
@@ -381,10 +385,14 @@ static mla_status decode_impl(
   p.out_f = out_dtype == MLA_DTYPE_F32 ? (float*)out : nullptr;
   p.lse = lse;
   p.ws_o = nullptr; p.ws_lse = nullptr; p.counters = nullptr; p.row_desc = nullptr; p.item_map = nullptr;
+  p.item_info = nullptr;
   char* ws_base = (char*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
-  if (plan.ordered) p.item_map = (int32_t*)ws_base;
+  if (plan.ordered) {
+    p.item_map = (int32_t*)ws_base;
+    p.item_info = (int2*)(ws_base + map_bytes(plan, T));
+  }
   if (splits_ws(plan)) {
-    char* base = ws_base + map_bytes(plan, T);
+    char* base = ws_base + map_bytes(plan, T) + info_bytes(plan, T);
     const size_t c_end = counters_bytes(plan, T);
     const size_t d_end = c_end + desc_bytes(plan, T);
     p.counters = (int32_t*)base;

@@ -393,12 +393,31 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams a) {
   ticket_and_merge(a, t, h0, 16 * MT, nsplit, SlotMap{t, a.T, 0}, (int)blockIdx.x);
 }
 
+// Up to this many requests the row search runs over a copy of query_start_loc
+// in LDS (one coalesced load instead of a chain of dependent global loads).
+constexpr int kSeqlensLdsRequests = 4096;
+
 __global__ __launch_bounds__(256) void local_seqlens_kernel(const int32_t* seq_lens, const int32_t* qsl,
                                                             int B, int T, int W, int r, int I, int mode,
                                                             int32_t* row_seqlen, int32_t* shard_len) {
+  __shared__ int qsl_lds[kSeqlensLdsRequests + 1];
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (row_seqlen && i < T) row_seqlen[i] = locate_row(qsl, seq_lens, B, i, W, r, I, mode).L;
   if (shard_len && i < B) shard_len[i] = shard_count(seq_lens[i], W, r, I);
+  if (!row_seqlen) return;
+  if (B <= kSeqlensLdsRequests) {
+    for (int b = threadIdx.x; b <= B; b += 256) qsl_lds[b] = qsl[b];
+    __syncthreads();
+    if (i >= T) return;
+    int lo = 0, hi = B - 1;                // last b with qsl[b] <= i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (qsl_lds[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    const int q0 = qsl_lds[lo];
+    row_seqlen[i] = row_key_count(seq_lens[lo], qsl_lds[lo + 1] - q0, i - q0, W, r, I, mode);
+  } else if (i < T) {
+    row_seqlen[i] = locate_row(qsl, seq_lens, B, i, W, r, I, mode).L;
+  }
 }
 
 

@@ -94,6 +94,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
   // own in blockIdx order.
   const int hblocks = a.H / kXHeads;
   int item;
+  int2 info = int2{-1, 0};                  // {request, the row's local keys} from the order, if known
   if (a.item_map) {
     // Ordered dispatch: grid position p holds the p-th item of the longest-first
     // order.  Groups of four consecutive positions (one request's rows and head
@@ -105,6 +106,7 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
     if (pos >= a.T * hblocks * a.max_splits) return;
     item = a.item_map[pos];
     if (item < 0) return;
+    info = a.item_info[pos];
   } else {
     // Item x*per_xcd + k goes to blockIdx 8k + x: consecutive items share an
     // XCD and are dispatched one after the other.
@@ -115,7 +117,9 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
   const int hb = item % hblocks;
   const int t = (item / hblocks) % a.T;
   const int split = item / (hblocks * a.T);
-  const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r, kRuns ? a.I : 1, a.mode);
+  // The order kernel already located the row; in token order it is found here.
+  const RowInfo ri = info.x >= 0 ? RowInfo{info.x, info.y}
+                                 : locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r, kRuns ? a.I : 1, a.mode);
   const int L = ri.L;
   const int nsplit = num_splits_of(L, a.chunk, a.max_splits);
   if (split >= nsplit) return;
@@ -571,7 +575,8 @@ __device__ __forceinline__ UnitInfo unit_info(const DecodeParams& a, int u, cons
 }
 
 __device__ __forceinline__ int block_excl_scan(int v, int* wsum) {
-  // Exclusive prefix sum over the 1024 threads of the workgroup.
+  // Exclusive prefix sum over the 1024 threads of the workgroup: a scan in
+  // every wave, then wave 0 scans the 16 wave totals.
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -581,10 +586,18 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum) {
   }
   if (lane == 63) wsum[wv] = x;
   __syncthreads();
-  int carry = 0;
-  for (int i = 0; i < wv; ++i) carry += wsum[i];
+  if (wv == 0) {
+    const int tot = lane < kOrdThreads / 64 ? wsum[lane] : 0;
+    int c = tot;
+#pragma unroll
+    for (int off = 1; off < kOrdThreads / 64; off <<= 1) {
+      const int y = __shfl_up(c, off, 64);
+      if (lane >= off) c += y;
+    }
+    if (lane < kOrdThreads / 64) wsum[kOrdThreads / 64 + lane] = c - tot;
+  }
   __syncthreads();
-  return carry + x - v;
+  return wsum[kOrdThreads / 64 + wv] + x - v;
 }
 
 __global__ __launch_bounds__(kOrdThreads) void h128_order_kernel(const DecodeParams a) {
@@ -592,7 +605,7 @@ __global__ __launch_bounds__(kOrdThreads) void h128_order_kernel(const DecodePar
   __shared__ int ord[kOrdMaxUnits];      // sorted units
   __shared__ int first_item[kOrdMaxUnits + 1];
   __shared__ int rq0[kOrdMaxRequests], rq[kOrdMaxRequests], rs[kOrdMaxRequests];   // per request
-  __shared__ int wsum[kOrdThreads / 64];
+  __shared__ int wsum[2 * (kOrdThreads / 64)];   // wave totals, then their exclusive scan
   const int tid = threadIdx.x;
   const int U = a.B * a.max_splits;
   const int hblocks = a.H / kXHeads;
@@ -653,6 +666,8 @@ __global__ __launch_bounds__(kOrdThreads) void h128_order_kernel(const DecodePar
       const int o = p - first_item[lo];
       const int row = ui.first + ui.rows - 1 - o / hblocks;      // last row first
       item = (s * a.T + ui.q0 + row) * hblocks + o % hblocks;
+      const int b = u - s * a.B;
+      a.item_info[p] = int2{b, row_key_count(rs[b], rq[b], row, a.W, a.r, a.I, a.mode)};
     }
     a.item_map[p] = item;
   }

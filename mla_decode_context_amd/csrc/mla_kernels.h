@@ -32,6 +32,7 @@ struct DecodeParams {
   int32_t* counters;       // int32 [T*hblocks] split tickets; zero between calls
   int4* row_desc;          // balanced schedule: per token {pieces, first slot, slot-0 offset, 0}
   int32_t* item_map;       // 128 heads: dispatch order, item of each grid position (-1: none); or null
+  int2* item_info;         // with item_map: {request, the row's local keys} of each grid position
 };
 
 struct MergeParams {

@@ -81,10 +81,11 @@ def test_workspace_size_host_logic():
     assert n >= 4 * 16 * (512 + 1) * 4
     assert ws(64, 64, 16, 1, 8192, 1, 0) > 0                 # the batch-64 decode splits automatically
     assert ws(64, 64, 16, 1, 8192, 1, 2) < ws(64, 64, 16, 1, 8192, 1, 16)
-    # 128 heads, never split: only the dispatch order (one int32 per token and
-    # 64-head block, in 256-byte units) plus the alignment slack
-    assert ws(2, 4, 128, 2, 100, 1, 1) == 256 + 256
-    assert ws(300, 600, 128, 2, 4000, 4, 1) == 4864 + 256     # 600 * 2 * 4 bytes, rounded up
+    # 128 heads, never split: only the dispatch order (one int32 item and one
+    # int2 {request, keys} per token and 64-head block, each array in 256-byte
+    # units) plus the alignment slack
+    assert ws(2, 4, 128, 2, 100, 1, 1) == 256 + 256 + 256
+    assert ws(300, 600, 128, 2, 4000, 4, 1) == 4864 + 9728 + 256     # 600 * 2 * {4, 8} bytes, rounded up
     # more (split, request) units than the order kernel sorts: no order, no workspace
     assert ws(9000, 9000, 128, 1, 4000, 4, 1) == 0
     # run layout: invalid run lengths are rejected; the split plan follows the
