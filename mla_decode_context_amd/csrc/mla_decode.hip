@@ -461,13 +461,20 @@ __device__ __forceinline__ void write_empty_row(const DecodeParams& a, int t) {
 // (counter `counter`, slots `sm`).
 //
 // kFP8: the cache holds FP8 E4M3 codes (576-byte rows, one scale per cache).
-// A wave's 36 KiB of LDS then holds two 9 KiB slots of E4M3 rows, filled by
-// direct-to-LDS loads as for bf16 (half the bytes per stage), and an 18 KiB
-// bf16 copy of the current stage: once a stage has landed the wave expands
-// it with the exact E4M3 -> bf16 conversion into the swizzled bf16 layout,
-// and the MFMA reads below run on that copy unchanged.  The cache scale is in
-// the scores' exponent factor (scale_log2) and in the final normalisation
-// (out_scale), so the conversion adds no rounding.
+// A wave's ring then holds two 9 KiB slots of E4M3 rows, filled by
+// direct-to-LDS loads as for bf16 (half the bytes per stage), and the MFMA
+// operands are converted in registers right after their LDS reads, with the
+// exact E4M3 -> bf16 conversion: a score operand is 8 codes of one key (an
+// 8-byte read), a PV operand pair comes from one transposed read of 16-bit
+// elements, each element being the codes of two adjacent dims of one key, so
+// that the read yields 4 keys of dims 2p and 2p + 1 (split into two operands by
+// byte permutes; the O^T tiles 2pt and 2pt + 1 then hold the even and the odd
+// dims of dims 32pt .. 32pt + 31).  In a stage row, 16-byte chunk c sits at
+// c ^ 2((row >> 2) & 1): the transposed reads are then free of bank conflicts
+// (the 8-byte score reads of 16 rows at one column take two passes, the
+// 576-byte row stride allows no better).  The cache scale is in the scores'
+// exponent factor (scale_log2) and in the final normalisation (out_scale), so
+// the conversion adds no rounding.
 template <bool kPage16, bool kDeferMerge, bool kFP8>
 __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_block, int t, int b,
                                           int j_begin, int j_end, int nsplit, int64_t my_slot, SlotMap sm,
@@ -507,7 +514,6 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
   constexpr int kBlk = kSlotB / 1024;                      // load instructions per stage
   constexpr int kElemB = kFP8 ? 1 : 2;                     // bytes per cache element
   uint8_t* ring = lds_block + w * kWRing * kWStageBytes;   // 36 KiB per wave either way
-  uint8_t* stage16 = ring + kWRing * kSlotB;               // FP8: bf16 copy of the stage
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring);
 
@@ -517,15 +523,16 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
   // different chunks).  Block i (1 KiB) is written by one load: lane l -> bytes
   // 1024i + 16l .. +16, fetched from the byte offset below within the stage's
   // 16 consecutive cache rows.
-  // FP8 stages land unswizzled (byte o of the slot = byte o of the 16 rows);
-  // the expansion into the bf16 copy applies the swizzle.
+  // FP8 stages: byte o of the 9 KiB slot is row o / 576, chunk position
+  // p = (o % 576) / 16, holding chunk p ^ 2((row >> 2) & 1) of the row.
   uint32_t doff[kBlk];
 #pragma unroll
   for (int i2 = 0; i2 < kBlk; ++i2) {
     const int o = 1024 * i2 + 16 * lane;
     const int row = o / kRowB;
     const int cpos = (o - row * kRowB) >> 4;
-    doff[i2] = kFP8 ? (uint32_t)o : (uint32_t)(row * kRowBytes + ((cpos ^ (row & 7)) << 4));
+    doff[i2] = kFP8 ? (uint32_t)(row * kRow + ((cpos ^ (2 * ((row >> 2) & 1))) << 4))
+                    : (uint32_t)(row * kRowBytes + ((cpos ^ (row & 7)) << 4));
   }
   // Issue piece stage st into ring slot `slot`.  Keys at or past j_end (the
   // ragged last stage) are clamped to key j_end - 1 -- a real cached row, masked
@@ -559,7 +566,7 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
         const int pg = j / a.P;                    // one of pgx[0..2]
         const int blk = pg == pgx[0] ? bx[0] : (pg == pgx[1] ? bx[1] : bx[2]);
         const int64_t rbase = (int64_t)blk * a.kv_bs + (int64_t)(j - pg * a.P) * kRow;
-        dma_16B_to_lds_stream(kv_bytes + rbase + (o - row * kRow), ring + slot * kSlotB + 1024 * i2);
+        dma_16B_to_lds_stream(kv_bytes + rbase + (doff[i2] - row * kRow), ring + slot * kSlotB + 1024 * i2);
       }
     } else {
 #pragma unroll
@@ -594,6 +601,13 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
   uint32_t vbase[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) vbase[m] = vr * kRowBytes + 16 * ((2 * m + vx) ^ v7) + 8 * (lr & 1);
+  // FP8 reads.  Scores: lane (key lr, group g) reads codes 32s + 8g .. +8 of
+  // row lr: chunk 2s + (g >> 1), i.e. byte lr*576 + 32(s ^ b) + 8g with
+  // b = (lr >> 2) & 1.  PV: source lane (key vr, pairs 16pt + 4(lr & 3) .. +4)
+  // reads 8 bytes at byte vr*576 + 32(pt ^ bv) + 8(lr & 3), bv = (vr >> 2) & 1.
+  const int fb = (lr >> 2) & 1, fbv = (vr >> 2) & 1;
+  const uint32_t fk0 = lr * kRow + 8 * g + 32 * fb, fk1 = lr * kRow + 8 * g - 32 * fb;   // even / odd s
+  const uint32_t fv0 = vr * kRow + 8 * (lr & 3) + 32 * fbv, fv1 = vr * kRow + 8 * (lr & 3) - 32 * fbv;
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[32];                    // O^T tiles over all 512 latent dims
@@ -616,32 +630,6 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
       __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
     }
     const uint8_t* sb = ring + slot * kSlotB;
-    if constexpr (kFP8) {
-      // Expand the E4M3 stage into the bf16 layout of the reads below: lane
-      // takes the 16-byte chunks lane + 64u (16 codes of one row each; 36 per
-      // row), converts them exactly and writes bf16 chunks 2ch and 2ch + 1 of
-      // the row at their swizzled places.  Same wave, LDS in order: the writes
-      // land after the previous stage's reads of the copy and before the reads
-      // below.
-#pragma unroll
-      for (int u = 0; u < kBlk; ++u) {
-        const int c = lane + 64 * u;
-        const int row = c / 36, ch = c - row * 36;
-        const u32x4 v = *(const u32x4*)(sb + 16 * c);
-        u32x4 lo, hi;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          lo[2 * e] = fp8x2_to_bf16x2<false>(v[e]);
-          lo[2 * e + 1] = fp8x2_to_bf16x2<true>(v[e]);
-          hi[2 * e] = fp8x2_to_bf16x2<false>(v[2 + e]);
-          hi[2 * e + 1] = fp8x2_to_bf16x2<true>(v[2 + e]);
-        }
-        const int d0 = row * kRowBytes + 16 * ((2 * ch) ^ (row & 7));
-        *(u32x4*)(stage16 + d0) = lo;
-        *(u32x4*)(stage16 + (d0 ^ 16)) = hi;
-      }
-      sb = stage16;
-    }
     const int j0 = j_begin + kWStage * (w + 4 * k);
 
     // S^T[key][head] over 576 dims (A = keys: lane key lr, dims 32s + 8g), two
@@ -653,7 +641,13 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
 #pragma unroll
       for (int u = 0; u < 9; ++u) {
         const int s = 9 * h2 + u;
-        kk[u] = *(const bf16x8*)(sb + ((s & 1) ? kbase1 : kbase0) + 128 * (s >> 1));
+        if constexpr (kFP8) {
+          const u32x2 c8 = *(const u32x2*)(sb + ((s & 1) ? fk1 : fk0) + 32 * s);
+          kk[u] = __builtin_bit_cast(bf16x8, u32x4{fp8x2_to_bf16x2<false>(c8[0]), fp8x2_to_bf16x2<true>(c8[0]),
+                                                   fp8x2_to_bf16x2<false>(c8[1]), fp8x2_to_bf16x2<true>(c8[1])});
+        } else {
+          kk[u] = *(const bf16x8*)(sb + ((s & 1) ? kbase1 : kbase0) + 128 * (s >> 1));
+        }
       }
 #pragma unroll
       for (int u = 0; u < 9; ++u) {
@@ -695,6 +689,31 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
     // keys 16..31 zero.  The transposed read gives lane (dim lr, group g) keys
     // 4g .. 4g+3 when source lane lr points at key 4g + (lr >> 2), dims
     // 16dt + 4(lr & 3) .. +4.
+    if constexpr (kFP8) {
+      // Pair tile pt: the transposed read gives lane (pair 16pt + lr, group g)
+      // the codes of dims 2p, 2p + 1 of keys 4g .. 4g+3; byte permutes gather
+      // the even and the odd dims, which convert to the two operands.
+#pragma unroll
+      for (int p8 = 0; p8 < 4; ++p8) {
+        s16x4 vt[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int pt = 4 * p8 + u;
+          vt[u] = lds_read_tr16_at(sb + ((pt & 1) ? fv1 : fv0) + 32 * pt);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int pt = 4 * p8 + u;
+          const u32x2 wv = __builtin_bit_cast(u32x2, vt[u]);
+          const uint32_t ev = __builtin_amdgcn_perm(wv[1], wv[0], 0x06040200u);   // keys 0..3, dim 2p
+          const uint32_t od = __builtin_amdgcn_perm(wv[1], wv[0], 0x07050301u);   // keys 0..3, dim 2p + 1
+          const bf16x8 va0 = __builtin_bit_cast(bf16x8, u32x4{fp8x2_to_bf16x2<false>(ev), fp8x2_to_bf16x2<true>(ev), 0u, 0u});
+          const bf16x8 va1 = __builtin_bit_cast(bf16x8, u32x4{fp8x2_to_bf16x2<false>(od), fp8x2_to_bf16x2<true>(od), 0u, 0u});
+          o[2 * pt] = mfma_16x16x32(va0, pb, o[2 * pt]);
+          o[2 * pt + 1] = mfma_16x16x32(va1, pb, o[2 * pt + 1]);
+        }
+      }
+    } else {
 #pragma unroll
     for (int d8 = 0; d8 < 4; ++d8) {
       s16x4 vt[8];
@@ -709,6 +728,7 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
         const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vt[u], s16x4{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7));
         o[dt] = mfma_16x16x32(va, pb, o[dt]);
       }
+    }
     }
   }
   l_run = col_sum(l_run);
@@ -753,7 +773,27 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
 #pragma unroll
         for (int u = 1; u < 4; ++u) x += c[u] * ost[(u * 32 + dt) * 64 + lane];
         x *= inv;
-        const int d = 16 * dt + 4 * g;     // lane holds dims d .. d+3 of head h
+        int d = 16 * dt + 4 * g;           // lane holds dims d .. d+3 of head h
+        if constexpr (kFP8) {
+          // Tiles 2pt, 2pt + 1 hold the even and odd dims 32pt + 8g + 2q (+ 1):
+          // tile 2pt writes dims 32pt + 8g .. +4, tile 2pt + 1 dims .. +4 .. +8,
+          // after the lanes swap halves with their partner tile's values.
+          const int pt = dt >> 1, e = dt & 1;
+          f32x4 yy;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            // the partner tile's element q, from LDS
+            float other = c[0] * ost[(0 * 32 + (dt ^ 1)) * 64 + lane][q];
+#pragma unroll
+            for (int u = 1; u < 4; ++u) other += c[u] * ost[(u * 32 + (dt ^ 1)) * 64 + lane][q];
+            yy[q] = other * inv;
+          }
+          // dims 32pt + 8g + 4e + r for r = 0..3: element r of the 8-dim run
+          // 32pt + 8g + m has m = 4e + r, even m from tile 2pt, odd from 2pt + 1.
+          const f32x4 ev = e ? yy : x, od = e ? x : yy;   // tile 2pt, tile 2pt + 1
+          x = e ? f32x4{ev[2], od[2], ev[3], od[3]} : f32x4{ev[0], od[0], ev[1], od[1]};
+          d = 32 * pt + 8 * g + 4 * e;
+        }
         if (nsplit == 1) {
           store_out4(a, (size_t)t * a.H + h, d, x);
         } else if (kDeferMerge) {
