@@ -536,7 +536,7 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
   }
   // Issue piece stage st into ring slot `slot`.  Keys at or past j_end (the
   // ragged last stage) are clamped to key j_end - 1 -- a real cached row, masked
-  // to probability 0 -- so every path issues exactly kWBlocks loads.
+  // to probability 0 -- so every path issues exactly kBlk loads.
   auto issue = [&](int st, int slot) {
     const int j0 = j_begin + kWStage * st;
     const uint32_t ldst = ring_lds + slot * kSlotB;
@@ -625,7 +625,7 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
     if (k + 1 < my_n) {
       __builtin_amdgcn_s_waitcnt(MLA_LGKMCNT0);
       issue(w + 4 * (k + 1), slot ^ 1);
-      __builtin_amdgcn_s_waitcnt(MLA_VMCNT(kWBlocks));
+      __builtin_amdgcn_s_waitcnt(MLA_VMCNT(kBlk));       // this stage's loads landed, the next one's may not
     } else {
       __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
     }
