@@ -180,11 +180,14 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const MergeParams a) {
 // tokens then stream through in blocks of 16: the merged latent rows of a
 // block (exact LSE-weighted combine of the participating ranks, rounded to
 // bf16) go to LDS, and y[tok][n] = o[tok][k] W[k][n] runs on MFMA 16x16x32
-// (wave w: n = 16w .. 16w+15), A = o from LDS, B = W through transposed LDS
-// reads.  Each thread merges one token's 16 dims, so three items' partials fit
-// in its registers: two items are always in flight while one is merged and
-// projected, and their valid counts come one item earlier through scalar
-// loads (a wait for a count never waits for partials).
+// (wave w: n = 16w .. 16w+15), A = o from LDS, B = W: the wave's 16 columns
+// of W_UV[h] are read once from the staged copy (transposed LDS reads) and stay
+// in registers for the whole launch, so per block only the merged rows are
+// read from LDS (keeping B in registers cut the exchange pack's time by a third
+// and the fused merge's by 9 %).  Each thread merges one token's 16 dims, so
+// three items' partials fit in its registers: two items are always in flight
+// while one is merged and projected, and their valid counts come one item
+// earlier through scalar loads (a wait for a count never waits for partials).
 //
 // LDS layouts (both swizzled so that the MFMA operand reads are conflict-free):
 //   W  row k (256 B) holds element n at byte (2n) ^ (32 * (k & 7));
@@ -196,11 +199,13 @@ constexpr int kWBytes = kLatent * kVHead * 2;      // 128 KiB
 
 // kOne (W = 1): the merge is the identity, and an item's slots are
 // consecutive token blocks of the one partial instead of ranks of one block,
-// so that several times the bytes are in flight per item.  An item has four
-// slots with bf16 partials and two with fp32 partials (kF32: the same bytes).
+// so that more bytes are in flight per item.  An item has two slots with bf16
+// partials and one with fp32 partials (kF32: the same bytes); with W_UV's
+// operands held in registers more slots no longer fit (measured: three slots
+// 14 % slower than two for the pack).
 template <bool kValid, bool kOne, bool kF32>
 __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const MergeParams a) {
-  constexpr int kSlots = kF32 ? 2 : 4;
+  constexpr int kSlots = kF32 ? 1 : 2;
   constexpr int kWords = kF32 ? 4 : 2;               // 16-byte loads per 16 values
   constexpr int kElem = kF32 ? 4 : 2;                // bytes per partial value
   const uint8_t* outs = kF32 ? (const uint8_t*)a.outs_f : (const uint8_t*)a.outs;
@@ -300,6 +305,25 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
     }
   };
 
+  // B operands (W_UV[h] columns n0 + lr, k = 32s + 8g .. +8) of this wave,
+  // read from the staged copy at the first block: source lane j of read r
+  // addresses row k = 32s + 8g + 4r + (j >> 2), columns n0 + 4(j & 3) .. +4.
+  bf16x8 bw[kLatent / 32];
+  bool bw_ready = false;
+  auto load_bw = [&]() {
+    const int n0 = 16 * wv;
+#pragma unroll
+    for (int s = 0; s < kLatent / 32; ++s) {
+      s16x4 half[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int k = 32 * s + 8 * g + 4 * r + (lr >> 2);
+        const int cb = 2 * (n0 + 4 * (lr & 3));
+        half[r] = lds_read_tr16_at(w_lds + k * 256 + (cb ^ (32 * (k & 7))));
+      }
+      bw[s] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
   float m = -INFINITY, ssum = 0.f;
   f32x4 acc[4];
   // One item: merge its ranks into the running (m, ssum, acc); after the last
@@ -339,6 +363,10 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
     // (they target registers, not LDS).
     if (tb == t_begin) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (!bw_ready) {                  // (uniform) W_UV has landed: its operands into registers
+      load_bw();
+      bw_ready = true;
+    }
 
     // ---- y[tok][n] for the block's 16 tokens, n = 16wv .. 16wv+15 ----
     f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -347,18 +375,8 @@ __global__ __launch_bounds__(kProjThreads, 1) void merge_v_up_kernel(const Merge
     for (int s = 0; s < kLatent / 32; ++s) {
       // A = o: lane (token lr, group g) takes dims 32s + 8g .. +8 (chunk 4s + g).
       const bf16x8 av = *(const bf16x8*)(o_lds + lr * 1024 + 16 * ((4 * s + g) ^ (lr & 7)));
-      // B = W: lane (column n = n0 + lr, group g) takes k = 32s + 8g .. +8 from
-      // two transposed reads: source lane j of read r addresses row
-      // k = 32s + 8g + 4r + (j >> 2), columns n0 + 4(j & 3) .. +4.
-      s16x4 half[2];
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int k = 32 * s + 8 * g + 4 * r + (lr >> 2);
-        const int cb = 2 * (n0 + 4 * (lr & 3));
-        half[r] = lds_read_tr16_at(w_lds + k * 256 + (cb ^ (32 * (k & 7))));
-      }
-      const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
-      y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, y, 0, 0, 0);
+      // B = W: lane (column n = n0 + lr, group g) holds k = 32s + 8g .. +8.
+      y = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw[s], y, 0, 0, 0);
     }
     // D: lane (column n = n0 + lr, group g) holds tokens 4g .. 4g+3 of the block.
     const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
