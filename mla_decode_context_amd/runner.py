@@ -71,9 +71,10 @@ class DeviceWorkload:
             name = f"decode_kernel_h128<{page32}, {runs}>"
             if self.workspace is None:
                 return name
-            # the workspace holds the dispatch order (one int32 per token and
-            # 64-head block, 256-byte aligned) and, when rows are split, the partials
-            order_only = -(-self.T * 2 * 4 // 256) * 256 + 256
+            # the workspace holds the dispatch order (one int32 item and one int2
+            # {request, keys} per token and 64-head block, each 256-byte aligned)
+            # and, when rows are split, the partials
+            order_only = -(-self.T * 2 * 4 // 256) * 256 + -(-self.T * 2 * 8 // 256) * 256 + 256
             name = "h128_order_kernel+" + name
             return name + "+combine_fixed_kernel" if self.workspace.numel() > order_only else name
         page16 = "true" if self.wl.P % 16 == 0 else "false"
