@@ -6,8 +6,8 @@ contexts drawn uniformly from 8192..32768 tokens (four requests shortened so
 that some shards hold empty rows), page 64 with permuted physical blocks.  One
 step = one pass of the whole path over that batch: every shard's
 mla_decode_partial (row seqlens, paged gather, scores, masked online softmax,
-PV, split-K where the plan splits, finalise), the per-row valid counts of every
-shard, and the LSE merge of the eight partials.
+PV, split-K where the plan splits, finalise; each call also writes its rows'
+valid counts), and the LSE merge of the eight partials.
 
 Other workloads (reported under "configs", not in the headline value): the
 plain 16-head decode (W = 1, no merge), the MTP DCP4 step, the mixed batch
@@ -124,11 +124,10 @@ def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True
         for r in range(wl.W):
             if evs is not None:
                 evs[r][0].record()
-            dw.partial(r)
+            dw.partial(r)                 # also writes rank r's valid counts
             if evs is not None:
                 evs[r][1].record()
         if merging:
-            dw.valid_counts()
             if evs is not None:
                 evs[wl.W][0].record()
             dw.merge_v_up() if proj else dw.merge()

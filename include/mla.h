@@ -139,6 +139,11 @@ const char* mla_status_string(mla_status status);
  *   out      [T,H,512] contiguous, bf16 (out_dtype = MLA_DTYPE_BF16, rounded
  *            to nearest even) or fp32 (MLA_DTYPE_F32, the normalised fp32
  *            accumulator);  lse fp32 [T,H] contiguous
+ *   row_keys int32 [T] or NULL: when given, receives every row's L (the count
+ *            of visible local keys above, under mask_mode), the values
+ *            mla_dcp_local_seqlens writes for this rank and the merges take
+ *            as valid counts; written by the launches of this call (no
+ *            further launch)
  *
  * Host integers: max_query_len >= every Q_b and max_seq_len >= every S_b are
  * upper bounds that size the launch grid (nothing is read back from the
@@ -184,7 +189,7 @@ mla_status mla_decode_partial(
     int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
     int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, int32_t mask_mode, float scale,
     int32_t num_splits,
-    void* out, int32_t out_dtype, float* lse,
+    void* out, int32_t out_dtype, float* lse, int32_t* row_keys,
     void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
@@ -219,7 +224,7 @@ mla_status mla_decode_partial_noalloc(
     int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
     int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, int32_t mask_mode, float scale,
     int32_t num_splits,
-    void* out, int32_t out_dtype, float* lse, void* hip_stream);
+    void* out, int32_t out_dtype, float* lse, int32_t* row_keys, void* hip_stream);
 
 /*
  * mla_check_decode_metadata -- the device-side contract of mla_decode_partial,

@@ -51,13 +51,13 @@ def load_library():
         _c_void_p, _i64, _i64, _c_void_p, _i64, _i64, _c_void_p, _i32, ctypes.c_float, _i64, _i32,
         _c_void_p, _i32, _c_void_p, _c_void_p,
         _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
-        _c_void_p, _i32, _c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p]
+        _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p]
     lib.mla_decode_partial_noalloc.restype = _i32
     lib.mla_decode_partial_noalloc.argtypes = [
         _c_void_p, _i64, _i64, _c_void_p, _i64, _i64, _c_void_p, _i32, ctypes.c_float, _i64, _i32,
         _c_void_p, _i32, _c_void_p, _c_void_p,
         _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32,
-        _c_void_p, _i32, _c_void_p, _c_void_p]
+        _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p]
     lib.mla_decode_workspace_size.restype = ctypes.c_size_t
     lib.mla_decode_workspace_size.argtypes = [_i32] * 8
     lib.mla_lse_merge.restype = _i32
@@ -154,9 +154,10 @@ def workspace_size(B, T, H, max_query_len, max_seq_len, cp_world, num_splits=0, 
 def mla_decode_partial(q_nope, q_pe, kv_cache, block_table, seq_lens, query_start_loc,
                        cp_world, cp_rank, scale, out, lse, *, max_query_len, max_seq_len,
                        workspace=None, num_splits=0, stream=None, cp_interleave=1, mask_mode=MASK_CAUSAL,
-                       kv_scale=None):
+                       kv_scale=None, row_keys=None):
     """One DCP rank's partial attention; writes ``out`` [T,H,512] (bf16, or fp32
-    partials when ``out`` is a float32 tensor) and ``lse`` [T,H] fp32.
+    partials when ``out`` is a float32 tensor) and ``lse`` [T,H] fp32, and when
+    given ``row_keys`` [T] int32 (every row's visible local key count).
     ``cp_interleave``: tokens per run of the shard layout (1 = token p on rank p mod W)."""
     lib = load_library()
     _need(q_nope, torch.bfloat16, "q_nope", 3)
@@ -191,6 +192,7 @@ def mla_decode_partial(q_nope, q_pe, kv_cache, block_table, seq_lens, query_star
         raise MlaError("lse: expected contiguous [T,H]")
     if not (seq_lens.is_contiguous() and query_start_loc.is_contiguous()):
         raise MlaError("seq_lens/query_start_loc must be contiguous")
+    _row_keys_ok(row_keys, T)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.mla_decode_partial(
         _ptr(q_nope), qn_st, qn_sh,
@@ -200,13 +202,23 @@ def mla_decode_partial(q_nope, q_pe, kv_cache, block_table, seq_lens, query_star
         _ptr(seq_lens), _ptr(query_start_loc),
         B, T, H, int(max_query_len), int(max_seq_len), int(cp_world), int(cp_rank), int(cp_interleave),
         int(mask_mode), float(scale),
-        int(num_splits), _ptr(out), out_dtype, _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream))
+        int(num_splits), _ptr(out), out_dtype, _ptr(lse), _ptr(row_keys), _ptr(workspace), ws_bytes,
+        _stream(stream))
     _check(st, "mla_decode_partial")
+
+
+def _row_keys_ok(row_keys, T):
+    if row_keys is None:
+        return
+    _need(row_keys, torch.int32, "row_keys", 1)
+    if row_keys.shape[0] != T or not row_keys.is_contiguous():
+        raise MlaError("row_keys: expected contiguous int32 [T]")
 
 
 def mla_decode_partial_noalloc(q_nope, q_pe, kv_cache, block_table, seq_lens, query_start_loc,
                                cp_world, cp_rank, scale, out, lse, *, max_query_len, max_seq_len,
-                               num_splits=0, stream=None, cp_interleave=1, mask_mode=MASK_CAUSAL, kv_scale=None):
+                               num_splits=0, stream=None, cp_interleave=1, mask_mode=MASK_CAUSAL, kv_scale=None,
+                               row_keys=None):
     """mla_decode_partial without a workspace (the library's per-GPU scratch array
     holds the split partials): for callers that cannot allocate."""
     lib = load_library()
@@ -223,13 +235,14 @@ def mla_decode_partial_noalloc(q_nope, q_pe, kv_cache, block_table, seq_lens, qu
         raise MlaError("mla_decode_partial_noalloc: shapes disagree")
     if T and not (out.is_contiguous() and lse.is_contiguous() and q_nope.stride(2) == 1 and q_pe.stride(2) == 1):
         raise MlaError("mla_decode_partial_noalloc: out/lse contiguous, q rows contiguous")
+    _row_keys_ok(row_keys, T)
     B = seq_lens.shape[0]
     st = lib.mla_decode_partial_noalloc(
         _ptr(q_nope), q_nope.stride(0), q_nope.stride(1), _ptr(q_pe), q_pe.stride(0), q_pe.stride(1),
         _ptr(kv_cache), kv_dtype, kv_sc, kv_cache.stride(0), page, _ptr(block_table), block_table.stride(0),
         _ptr(seq_lens), _ptr(query_start_loc), B, T, H, int(max_query_len), int(max_seq_len),
         int(cp_world), int(cp_rank), int(cp_interleave), int(mask_mode), float(scale), int(num_splits),
-        _ptr(out), out_dtype, _ptr(lse), _stream(stream))
+        _ptr(out), out_dtype, _ptr(lse), _ptr(row_keys), _stream(stream))
     _check(st, "mla_decode_partial_noalloc")
 
 

@@ -306,7 +306,7 @@ static mla_status decode_impl(
     int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
     int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, int32_t mask_mode, float scale,
     int32_t num_splits,
-    void* out, int32_t out_dtype, float* lse,
+    void* out, int32_t out_dtype, float* lse, int32_t* row_keys,
     void* workspace, size_t workspace_bytes, void* hip_stream, bool noalloc) {
   if (B < 0 || T < 0 || H < 1 || H > MLA_MAX_HEADS || page_size < 1 || !layout_ok(cp_world, cp_interleave) ||
       cp_rank < 0 || cp_rank >= cp_world || max_query_len < 0 || max_seq_len < 0 ||
@@ -384,6 +384,7 @@ static mla_status decode_impl(
   p.out = out_dtype == MLA_DTYPE_BF16 ? (uint16_t*)out : nullptr;
   p.out_f = out_dtype == MLA_DTYPE_F32 ? (float*)out : nullptr;
   p.lse = lse;
+  p.row_keys = row_keys;
   p.ws_o = nullptr; p.ws_lse = nullptr; p.counters = nullptr; p.row_desc = nullptr; p.item_map = nullptr;
   p.item_info = nullptr;
   char* ws_base = (char*)(((uintptr_t)workspace + 255) & ~(uintptr_t)255);
@@ -423,12 +424,12 @@ mla_status mla_decode_partial(
     int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
     int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, int32_t mask_mode, float scale,
     int32_t num_splits,
-    void* out, int32_t out_dtype, float* lse,
+    void* out, int32_t out_dtype, float* lse, int32_t* row_keys,
     void* workspace, size_t workspace_bytes, void* hip_stream) {
   return decode_impl(q_nope, qn_stride_t, qn_stride_h, q_pe, qp_stride_t, qp_stride_h, kv_cache, kv_dtype, kv_scale,
                      kv_block_stride,
                      page_size, block_table, bt_stride, seq_lens, query_start_loc, B, T, H, max_query_len,
-                     max_seq_len, cp_world, cp_rank, cp_interleave, mask_mode, scale, num_splits, out, out_dtype, lse,
+                     max_seq_len, cp_world, cp_rank, cp_interleave, mask_mode, scale, num_splits, out, out_dtype, lse, row_keys,
                      workspace, workspace_bytes, hip_stream, false);
 }
 
@@ -441,11 +442,11 @@ mla_status mla_decode_partial_noalloc(
     int32_t B, int32_t T, int32_t H, int32_t max_query_len, int32_t max_seq_len,
     int32_t cp_world, int32_t cp_rank, int32_t cp_interleave, int32_t mask_mode, float scale,
     int32_t num_splits,
-    void* out, int32_t out_dtype, float* lse, void* hip_stream) {
+    void* out, int32_t out_dtype, float* lse, int32_t* row_keys, void* hip_stream) {
   return decode_impl(q_nope, qn_stride_t, qn_stride_h, q_pe, qp_stride_t, qp_stride_h, kv_cache, kv_dtype, kv_scale,
                      kv_block_stride,
                      page_size, block_table, bt_stride, seq_lens, query_start_loc, B, T, H, max_query_len,
-                     max_seq_len, cp_world, cp_rank, cp_interleave, mask_mode, scale, num_splits, out, out_dtype, lse,
+                     max_seq_len, cp_world, cp_rank, cp_interleave, mask_mode, scale, num_splits, out, out_dtype, lse, row_keys,
                      nullptr, 0, hip_stream, true);
 }
 

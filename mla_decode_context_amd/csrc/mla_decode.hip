@@ -137,6 +137,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams a) {
   const int nsplit = num_splits_of(L, a.chunk, (int)gridDim.y);
   if (split >= nsplit) return;
   const int h0 = hb * 16 * MT;
+  if (a.row_keys && split == 0 && hb == 0 && threadIdx.x == 0) a.row_keys[t] = L;
 
   if (L == 0) {
     // The row sees no key on this rank: out = 0, lse = -inf.
@@ -877,6 +878,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a
     const RowInfo ri = locate_row(a.qsl, a.seq_lens, a.B, t, a.W, a.r, I, a.mode);
     const int nsplit = num_splits_of(ri.L, a.chunk, (int)gridDim.y);
     if (split >= nsplit) return;
+    if (a.row_keys && split == 0 && threadIdx.x == 0) a.row_keys[t] = ri.L;
     if (ri.L == 0) {
       write_empty_row(a, t);
       return;
@@ -957,7 +959,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a
         if (L == 0) {
           if (pos >= x0) {                           // the row's owner is the worker holding its start
             write_empty_row(a, t);
-            if (threadIdx.x == 0) a.row_desc[t] = int4{0, 0, 0, 0};
+            if (threadIdx.x == 0) {
+              a.row_desc[t] = int4{0, 0, 0, 0};
+              if (a.row_keys) a.row_keys[t] = 0;
+            }
           }
         } else {
           const int s0 = pos + kRowUnits;           // unit of the row's first stage
@@ -969,7 +974,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a
             const SlotMap sm{2 * gf, 2, s0 == gf * per ? 0 : 1};
             // The worker of the row's first piece tells the combine kernel how
             // to find the row's pieces.
-            if (g == gf && threadIdx.x == 0) a.row_desc[t] = int4{gl - gf + 1, sm.base, sm.adj0, 0};
+            if (g == gf && threadIdx.x == 0) {
+              a.row_desc[t] = int4{gl - gf + 1, sm.base, sm.adj0, 0};
+              if (a.row_keys) a.row_keys[t] = L;
+            }
             h16_piece<kPage16, true, kFP8>(a, lds_block, t, b, lo * kWStage, min(hi * kWStage, L), gl - gf + 1,
                                      sm.row(g - gf), sm, t);
             __syncthreads();                         // LDS is reused by the next piece

@@ -123,6 +123,8 @@ __global__ __launch_bounds__(512, 1) void decode_kernel_h128(const DecodeParams 
   const int L = ri.L;
   const int nsplit = num_splits_of(L, a.chunk, a.max_splits);
   if (split >= nsplit) return;
+  // The row's key count (with the dispatch order the order kernel wrote it).
+  if (a.row_keys && !a.item_map && split == 0 && hb == 0 && threadIdx.x == 0) a.row_keys[t] = L;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -667,7 +669,10 @@ __global__ __launch_bounds__(kOrdThreads) void h128_order_kernel(const DecodePar
       const int row = ui.first + ui.rows - 1 - o / hblocks;      // last row first
       item = (s * a.T + ui.q0 + row) * hblocks + o % hblocks;
       const int b = u - s * a.B;
-      a.item_info[p] = int2{b, row_key_count(rs[b], rq[b], row, a.W, a.r, a.I, a.mode)};
+      const int L = row_key_count(rs[b], rq[b], row, a.W, a.r, a.I, a.mode);
+      a.item_info[p] = int2{b, L};
+      // Every row has exactly one split-0 item of head block 0.
+      if (a.row_keys && s == 0 && o % hblocks == 0) a.row_keys[ui.q0 + row] = L;
     }
     a.item_map[p] = item;
   }

@@ -27,6 +27,7 @@ struct DecodeParams {
   uint16_t* out;           // bf16 [T,H,512] (when out_f is null)
   float* out_f;            // fp32 [T,H,512] partials instead of bf16, or null
   float* lse;              // fp32 [T,H]
+  int32_t* row_keys;       // int32 [T]: each row's visible local keys, or null
   float* ws_o;             // fp32 [slots,H,512] split partials (normalised)
   float* ws_lse;           // fp32 [slots,H]
   int32_t* counters;       // int32 [T*hblocks] split tickets; zero between calls

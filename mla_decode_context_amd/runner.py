@@ -87,14 +87,17 @@ class DeviceWorkload:
         return f"decode_kernel<2, 3, {page16}>"
 
     def partial(self, r: int, stream=None):
+        """Rank r's partial, and its rows' key counts into valid[r] (the merge's
+        valid counts, written by the decode's own launches)."""
         mla.mla_decode_partial(
             self.q_nope, self.q_pe, self.caches[r], self.tables[r], self.seq_lens, self.qsl,
             self.W, r, self.scale, self.outs[r], self.lses[r],
             max_query_len=self.max_query_len, max_seq_len=self.max_seq_len,
             workspace=self.workspace, num_splits=self.num_splits, stream=stream, cp_interleave=self.I,
-            kv_scale=self.kv_scale)
+            kv_scale=self.kv_scale, row_keys=self.valid[r])
 
     def valid_counts(self, stream=None):
+        """The same counts through mla_dcp_local_seqlens (one launch per rank)."""
         for r in range(self.W):
             mla.mla_dcp_local_seqlens(self.seq_lens, self.qsl, self.T, self.W, r,
                                       row_seqlen=self.valid[r], stream=stream, cp_interleave=self.I)
@@ -123,16 +126,18 @@ class DeviceWorkload:
             self.W, r, self.scale, self.outs2[r], self.lses2[r],
             max_query_len=self.max_query_len, max_seq_len=self.max_seq_len, workspace=self.workspace,
             num_splits=self.num_splits, stream=stream, cp_interleave=self.I, mask_mode=mla.MASK_CONTEXT,
-            kv_scale=self.kv_scale)
+            kv_scale=self.kv_scale, row_keys=self.valid2[r])
 
     def query_partial(self, stream=None):
         mla.mla_decode_partial(
             self.q_nope, self.q_pe, self.qkv, self.q_table, self.q_lens, self.qsl, 1, 0, self.scale,
             self.outs2[self.W], self.lses2[self.W], max_query_len=self.max_query_len,
             max_seq_len=self.max_query_len, workspace=self.q_workspace, num_splits=self.num_splits, stream=stream,
-            kv_scale=self.kv_scale)
+            kv_scale=self.kv_scale, row_keys=self.valid2[self.W])
 
     def two_stage_counts(self, stream=None):
+        """The two stages' counts through mla_dcp_local_seqlens (the partials
+        already write them)."""
         for r in range(self.W):
             mla.mla_dcp_local_seqlens(self.seq_lens, self.qsl, self.T, self.W, r, row_seqlen=self.valid2[r],
                                       stream=stream, cp_interleave=self.I, mask_mode=mla.MASK_CONTEXT)
@@ -146,7 +151,6 @@ class DeviceWorkload:
         for r in range(self.W):
             self.context_partial(r, stream)
         self.query_partial(stream)
-        self.two_stage_counts(stream)
         if self.w_uv is not None:
             mla.mla_merge_v_up_proj(self.outs2, self.lses2, self.valid2, self.w_uv, self.out_proj, self.out_lse,
                                     stream=stream)
@@ -161,10 +165,10 @@ class DeviceWorkload:
                                 stream=stream)
 
     def step(self, stream=None):
-        """One pass of the whole path: all ranks' partials, valid counts, merge."""
+        """One pass of the whole path: all ranks' partials (with their valid
+        counts), merge."""
         for r in range(self.W):
             self.partial(r, stream)
-        self.valid_counts(stream)
         if self.w_uv is not None:
             self.merge_v_up(stream)
         else:

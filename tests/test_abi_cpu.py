@@ -40,7 +40,7 @@ def _decode(**kw):
                                   a["kvt"], a["kvs"], a["kv_bs"], a["page"], a["bt"], a["bt_stride"], a["seq"], a["qsl"], a["B"],
                                   a["T"], a["H"], a["mq"], a["ms"], a["W"], a["r"], a["I"], a["mask"], a["scale"],
                                   a["splits"],
-                                  a["out"], a["dtype"], a["lse"], a["ws"], a["ws_bytes"], None)
+                                  a["out"], a["dtype"], a["lse"], None, a["ws"], a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
