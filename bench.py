@@ -426,6 +426,11 @@ def calibrate(torch, reps=5):
 
     rd, rd_med = best_ms(lambda: mla.calib_hbm_read(buf, sink, nontemporal=False))
     rn, rn_med = best_ms(lambda: mla.calib_hbm_read(buf, sink, nontemporal=True))
+    # The merges' pattern: eight streams of 72 MiB read (2.3x the last-level
+    # cache together), one written.
+    gb = 72 << 20
+    gbytes = (8 + 1) * gb
+    rg, rg_med = best_ms(lambda: mla.calib_hbm_gather(buf, gb, 8))
     del buf
     iters = 40000
     flops = mla.calib_mfma_bf16(iters, sink)
@@ -436,9 +441,12 @@ def calibrate(torch, reps=5):
             "hbm_read_GBps_median": round(nbytes / (rd_med * 1e-3) / 1e9, 1),
             "hbm_read_nt_GBps": round(nbytes / (rn * 1e-3) / 1e9, 1),
             "hbm_read_nt_GBps_median": round(nbytes / (rn_med * 1e-3) / 1e9, 1),
+            "hbm_8read_1write_GBps": round(gbytes / (rg * 1e-3) / 1e9, 1),
+            "hbm_8read_1write_GBps_median": round(gbytes / (rg_med * 1e-3) / 1e9, 1),
             "mfma_bf16_TFLOPs": round(flops / (mf * 1e-3) / 1e12, 1),
             "mfma_bf16_TFLOPs_median": round(flops / (mf_med * 1e-3) / 1e12, 1),
-            "method": "mla_calib_hbm_read over 4 GiB (plain / non-temporal loads), mla_calib_mfma_bf16 "
+            "method": "mla_calib_hbm_read over 4 GiB (plain / non-temporal loads), mla_calib_hbm_gather "
+                      "(8 x 72 MiB read, 72 MiB written), mla_calib_mfma_bf16 "
                       f"({iters} rounds of 8 chains of v_mfma_f32_16x16x32_bf16, 2 waves per SIMD); "
                       f"best of {reps} event-timed calls"}
 
@@ -530,6 +538,8 @@ def main():
         res, _ = time_workload(name, 20 * args.config_steps if plain_like else args.config_steps,
                                300 if plain_like else 3, torch, alternate=plain_like)
         res["roofline"] = make_roofline(res, name, calib)
+        if calib and res.get("merge_GBps"):
+            res["merge_frac_of_achievable"] = res["merge_GBps"] / calib["hbm_8read_1write_GBps"]
         configs[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()
                          if not k.startswith("_")}
         print(f"[bench] {name}: {json.dumps(configs[name])}", file=sys.stderr, flush=True)
@@ -564,6 +574,8 @@ def main():
         "merge_ms": None if head.get("merge_ms") is None else round(head["merge_ms"], 5),
         "merge_GBps": None if head.get("merge_GBps") is None else round(head["merge_GBps"], 1),
         "merge_pct_hbm_peak": None if head.get("merge_pct_hbm_peak") is None else round(head["merge_pct_hbm_peak"], 2),
+        "merge_frac_of_achievable": None if not (calib and head.get("merge_GBps")) else
+        round(head["merge_GBps"] / calib["hbm_8read_1write_GBps"], 4),
         "calibration": calib,
         "cpu_baseline": cpu,
         "configs": configs,

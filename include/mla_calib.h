@@ -1,6 +1,7 @@
 /*
- * mla_calib.h -- calibration calls of libmla: the streaming HBM read rate and
- * the dense bf16 MFMA rate that one gfx950 GPU actually delivers.
+ * mla_calib.h -- calibration calls of libmla: the streaming HBM read rate, the
+ * rate of the merges' several-reads-one-write pattern and the dense bf16 MFMA
+ * rate that one gfx950 GPU actually delivers.
  *
  * They are measurement aids, not part of the attention path: the roofline
  * fractions of the decode and merge kernels are quoted against the vendor
@@ -44,6 +45,20 @@ extern "C" {
  */
 mla_status mla_calib_hbm_read(const void* buf, size_t bytes, int32_t nontemporal, uint32_t* sink,
                               void* hip_stream);
+
+/*
+ * mla_calib_hbm_gather -- the merges' access pattern: `inputs` (1, 2, 4 or 8)
+ * buffers of bytes_per_input bytes, consecutive at `in`, each read once, and
+ * one buffer of bytes_per_input bytes at `out` written once with their xor
+ * (16-byte words, a grid of up to 1024 workgroups striding over them).  The
+ * rate is (inputs + 1) * bytes_per_input over the call's time; use inputs
+ * larger than the 256 MB last-level cache together.  Returns MLA_OK
+ * (bytes_per_input == 0: nothing enqueued), MLA_ERR_NULL, MLA_ERR_SHAPE
+ * (sizes or pointers not multiples of 16, inputs not 1, 2, 4 or 8) or
+ * MLA_ERR_HIP.
+ */
+mla_status mla_calib_hbm_gather(const void* in, size_t bytes_per_input, int32_t inputs, void* out,
+                                void* hip_stream);
 
 /*
  * mla_calib_mfma_bf16 -- MLA_CALIB_MFMA_GROUPS workgroups, every wave running

@@ -80,6 +80,8 @@ def load_library():
                                               _i32, _i32, _i32, _i32, _i32, _i64, ctypes.c_char_p, ctypes.c_size_t]
     lib.mla_calib_hbm_read.restype = _i32
     lib.mla_calib_hbm_read.argtypes = [_c_void_p, ctypes.c_size_t, _i32, _c_void_p, _c_void_p]
+    lib.mla_calib_hbm_gather.restype = _i32
+    lib.mla_calib_hbm_gather.argtypes = [_c_void_p, ctypes.c_size_t, _i32, _c_void_p, _c_void_p]
     lib.mla_calib_mfma_bf16.restype = _i32
     lib.mla_calib_mfma_bf16.argtypes = [_i32, _c_void_p, _c_void_p]
     lib.mla_calib_mfma_flops.restype = ctypes.c_double
@@ -358,6 +360,21 @@ def calib_hbm_read(buf, sink, nontemporal=False, stream=None):
         raise MlaError("calib_hbm_read: contiguous GPU buffer and a 2^20-word GPU sink expected")
     _check(lib.mla_calib_hbm_read(_ptr(buf), buf.numel() * buf.element_size(), int(bool(nontemporal)), _ptr(sink),
                                   _stream(stream)), "mla_calib_hbm_read")
+
+
+def calib_hbm_gather(buf, bytes_per_input, inputs, stream=None) -> int:
+    """Read ``inputs`` consecutive buffers of ``bytes_per_input`` bytes at the
+    start of the GPU tensor ``buf`` and write their xor right after them (the
+    merges' pattern); returns the bytes moved."""
+    lib = load_library()
+    need = (inputs + 1) * bytes_per_input
+    if not buf.is_cuda or not buf.is_contiguous() or buf.numel() * buf.element_size() < need:
+        raise MlaError("calib_hbm_gather: a contiguous GPU buffer of (inputs + 1) * bytes_per_input bytes expected")
+    base = buf.data_ptr()
+    _check(lib.mla_calib_hbm_gather(ctypes.c_void_p(base), int(bytes_per_input), int(inputs),
+                                    ctypes.c_void_p(base + inputs * bytes_per_input), _stream(stream)),
+           "mla_calib_hbm_gather")
+    return need
 
 
 def calib_mfma_bf16(iters, sink, stream=None) -> float:

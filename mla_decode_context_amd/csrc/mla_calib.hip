@@ -1,5 +1,6 @@
-// Calibration kernels: what one gfx950 GPU delivers for a streaming HBM read
-// and for a register-resident bf16 MFMA loop.  The decode and merge kernels'
+// Calibration kernels: what one gfx950 GPU delivers for a streaming HBM read,
+// for the merges' pattern of several read streams and one write stream, and
+// for a register-resident bf16 MFMA loop.  The decode and merge kernels'
 // roofline fractions are quoted against the vendor peaks (8 TB/s HBM, 2.5
 // PFLOP/s dense bf16) and against these measured ceilings.  Contracts in
 // include/mla_calib.h.
@@ -34,6 +35,30 @@ __global__ __launch_bounds__(kReadThreads) void calib_read_kernel(const u32x4* _
   for (; i < n16; i += stride) acc ^= buf[i];
   const int64_t gid = (int64_t)blockIdx.x * kReadThreads + threadIdx.x;
   if (gid < MLA_CALIB_SINK_WORDS) sink[gid] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+// The merges' access pattern: R input streams read once, one output stream
+// written once (16-byte words, two per thread and input in flight, grid
+// stride); the output is the xor of the inputs so that no load is dead.
+template <int R>
+__global__ __launch_bounds__(kReadThreads) void calib_gather_kernel(const u32x4* __restrict__ in, int64_t n16,
+                                                                    u32x4* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * kReadThreads * 2;
+  for (int64_t base = (int64_t)blockIdx.x * kReadThreads * 2 + threadIdx.x; base < n16; base += stride) {
+    u32x4 acc[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int64_t i = base + u * kReadThreads;
+        if (i < n16) acc[u] ^= in[r * n16 + i];
+      }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t i = base + u * kReadThreads;
+      if (i < n16) out[i] = acc[u];
+    }
+  }
 }
 
 // Each wave runs `iters` rounds of kMfmaChains independent MFMA 16x16x32 bf16
@@ -84,6 +109,31 @@ mla_status mla_calib_hbm_read(const void* buf, size_t bytes, int32_t nontemporal
   else
     hipLaunchKernelGGL(mla::calib_read_kernel<false>, dim3((unsigned)grid), dim3(mla::kReadThreads), 0, s,
                        (const mla::u32x4*)buf, n16, sink);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status mla_calib_hbm_gather(const void* in, size_t bytes_per_input, int32_t inputs, void* out,
+                                void* hip_stream) {
+  if (bytes_per_input == 0) return MLA_OK;
+  if (!in || !out) return MLA_ERR_NULL;
+  if (bytes_per_input % 16 != 0 || ((uintptr_t)in & 15) != 0 || ((uintptr_t)out & 15) != 0 ||
+      (inputs != 1 && inputs != 2 && inputs != 4 && inputs != 8))
+    return MLA_ERR_SHAPE;
+  const int64_t n16 = (int64_t)(bytes_per_input / 16);
+  // Four 256-thread workgroups per CU of the 256-CU part (measured best of
+  // 1024..8192 for eight inputs).
+  int64_t grid = 1024;
+  const int64_t need = (n16 + 2 * mla::kReadThreads - 1) / (2 * mla::kReadThreads);
+  if (grid > need) grid = need;
+  hipStream_t s = (hipStream_t)hip_stream;
+  const mla::u32x4* pi = (const mla::u32x4*)in;
+  mla::u32x4* po = (mla::u32x4*)out;
+  switch (inputs) {
+    case 1: hipLaunchKernelGGL(mla::calib_gather_kernel<1>, dim3((unsigned)grid), dim3(mla::kReadThreads), 0, s, pi, n16, po); break;
+    case 2: hipLaunchKernelGGL(mla::calib_gather_kernel<2>, dim3((unsigned)grid), dim3(mla::kReadThreads), 0, s, pi, n16, po); break;
+    case 4: hipLaunchKernelGGL(mla::calib_gather_kernel<4>, dim3((unsigned)grid), dim3(mla::kReadThreads), 0, s, pi, n16, po); break;
+    default: hipLaunchKernelGGL(mla::calib_gather_kernel<8>, dim3((unsigned)grid), dim3(mla::kReadThreads), 0, s, pi, n16, po); break;
+  }
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -19,7 +19,8 @@ def test_exports_every_declared_symbol():
                           "mla_lse_merge", "mla_merge_v_up_proj", "mla_dcp_local_seqlens",
                           "mla_dcp_a2a_pack", "mla_dcp_a2a_combine", "mla_check_decode_metadata",
                           "mla_decode_partial_noalloc",
-                          "mla_calib_hbm_read", "mla_calib_mfma_bf16", "mla_calib_mfma_flops"}
+                          "mla_calib_hbm_read", "mla_calib_hbm_gather", "mla_calib_mfma_bf16",
+                          "mla_calib_mfma_flops"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -141,6 +142,12 @@ def test_calibration_argument_checks():
     assert lib.mla_calib_hbm_read(None, 1024, 0, P, None) == NULL
     assert lib.mla_calib_hbm_read(P, 1000, 0, P, None) == SHAPE        # not whole 16-byte words
     assert lib.mla_calib_hbm_read(ctypes.c_void_p(16 * 1024 + 4), 1024, 0, P, None) == SHAPE
+    assert lib.mla_calib_hbm_gather(P, 0, 8, P, None) == OK            # nothing to move
+    assert lib.mla_calib_hbm_gather(None, 1024, 8, P, None) == NULL
+    assert lib.mla_calib_hbm_gather(P, 1024, 8, None, None) == NULL
+    assert lib.mla_calib_hbm_gather(P, 1000, 8, P, None) == SHAPE      # not whole 16-byte words
+    assert lib.mla_calib_hbm_gather(P, 1024, 3, P, None) == SHAPE      # 1, 2, 4 or 8 inputs
+    assert lib.mla_calib_hbm_gather(ctypes.c_void_p(16 * 1024 + 4), 1024, 8, P, None) == SHAPE
     assert lib.mla_calib_mfma_bf16(-1, P, None) == SHAPE
     assert lib.mla_calib_mfma_bf16(10, None, None) == NULL
     # 512 workgroups x 4 waves x iters x 8 chains x 16384 flop per MFMA
