@@ -576,24 +576,24 @@ __device__ __forceinline__ UnitInfo unit_info(const DecodeParams& a, int u, cons
   return ui;
 }
 
-__device__ __forceinline__ int block_excl_scan(int v, int* wsum) {
-  // Exclusive prefix sum over the 1024 threads of the workgroup: a scan in
-  // every wave, then wave 0 scans the 16 wave totals.
+// Exclusive prefix sum of 64-bit values over the 1024 threads of the
+// workgroup: a scan in every wave, then wave 0 scans the 16 wave totals.
+__device__ __forceinline__ unsigned long long block_excl_scan64(unsigned long long v, unsigned long long* wsum) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int x = v;
+  unsigned long long x = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
+    const unsigned long long y = __shfl_up(x, off, 64);
     if (lane >= off) x += y;
   }
   if (lane == 63) wsum[wv] = x;
   __syncthreads();
   if (wv == 0) {
-    const int tot = lane < kOrdThreads / 64 ? wsum[lane] : 0;
-    int c = tot;
+    const unsigned long long tot = lane < kOrdThreads / 64 ? wsum[lane] : 0ull;
+    unsigned long long c = tot;
 #pragma unroll
     for (int off = 1; off < kOrdThreads / 64; off <<= 1) {
-      const int y = __shfl_up(c, off, 64);
+      const unsigned long long y = __shfl_up(c, off, 64);
       if (lane >= off) c += y;
     }
     if (lane < kOrdThreads / 64) wsum[kOrdThreads / 64 + lane] = c - tot;
@@ -603,11 +603,14 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum) {
 }
 
 __global__ __launch_bounds__(kOrdThreads) void h128_order_kernel(const DecodeParams a) {
-  __shared__ int start[kOrdBuckets];
+  // Per bucket (stage count): units in the high 32 bits, their items in the
+  // low 32 bits, so that one 64-bit atomic gives a unit both its rank among
+  // the sorted units and its first item.
+  __shared__ unsigned long long bucket[kOrdBuckets];
   __shared__ int ord[kOrdMaxUnits];      // sorted units
   __shared__ int first_item[kOrdMaxUnits + 1];
   __shared__ int rq0[kOrdMaxRequests], rq[kOrdMaxRequests], rs[kOrdMaxRequests];   // per request
-  __shared__ int wsum[2 * (kOrdThreads / 64)];   // wave totals, then their exclusive scan
+  __shared__ unsigned long long wsum[2 * (kOrdThreads / 64)];   // wave totals, then their exclusive scan
   const int tid = threadIdx.x;
   const int U = a.B * a.max_splits;
   const int hblocks = a.H / kXHeads;
@@ -619,38 +622,30 @@ __global__ __launch_bounds__(kOrdThreads) void h128_order_kernel(const DecodePar
     rq[b] = a.qsl[b + 1] - q0;
     rs[b] = a.seq_lens[b];
   }
-  start[tid] = 0;
-  __syncthreads();
-  for (int u = tid; u < U; u += kOrdThreads)
-    atomicAdd(&start[min(unit_info(a, u, rq0, rq, rs).stages, kOrdBuckets - 1)], 1);
-  __syncthreads();
-  // Longest first: bucket k starts after every unit of the buckets above it.
-  const int kb = kOrdBuckets - 1 - tid;
-  const int cnt = start[kb];
-  const int before = block_excl_scan(cnt, wsum);
-  start[kb] = before;
+  bucket[tid] = 0ull;
   __syncthreads();
   for (int u = tid; u < U; u += kOrdThreads) {
-    const int k = min(unit_info(a, u, rq0, rq, rs).stages, kOrdBuckets - 1);
-    ord[atomicAdd(&start[k], 1)] = u;
+    const UnitInfo ui = unit_info(a, u, rq0, rq, rs);
+    atomicAdd(&bucket[min(ui.stages, kOrdBuckets - 1)], (1ull << 32) | (unsigned long long)(ui.rows * hblocks));
   }
   __syncthreads();
-  // Item offsets of the sorted units: thread tid sums positions tid*per .. +per.
-  const int per = (U + kOrdThreads - 1) / kOrdThreads;
-  int local = 0;
-  for (int i = 0; i < per; ++i) {
-    const int pos = tid * per + i;
-    if (pos < U) local += unit_info(a, ord[pos], rq0, rq, rs).rows * hblocks;
+  // Longest first: bucket k starts after every unit (and item) of the buckets
+  // above it.  Units stay below 2^13 and items below 2^31, so the two halves
+  // of the sums never carry into each other.
+  const int kb = kOrdBuckets - 1 - tid;
+  const unsigned long long cnt = bucket[kb];
+  const unsigned long long before = block_excl_scan64(cnt, wsum);
+  bucket[kb] = before;
+  if (kb == 0) first_item[U] = (int)((before + cnt) & 0xffffffffull);   // the item count
+  __syncthreads();
+  for (int u = tid; u < U; u += kOrdThreads) {
+    const UnitInfo ui = unit_info(a, u, rq0, rq, rs);
+    const unsigned long long v =
+        atomicAdd(&bucket[min(ui.stages, kOrdBuckets - 1)], (1ull << 32) | (unsigned long long)(ui.rows * hblocks));
+    const int rank = (int)(v >> 32);
+    ord[rank] = u;
+    first_item[rank] = (int)(v & 0xffffffffull);
   }
-  int run = block_excl_scan(local, wsum);
-  for (int i = 0; i < per; ++i) {
-    const int pos = tid * per + i;
-    if (pos < U) {
-      first_item[pos] = run;
-      run += unit_info(a, ord[pos], rq0, rq, rs).rows * hblocks;
-    }
-  }
-  if (tid == kOrdThreads - 1) first_item[U] = run;   // the last thread's range ends the sequence
   __syncthreads();
   const int n_items = first_item[U];
   for (int p = tid; p < n_map; p += kOrdThreads) {
