@@ -636,6 +636,18 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
     // S^T[key][head] over 576 dims (A = keys: lane key lr, dims 32s + 8g), two
     // accumulation chains.
     f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = f32x4{0.f, 0.f, 0.f, 0.f};
+    // FP8: every LDS read of the stage is issued up front (36 + 32 VGPRs), so
+    // that one wave per SIMD waits for LDS once per stage, not once per batch:
+    // the 18 score operands, then the 16 transposed V reads, which the softmax
+    // does not need.
+    u32x2 c8s[kFP8 ? 18 : 1];
+    s16x4 vts[kFP8 ? 16 : 1];
+    if constexpr (kFP8) {
+#pragma unroll
+      for (int s = 0; s < 18; ++s) c8s[s] = *(const u32x2*)(sb + ((s & 1) ? fk1 : fk0) + 32 * s);
+#pragma unroll
+      for (int pt = 0; pt < 16; ++pt) vts[pt] = lds_read_tr16_at(sb + ((pt & 1) ? fv1 : fv0) + 32 * pt);
+    }
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       bf16x8 kk[9];
@@ -643,7 +655,7 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
       for (int u = 0; u < 9; ++u) {
         const int s = 9 * h2 + u;
         if constexpr (kFP8) {
-          const u32x2 c8 = *(const u32x2*)(sb + ((s & 1) ? fk1 : fk0) + 32 * s);
+          const u32x2 c8 = c8s[s];
           kk[u] = __builtin_bit_cast(bf16x8, u32x4{fp8x2_to_bf16x2<false>(c8[0]), fp8x2_to_bf16x2<true>(c8[0]),
                                                    fp8x2_to_bf16x2<false>(c8[1]), fp8x2_to_bf16x2<true>(c8[1])});
         } else {
@@ -696,16 +708,10 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
       // the even and the odd dims, which convert to the two operands.
 #pragma unroll
       for (int p8 = 0; p8 < 4; ++p8) {
-        s16x4 vt[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int pt = 4 * p8 + u;
-          vt[u] = lds_read_tr16_at(sb + ((pt & 1) ? fv1 : fv0) + 32 * pt);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int pt = 4 * p8 + u;
-          const u32x2 wv = __builtin_bit_cast(u32x2, vt[u]);
+          const u32x2 wv = __builtin_bit_cast(u32x2, vts[pt]);
           const uint32_t ev = __builtin_amdgcn_perm(wv[1], wv[0], 0x06040200u);   // keys 0..3, dim 2p
           const uint32_t od = __builtin_amdgcn_perm(wv[1], wv[0], 0x07050301u);   // keys 0..3, dim 2p + 1
           const bf16x8 va0 = __builtin_bit_cast(bf16x8, u32x4{fp8x2_to_bf16x2<false>(ev), fp8x2_to_bf16x2<true>(ev), 0u, 0u});
