@@ -85,14 +85,40 @@ H128_SOURCES = ["mla_api.hip", "mla_common.h", "mla_decode_h128.hip", "mla_devic
 MERGE_SOURCES = ["mla_api.hip", "mla_common.h", "mla_merge.hip", "mla_device.h", "mla_kernels.h"]
 
 
+def strip_comments(src: str) -> str:
+    """C/C++ source without its comments, whitespace runs collapsed: what the
+    compiler sees, so that an edit of comments alone keeps a measurement valid."""
+    out = []
+    i, n = 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":                      # string or character literal, kept whole
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash(files=None) -> str:
     """Hash of the given kernel sources (file names under the package's csrc/;
-    all of them when None)."""
+    all of them when None), comments and whitespace left out."""
     csrc = os.path.join(ROOT, "mla_decode_context_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(files if files is not None else os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(strip_comments(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -22,8 +22,9 @@
 // wave from seq_lens alone; rows cut at share boundaries become pieces with
 // fp32 partials, merged by split_combine_kernel in a second launch.  With a
 // fixed split count, each split of a row is one workgroup and the last one to
-// finish merges the row (ticket).  An FP8 E4M3 cache is expanded to bf16 per
-// stage in LDS (see h16_piece).
+// finish merges the row (ticket).  An FP8 E4M3 cache stays FP8 in the LDS ring;
+// its MFMA operands are converted to bf16 in registers after their LDS reads,
+// all of a stage's reads issued at its start (see h16_piece).
 //
 // decode_kernel (other head counts; 32 heads per workgroup).  Four waves split
 // the 576-wide contraction and the 512-wide output: wave w owns latent dims
