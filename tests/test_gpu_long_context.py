@@ -1,6 +1,7 @@
-"""GPU parity at the long end of the context range: a request of 131 074
-tokens (past 2^16 and 2^17 keys per row, where 16- or 17-bit index and offset
-arithmetic would wrap), beside short ones.
+"""GPU parity at the size extremes.
+
+A request of 131 074 tokens (past 2^16 and 2^17 keys per row, where 16- or
+17-bit index and offset arithmetic would wrap), beside short ones:
 
 * 128 heads, two shards: about 65 500 keys per row and shard, so the dispatch
   splits the long rows into fixed-size pieces merged by the combine kernel.
@@ -9,7 +10,9 @@ arithmetic would wrap), beside short ones.
   combine's loop over pieces runs more than once), bf16 and FP8 caches.
 
 Every row against the oracle's partial, and the merged rows against the
-oracle's unsharded attention.
+oracle's unsharded attention.  Many rows per call: a 4096-row prefill chunk
+at 128 heads (8192 work items per shard for the dispatch order; sampled rows)
+and 2048 single-row requests at 16 heads (every row).
 """
 from __future__ import annotations
 
@@ -66,3 +69,45 @@ def test_long_context_rows(name, S, Q, H, W, P, fp8):
         full_o, full_l = _oracle(wl, toks, kv, unsharded=True)
         st = check_rows(dw.out, dw.out_lse, full_o, full_l, f"{name} merged")
         log(f"[{name}] merged vs unsharded: {st}")
+
+
+def test_many_rows_prefill_chunk_h128():
+    # A 4096-row prefill chunk (8192 work items per shard for the dispatch
+    # order) beside a single decode row; sampled rows of both.
+    name = "h128_chunk4096"
+    wl = WL.make_custom(name, [8192, 40], [4096, 1], H=128, W=2, P=64, seed=98)
+    dw = DeviceWorkload(wl)
+    log(f"[{name}] T={wl.T}; running")
+    dw.outs.fill_(float("nan"))
+    dw.step()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    toks = sorted({0, 1, 2, 2047, 2048, 4094, 4095, 4096} | set(int(x) for x in rng.integers(0, wl.T, 16)))
+    kv = {}
+    ref_o, ref_l = _oracle(wl, toks, kv)
+    idx = torch.tensor(toks, device="cuda")
+    for r in range(wl.W):
+        st = check_rows(dw.outs[r][idx], dw.lses[r][idx], ref_o[r], ref_l[r], f"{name} r={r}")
+        log(f"[{name}] rank {r}: {st}")
+    full_o, full_l = _oracle(wl, toks, kv, unsharded=True)
+    check_rows(dw.out[idx], dw.out_lse[idx], full_o, full_l, f"{name} merged")
+    assert np.array_equal(dw.valid.cpu().numpy(), np.stack(
+        [O.row_counts(wl.seq_lens, wl.query_start_loc, wl.W, r, wl.I) for r in range(wl.W)]))
+
+
+def test_many_requests_h16():
+    # 2048 short requests: the balanced schedule's per-wave scan runs over 32
+    # chunks of 64 requests; every row checked.
+    name = "h16_b2048"
+    rng = np.random.default_rng(6)
+    S = [int(x) for x in rng.integers(1, 600, 2048)]
+    wl = WL.make_custom(name, S, [1] * 2048, H=16, W=1, P=16, seed=99)
+    dw = DeviceWorkload(wl)
+    log(f"[{name}] T={wl.T}; running")
+    dw.outs.fill_(float("nan"))
+    dw.step()
+    torch.cuda.synchronize()
+    toks = list(range(wl.T))
+    ref_o, ref_l = _oracle(wl, toks, {})
+    st = check_rows(dw.outs[0], dw.lses[0], ref_o[0], ref_l[0], f"{name}")
+    log(f"[{name}] every row: {st}")
