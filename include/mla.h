@@ -153,7 +153,7 @@ const char* mla_status_string(mla_status status);
  * `workspace` of at least mla_decode_workspace_size(...) bytes (any
  * alignment); with workspace == NULL the call runs unsplit.  The workspace
  * holds the split partials and the split tickets of the in-kernel combine,
- * and, for H = 128, the order in which the call dispatches its work
+ * and, for H = 64 or 128, the order in which the call dispatches its work
  * (longest rows first, computed on the device by the call itself; without a
  * workspace the rows run in token order, with the same results).  It must be
  * zero-filled before its first use, every call leaves it ready for the next
@@ -249,7 +249,7 @@ mla_status mla_check_decode_metadata(const int32_t* seq_lens, const int32_t* que
 
 /*
  * Bytes of workspace mla_decode_partial needs for the same host arguments
- * (0 when the plan neither splits nor, for H = 128, orders its work).  Pure
+ * (0 when the plan neither splits nor, for H = 64 or 128, orders its work).  Pure
  * host arithmetic, no device access.
  * Returns (size_t)-1 for invalid arguments.
  */

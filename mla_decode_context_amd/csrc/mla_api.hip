@@ -70,8 +70,9 @@ constexpr int kMaxGridY = 65535;
 // Balanced schedule of the 16-head kernel: one workgroup per CU of the
 // 256-CU part (the kernel's LDS allows one per CU).
 constexpr int kWorkers = 256;
-// 128-head kernel: one workgroup per CU; automatic splits aim for this many
-// workgroups and never cut a row below kH128MinChunk keys.
+// 128-head kernel (64 or 128 heads, one workgroup per 64-head block): one
+// workgroup per CU; automatic splits aim for 2 * kH128Groups workgroups (rows x
+// head blocks x splits) and never cut a row below kH128MinChunk keys.
 constexpr int kH128Groups = 256;
 constexpr int kH128MinChunk = 512;
 constexpr int kH128Stage = 32;
@@ -85,7 +86,7 @@ struct Plan {
   int chunk;        // keys per split (fixed-split grid)
   int max_splits;   // grid extent along splits (fixed-split grid)
   int workers;      // > 0: balanced schedule over this many workgroups
-  bool ordered;     // 128 heads: longest-first dispatch order in the workspace
+  bool ordered;     // 64 or 128 heads: longest-first dispatch order in the workspace
 };
 
 // The 128-head kernel's dispatch order sorts (split, request) units in one
@@ -110,22 +111,22 @@ Plan make_plan(int B, int T, int H, int max_seq_len, int W, int I, int num_split
   p.mtiles = ht >= 2 ? 2 : 1;
   p.hblocks = (int)ceil_div(ht, p.mtiles);
   p.workers = 0;
-  p.h128 = H == 128;
-  if (p.h128) p.hblocks = 2;      // 64-head blocks of the 128-head kernel
+  p.h128 = H % 64 == 0;           // 64 or 128 heads: the 128-head kernel, one workgroup per 64-head block
+  if (p.h128) p.hblocks = H / 64;
   // A row's visible local keys never exceed what rank 0 (the first run of every
   // round) holds of max_seq_len tokens: ceil(max_seq_len / W) when I = 1.
   const int64_t lmax = host_shard_count(max_seq_len, W, 0, I);
   const int64_t lr = round_up(lmax > 0 ? lmax : 1, kStep);
   int64_t chunk = lr;
   if (p.h128) {
-    // A split's partial is 256 KiB (128 heads x 512 fp32): split only when
-    // there are fewer tokens than CUs, or when asked to.  Splits are multiples
-    // of the kernel's 32-key stage.
+    // A split's partial is 128 KiB per 64-head block (64 heads x 512 fp32):
+    // split only when there are too few rows to fill the CUs, or when asked
+    // to.  Splits are multiples of the kernel's 32-key stage.
     if (split_ok && lmax > 0 && num_splits != 1) {
       if (num_splits > 1) {
         chunk = round_up(ceil_div(lmax, num_splits), kH128Stage);
       } else {
-        const int64_t want = ceil_div(kH128Groups, T > 0 ? T : 1);
+        const int64_t want = ceil_div(2 * kH128Groups, (T > 0 ? T : 1) * (int64_t)p.hblocks);
         if (want > 1) chunk = round_up(ceil_div(lmax, want), kH128Stage);
         if (chunk < kH128MinChunk) chunk = kH128MinChunk;
       }
@@ -154,8 +155,8 @@ Plan make_plan(int B, int T, int H, int max_seq_len, int W, int I, int num_split
 }
 
 // Workspace layout (offsets from the 256-byte aligned base):
-//   int32 item_map[T * hblocks * max_splits]  128 heads only: dispatch order
-//   int2  item_info[T * hblocks * max_splits] 128 heads only: {request, keys} per position
+//   int32 item_map[T * hblocks * max_splits]  64 or 128 heads only: dispatch order
+//   int2  item_info[T * hblocks * max_splits] 64 or 128 heads only: {request, keys} per position
 //   int32 counters[T * hblocks]          split tickets, zero between calls
 //   int4  row_desc[T]                    balanced schedule only: pieces per row
 //   fp32  lse[slots][H]                  split LSEs

@@ -2,9 +2,10 @@
 //
 // What is computed is the same as in mla_decode.hip ("flashattn_mla" API page,
 // _forward_decode; PR #24453 review thread for the per-row, per-rank
-// seqlen_k).  This file holds the kernel for H = 128, where every cache row is
-// used by 128 heads of every query row and the contraction dominates (about
-// 240 flop per cache byte per query row).
+// seqlen_k).  This file holds the kernel for H = 128 (and H = 64, one head
+// block per row), where every cache row is used by 64 or 128 heads of every
+// query row and the contraction dominates (about 240 flop per cache byte per
+// query row at 128 heads).
 //
 // Work decomposition.  A workgroup of 8 waves owns one query token, a block of
 // 64 heads and one split of the row's visible keys, in 32-key stages.  The

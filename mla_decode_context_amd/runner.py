@@ -65,7 +65,7 @@ class DeviceWorkload:
     def decode_kernel_name(self) -> str:
         """Kernels one mla_decode_partial call launches for this shape (with the
         automatic split plan), joined by "+"."""
-        if self.H == 128:
+        if self.H % 64 == 0:
             page32 = "true" if self.wl.P % 32 == 0 else "false"
             runs = "true" if self.I != 1 else "false"
             name = f"decode_kernel_h128<{page32}, {runs}>"
@@ -74,7 +74,8 @@ class DeviceWorkload:
             # the workspace holds the dispatch order (one int32 item and one int2
             # {request, keys} per token and 64-head block, each 256-byte aligned)
             # and, when rows are split, the partials
-            order_only = -(-self.T * 2 * 4 // 256) * 256 + -(-self.T * 2 * 8 // 256) * 256 + 256
+            hb = self.H // 64
+            order_only = -(-self.T * hb * 4 // 256) * 256 + -(-self.T * hb * 8 // 256) * 256 + 256
             name = "h128_order_kernel+" + name
             return name + "+combine_fixed_kernel" if self.workspace.numel() > order_only else name
         page16 = "true" if self.wl.P % 16 == 0 else "false"

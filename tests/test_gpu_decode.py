@@ -176,6 +176,10 @@ EDGE = [
     ("h16_long_tail", [1100, 31, 33], [1, 1, 1], 16, 1, 64),
     ("h16_w16_sparse", [40, 3, 100, 17], [2, 1, 3, 4], 16, 16, 16),
     ("h128_w16_sparse", [70, 5, 33], [3, 2, 1], 128, 16, 16),
+    # 64 heads run on the 128-head kernel with one 64-head block per row
+    ("h64_w1_p64", [300, 65], [2, 1], 64, 1, 64),
+    ("h64_w8_ragged", [2, 3, 5, 7, 200], [2, 3, 1, 2, 4], 64, 8, 64),
+    ("h64_w2_p48", [500, 90, 33], [1, 3, 2], 64, 2, 48),
 ]
 
 
@@ -206,6 +210,7 @@ RUN_EDGE = [
     ("runs_h128_w2_i3_p48", [200, 33], [3, 2], 128, 2, 48, 3),
     ("runs_h128_w3_long_run", [2100, 40], [4, 2], 128, 3, 64, 512),
     ("runs_h16_w16_i4", [300, 9, 65], [3, 1, 2], 16, 16, 16, 4),
+    ("runs_h64_w4_page", [700, 64, 129, 5], [2, 2, 1, 3], 64, 4, 64, 64),
 ]
 
 

@@ -46,6 +46,7 @@ CASES = [
     ("h128_ordered", [700, 90, 2, 1500], [2, 1, 2, 4], 128, 2, 64, 1, 0),
     ("h128_split", [5000, 900, 3], [1, 2, 3], 128, 2, 64, 1, 4),
     ("h128_pages", [700, 64, 129, 5], [2, 2, 1, 3], 128, 4, 64, 64, 0),
+    ("h64_ordered", [700, 90, 2, 1500], [2, 1, 2, 4], 64, 2, 64, 1, 0),
     ("h8_w8_empty_rows", [2, 3, 5, 7, 60], [2, 3, 1, 2, 4], 8, 8, 16, 1, 0),
 ]
 

@@ -46,6 +46,7 @@ def _oracle(wl, toks, kv, unsharded=False):
 
 @pytest.mark.parametrize("name,S,Q,H,W,P,fp8", [
     ("h128_w2_131k", [LONG, 300], [2, 1], 128, 2, 64, False),
+    ("h64_w2_131k", [LONG, 300], [2, 1], 64, 2, 64, False),
     ("h16_w1_131k", [LONG, 40, 5000], [1, 1, 1], 16, 1, 16, False),
     ("h16_w1_131k_fp8", [LONG, 40, 5000], [1, 1, 1], 16, 1, 16, True),
 ])

@@ -29,6 +29,8 @@ CASES = [
     ("h128_split", [5000, 900, 3], [1, 2, 3], 128, 2, 64, 1, 4, True),
     ("h16_runs", [700, 64, 129, 5], [2, 2, 1, 3], 16, 4, 16, 16, 0, True),
     ("h128_runs", [700, 64, 129, 5], [2, 2, 1, 3], 128, 4, 64, 64, 0, True),
+    ("h64_ordered", [700, 90, 2, 1500, 3], [2, 1, 2, 4, 3], 64, 8, 64, 1, 0, True),
+    ("h64_split", [5000, 900, 3], [1, 2, 3], 64, 2, 64, 1, 4, True),
 ]
 
 
