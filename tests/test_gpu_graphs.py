@@ -50,6 +50,7 @@ def _replay_matches(run, outputs):
     ("f32_h16_balanced", 16, 4, 16, False, True, 0),
     ("f32_h128_ordered", 128, 2, 64, False, True, 0),
     ("f32_h128_split", 128, 2, 64, False, True, 4),
+    ("h64_ordered", 64, 2, 64, False, False, 0),
 ])
 def test_graph_replay_step(name, H, W, P, fp8, f32, splits):
     log(f"graph {name}")

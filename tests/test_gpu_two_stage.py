@@ -54,6 +54,8 @@ CASES = [
     ("h128_w8_short", [2, 3, 5, 7, 200], [2, 3, 1, 2, 4], 128, 8, 64, 1, 0),
     ("h128_w4_pages", [700, 64, 129, 5], [2, 2, 1, 3], 128, 4, 64, 64, 0),
     ("h128_split", [5000, 900, 3], [1, 2, 3], 128, 2, 64, 1, 4),
+    ("h64_w2", [700, 90, 2, 1500], [2, 1, 2, 4], 64, 2, 64, 1, 0),
+    ("h64_w4_pages_split", [3000, 64, 129, 5], [2, 2, 1, 3], 64, 4, 64, 64, 3),
     ("h8_q_equals_s", [3, 5, 40, 1], [3, 5, 2, 1], 8, 2, 16, 1, 0),
 ]
 

@@ -39,6 +39,8 @@ CASES = [
     ("h128_ordered", ([1500, 700, 90, 2, 2200], [2, 2, 1, 2, 4]), ([300, 65], [2, 1]), 128, 2, 64, 0,
      torch.bfloat16),
     ("h128_split", ([5000, 900], [1, 2]), ([1200, 3], [1, 3]), 128, 2, 64, 4, torch.bfloat16),
+    ("h64_ordered", ([1500, 700, 90, 2, 2200], [2, 2, 1, 2, 4]), ([300, 65], [2, 1]), 64, 2, 64, 0,
+     torch.bfloat16),
     ("h16_fp32_partials", ([3000, 700, 5000], [1, 2, 1]), ([40, 70], [2, 1]), 16, 2, 16, 0, torch.float32),
 ]
 
