@@ -218,8 +218,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams a) {
       // one 64-bit add per load give every address.
       const int pg0 = j0 / a.P;
       const int pg1 = (j0 + 16) / a.P;
-      const int blk0 = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pg0];
-      const int blk1 = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pg1];
+      const int blk0 = load_uniform_i32(bt_row + pg0);
+      const int blk1 = load_uniform_i32(bt_row + pg1);
       const uint8_t* base0 = kv_bytes + ((int64_t)blk0 * a.kv_bs + (int64_t)(j0 - pg0 * a.P) * kRow) * 2;
       const uint8_t* base1 = kv_bytes + ((int64_t)blk1 * a.kv_bs + (int64_t)(j0 - pg1 * a.P) * kRow) * 2;
 #pragma unroll
@@ -241,8 +241,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams a) {
       const int j = min(j0 + row, j_end - 1);
       const int pa = __builtin_amdgcn_readfirstlane(min(j0 + ra, j_end - 1) / a.P);
       const int pb2 = __builtin_amdgcn_readfirstlane(min(j0 + ra + 1, j_end - 1) / a.P);
-      const int ba = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pa];
-      const int bb = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pb2];
+      const int ba = load_uniform_i32(bt_row + pa);
+      const int bb = load_uniform_i32(bt_row + pb2);
       const int pg = j / a.P;              // pa or pb2
       const int64_t rbase = (int64_t)(pg == pa ? ba : bb) * a.kv_bs + (int64_t)(j - pg * a.P) * kRow;
       dma_src[i] = (const uint16_t*)(kv_bytes + rbase * 2 + (lane_off[i] - row * kRowBytes));
@@ -544,8 +544,8 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
     const uint32_t ldst = ring_lds + slot * kSlotB;
     if (kPage16 && j0 + kWStage <= j_end) {
       // page_size % 16 == 0: the stage's 16 rows are consecutive slots of one page.
-      const int pg = a.page_shift >= 0 ? j0 >> a.page_shift : j0 / a.P;
-      const int blk = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pg];
+      const int pg = __builtin_amdgcn_readfirstlane(a.page_shift >= 0 ? j0 >> a.page_shift : j0 / a.P);
+      const int blk = load_uniform_i32(bt_row + pg);
       const uint64_t sbase =
           make_sbase(kv_bytes + ((int64_t)blk * a.kv_bs + (int64_t)(j0 - pg * a.P) * kRow) * kElemB);
 #pragma unroll
@@ -563,7 +563,7 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
 #pragma unroll
         for (int x = 0; x < 3; ++x) {
           pgx[x] = __builtin_amdgcn_readfirstlane(min(j0 + ra + x, j_end - 1) / a.P);
-          bx[x] = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pgx[x]];
+          bx[x] = load_uniform_i32(bt_row + pgx[x]);
         }
         const int pg = j / a.P;                    // one of pgx[0..2]
         const int blk = pg == pgx[0] ? bx[0] : (pg == pgx[1] ? bx[1] : bx[2]);
@@ -578,8 +578,8 @@ __device__ __forceinline__ void h16_piece(const DecodeParams& a, uint8_t* lds_bl
         const int j = min(j0 + row, j_end - 1);
         const int pa = __builtin_amdgcn_readfirstlane(min(j0 + ra, j_end - 1) / a.P);
         const int pb2 = __builtin_amdgcn_readfirstlane(min(j0 + ra + 1, j_end - 1) / a.P);
-        const int ba = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pa];
-        const int bb = ((const __attribute__((address_space(4))) int32_t*)bt_row)[pb2];
+        const int ba = load_uniform_i32(bt_row + pa);
+        const int bb = load_uniform_i32(bt_row + pb2);
         const int pg = j / a.P;                    // pa or pb2
         const int64_t rbase = (int64_t)(pg == pa ? ba : bb) * a.kv_bs + (int64_t)(j - pg * a.P) * kRow;
         dma_16B_to_lds_stream(kv_bytes + rbase * 2 + (doff[i2] - row * kRowBytes), ring + slot * kWStageBytes + 1024 * i2);

@@ -132,6 +132,17 @@ __device__ __forceinline__ uint64_t make_sbase(const void* base) {
   return sbase;
 }
 
+// Block-table entry p[0], the same for every lane, read with a scalar load:
+// both halves of the address go through readfirstlane, so the compiler sees a
+// wave-uniform address even when it keeps the row pointer in VGPRs.  (A vector
+// load would be waited for with vmcnt, i.e. behind every stage load in flight.)
+__device__ __forceinline__ int load_uniform_i32(const int32_t* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return *(const __attribute__((address_space(4))) int32_t*)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+
 template <bool kNT>
 __device__ __forceinline__ void dma_16B_to_lds_sbase(uint32_t lds_off, uint32_t voff, uint64_t sbase) {
   if (kNT)
