@@ -197,8 +197,6 @@ def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True
     if spare is not None:
         # The same steps on one cache copy (rows may survive in the last-level
         # cache between calls): reported beside the value, never as it.
-        del spare
-        spare = None
         a2, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         step()
         a2.record()
@@ -220,11 +218,17 @@ def time_workload(name, steps, warmup, torch, wl=None, headline=False, cold=True
         torch.cuda.synchronize()
         return a.elapsed_time(b) / steps
 
-    dec_avg = np.array([loop_ms(lambda r=r: dw.partial(r)) for r in range(wl.W)])   # per shard, ms
+    # With a spare cache copy the calls alternate between the copies here too.
+    def partial_alt(r):
+        dw.partial(r)
+        swap()
+
+    dec_avg = np.array([loop_ms(lambda r=r: partial_alt(r)) for r in range(wl.W)])   # per shard, ms
     # Every shard's decode back to back, as a step issues them (consecutive
     # calls read different shards' caches, so a shard whose cache fits in the
     # last-level cache gains nothing from the previous call): ms per shard.
-    dec_step = loop_ms(lambda: [dw.partial(r) for r in range(wl.W)]) / wl.W
+    dec_step = loop_ms(lambda: [dw.partial(r) for r in range(wl.W)] + [swap()]) / wl.W
+    spare = None                          # either copy holds the same rows
     mg_ms = mg_step_ms = None
     if merging:
         dw.valid_counts()
@@ -554,7 +558,7 @@ def main():
         print(f"[bench] calibration: {json.dumps(calib)}", file=sys.stderr, flush=True)
     print(f"[bench] {args.workload}: generating inputs", file=sys.stderr, flush=True)
     head, wl = time_workload(args.workload, args.steps, args.warmup, torch, headline=True,
-                             cold=not args.no_cold, alternate=args.workload == "plain")
+                             cold=not args.no_cold, alternate=args.workload.startswith("plain"))
     print(f"[bench] {args.workload}: {head['ms_per_step']:.4f} ms/step, {head['kv_GBps']:.1f} GB/s",
           file=sys.stderr, flush=True)
     configs = {}
