@@ -844,7 +844,8 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // pipeline fill, the four-wave merge and the waves' uneven finish; measured, a
 // second piece costs a worker about 3.5 stage-times of each wave, and timing
 // 10, 14, 18 and 24 units per row put the optimum at 18) followed by one unit
-// per 16-key stage.
+// per 16-key stage.  An FP8 stage takes less time than a bf16 one, so the same
+// fixed cost is more of them: 24 units per row (timing 18, 24, 30 and 40).
 // Worker g (one workgroup) takes units [g*per, (g+1)*per) with
 // per = ceil(total / workers), so every worker streams the same number of cache
 // rows (to within one stage) whatever the length mix; a row cut by worker
@@ -856,17 +857,19 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // it hands on, so pieces never share a slot.  Every wave computes the schedule
 // itself (same inputs, same result), so no barrier is needed.
 constexpr int kRowUnits = 18;
+constexpr int kRowUnitsFP8 = 24;
 constexpr int kMinUnitsPerWorker = 8;
 
 __device__ __forceinline__ int h16_stages(int L) { return (L + kWStage - 1) / kWStage; }
 
 // Units of request b; also returns its first token q0, rows Q and length S.
-__device__ __forceinline__ int request_units(const DecodeParams& a, int I, int b, int& q0, int& Q, int& S) {
+__device__ __forceinline__ int request_units(const DecodeParams& a, int I, int row_units, int b, int& q0, int& Q,
+                                             int& S) {
   q0 = a.qsl[b];
   Q = a.qsl[b + 1] - q0;
   S = a.seq_lens[b];
   int u = 0;
-  for (int i = 0; i < Q; ++i) u += kRowUnits + h16_stages(row_key_count(S, Q, i, a.W, a.r, I, a.mode));
+  for (int i = 0; i < Q; ++i) u += row_units + h16_stages(row_key_count(S, Q, i, a.W, a.r, I, a.mode));
   return u;
 }
 
@@ -875,6 +878,7 @@ __device__ __forceinline__ int request_units(const DecodeParams& a, int I, int b
 template <bool kPage16, bool kBalanced, bool kRuns, bool kFP8>
 __global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a) {
   const int I = kRuns ? a.I : 1;
+  constexpr int kRU = kFP8 ? kRowUnitsFP8 : kRowUnits;   // units of a row's fixed cost
   // Four wave rings of two 18 KiB slots; reused for the four-wave merge.
   __shared__ __attribute__((aligned(16))) uint8_t lds_block[kWLdsBytes];
 
@@ -901,13 +905,13 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a
     // Every lane holds one request of the chunk [b0c, b0c + 64): its first
     // token, rows, length and units.  Chunk 0 is kept; the total runs over all.
     int lq0 = 0, lQ = 0, lS = 0;
-    const int u_first = lane < a.B ? request_units(a, I, lane, lq0, lQ, lS) : 0;
+    const int u_first = lane < a.B ? request_units(a, I, kRU, lane, lq0, lQ, lS) : 0;
     const int inc_first = wave_incl_scan(u_first);
     int total = __shfl(inc_first, 63, 64);
     for (int b0 = 64; b0 < a.B; b0 += 64) {
       const int bb = b0 + lane;
       int x, y, z;
-      total += __shfl(wave_incl_scan(bb < a.B ? request_units(a, I, bb, x, y, z) : 0), 63, 64);
+      total += __shfl(wave_incl_scan(bb < a.B ? request_units(a, I, kRU, bb, x, y, z) : 0), 63, 64);
     }
     int per = (total + G - 1) / G;
     if (per < kMinUnitsPerWorker) per = kMinUnitsPerWorker;
@@ -920,7 +924,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a
       const int bb = b0 + lane;
       int u = u_first, inc = inc_first;
       if (b0 > 0) {
-        u = bb < a.B ? request_units(a, I, bb, lq0, lQ, lS) : 0;
+        u = bb < a.B ? request_units(a, I, kRU, bb, lq0, lQ, lS) : 0;
         inc = wave_incl_scan(u);
       }
       const bool hit = bb < a.B && carry + inc - u <= x0 && x0 < carry + inc;
@@ -962,7 +966,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a
       const int L = row_key_count(S, Q, i, a.W, a.r, I, a.mode);
       const int n = h16_stages(L);
       const int t = q0 + i;
-      if (pos + kRowUnits + n > x0) {
+      if (pos + kRU + n > x0) {
         if (L == 0) {
           if (pos >= x0) {                           // the row's owner is the worker holding its start
             write_empty_row(a, t);
@@ -972,7 +976,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a
             }
           }
         } else {
-          const int s0 = pos + kRowUnits;           // unit of the row's first stage
+          const int s0 = pos + kRU;           // unit of the row's first stage
           const int lo = max(x0 - s0, 0);
           const int hi = min(x1 - s0, n);
           if (lo < hi) {
@@ -991,7 +995,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel_h16(const DecodeParams a
           }
         }
       }
-      pos += kRowUnits + n;
+      pos += kRU + n;
       ++i;
     }
   }
