@@ -126,3 +126,42 @@ def test_checker_sees_a_short_gap():
     assert _check(good) == 1
     with pytest.raises(AssertionError):
         _check("\ts_mov_b32 m0, s1\n\tv_mov_b32 v0, m0\n")
+
+
+def _vector_load_waits_before_dma(text: str, window: int = 40):
+    """Places where a 32-bit vector load is waited for with vmcnt(0) within
+    `window` instructions before an LDS-DMA load: the shape of a block id read
+    through the vector memory path, whose wait also waits for every stage load
+    in flight.  Block ids are read with scalar loads, so there must be none."""
+    ins = [(mn, ops) for mn, ops, lab in _instructions(text) if not lab]
+    found = []
+    for k, (mn, ops) in enumerate(ins):
+        if not mn.startswith("global_load_lds"):
+            continue
+        seen_wait = False
+        for j in range(k - 1, max(k - window, -1), -1):
+            pmn, pops = ins[j]
+            if pmn.startswith("global_load_lds"):
+                break                      # an earlier load of the same stage
+            if pmn == "s_waitcnt" and "vmcnt(0)" in pops:
+                seen_wait = True
+            elif pmn == "global_load_dword" and seen_wait:
+                found.append(k)
+                break
+    return found
+
+
+@pytest.mark.parametrize("src", ["mla_decode.hip", "mla_decode_h128.hip"])
+def test_stage_issue_reads_block_ids_with_scalar_loads(src):
+    with tempfile.TemporaryDirectory() as d:
+        text = _compile(src, os.path.join(d, "k.s"))
+    assert _vector_load_waits_before_dma(text) == []
+
+
+def test_vector_block_id_check_sees_the_old_shape():
+    bad = ("\tglobal_load_dword v3, v[84:85], off\n\tv_mul_lo_u32 v2, v2, s56\n\ts_waitcnt vmcnt(0)\n"
+           "\tv_readfirstlane_b32 s88, v2\n\ts_mov_b32 m0, s4\n\ts_nop 0\n"
+           "\tglobal_load_lds_dwordx4 v212, s[88:89] nt\n")
+    assert _vector_load_waits_before_dma(bad) == [6]
+    good = bad.replace("global_load_dword v3, v[84:85], off", "s_load_dword s3, s[84:85], 0x0")
+    assert _vector_load_waits_before_dma(good) == []
