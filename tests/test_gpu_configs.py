@@ -8,6 +8,9 @@ sampled rows the oracle computes one by one: the first and last rows, the
 shortened and prefill-chunk requests, every row of the four longest requests
 (the first items of the longest-first dispatch order) and seeded random rows.
 
+A 64-head batch at the MTP DCP4 shape (a 128-head model on two
+tensor-parallel ranks) is checked on every row as well.
+
 For each workload: every rank's partial against the oracle's partial, the
 merged rows against the oracle's unsharded attention (merge(shards) ==
 unsharded), valid counts bit-exact, and for the mixed batch the fused merge +
@@ -72,3 +75,29 @@ def test_full_config_sampled_rows(name):
         assert torch.isfinite(dw.outs[r]).all()
         assert torch.all(lse[empty] == float("-inf")) and torch.all(dw.outs[r][empty] == 0)
         assert torch.isfinite(lse[~empty]).all()
+
+
+def test_h64_at_the_mtp_dcp4_shape():
+    # 64 heads (a 128-head model on two tensor-parallel ranks) at the MTP DCP4
+    # batch shape: 128 requests of two query rows, contexts 1024..4096, four
+    # shards, pages of 64.  The 128-head kernel serves it with one 64-head block
+    # per row and the dispatch order; every row against the oracle.
+    name = "h64_mtp_dcp4_shape"
+    rng = np.random.default_rng(44)
+    S = [int(x) for x in rng.integers(1024, 4097, 128)]
+    wl = WL.make_custom(name, S, [2] * 128, H=64, W=4, P=64, seed=44, threads=16)
+    log(f"[{name}] T={wl.T}; running")
+    dw = DeviceWorkload(wl)
+    dw.outs.fill_(float("nan"))
+    dw.step()
+    torch.cuda.synchronize()
+    toks = list(range(wl.T))
+    kv = {}
+    ref_o, ref_l = oracle_partials(wl, toks, kv)
+    for r in range(wl.W):
+        st = check_rows(dw.outs[r], dw.lses[r], ref_o[r], ref_l[r], f"{name} r={r}")
+        log(f"[{name}] rank {r}: {st}")
+    assert np.array_equal(dw.valid.cpu().numpy(), oracle_valid(wl, toks))
+    full_o, full_l = oracle_unsharded(wl, toks, kv)
+    st = check_rows(dw.out, dw.out_lse, full_o, full_l, f"{name} merged")
+    log(f"[{name}] merged vs unsharded: {st}")
